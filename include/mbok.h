@@ -1,0 +1,208 @@
+/*
+ * mbok.h -- C ABI of the Multi-Boolean-kernel (MBOK) linear layer for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operation is the linear-layer product of a weight matrix stored as K
+ * Boolean kernels with group scales:
+ *
+ *     W_hat = sum_{k=1..K} alpha_k (.) B_k,   B_k in {-1,+1}^{m x n},
+ *     y     = W_hat . x      (decode, one token)
+ *     Y     = X . W_hat^T    (several tokens)
+ *
+ * Sources (page title, then the section on that page):
+ *   [RN]  "Highly Efficient and Effective LLMs with Multi-Boolean
+ *         Architectures", Paper-Notes reading note (zhaoyang97.github.io),
+ *         sections 关键设计 (key design: multi-kernel Boolean parameters,
+ *         closed-form scale fit, group-wise scales), 消融实验 (ablation table:
+ *         group size 128 is the usual choice), 训练策略 (initialisation by SVD or
+ *         greedy search) and 局限与展望 (activations stay full precision).
+ *   [GS]  the same paper's gist.science summaries (Italian, Dutch, Spanish),
+ *         sections "Architetture Multi-Kernel" / "Successive SVID" /
+ *         "Extracción Sucesiva": successive kernels are fitted to the residual
+ *         of the previous ones.
+ *
+ * Conventions shared by every call
+ * ---------------------------------
+ *  - m = output features (rows of W), n = input features (columns of W).
+ *    W is row-major [m, n]; x has n entries; y has m entries; X is row-major
+ *    [T, ldx >= n]; Y is row-major [T, ldy >= m].
+ *  - Scales: one alpha per (kernel k, output row i, group g) where group g is
+ *    the 128 consecutive input columns 128g .. 128g+127 ([RN] group-wise scales,
+ *    group size 128).  n must be a multiple of 128.
+ *  - Sign encoding: bit 1 <-> +1, bit 0 <-> -1.  sign(0) and sign(-0.0) are +1.
+ *  - All data pointers are DEVICE memory owned by the caller.  The library
+ *    allocates nothing, keeps no mutable global state, and every call only
+ *    enqueues work on `stream` (a hipStream_t; NULL = the default stream) and
+ *    returns without synchronising.
+ *  - Every argument check runs on the host before anything is enqueued, so an
+ *    error return means nothing was launched and no output was touched.
+ *    MBOK_ERR_HIP is returned when a launch itself fails (hipGetLastError).
+ *  - Results are deterministic: the same inputs give the same output bits
+ *    (no atomics, fixed reduction order).
+ *
+ * Packed layout MBOK_LAYOUT_L64 (what mbok_pack writes and mbok_gemv /
+ * mbok_gemm read)
+ * -------------------------------------------------------------------------
+ *  m_pad = m rounded up to a multiple of 64, G = n / 128.
+ *  The buffer has two regions:
+ *
+ *  1. sign bits, K * m_pad * n / 8 bytes, starting at byte 0.  It is a
+ *     sequence of 16-byte chunks; chunk c holds the 128 signs of one
+ *     (row i, group g, kernel k) with
+ *         c = ((rb * G + g) * K + k) * 64 + r,   rb = i / 64,  r = i % 64.
+ *     Byte q (0..15) of a chunk holds columns 128g + 8q .. 128g + 8q + 7,
+ *     least significant bit first (bit t <-> column 128g + 8q + t).
+ *     Equivalently: read as four little-endian uint32 words, bit t of word w
+ *     is column 128g + 32w + t.  Rows m .. m_pad-1 are all-zero bits.
+ *
+ *  2. scales, starting at byte K * m_pad * n / 8 (a multiple of 1024):
+ *     K * m_pad * G values of the descriptor's alpha dtype (fp32 or IEEE
+ *     fp16), value index ((rb * G + g) * K + k) * 64 + r, i.e. in the same
+ *     order as the chunks.  Scales of padding rows are 0.
+ *
+ *  So one (row block, group) holds K consecutive 1 KB sign planes of 64 rows,
+ *  and 64 consecutive scales per plane: a wavefront of 64 lanes, one lane per
+ *  row, reads one plane with one 16-byte load per lane (1 KB contiguous).
+ */
+#ifndef MBOK_H
+#define MBOK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MBOK_GROUP 128      /* input columns per scale group */
+#define MBOK_ROW_BLOCK 64   /* rows per packed row block */
+#define MBOK_MAX_K 4        /* kernels per layer accepted by the library */
+#define MBOK_MAX_T 65536    /* tokens per mbok_gemm call */
+
+/* Status codes.  0 is success; errors are negative. */
+enum {
+  MBOK_OK = 0,
+  MBOK_ERR_INVALID_ARG = -1, /* NULL pointer, unknown enum, bad leading dim */
+  MBOK_ERR_SHAPE = -2,       /* m < 1, n < 128, n % 128 != 0, T out of range */
+  MBOK_ERR_DTYPE = -3,       /* dtype not accepted by this call */
+  MBOK_ERR_ALIGN = -4,       /* pointer or leading dimension misaligned */
+  MBOK_ERR_HIP = -5,         /* the HIP runtime rejected a launch */
+  MBOK_ERR_UNSUPPORTED = -6  /* K or group outside what the library runs */
+};
+
+/* Element types. */
+enum { MBOK_F32 = 0, MBOK_F16 = 1, MBOK_BF16 = 2 };
+
+/* Packed layouts. */
+enum { MBOK_LAYOUT_L64 = 1 };
+
+/* Shape of one MBOK layer.  Fill it with mbok_desc_init. */
+typedef struct mbok_desc {
+  int32_t m;           /* output features, >= 1 */
+  int32_t n;           /* input features, a positive multiple of 128 */
+  int32_t K;           /* Boolean kernels, 1 .. MBOK_MAX_K */
+  int32_t group;       /* always MBOK_GROUP */
+  int32_t alpha_dtype; /* MBOK_F32 or MBOK_F16 */
+  int32_t layout;      /* always MBOK_LAYOUT_L64 */
+} mbok_desc;
+
+/*
+ * Fills *d after checking the shape: 1 <= m <= 2^24, 128 <= n <= 2^20 with
+ * n % 128 == 0, 1 <= K <= MBOK_MAX_K, alpha_dtype in {MBOK_F32, MBOK_F16}.
+ * Host only.  Returns MBOK_OK, MBOK_ERR_INVALID_ARG (d NULL),
+ * MBOK_ERR_SHAPE, MBOK_ERR_UNSUPPORTED (K) or MBOK_ERR_DTYPE.
+ */
+int mbok_desc_init(mbok_desc* d, int32_t m, int32_t n, int32_t K,
+                   int32_t alpha_dtype);
+
+/* Bytes of the packed buffer (both regions of MBOK_LAYOUT_L64).  Host only;
+ * returns 0 for a NULL or invalid descriptor. */
+size_t mbok_packed_bytes(const mbok_desc* d);
+
+/* Bytes of the natural-order scale array alpha[K][m][n/128] that
+ * mbok_residual_binarize writes and mbok_pack reads.  Host only; 0 for a NULL
+ * or invalid descriptor. */
+size_t mbok_alpha_bytes(const mbok_desc* d);
+
+/*
+ * Greedy residual binarization: the data-free extraction of the K kernels
+ * from a floating-point weight ([RN] 训练策略: initialisation by greedy
+ * search; [GS] successive kernels fitted to the residual; [RN] 关键设计: for
+ * fixed signs the least-squares scale has a closed form).  Per (row, group),
+ * in float64:
+ *     R_0 = W
+ *     for k = 1..K:
+ *         B_k   = sign(R_{k-1})                  (0 and -0.0 map to +1)
+ *         a     = mean over the group of |R_{k-1}|   (the LS-optimal scale)
+ *         alpha = a rounded to nearest-even in the alpha dtype
+ *         R_k   = R_{k-1} - alpha * B_k          (uses the rounded alpha)
+ *
+ *  W      device, fp32, row-major [m, ldw], ldw >= n (elements).
+ *  signs  device, int8 [K][m][n] row-major, written with +1 / -1.
+ *  alpha  device, [K][m][n/128] of d->alpha_dtype (natural order).
+ *  flag   device int32 or NULL.  If W holds a NaN or an Inf the call stores 1
+ *         there (it never stores 0: the caller clears it beforehand) and the
+ *         outputs for the affected groups are unspecified.
+ * Errors: INVALID_ARG (NULL, ldw < n), SHAPE/DTYPE/UNSUPPORTED from d,
+ * ALIGN (W, signs or alpha not 16-byte aligned, ldw % 4 != 0), HIP.
+ */
+int mbok_residual_binarize(const mbok_desc* d, const float* W, int64_t ldw,
+                           int8_t* signs, void* alpha, int32_t* flag,
+                           void* stream);
+
+/*
+ * Packs Boolean kernels and their scales into MBOK_LAYOUT_L64 (see the top
+ * of this header).  Any +-1 signs are accepted, e.g. those of a finetuned
+ * model; an entry >= 0 packs as bit 1 (+1) and < 0 as bit 0 (-1).
+ *  signs   device int8 [K][m][n].
+ *  alpha   device [K][m][n/128] of d->alpha_dtype.
+ *  packed  device, mbok_packed_bytes(d) bytes; fully overwritten, padding
+ *          included.
+ * Errors: INVALID_ARG, SHAPE/DTYPE/UNSUPPORTED, ALIGN (16 bytes), HIP.
+ */
+int mbok_pack(const mbok_desc* d, const int8_t* signs, const void* alpha,
+              void* packed, void* stream);
+
+/*
+ * Decode product for one token ([RN] 关键设计: Wx splits into K Boolean
+ * matrix-vector products, so each weight multiply becomes an add or a
+ * subtract of an activation; [RN] 局限与展望: activations stay full
+ * precision):
+ *     y[i] = sum_k sum_g alpha_k[i,g] * sum_{j in group g} b_k[i,j] * x[j]
+ * with fp32 accumulation.
+ *  packed   device, MBOK_LAYOUT_L64 buffer of this descriptor.
+ *  x        device, n values of x_dtype (MBOK_BF16 or MBOK_F32).
+ *  y        device fp32 [m]; overwritten (not accumulated).
+ * Errors: INVALID_ARG, SHAPE/UNSUPPORTED, DTYPE (x_dtype), ALIGN (packed and
+ * x 16-byte aligned, y 4-byte aligned), HIP.
+ */
+int mbok_gemv(const mbok_desc* d, const void* packed, const void* x,
+              int32_t x_dtype, float* y, void* stream);
+
+/*
+ * The same product for T tokens:  Y[t, i] = sum_j W_hat[i, j] * X[t, j].
+ * T <= 16 runs the weight-streaming skinny kernel (exact fp32 scaling of
+ * +-1 products).  T > 16 is the prefill GEMM: each tile of W_hat is formed
+ * as sum_k alpha_k * b_k in fp32, rounded to bf16 (nearest-even) in LDS, and
+ * contracted with the bf16 X tile on the matrix cores with fp32 accumulation.
+ *  X        device bf16 [T, ldx], ldx >= n, ldx % 8 == 0.
+ *  Y        device fp32 [T, ldy], ldy >= m; overwritten.
+ *  T        1 .. MBOK_MAX_T.
+ * Errors: INVALID_ARG (NULL, ldx < n, ldy < m), SHAPE (T), DTYPE (x_dtype
+ * other than MBOK_BF16), ALIGN (packed/X 16 bytes, ldx % 8, Y 4 bytes), HIP.
+ */
+int mbok_gemm(const mbok_desc* d, const void* packed, const void* X,
+              int32_t x_dtype, int64_t T, int64_t ldx, float* Y, int64_t ldy,
+              void* stream);
+
+/* Static description of a status code ("unknown status" for others). */
+const char* mbok_status_str(int status);
+
+/* Library version, e.g. "mbok 0.1.0 gfx950". */
+const char* mbok_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MBOK_H */

@@ -1,0 +1,241 @@
+"""CPU oracle for the Multi-Boolean-kernel (MBOK) linear layer.
+
+TEST INFRASTRUCTURE.  Only tests/, __graft_entry__.smoke() and the
+cpu_baseline leg of bench.py may import this module.  The product path
+(boolean_weight_amd and its HIP library) never imports, calls or links it,
+and this module imports nothing from the product path.
+
+Plain and slow on purpose: float64 NumPy, math.fsum and fractions.Fraction,
+with no blocking, fusion or reordering beyond what each definition states.
+
+Sources (page title, then the section on that page):
+  [RN] "Highly Efficient and Effective LLMs with Multi-Boolean Architectures",
+       Paper-Notes reading note (zhaoyang97.github.io):
+         - 关键设计 / multi-kernel Boolean parameters: W ~ sum_k alpha_k B_k with
+           B_k in {-1,+1}^{m x n}; K kernels give 2^K weight levels; Wx splits
+           into K Boolean matrix-vector products.
+         - 关键设计 / efficient scale optimisation: for fixed B_k the scales have
+           a closed-form least-squares solution.
+         - 关键设计 / group-wise strategy: an independent scale per group of
+           columns; 消融实验 table: group size 128 is the usual choice.
+         - 训练策略: kernels are initialised from the pretrained weight by SVD
+           or greedy search.
+  [GS] gist.science summaries of the same paper ("Successive SVID",
+       "Extracción Sucesiva"): each further kernel is fitted to the residual
+       error left by the previous ones.
+
+Readings taken where the pages are silent (each is listed in the design doc):
+  * scale structure: one scale per (kernel k, output row i, group g of 128
+    consecutive input columns), as the group-wise strategy of [RN];
+  * initialisation: greedy residual binarization, i.e. the residual chain of
+    [GS] with the sign of the residual and its LS scale;
+  * sign(0) = sign(-0.0) = +1 (B has no zero entry; either choice has the same
+    squared error);
+  * the scale is the exact float64 group mean of |R| (math.fsum, one
+    rounding) rounded once, nearest-even, to the storage dtype, and the
+    residual update uses that rounded scale, so W = W_hat + R_K exactly;
+  * y is produced in fp32 by the device; the oracle keeps float64.
+
+parity pins: every function here is pinned in tests/test_oracle_pins.py
+against closed forms, constructed examples, brute force (Fraction,
+exhaustive sign search) and library routines (numpy lstsq, integer matmul).
+"""
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+
+import numpy as np
+
+GROUP = 128
+ROW_BLOCK = 64
+
+_ALPHA_NP = {"f32": np.float32, "f16": np.float16}
+
+
+def round_alpha(a: np.ndarray, alpha_dtype: str) -> np.ndarray:
+    """Round float64 values once, nearest-even, to the scale storage dtype.
+
+    NumPy converts float64 directly to float16 / float32 with one
+    round-to-nearest-even step (pinned against an exact Fraction rounding in
+    the tests)."""
+    return np.asarray(a, dtype=np.float64).astype(_ALPHA_NP[alpha_dtype])
+
+
+def residual_binarize(W: np.ndarray, K: int, group: int = GROUP,
+                      alpha_dtype: str = "f16", return_chain: bool = False):
+    """Greedy residual binarization of W (m x n) into K Boolean kernels.
+
+    [RN] 训练策略 (greedy initialisation) with the residual chain of [GS] and
+    the closed-form scale of [RN] 关键设计.  For every row i and group g
+    (columns group*g .. group*g+group-1), k = 1..K:
+        S_k = sign(R_{k-1})         with sign(0) = +1
+        a   = fsum(|R_{k-1}|) / group   (exact sum, one rounding)
+        A_k = round-to-nearest-even(a) in alpha_dtype
+        R_k = R_{k-1} - A_k * S_k   (float64)
+    Returns S int8 [K, m, n], A [K, m, n/group] (alpha dtype) and R_K float64
+    [m, n]; with return_chain also the list [R_0, ..., R_K].
+    """
+    W = np.asarray(W)
+    m, n = W.shape
+    if n % group:
+        raise ValueError("n must be a multiple of the group size")
+    G = n // group
+    R = W.astype(np.float64)
+    chain = [R.copy()]
+    S = np.empty((K, m, n), dtype=np.int8)
+    A = np.empty((K, m, G), dtype=_ALPHA_NP[alpha_dtype])
+    for k in range(K):
+        Sk = np.where(R >= 0.0, 1, -1).astype(np.int8)
+        a = np.empty((m, G), dtype=np.float64)
+        absR = np.abs(R)
+        for i in range(m):
+            row = absR[i]
+            for g in range(G):
+                a[i, g] = math.fsum(row[g * group:(g + 1) * group].tolist()) / group
+        Ak = round_alpha(a, alpha_dtype)
+        alpha_cols = np.repeat(Ak.astype(np.float64), group, axis=1)
+        R = R - alpha_cols * Sk.astype(np.float64)
+        S[k] = Sk
+        A[k] = Ak
+        chain.append(R.copy())
+    if return_chain:
+        return S, A, R, chain
+    return S, A, R
+
+
+def dequantize(S: np.ndarray, A: np.ndarray, group: int = GROUP) -> np.ndarray:
+    """W_hat[i, j] = sum_k A_k[i, j // group] * S_k[i, j] in float64 ([RN]
+    关键设计: W ~ sum_k alpha_k B_k, with group-wise alpha)."""
+    K, m, n = S.shape
+    What = np.zeros((m, n), dtype=np.float64)
+    for k in range(K):
+        alpha_cols = np.repeat(np.asarray(A[k], dtype=np.float64), group, axis=1)
+        What += alpha_cols * S[k].astype(np.float64)
+    return What
+
+
+def product(S: np.ndarray, A: np.ndarray, X: np.ndarray,
+            group: int = GROUP) -> np.ndarray:
+    """Y = X . W_hat^T in float64: Y[t, i] = sum_j W_hat[i, j] X[t, j].
+
+    X is [T, n] (a 1-D x is treated as T = 1 and a 1-D y is returned)."""
+    X = np.asarray(X, dtype=np.float64)
+    one = X.ndim == 1
+    X2 = X[None, :] if one else X
+    Y = X2 @ dequantize(S, A, group).T
+    return Y[0] if one else Y
+
+
+def bound(S: np.ndarray, A: np.ndarray, X: np.ndarray,
+          group: int = GROUP) -> np.ndarray:
+    """E[t, i] = sum_j |W_hat[i, j]| |X[t, j]|: the scale of the accepted error."""
+    X = np.asarray(X, dtype=np.float64)
+    one = X.ndim == 1
+    X2 = X[None, :] if one else X
+    E = np.abs(X2) @ np.abs(dequantize(S, A, group)).T
+    return E[0] if one else E
+
+
+def product_rows(S: np.ndarray, A: np.ndarray, X: np.ndarray, rows,
+                 group: int = GROUP):
+    """Y[:, rows] and E[:, rows] for a subset of output rows only, so that very
+    large layers can be checked on sampled outputs."""
+    rows = np.asarray(rows)
+    return (product(S[:, rows], A[:, rows], X, group),
+            bound(S[:, rows], A[:, rows], X, group))
+
+
+def product_fraction(S: np.ndarray, A: np.ndarray, X: np.ndarray,
+                     group: int = GROUP):
+    """Exact rational Y[t][i] by the triple loop (tiny shapes only)."""
+    K, m, n = S.shape
+    T = X.shape[0]
+    Af = [[[Fraction(float(A[k, i, g])) for g in range(n // group)]
+           for i in range(m)] for k in range(K)]
+    Y = []
+    for t in range(T):
+        row = []
+        for i in range(m):
+            acc = Fraction(0)
+            for j in range(n):
+                w = Fraction(0)
+                for k in range(K):
+                    w += Af[k][i][j // group] * int(S[k, i, j])
+                acc += w * Fraction(float(X[t, j]))
+            row.append(acc)
+        Y.append(row)
+    return Y
+
+
+def max_error_ratio(Y_dev: np.ndarray, Y_ref: np.ndarray, E: np.ndarray) -> float:
+    """max |Y_dev - Y_ref| / E (entries with E == 0 must match exactly)."""
+    Y_dev = np.asarray(Y_dev, dtype=np.float64)
+    diff = np.abs(Y_dev - Y_ref)
+    zero = E == 0
+    if np.any(diff[zero] != 0):
+        return math.inf
+    if not np.any(~zero):
+        return 0.0
+    return float(np.max(diff[~zero] / E[~zero]))
+
+
+# --------------------------------------------------------------------------
+# Packed layout MBOK_LAYOUT_L64, written from its specification in the
+# library header: sign chunks of 16 bytes at chunk index
+# ((rb*G + g)*K + k)*64 + r (rb = i // 64, r = i % 64), byte q holding columns
+# 128g+8q .. 128g+8q+7 LSB first, bit 1 = +1; then the scales in the same
+# (rb, g, k, r) order, in the scale dtype; padding rows zero.
+# --------------------------------------------------------------------------
+
+def packed_nbytes(m: int, n: int, K: int, alpha_dtype: str) -> int:
+    m_pad = -(-m // ROW_BLOCK) * ROW_BLOCK
+    G = n // GROUP
+    return K * m_pad * n // 8 + K * m_pad * G * np.dtype(_ALPHA_NP[alpha_dtype]).itemsize
+
+
+def pack(S: np.ndarray, A: np.ndarray, alpha_dtype: str) -> np.ndarray:
+    """Pack int8 signs [K, m, n] and scales [K, m, G] into the L64 byte buffer."""
+    K, m, n = S.shape
+    G = n // GROUP
+    m_pad = -(-m // ROW_BLOCK) * ROW_BLOCK
+    RB = m_pad // ROW_BLOCK
+    nbits = K * m_pad * n // 8
+    buf = np.zeros(packed_nbytes(m, n, K, alpha_dtype), dtype=np.uint8)
+    # bit value per (k, i, j): 1 for +1 (entries >= 0), 0 for -1; padding rows 0
+    b = np.zeros((K, m_pad, n), dtype=np.uint8)
+    b[:, :m, :] = (S >= 0)
+    # byte q of chunk (i, g, k) holds columns 128g+8q..+7, least significant first
+    by = np.packbits(b.reshape(K, m_pad, G, 16, 8), axis=-1, bitorder="little")
+    by = by.reshape(K, RB, ROW_BLOCK, G, 16)            # [k, rb, r, g, q]
+    buf[:nbits] = by.transpose(1, 3, 0, 2, 4).reshape(-1)  # [rb, g, k, r, q]
+    scale_dt = _ALPHA_NP[alpha_dtype]
+    a = np.zeros((K, m_pad, G), dtype=scale_dt)
+    a[:, :m, :] = A
+    a = a.reshape(K, RB, ROW_BLOCK, G).transpose(1, 3, 0, 2)  # [rb, g, k, r]
+    buf[nbits:] = np.ascontiguousarray(a).reshape(-1).view(np.uint8)
+    return buf
+
+
+def unpack(buf: np.ndarray, m: int, n: int, K: int, alpha_dtype: str):
+    """Read an L64 buffer back into int8 signs [K, m, n] and scales [K, m, G].
+
+    Also returns whether every padding bit and padding scale is zero."""
+    buf = np.asarray(buf, dtype=np.uint8)
+    G = n // GROUP
+    m_pad = -(-m // ROW_BLOCK) * ROW_BLOCK
+    RB = m_pad // ROW_BLOCK
+    nbits = K * m_pad * n // 8
+    if buf.size != packed_nbytes(m, n, K, alpha_dtype):
+        raise ValueError("packed buffer has the wrong size")
+    by = buf[:nbits].reshape(RB, G, K, ROW_BLOCK, 16)    # [rb, g, k, r, q]
+    by = by.transpose(2, 0, 3, 1, 4)                      # [k, rb, r, g, q]
+    bits = np.unpackbits(by, axis=-1, bitorder="little")  # [k, rb, r, g, q*8+t]
+    bits = bits.reshape(K, m_pad, n)
+    S = np.where(bits[:, :m, :] == 1, 1, -1).astype(np.int8)
+    scale_dt = _ALPHA_NP[alpha_dtype]
+    sc = buf[nbits:].view(scale_dt).reshape(RB, G, K, ROW_BLOCK)
+    sc = sc.transpose(2, 0, 3, 1).reshape(K, m_pad, G)   # [k, i, g]
+    A = np.ascontiguousarray(sc[:, :m, :])
+    pad_clean = bool(np.all(bits[:, m:, :] == 0) and np.all(sc[:, m:, :] == 0))
+    return S, A, pad_clean

@@ -1,0 +1,96 @@
+"""Planted mistakes in the oracle must be caught by its pins.
+
+Each case edits the source text of one oracle function (a dropped term, a
+wrong sign, a transposed operand, an off-by-one, a wrong bit order ...),
+executes the edited function into a fresh copy of the oracle module, and runs
+every pin of oracle_pins.py against that copy.  The case passes when at least
+one pin fails.  All of this happens on the CPU; the real oracle is untouched.
+"""
+import importlib.util
+import inspect
+import os
+
+import pytest
+
+import oracle_pins as P
+
+ORACLE_FILE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                           "oracle", "mbok_oracle.py")
+
+# (case id, function, exact text in its source, replacement)
+MUTATIONS = [
+    ("sign_tie_to_minus_one", "residual_binarize",
+     "np.where(R >= 0.0, 1, -1)", "np.where(R > 0.0, 1, -1)"),
+    ("sign_flipped", "residual_binarize",
+     "np.where(R >= 0.0, 1, -1)", "np.where(R >= 0.0, -1, 1)"),
+    ("scale_from_original_weight", "residual_binarize",
+     "absR = np.abs(R)", "absR = np.abs(W.astype(np.float64))"),
+    ("scale_of_signed_residual", "residual_binarize",
+     "absR = np.abs(R)", "absR = R"),
+    ("scale_divisor_off_by_one", "residual_binarize",
+     ".tolist()) / group", ".tolist()) / (group - 1)"),
+    ("residual_uses_unrounded_scale", "residual_binarize",
+     "alpha_cols = np.repeat(Ak.astype(np.float64), group, axis=1)",
+     "alpha_cols = np.repeat(a, group, axis=1)"),
+    ("residual_not_updated", "residual_binarize",
+     "R = R - alpha_cols * Sk.astype(np.float64)", "R = R"),
+    ("scale_double_rounded", "round_alpha",
+     "np.asarray(a, dtype=np.float64).astype(_ALPHA_NP[alpha_dtype])",
+     "np.asarray(a, dtype=np.float64).astype(np.float32).astype(_ALPHA_NP[alpha_dtype])"),
+    ("scale_truncated", "round_alpha",
+     "np.asarray(a, dtype=np.float64).astype(_ALPHA_NP[alpha_dtype])",
+     "np.asarray(a, dtype=np.float64).astype(np.float32)"),
+    ("dequantize_columns_tiled", "dequantize",
+     "np.repeat(np.asarray(A[k], dtype=np.float64), group, axis=1)",
+     "np.tile(np.asarray(A[k], dtype=np.float64), (1, group))"),
+    ("dequantize_drops_last_kernel", "dequantize",
+     "for k in range(K):", "for k in range(K - 1):"),
+    ("dequantize_sign_inverted", "dequantize",
+     "What += alpha_cols", "What -= alpha_cols"),
+    ("product_transposed_operand", "product",
+     "Y = X2 @ dequantize(S, A, group).T", "Y = dequantize(S, A, group) @ X2.T"),
+    ("bound_without_abs_x", "bound",
+     "E = np.abs(X2) @", "E = X2 @"),
+    ("pack_msb_first", "pack",
+     'axis=-1, bitorder="little")', 'axis=-1, bitorder="big")'),
+    ("pack_kernel_group_swapped", "pack",
+     "by.transpose(1, 3, 0, 2, 4)", "by.transpose(1, 0, 3, 2, 4)"),
+    ("pack_scales_natural_order", "pack",
+     "a = a.reshape(K, RB, ROW_BLOCK, G).transpose(1, 3, 0, 2)",
+     "a = a.reshape(K, RB, ROW_BLOCK, G)"),
+    ("unpack_msb_first", "unpack",
+     'axis=-1, bitorder="little")', 'axis=-1, bitorder="big")'),
+    ("unpack_bit_means_minus", "unpack",
+     "np.where(bits[:, :m, :] == 1, 1, -1)", "np.where(bits[:, :m, :] == 1, -1, 1)"),
+]
+
+
+def _mutated_oracle(func: str, old: str, new: str):
+    spec = importlib.util.spec_from_file_location("mbok_oracle_mutant", ORACLE_FILE)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    src = inspect.getsource(getattr(mod, func))
+    assert old in src, f"mutation text not found in {func}: {old!r}"
+    exec(compile(src.replace(old, new, 1), ORACLE_FILE, "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("case", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(case):
+    _, func, old, new = case
+    mod = _mutated_oracle(func, old, new)
+    caught = []
+    for pin in P.ALL_PINS:
+        try:
+            pin(mod)
+        except Exception as e:  # an assertion or a crash both expose the mistake
+            caught.append(f"{pin.__name__}: {type(e).__name__}")
+    assert caught, f"no pin caught the planted mistake {case[0]}"
+
+
+def test_unmutated_copy_passes_every_pin():
+    spec = importlib.util.spec_from_file_location("mbok_oracle_copy", ORACLE_FILE)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    for pin in P.ALL_PINS:
+        pin(mod)
