@@ -1,0 +1,249 @@
+"""Python binding of the MBOK C ABI (include/mbok.h): argument marshalling only.
+
+Every step of the layer runs in the HIP library libmbok.so built in this
+directory; this module turns torch tensors into device pointers and sizes,
+checks that the buffers are large enough and on the GPU (the C ABI receives
+plain pointers and cannot check sizes), and raises MbokError on a nonzero
+status.  There is no CPU fallback: without the built library every call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "MBOK_F32", "MBOK_F16", "MBOK_BF16", "MBOK_GROUP", "MBOK_MAX_K", "MBOK_MAX_T",
+    "MbokError", "mbok_desc", "library_path", "load_library",
+    "mbok_desc_init", "mbok_packed_bytes", "mbok_alpha_bytes", "mbok_residual_binarize",
+    "mbok_pack", "mbok_gemv", "mbok_gemm", "mbok_status_str", "mbok_version",
+    "alpha_torch_dtype", "quantize_and_pack",
+]
+
+MBOK_F32, MBOK_F16, MBOK_BF16 = 0, 1, 2
+MBOK_GROUP = 128
+MBOK_ROW_BLOCK = 64
+MBOK_MAX_K = 4
+MBOK_MAX_T = 65536
+MBOK_LAYOUT_L64 = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+class MbokError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {mbok_status_str(status)} ({status})")
+
+
+class mbok_desc(ctypes.Structure):
+    _fields_ = [("m", ctypes.c_int32), ("n", ctypes.c_int32), ("K", ctypes.c_int32),
+                ("group", ctypes.c_int32), ("alpha_dtype", ctypes.c_int32),
+                ("layout", ctypes.c_int32)]
+
+    def __repr__(self):
+        return (f"mbok_desc(m={self.m}, n={self.n}, K={self.K}, group={self.group}, "
+                f"alpha_dtype={self.alpha_dtype}, layout={self.layout})")
+
+
+def library_path() -> str:
+    return os.environ.get("MBOK_LIBRARY", os.path.join(_HERE, "libmbok.so"))
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libmbok.so (once).  Raises RuntimeError if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"MBOK HIP library not built: {path} is missing "
+                           "(run `python -m boolean_weight_amd.build`)")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    D = ctypes.POINTER(mbok_desc)
+    sigs = {
+        "mbok_desc_init": (ctypes.c_int, [D, I32, I32, I32, I32]),
+        "mbok_packed_bytes": (SZ, [D]),
+        "mbok_alpha_bytes": (SZ, [D]),
+        "mbok_residual_binarize": (ctypes.c_int, [D, P, I64, P, P, P, P]),
+        "mbok_pack": (ctypes.c_int, [D, P, P, P, P]),
+        "mbok_gemv": (ctypes.c_int, [D, P, P, I32, P, P]),
+        "mbok_gemm": (ctypes.c_int, [D, P, P, I32, I64, I64, P, I64, P]),
+        "mbok_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+        "mbok_version": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _LIB = lib
+    return lib
+
+
+# ------------------------------------------------------------------ helpers
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _dev(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU (the library takes device pointers)")
+    return t
+
+
+def _nbytes_from(t: torch.Tensor) -> int:
+    """Bytes addressable from t.data_ptr() to the end of its storage."""
+    st = t.untyped_storage()
+    return st.nbytes() - (t.data_ptr() - st.data_ptr())
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise MbokError(status, where)
+
+
+def alpha_torch_dtype(alpha_dtype: int) -> torch.dtype:
+    return {MBOK_F32: torch.float32, MBOK_F16: torch.float16}[alpha_dtype]
+
+
+def _x_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MBOK_BF16
+    if t.dtype == torch.float32:
+        return MBOK_F32
+    raise ValueError(f"activations must be bfloat16 or float32, got {t.dtype}")
+
+
+# ---------------------------------------------------------------- the C ABI
+
+def mbok_status_str(status: int) -> str:
+    return load_library().mbok_status_str(int(status)).decode()
+
+
+def mbok_version() -> str:
+    return load_library().mbok_version().decode()
+
+
+def mbok_desc_init(m: int, n: int, K: int, alpha_dtype: int = MBOK_F16) -> mbok_desc:
+    d = mbok_desc()
+    _check(load_library().mbok_desc_init(ctypes.byref(d), m, n, K, alpha_dtype), "mbok_desc_init")
+    return d
+
+
+def mbok_packed_bytes(d: mbok_desc) -> int:
+    return int(load_library().mbok_packed_bytes(ctypes.byref(d)))
+
+
+def mbok_alpha_bytes(d: mbok_desc) -> int:
+    return int(load_library().mbok_alpha_bytes(ctypes.byref(d)))
+
+
+def mbok_residual_binarize(d: mbok_desc, W: torch.Tensor, signs: torch.Tensor,
+                           alpha: torch.Tensor, flag: torch.Tensor | None = None,
+                           stream=None) -> None:
+    """W fp32 [m, ldw] -> signs int8 [K, m, n] and alpha [K, m, n/128]."""
+    _dev(W, "W"), _dev(signs, "signs"), _dev(alpha, "alpha")
+    if W.dtype != torch.float32 or W.dim() != 2 or W.shape[0] != d.m or W.shape[1] < d.n:
+        raise ValueError("W must be float32 [m, >= n]")
+    if W.stride(1) != 1:
+        raise ValueError("W rows must be contiguous")
+    ldw = W.stride(0)
+    if _nbytes_from(W) < ((d.m - 1) * ldw + d.n) * 4:
+        raise ValueError("W buffer too small")
+    if signs.dtype != torch.int8 or _nbytes_from(signs) < d.K * d.m * d.n:
+        raise ValueError("signs must be int8 with K*m*n elements")
+    if alpha.dtype != alpha_torch_dtype(d.alpha_dtype) or _nbytes_from(alpha) < mbok_alpha_bytes(d):
+        raise ValueError("alpha has the wrong dtype or size")
+    fptr = None
+    if flag is not None:
+        _dev(flag, "flag")
+        if flag.dtype != torch.int32 or flag.numel() < 1:
+            raise ValueError("flag must be int32 with >= 1 element")
+        fptr = flag.data_ptr()
+    _check(load_library().mbok_residual_binarize(
+        ctypes.byref(d), W.data_ptr(), ldw, signs.data_ptr(), alpha.data_ptr(), fptr,
+        _stream(stream)), "mbok_residual_binarize")
+
+
+def mbok_pack(d: mbok_desc, signs: torch.Tensor, alpha: torch.Tensor, packed: torch.Tensor,
+              stream=None) -> None:
+    """signs int8 [K, m, n] + alpha [K, m, n/128] -> packed uint8 [mbok_packed_bytes]."""
+    _dev(signs, "signs"), _dev(alpha, "alpha"), _dev(packed, "packed")
+    if signs.dtype != torch.int8 or not signs.is_contiguous() or signs.numel() < d.K * d.m * d.n:
+        raise ValueError("signs must be contiguous int8 with K*m*n elements")
+    if alpha.dtype != alpha_torch_dtype(d.alpha_dtype) or not alpha.is_contiguous() \
+            or _nbytes_from(alpha) < mbok_alpha_bytes(d):
+        raise ValueError("alpha has the wrong dtype or size")
+    if _nbytes_from(packed) < mbok_packed_bytes(d):
+        raise ValueError("packed buffer too small")
+    _check(load_library().mbok_pack(ctypes.byref(d), signs.data_ptr(), alpha.data_ptr(),
+                                    packed.data_ptr(), _stream(stream)), "mbok_pack")
+
+
+def mbok_gemv(d: mbok_desc, packed: torch.Tensor, x: torch.Tensor, y: torch.Tensor,
+              stream=None) -> None:
+    """y[m] (fp32, overwritten) = W_hat x for x bf16 / fp32 [n]."""
+    _dev(packed, "packed"), _dev(x, "x"), _dev(y, "y")
+    if _nbytes_from(packed) < mbok_packed_bytes(d):
+        raise ValueError("packed buffer too small")
+    xd = _x_dtype(x)
+    if x.numel() < d.n or not x.is_contiguous():
+        raise ValueError("x must be contiguous with n elements")
+    if y.dtype != torch.float32 or y.numel() < d.m or not y.is_contiguous():
+        raise ValueError("y must be contiguous float32 with m elements")
+    _check(load_library().mbok_gemv(ctypes.byref(d), packed.data_ptr(), x.data_ptr(), xd,
+                                    y.data_ptr(), _stream(stream)), "mbok_gemv")
+
+
+def mbok_gemm(d: mbok_desc, packed: torch.Tensor, X: torch.Tensor, Y: torch.Tensor,
+              stream=None) -> None:
+    """Y[T, m] (fp32, overwritten) = X W_hat^T for X bf16 [T, n] (row stride ldx)."""
+    _dev(packed, "packed"), _dev(X, "X"), _dev(Y, "Y")
+    if _nbytes_from(packed) < mbok_packed_bytes(d):
+        raise ValueError("packed buffer too small")
+    xd = _x_dtype(X)
+    if X.dim() != 2 or X.shape[1] < d.n or X.stride(1) != 1:
+        raise ValueError("X must be 2-D [T, >= n] with contiguous rows")
+    if Y.dtype != torch.float32 or Y.dim() != 2 or Y.shape[0] != X.shape[0] or \
+            Y.shape[1] < d.m or Y.stride(1) != 1:
+        raise ValueError("Y must be float32 [T, >= m] with contiguous rows")
+    T = X.shape[0]
+    ldx, ldy = X.stride(0), Y.stride(0)
+    if T > 0:
+        if _nbytes_from(X) < ((T - 1) * ldx + d.n) * X.element_size():
+            raise ValueError("X buffer too small")
+        if _nbytes_from(Y) < ((T - 1) * ldy + d.m) * 4:
+            raise ValueError("Y buffer too small")
+    _check(load_library().mbok_gemm(ctypes.byref(d), packed.data_ptr(), X.data_ptr(), xd, T,
+                                    ldx, Y.data_ptr(), ldy, _stream(stream)), "mbok_gemm")
+
+
+# ---------------------------------------------------------------- conveniences
+
+def quantize_and_pack(W: torch.Tensor, K: int, alpha_dtype: int = MBOK_F16, stream=None):
+    """Greedy residual binarization of a device fp32 W, then packing.
+
+    Returns (desc, packed, signs, alpha); every step runs in the library."""
+    m, n = W.shape
+    d = mbok_desc_init(m, n, K, alpha_dtype)
+    signs = torch.empty((K, m, n), dtype=torch.int8, device=W.device)
+    alpha = torch.empty((K, m, n // MBOK_GROUP), dtype=alpha_torch_dtype(alpha_dtype),
+                        device=W.device)
+    flag = torch.zeros(1, dtype=torch.int32, device=W.device)
+    mbok_residual_binarize(d, W, signs, alpha, flag, stream)
+    packed = torch.empty(mbok_packed_bytes(d), dtype=torch.uint8, device=W.device)
+    mbok_pack(d, signs, alpha, packed, stream)
+    if int(flag.item()) != 0:
+        raise ValueError("W holds NaN or Inf")
+    return d, packed, signs, alpha

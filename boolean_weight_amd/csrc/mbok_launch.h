@@ -1,0 +1,21 @@
+// Host-side launchers of the MBOK kernels; called by the C ABI after it has
+// validated every argument.  Internal header.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mbok.h"
+
+namespace mbok {
+
+int launch_residual_binarize(const mbok_desc* d, const float* W, int64_t ldw, int8_t* signs,
+                             void* alpha, int32_t* flag, hipStream_t stream);
+int launch_pack(const mbok_desc* d, const int8_t* signs, const void* alpha, void* packed,
+                hipStream_t stream);
+int launch_gemv(const mbok_desc* d, const void* packed, const void* x, int32_t x_dtype,
+                float* y, hipStream_t stream);
+int launch_gemm(const mbok_desc* d, const void* packed, const void* X, int64_t T, int64_t ldx,
+                float* Y, int64_t ldy, hipStream_t stream);
+
+}  // namespace mbok

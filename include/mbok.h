@@ -50,10 +50,15 @@
  *     sequence of 16-byte chunks; chunk c holds the 128 signs of one
  *     (row i, group g, kernel k) with
  *         c = ((rb * G + g) * K + k) * 64 + r,   rb = i / 64,  r = i % 64.
- *     Byte q (0..15) of a chunk holds columns 128g + 8q .. 128g + 8q + 7,
- *     least significant bit first (bit t <-> column 128g + 8q + t).
- *     Equivalently: read as four little-endian uint32 words, bit t of word w
- *     is column 128g + 32w + t.  Rows m .. m_pad-1 are all-zero bits.
+ *     A chunk is four little-endian uint32 words; word w (0..3) covers
+ *     columns 128g + 32w .. 128g + 32w + 31, and
+ *         bit (8e + q) of word w  <->  column 128g + 32w + 4q + e
+ *     for e in 0..3, q in 0..7.  Equivalently: byte 4w + e of the chunk,
+ *     bit q, is column 128g + 32w + 4q + e.  So each 4-bit nibble of a word
+ *     holds 4 columns spaced 4 apart (one signed-sum lookup in the decode
+ *     kernel), and the 4 bits of 4 consecutive columns 4q..4q+3 sit at the
+ *     same position q of the word's 4 bytes (one byte-select in the prefill
+ *     unpack).  Rows m .. m_pad-1 are all-zero bits.
  *
  *  2. scales, starting at byte K * m_pad * n / 8 (a multiple of 1024):
  *     K * m_pad * G values of the descriptor's alpha dtype (fp32 or IEEE

@@ -183,9 +183,9 @@ def max_error_ratio(Y_dev: np.ndarray, Y_ref: np.ndarray, E: np.ndarray) -> floa
 # --------------------------------------------------------------------------
 # Packed layout MBOK_LAYOUT_L64, written from its specification in the
 # library header: sign chunks of 16 bytes at chunk index
-# ((rb*G + g)*K + k)*64 + r (rb = i // 64, r = i % 64), byte q holding columns
-# 128g+8q .. 128g+8q+7 LSB first, bit 1 = +1; then the scales in the same
-# (rb, g, k, r) order, in the scale dtype; padding rows zero.
+# ((rb*G + g)*K + k)*64 + r (rb = i // 64, r = i % 64); byte 4w + e of a
+# chunk, bit q, is column 128g + 32w + 4q + e; bit 1 = +1.  Then the scales in
+# the same (rb, g, k, r) order, in the scale dtype.  Padding rows are zero.
 # --------------------------------------------------------------------------
 
 def packed_nbytes(m: int, n: int, K: int, alpha_dtype: str) -> int:
@@ -205,10 +205,12 @@ def pack(S: np.ndarray, A: np.ndarray, alpha_dtype: str) -> np.ndarray:
     # bit value per (k, i, j): 1 for +1 (entries >= 0), 0 for -1; padding rows 0
     b = np.zeros((K, m_pad, n), dtype=np.uint8)
     b[:, :m, :] = (S >= 0)
-    # byte q of chunk (i, g, k) holds columns 128g+8q..+7, least significant first
-    by = np.packbits(b.reshape(K, m_pad, G, 16, 8), axis=-1, bitorder="little")
-    by = by.reshape(K, RB, ROW_BLOCK, G, 16)            # [k, rb, r, g, q]
-    buf[:nbits] = by.transpose(1, 3, 0, 2, 4).reshape(-1)  # [rb, g, k, r, q]
+    # column 128g + 32w + 4q + e -> byte 4w + e of chunk (i, g, k), bit q
+    cols = b.reshape(K, m_pad, G, 4, 8, 4)                # [k, i, g, w, q, e]
+    cols = cols.transpose(0, 1, 2, 3, 5, 4)               # [k, i, g, w, e, q]
+    by = np.packbits(cols, axis=-1, bitorder="little")    # [k, i, g, w, e]
+    by = by.reshape(K, RB, ROW_BLOCK, G, 16)              # [k, rb, r, g, 4w+e]
+    buf[:nbits] = by.transpose(1, 3, 0, 2, 4).reshape(-1)  # [rb, g, k, r, byte]
     scale_dt = _ALPHA_NP[alpha_dtype]
     a = np.zeros((K, m_pad, G), dtype=scale_dt)
     a[:, :m, :] = A
@@ -228,10 +230,11 @@ def unpack(buf: np.ndarray, m: int, n: int, K: int, alpha_dtype: str):
     nbits = K * m_pad * n // 8
     if buf.size != packed_nbytes(m, n, K, alpha_dtype):
         raise ValueError("packed buffer has the wrong size")
-    by = buf[:nbits].reshape(RB, G, K, ROW_BLOCK, 16)    # [rb, g, k, r, q]
-    by = by.transpose(2, 0, 3, 1, 4)                      # [k, rb, r, g, q]
-    bits = np.unpackbits(by, axis=-1, bitorder="little")  # [k, rb, r, g, q*8+t]
-    bits = bits.reshape(K, m_pad, n)
+    by = buf[:nbits].reshape(RB, G, K, ROW_BLOCK, 4, 4)   # [rb, g, k, r, w, e]
+    by = by.transpose(2, 0, 3, 1, 4, 5)                   # [k, rb, r, g, w, e]
+    bits = np.unpackbits(by[..., None], axis=-1, bitorder="little")  # [..., w, e, q]
+    bits = bits.transpose(0, 1, 2, 3, 4, 6, 5)            # [k, rb, r, g, w, q, e]
+    bits = bits.reshape(K, m_pad, n)                      # column 128g+32w+4q+e
     S = np.where(bits[:, :m, :] == 1, 1, -1).astype(np.int8)
     scale_dt = _ALPHA_NP[alpha_dtype]
     sc = buf[nbits:].view(scale_dt).reshape(RB, G, K, ROW_BLOCK)

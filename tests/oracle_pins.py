@@ -409,13 +409,14 @@ def pin_pack_roundtrip(o):
 
 def pin_layout_single_bit(o):
     """The header's addressing rule, evaluated by hand for single +1 entries:
-    chunk ((rb G + g) K + k) 64 + r, byte (j mod 128) div 8, bit j mod 8; the
-    scale of (i, g, k) at value index ((rb G + g) K + k) 64 + r after the
-    sign region."""
+    chunk ((rb G + g) K + k) 64 + r; within it, for column j = 128g + 32w +
+    4q + e, byte 4w + e and bit q; the scale of (i, g, k) at value index
+    ((rb G + g) K + k) 64 + r after the sign region."""
     K, m, n = 3, 130, 384
     G = n // 128
     m_pad = 192
-    for (k, i, j) in ((0, 0, 0), (2, 129, 383), (1, 64, 130), (0, 63, 255), (2, 5, 9)):
+    for (k, i, j) in ((0, 0, 0), (2, 129, 383), (1, 64, 130), (0, 63, 255), (2, 5, 9),
+                      (1, 7, 1), (0, 9, 4), (2, 3, 32 + 29), (1, 100, 256 + 127)):
         S = -np.ones((K, m, n), dtype=np.int8)
         S[k, i, j] = 1
         A = np.zeros((K, m, G), dtype=np.float32)
@@ -424,10 +425,12 @@ def pin_layout_single_bit(o):
         nbits = K * m_pad * n // 8
         rb, r, g = i // 64, i % 64, j // 128
         chunk = ((rb * G + g) * K + k) * 64 + r
-        byte = chunk * 16 + (j % 128) // 8
+        jj = j % 128
+        w, q, e = jj // 32, (jj % 32) // 4, jj % 4
+        byte = chunk * 16 + 4 * w + e
         nz = np.flatnonzero(buf[:nbits])
         assert nz.tolist() == [byte], ((k, i, j), nz[:4], byte)
-        assert buf[byte] == 1 << (j % 8)
+        assert buf[byte] == 1 << q
         sc = buf[nbits:].view(np.float32)
         assert np.flatnonzero(sc).tolist() == [chunk] and sc[chunk] == 1.5
 

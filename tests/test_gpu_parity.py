@@ -1,0 +1,275 @@
+"""GPU parity: the HIP path against the CPU oracle, through the C ABI.
+
+Bars (from the statement of the problem):
+  * quantizer: signs identical, scales bit-identical in their dtype;
+  * pack: the oracle's own unpacker reads back exactly the signs and scales;
+  * product, exact regime (integer x in [-8, 8], scales 2^-e, e in 4..8):
+    equal values;
+  * product, general inputs: |y - y_ref| <= 1e-3 * sum_j |W_hat_ij| |x_j| for
+    every output, with fp32 accumulation on the device.
+Full-size layers are checked on sampled output rows that the oracle computes
+on its own from the same seeded W and x.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import boolean_weight_amd as bw
+import mbok_synth as syn
+import oracle
+from gpu_util import DEV, alpha_enum, gemm, gemv, np_alpha, pack_on_gpu, say, to_dev, x_to_dev
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    bw.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+@pytest.fixture(params=["lut", "direct"])
+def gemv_variant(request):
+    old = os.environ.get("MBOK_GEMV_VARIANT")
+    os.environ["MBOK_GEMV_VARIANT"] = request.param
+    yield request.param
+    if old is None:
+        os.environ.pop("MBOK_GEMV_VARIANT", None)
+    else:
+        os.environ["MBOK_GEMV_VARIANT"] = old
+
+
+def quantize_on_gpu(W: np.ndarray, K: int, dt: str):
+    m, n = W.shape
+    d = bw.mbok_desc_init(m, n, K, alpha_enum(dt))
+    Wt = to_dev(W)
+    signs = torch.empty((K, m, n), dtype=torch.int8, device=DEV)
+    alpha = torch.empty((K, m, n // 128), dtype=bw.alpha_torch_dtype(d.alpha_dtype), device=DEV)
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    bw.mbok_residual_binarize(d, Wt, signs, alpha, flag)
+    packed = torch.empty(bw.mbok_packed_bytes(d), dtype=torch.uint8, device=DEV)
+    bw.mbok_pack(d, signs, alpha, packed)
+    return d, signs, alpha, packed, int(flag.item())
+
+
+def sample_rows(m: int, count: int, seed: int) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(m, size=min(count, m), replace=False).tolist())
+    rows |= {0, m - 1, min(63, m - 1), min(64, m - 1)}
+    return np.array(sorted(rows))
+
+
+# ----------------------------------------------------------------- quantizer
+
+@pytest.mark.parametrize("K", [1, 2, 3, 4])
+@pytest.mark.parametrize("dt", ["f16", "f32"])
+def test_quantizer_bit_exact_small(K, dt):
+    say(f"quantizer small K={K} {dt}")
+    W = syn.weight(100, 384, seed=300 + K)
+    W[3, :9] = 0.0
+    W[4, 5:11] = -0.0
+    W[7, 128:256] = 0.0          # a whole zero group
+    S, A, R = oracle.residual_binarize(W, K, alpha_dtype=dt)
+    d, signs, alpha, packed, flag = quantize_on_gpu(W, K, dt)
+    assert flag == 0
+    assert np.array_equal(signs.cpu().numpy(), S)
+    assert np.array_equal(alpha.cpu().numpy().view(np.uint8), A.view(np.uint8))
+    S2, A2, clean = oracle.unpack(packed.cpu().numpy(), 100, 384, K, dt)
+    assert np.array_equal(S2, S) and np.array_equal(A2.view(np.uint8), A.view(np.uint8)) and clean
+    assert np.array_equal(packed.cpu().numpy(), oracle.pack(S, A, dt))
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_quantizer_bit_exact_workloads_sampled(cfg):
+    w = syn.WORKLOADS[cfg]
+    dt = w["alpha_dtype"]
+    for li, (name, m, n) in enumerate(w["linears"]):
+        say(f"quantizer config {cfg} {name} {m}x{n} K={w['K']}")
+        W = syn.weight(m, n, syn.weight_seed(cfg, li))
+        d, signs, alpha, packed, flag = quantize_on_gpu(W, w["K"], dt)
+        assert flag == 0
+        rows = sample_rows(m, 24, cfg * 10 + li)
+        S, A, _ = oracle.residual_binarize(W[rows], w["K"], alpha_dtype=dt)
+        assert np.array_equal(signs.cpu().numpy()[:, rows], S), name
+        assert np.array_equal(alpha.cpu().numpy()[:, rows].view(np.uint8), A.view(np.uint8)), name
+        del signs, alpha, packed
+        torch.cuda.empty_cache()
+
+
+def test_quantizer_flags_non_finite():
+    say("quantizer non-finite flag")
+    W = syn.weight(64, 256, seed=7)
+    W[10, 20] = np.nan
+    d, signs, alpha, packed, flag = quantize_on_gpu(W, 2, "f16")
+    assert flag == 1
+    W[10, 20] = np.inf
+    assert quantize_on_gpu(W, 2, "f16")[4] == 1
+    W[10, 20] = 0.5
+    assert quantize_on_gpu(W, 2, "f16")[4] == 0
+
+
+def test_quantizer_row_stride():
+    say("quantizer with ldw > n")
+    W = syn.weight(70, 512, seed=8)
+    Wbig = np.zeros((70, 640), dtype=np.float32)
+    Wbig[:, :512] = W
+    Wbig[:, 512:] = np.nan  # must never be read
+    d = bw.mbok_desc_init(70, 512, 3, bw.MBOK_F16)
+    signs = torch.empty((3, 70, 512), dtype=torch.int8, device=DEV)
+    alpha = torch.empty((3, 70, 4), dtype=torch.float16, device=DEV)
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    bw.mbok_residual_binarize(d, to_dev(Wbig), signs, alpha, flag)
+    S, A, _ = oracle.residual_binarize(W, 3, alpha_dtype="f16")
+    assert int(flag.item()) == 0
+    assert np.array_equal(signs.cpu().numpy(), S)
+    assert np.array_equal(alpha.cpu().numpy(), A)
+
+
+# --------------------------------------------------------------------- pack
+
+@pytest.mark.parametrize("K,m,n,dt", [(1, 1, 128, "f32"), (2, 63, 256, "f16"), (3, 65, 384, "f16"),
+                                      (4, 130, 512, "f32"), (3, 256, 128, "f16")])
+def test_pack_matches_oracle_layout(K, m, n, dt):
+    say(f"pack K={K} m={m} n={n} {dt}")
+    S = syn.random_signs(K, m, n, seed=K * 1000 + m)
+    A = syn.exact_alpha(K, m, n // 128, seed=m).astype(np_alpha(dt))
+    d, packed = pack_on_gpu(S, A, dt)
+    buf = packed.cpu().numpy()
+    assert np.array_equal(buf, oracle.pack(S, A, dt))
+    S2, A2, clean = oracle.unpack(buf, m, n, K, dt)
+    assert np.array_equal(S2, S) and np.array_equal(A2, A) and clean
+
+
+# ------------------------------------------------------------ decode GEMV
+
+EXACT_SHAPES = [(1, 128), (63, 256), (64, 128), (65, 384), (100, 512), (130, 1024),
+                (256, 4096), (200, 5120), (70, 13824)]
+
+
+@pytest.mark.parametrize("K", [1, 2, 3, 4])
+@pytest.mark.parametrize("m,n", EXACT_SHAPES)
+def test_gemv_exact_regime(m, n, K, gemv_variant):
+    for dt, xdt in (("f16", "bf16"), ("f32", "f32")):
+        say(f"gemv exact {gemv_variant} m={m} n={n} K={K} {dt}/{xdt}")
+        S = syn.random_signs(K, m, n, seed=m * 7 + n + K)
+        A = syn.exact_alpha(K, m, n // 128, seed=m + K).astype(np_alpha(dt))
+        x = syn.exact_activations(1, n, seed=n + K)[0]
+        d, packed = pack_on_gpu(S, A, dt)
+        y = gemv(d, packed, x, xdt, guard=17)
+        want = oracle.product(S, A, x)
+        assert np.array_equal(y, want), np.max(np.abs(y - want))
+
+
+def test_gemv_one_hot_and_all_ones(gemv_variant):
+    say(f"gemv one-hot {gemv_variant}")
+    K, m, n = 3, 70, 384
+    S = syn.random_signs(K, m, n, seed=5)
+    A = syn.exact_alpha(K, m, 3, seed=6).astype(np.float16)
+    d, packed = pack_on_gpu(S, A, "f16")
+    for j in (0, 1, 4, 31, 32, 127, 128, 200, 383):
+        x = np.zeros(n, dtype=np.float32)
+        x[j] = 1.0
+        y = gemv(d, packed, x, "bf16")
+        want = np.array([sum(float(A[k, i, j // 128]) * int(S[k, i, j]) for k in range(K))
+                         for i in range(m)])
+        assert np.array_equal(y, want), j
+    for g in range(3):
+        x = np.zeros(n, dtype=np.float32)
+        x[128 * g:128 * g + 128] = 1.0
+        y = gemv(d, packed, x, "bf16")
+        want = [sum(float(A[k, i, g]) * (2 * int(np.count_nonzero(S[k, i, 128 * g:128 * g + 128] > 0)) - 128)
+                    for k in range(K)) for i in range(m)]
+        assert np.array_equal(y, np.array(want)), g
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_gemv_workloads_tolerance(cfg):
+    """Full pipeline on the device (quantize, pack, gemv) at the workload
+    shapes; the oracle quantizes and multiplies sampled rows on its own."""
+    w = syn.WORKLOADS[cfg]
+    dt, xdt = w["alpha_dtype"], w["x_dtype"]
+    for li, (name, m, n) in enumerate(w["linears"]):
+        say(f"gemv config {cfg} {name} {m}x{n} K={w['K']}")
+        W = syn.weight(m, n, syn.weight_seed(cfg, li))
+        x = syn.activations(1, n, syn.act_seed(cfg, li), xdt)[0]
+        d, signs, alpha, packed, flag = quantize_on_gpu(W, w["K"], dt)
+        del signs, alpha
+        y = gemv(d, packed, x, xdt, guard=5)
+        rows = sample_rows(m, 48, li)
+        S, A, _ = oracle.residual_binarize(W[rows], w["K"], alpha_dtype=dt)
+        want, E = oracle.product(S, A, x), oracle.bound(S, A, x)
+        ratio = oracle.max_error_ratio(y[rows], want, E)
+        assert ratio <= TOL, (name, ratio)
+        # determinism: a second call gives the same bits
+        y2 = gemv(d, packed, x, xdt)
+        assert np.array_equal(y, y2)
+        del packed
+        torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("K", [1, 2, 3])
+def test_gemv_k_sweep_first_linear(cfg, K):
+    w = syn.WORKLOADS[cfg]
+    dt = w["alpha_dtype"]
+    xdt = w["x_dtype"]
+    name, m, n = w["linears"][0]
+    say(f"gemv K sweep config {cfg} {name} K={K}")
+    W = syn.weight(m, n, syn.weight_seed(cfg, 0))
+    x = syn.activations(1, n, syn.act_seed(cfg, 0), xdt)[0]
+    d, signs, alpha, packed, flag = quantize_on_gpu(W, K, dt)
+    y = gemv(d, packed, x, xdt)
+    rows = sample_rows(m, 32, 100 + K)
+    S, A, _ = oracle.residual_binarize(W[rows], K, alpha_dtype=dt)
+    ratio = oracle.max_error_ratio(y[rows], oracle.product(S, A, x), oracle.bound(S, A, x))
+    assert ratio <= TOL, ratio
+
+
+def test_gemv_config1_full_oracle():
+    """Config 1 is small enough for the oracle to do every row."""
+    say("gemv config 1 full")
+    w = syn.WORKLOADS[1]
+    W = syn.weight(256, 512, syn.weight_seed(1))
+    x = syn.activations(1, 512, syn.act_seed(1), "f32")[0]
+    S, A, _ = oracle.residual_binarize(W, 2, alpha_dtype="f32")
+    d, signs, alpha, packed, flag = quantize_on_gpu(W, 2, "f32")
+    y = gemv(d, packed, x, "f32")
+    assert oracle.max_error_ratio(y, oracle.product(S, A, x), oracle.bound(S, A, x)) <= TOL
+
+
+# ---------------------------------------------------------- multi-token GEMM
+
+@pytest.mark.parametrize("T", [1, 3, 4, 16, 17, 40])
+@pytest.mark.parametrize("K", [1, 2, 3])
+def test_gemm_exact_regime(T, K):
+    m, n = 130, 512
+    say(f"gemm exact T={T} K={K}")
+    S = syn.random_signs(K, m, n, seed=T * 10 + K)
+    A = syn.exact_alpha(K, m, n // 128, seed=T + K).astype(np.float16)
+    X = syn.exact_activations(T, n, seed=T + 50 * K)
+    d, packed = pack_on_gpu(S, A, "f16")
+    Y = gemm(d, packed, X, ldx=n + 8, ldy=m + 3)
+    assert np.array_equal(Y, oracle.product(S, A, X))
+
+
+@pytest.mark.parametrize("T", [4, 16])
+def test_gemm_config3_tolerance(T):
+    w = syn.WORKLOADS[3]
+    for li, (name, m, n) in enumerate(w["linears"]):
+        say(f"gemm config 3 {name} T={T}")
+        W = syn.weight(m, n, syn.weight_seed(3, li))
+        X = syn.activations(T, n, syn.act_seed(3, li), "bf16")
+        d, signs, alpha, packed, flag = quantize_on_gpu(W, 3, "f16")
+        del signs, alpha
+        Y = gemm(d, packed, X)
+        rows = sample_rows(m, 24, li)
+        S, A, _ = oracle.residual_binarize(W[rows], 3, alpha_dtype="f16")
+        ratio = oracle.max_error_ratio(Y[:, rows], oracle.product(S, A, X), oracle.bound(S, A, X))
+        assert ratio <= TOL, (name, ratio)
