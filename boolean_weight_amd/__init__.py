@@ -18,7 +18,8 @@ __all__ = [
     "MBOK_F32", "MBOK_F16", "MBOK_BF16", "MBOK_GROUP", "MBOK_MAX_K", "MBOK_MAX_T",
     "MbokError", "mbok_desc", "library_path", "load_library",
     "mbok_desc_init", "mbok_packed_bytes", "mbok_alpha_bytes", "mbok_residual_binarize",
-    "mbok_pack", "mbok_gemv", "mbok_gemm", "mbok_status_str", "mbok_version",
+    "mbok_pack", "mbok_gemv", "mbok_gemv_workspace_bytes", "mbok_gemm", "mbok_status_str",
+    "mbok_version", "workspace_for",
     "alpha_torch_dtype", "quantize_and_pack",
 ]
 
@@ -71,7 +72,8 @@ def load_library() -> ctypes.CDLL:
         "mbok_alpha_bytes": (SZ, [D]),
         "mbok_residual_binarize": (ctypes.c_int, [D, P, I64, P, P, P, P]),
         "mbok_pack": (ctypes.c_int, [D, P, P, P, P]),
-        "mbok_gemv": (ctypes.c_int, [D, P, P, I32, P, P]),
+        "mbok_gemv_workspace_bytes": (SZ, [D]),
+        "mbok_gemv": (ctypes.c_int, [D, P, P, I32, P, P, P]),
         "mbok_gemm": (ctypes.c_int, [D, P, P, I32, I64, I64, P, I64, P]),
         "mbok_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "mbok_version": (ctypes.c_char_p, []),
@@ -191,9 +193,33 @@ def mbok_pack(d: mbok_desc, signs: torch.Tensor, alpha: torch.Tensor, packed: to
                                     packed.data_ptr(), _stream(stream)), "mbok_pack")
 
 
+def mbok_gemv_workspace_bytes(d: mbok_desc) -> int:
+    return int(load_library().mbok_gemv_workspace_bytes(ctypes.byref(d)))
+
+
+_WORKSPACES: dict = {}
+
+
+def workspace_for(nbytes: int, device=None, stream=None) -> torch.Tensor | None:
+    """A workspace of at least nbytes, kept per (device, stream) so that calls
+    which may overlap never share one."""
+    if nbytes == 0:
+        return None
+    dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+    key = (dev.index, _stream(stream))
+    ws = _WORKSPACES.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
+        _WORKSPACES[key] = ws
+    return ws
+
+
 def mbok_gemv(d: mbok_desc, packed: torch.Tensor, x: torch.Tensor, y: torch.Tensor,
-              stream=None) -> None:
-    """y[m] (fp32, overwritten) = W_hat x for x bf16 / fp32 [n]."""
+              workspace: torch.Tensor | None | bool = True, stream=None) -> None:
+    """y[m] (fp32, overwritten) = W_hat x for x bf16 / fp32 [n].
+
+    workspace: True (default) uses a cached workspace for this device and
+    stream; a tensor is used as given; None/False runs without one."""
     _dev(packed, "packed"), _dev(x, "x"), _dev(y, "y")
     if _nbytes_from(packed) < mbok_packed_bytes(d):
         raise ValueError("packed buffer too small")
@@ -202,8 +228,19 @@ def mbok_gemv(d: mbok_desc, packed: torch.Tensor, x: torch.Tensor, y: torch.Tens
         raise ValueError("x must be contiguous with n elements")
     if y.dtype != torch.float32 or y.numel() < d.m or not y.is_contiguous():
         raise ValueError("y must be contiguous float32 with m elements")
+    need = mbok_gemv_workspace_bytes(d)
+    if workspace is True:
+        workspace = workspace_for(need, y.device, stream)
+    elif workspace is False:
+        workspace = None
+    wptr = None
+    if workspace is not None and need > 0:
+        _dev(workspace, "workspace")
+        if _nbytes_from(workspace) < need:
+            raise ValueError("workspace too small")
+        wptr = workspace.data_ptr()
     _check(load_library().mbok_gemv(ctypes.byref(d), packed.data_ptr(), x.data_ptr(), xd,
-                                    y.data_ptr(), _stream(stream)), "mbok_gemv")
+                                    y.data_ptr(), wptr, _stream(stream)), "mbok_gemv")
 
 
 def mbok_gemm(d: mbok_desc, packed: torch.Tensor, X: torch.Tensor, Y: torch.Tensor,

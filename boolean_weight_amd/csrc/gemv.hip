@@ -131,6 +131,45 @@ __device__ __forceinline__ float lut_dot128(const uint4 b, uint32_t tab) {
   return (part[0] + part[1]) + (part[2] + part[3]);
 }
 
+// byte k of v added to base: one VOP2 add with a byte-select operand
+#define MBOK_ADD_BYTE(out, base, v, k)                                              \
+  asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD " \
+      "src1_sel:BYTE_" #k                                                           \
+      : "=v"(out)                                                                   \
+      : "v"(base), "v"(v))
+
+// As lut_dot128, with the nibble addresses formed per word: the even nibbles
+// shifted to bits 2..5 of each byte with one shift and one mask, the odd ones
+// likewise, then each entry address is one add of a selected byte to `tab`
+// (any table base works: it is an ordinary register operand).  2.5 VALU
+// operations per 4 weights.
+__device__ __forceinline__ float lut_dot128_sdwa(const uint4 b, uint32_t tab) {
+  typedef __attribute__((address_space(3))) const float lds_f32;
+  const uint32_t wv[4] = {b.x, b.y, b.z, b.w};
+  float part[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t ev = (wv[w] << 2) & 0x3c3c3c3cu;  // byte k: nibble 2k, times 4
+    const uint32_t od = (wv[w] >> 2) & 0x3c3c3c3cu;  // byte k: nibble 2k+1, times 4
+    uint32_t a0, a1, a2, a3, a4, a5, a6, a7;
+    MBOK_ADD_BYTE(a0, tab, ev, 0);
+    MBOK_ADD_BYTE(a1, tab, od, 0);
+    MBOK_ADD_BYTE(a2, tab, ev, 1);
+    MBOK_ADD_BYTE(a3, tab, od, 1);
+    MBOK_ADD_BYTE(a4, tab, ev, 2);
+    MBOK_ADD_BYTE(a5, tab, od, 2);
+    MBOK_ADD_BYTE(a6, tab, ev, 3);
+    MBOK_ADD_BYTE(a7, tab, od, 3);
+    const uint32_t ad[8] = {a0, a1, a2, a3, a4, a5, a6, a7};
+    float s = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      s += reinterpret_cast<lds_f32*>((uintptr_t)ad[q])[(w * 8 + q) * kTableFloats];
+    part[w] = s;
+  }
+  return (part[0] + part[1]) + (part[2] + part[3]);
+}
+
 // LDS byte address of a shared-memory pointer.
 __device__ __forceinline__ uint32_t lds_addr(const float* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const float*)p;
@@ -182,7 +221,7 @@ __global__ void __launch_bounds__(NW * kWave) gemv_lut_kernel(
       if (gl < sg) {
         const uint32_t tab = lds_addr(lds + gl * kChunksPerGroup * kTableFloats);
 #pragma unroll
-        for (int k = 0; k < K; ++k) yacc = fmaf(a[j][k], lut_dot128(b[j][k], tab), yacc);
+        for (int k = 0; k < K; ++k) yacc = fmaf(a[j][k], lut_dot128_sdwa(b[j][k], tab), yacc);
       }
     }
   }
@@ -196,6 +235,203 @@ __global__ void __launch_bounds__(NW * kWave) gemv_lut_kernel(
     const int i = rb * kRowBlock + lane;
     if (i < m) y[i] = s;
   }
+}
+
+// Row-slice variant: a wavefront covers R = 64/NS rows and NS column slices
+// (lane = c*R + r), a workgroup covers R rows and every column, so no
+// cross-workgroup step is needed and small layers still give m/R workgroups.
+// The NW*NS slices ("streams") of a workgroup take groups p, p+NW*NS, ...;
+// all streams of the workgroup read the same slab of tables.  Group tables
+// are kGroupStride = 2112 bytes apart (33 x 64): the NS slices of a
+// wavefront read consecutive groups, whose tables then start 16 banks apart,
+// so one ds_read of the whole wavefront stays free of bank conflicts.  The
+// next group's sign planes are loaded before the current one is summed.
+constexpr int kGroupStride = 2112;  // bytes between the tables of two groups
+
+template <typename XT>
+__device__ __forceinline__ float load_x1(const XT* __restrict__ x, int64_t col);
+template <>
+__device__ __forceinline__ float load_x1<float>(const float* __restrict__ x, int64_t col) {
+  return x[col];
+}
+template <>
+__device__ __forceinline__ float load_x1<uint16_t>(const uint16_t* __restrict__ x, int64_t col) {
+  return bf16_bits_to_f32(x[col]);
+}
+
+// Tables of groups g0 .. g0+sg-1.  Work item u = (table t, quarter h) writes
+// entries 4h .. 4h+3 of table t (one float4); consecutive threads write
+// consecutive 16-byte slots, so the stores are free of bank conflicts.
+// Table t = 8w + a of a group covers columns c0 + 4j (j = 0..3) with
+// c0 = 32w + 16(a%2) + a/2; entry p = sum_j (bit j of p ? x : -x), and the
+// quarter h fixes bits 2 and 3 of p.
+template <typename XT>
+__device__ __forceinline__ void build_group_tables(const XT* __restrict__ x, int g0, int sg,
+                                                   float* lds, int tid, int nthreads) {
+  for (int u = tid; u < sg * kChunksPerGroup * 4; u += nthreads) {
+    const int h = u & 3;
+    const int t = (u >> 2) & (kChunksPerGroup - 1);
+    const int gl = u >> 7;
+    const int w = t >> 3, a = t & 7;
+    const int64_t c0 = (int64_t)(g0 + gl) * kGroup + 32 * w + 16 * (a & 1) + (a >> 1);
+    const float x0 = load_x1<XT>(x, c0), x1 = load_x1<XT>(x, c0 + 4);
+    const float x2 = load_x1<XT>(x, c0 + 8), x3 = load_x1<XT>(x, c0 + 12);
+    const float hi = ((h & 1) ? x2 : -x2) + ((h & 2) ? x3 : -x3);
+    float4* dst = reinterpret_cast<float4*>(lds + (gl * kGroupStride) / 4 + t * kTableFloats) + h;
+    *dst = make_float4(-x0 - x1 + hi, x0 - x1 + hi, -x0 + x1 + hi, x0 + x1 + hi);
+  }
+}
+
+template <typename XT, typename AT, int K, int NW, int NS>
+__global__ void __launch_bounds__(NW * kWave) gemv_rows_kernel(
+    const uint4* __restrict__ bits, const AT* __restrict__ scales, const XT* __restrict__ x,
+    float* __restrict__ y, int m, int G, int slab_groups) {
+  constexpr int R = kWave / NS;
+  constexpr int NP = NW * NS;
+  extern __shared__ float lds[];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int c = lane / R, r = lane % R;
+  const int p = wave * NS + c;
+  const int i = blockIdx.x * R + r;  // < m_pad: R divides the 64-row block
+  const int rb = i / kRowBlock, rr = i % kRowBlock;
+  const uint32_t lbase = lds_addr(lds);
+  float yacc = 0.f;
+  for (int g0 = 0; g0 < G; g0 += slab_groups) {
+    const int sg = min(slab_groups, G - g0);
+    if (g0 > 0) __syncthreads();
+    build_group_tables<XT>(x, g0, sg, lds, threadIdx.x, NW * kWave);
+    __syncthreads();
+    int gl = p;
+    uint4 b[K];
+    float a[K];
+    if (gl < sg) {
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const int64_t cidx = (((int64_t)rb * G + g0 + gl) * K + k) * kRowBlock + rr;
+        b[k] = bits[cidx];
+        a[k] = alpha_to_f32<AT>(scales[cidx]);
+      }
+    }
+    while (gl < sg) {
+      const int gn = gl + NP;
+      uint4 bn[K];
+      float an[K];
+      if (gn < sg) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          const int64_t cidx = (((int64_t)rb * G + g0 + gn) * K + k) * kRowBlock + rr;
+          bn[k] = bits[cidx];
+          an[k] = alpha_to_f32<AT>(scales[cidx]);
+        }
+      }
+      const uint32_t tab = lbase + gl * kGroupStride;
+#pragma unroll
+      for (int k = 0; k < K; ++k) yacc = fmaf(a[k], lut_dot128_sdwa(b[k], tab), yacc);
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        b[k] = bn[k];
+        a[k] = an[k];
+      }
+      gl = gn;
+    }
+  }
+  // fixed-order sum over the NS slices of the wavefront, then over wavefronts
+#pragma unroll
+  for (int off = R; off < kWave; off <<= 1) yacc += __shfl_xor(yacc, off, kWave);
+  if (NW > 1) {
+    __syncthreads();
+    if (c == 0) lds[wave * R + r] = yacc;
+    __syncthreads();
+    if (wave != 0 || c != 0) return;
+    yacc = lds[r];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) yacc += lds[w * R + r];
+  } else if (c != 0) {
+    return;
+  }
+  if (i < m) y[i] = yacc;
+}
+
+// Column-split variant (the default when a workspace is given): workgroup
+// (rb, s) covers the 64 rows of row block rb and the GPW*NW groups of column
+// slice s; its wavefronts own GPW groups each and build only their slice's
+// tables, so a layer becomes RB*S workgroups spread over every compute unit
+// while each table is still shared by 64 rows.  With S > 1 slices each
+// workgroup stores its 64 partial sums to partials[s][row]; gemv_reduce_kernel,
+// launched next on the same stream, adds them in slice order 0..S-1 (a fixed
+// order: the result does not depend on scheduling).  The kernel boundary
+// orders the two, so no device-wide fence or atomic is needed.
+template <typename XT, typename AT, int K, int NW, int GPW>
+__global__ void __launch_bounds__(NW * kWave) gemv_split_kernel(
+    const uint4* __restrict__ bits, const AT* __restrict__ scales, const XT* __restrict__ x,
+    float* __restrict__ y, int m, int m_pad, int G, int S, float* __restrict__ partials) {
+  extern __shared__ float lds[];
+  const int rb = blockIdx.x / S;
+  const int s = blockIdx.x - rb * S;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int g0 = s * (NW * GPW);
+  const int ng = min(NW * GPW, G - g0);
+  uint4 b[GPW][K];
+  float a[GPW][K];
+#pragma unroll
+  for (int j = 0; j < GPW; ++j) {
+    const int gl = wave * GPW + j;
+    if (gl < ng) {
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const int64_t c = (((int64_t)rb * G + g0 + gl) * K + k) * kRowBlock + lane;
+        b[j][k] = bits[c];
+        a[j][k] = alpha_to_f32<AT>(scales[c]);
+      }
+    }
+  }
+  for (int blk = threadIdx.x; blk < ng * 8; blk += NW * kWave) {
+    float v[16];
+    load_x16<XT>(x, (int64_t)g0 * kGroup + 16 * blk, v);
+    const int gl = blk >> 3, bb = blk & 7;
+    float* tab = lds + (gl * kChunksPerGroup + 8 * (bb >> 1) + (bb & 1)) * kTableFloats;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      build_table4(v[e], v[4 + e], v[8 + e], v[12 + e], tab + 2 * e * kTableFloats);
+  }
+  __syncthreads();
+  float yacc = 0.f;
+#pragma unroll
+  for (int j = 0; j < GPW; ++j) {
+    const int gl = wave * GPW + j;
+    if (gl < ng) {
+      const uint32_t tab = lds_addr(lds + gl * kChunksPerGroup * kTableFloats);
+#pragma unroll
+      for (int k = 0; k < K; ++k) yacc = fmaf(a[j][k], lut_dot128_sdwa(b[j][k], tab), yacc);
+    }
+  }
+  if (NW > 1) {
+    __syncthreads();
+    lds[wave * kWave + lane] = yacc;
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int w = 1; w < NW; ++w) yacc += lds[w * kWave + lane];
+  }
+  const int i = rb * kRowBlock + lane;
+  if (S == 1) {
+    if (i < m) y[i] = yacc;
+  } else {
+    partials[(int64_t)s * m_pad + i] = yacc;
+  }
+}
+
+// y[i] = sum over slices s = 0..S-1 of partials[s][i], in that order.
+__global__ void __launch_bounds__(256) gemv_reduce_kernel(const float* __restrict__ partials,
+                                                          float* __restrict__ y, int m,
+                                                          int m_pad, int S) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= m) return;
+  float t = partials[i];
+  for (int q = 1; q < S; ++q) t += partials[(int64_t)q * m_pad + i];
+  y[i] = t;
 }
 
 // Reference-style variant: no tables, x staged in LDS as fp32, one select and
@@ -246,25 +482,141 @@ __global__ void __launch_bounds__(NW * kWave) gemv_direct_kernel(
   }
 }
 
-enum Variant { kLut = 0, kDirect = 1 };
+enum Variant { kSplit = 0, kFullRow = 1, kDirect = 2, kRows = 3 };
 
 int variant_from_env() {
   const char* v = getenv("MBOK_GEMV_VARIANT");
   if (v && strcmp(v, "direct") == 0) return kDirect;
-  return kLut;
+  if (v && strcmp(v, "fullrow") == 0) return kFullRow;
+  if (v && strcmp(v, "split") == 0) return kSplit;
+  return kRows;
+}
+
+constexpr int kSplitNW = 4;           // wavefronts per split workgroup
+constexpr int kTargetWaves = 4096;    // 16 per compute unit
+
+}  // namespace
+
+// Column slices of the split kernel: groups per wavefront (1..4) and slices.
+void gemv_split_shape(int RB, int G, int* gpw, int* S) {
+  int s_target = (kTargetWaves + RB * kSplitNW - 1) / (RB * kSplitNW);
+  if (s_target < 1) s_target = 1;
+  const int per_slice = (G + s_target - 1) / s_target;
+  int g = (per_slice + kSplitNW - 1) / kSplitNW;
+  if (g < 1) g = 1;
+  if (g > 4) g = 4;
+  *gpw = g;
+  *S = (G + kSplitNW * g - 1) / (kSplitNW * g);
+}
+
+size_t gemv_workspace_bytes(const mbok_desc* d) {
+  const Geom geo = make_geom(d);
+  int gpw, S;
+  gemv_split_shape(geo.RB, geo.G, &gpw, &S);
+  if (S <= 1) return 0;
+  return (size_t)S * geo.RB * kRowBlock * sizeof(float);  // partials[S][m_pad]
+}
+
+namespace {
+
+template <typename XT, typename AT, int K, int GPW>
+int launch_split(const Geom& geo, int S, const uint4* bits, const AT* scales, const void* x,
+                 float* y, void* ws, hipStream_t stream) {
+  constexpr int NW = kSplitNW;
+  float* partials = reinterpret_cast<float*>(ws);
+  const int m_pad = geo.RB * kRowBlock;
+  const size_t tab = (size_t)NW * GPW * kChunksPerGroup * kTableFloats * sizeof(float);
+  const size_t lds = tab > NW * kWave * sizeof(float) ? tab : NW * kWave * sizeof(float);
+  hipLaunchKernelGGL((gemv_split_kernel<XT, AT, K, NW, GPW>), dim3(geo.RB * S), dim3(NW * kWave),
+                     lds, stream, bits, scales, reinterpret_cast<const XT*>(x), y, geo.m, m_pad,
+                     geo.G, S, partials);
+  if (hipGetLastError() != hipSuccess) return MBOK_ERR_HIP;
+  if (S > 1) {
+    hipLaunchKernelGGL(gemv_reduce_kernel, dim3((geo.m + 255) / 256), dim3(256), 0, stream,
+                       partials, y, geo.m, m_pad, S);
+    if (hipGetLastError() != hipSuccess) return MBOK_ERR_HIP;
+  }
+  return MBOK_OK;
+}
+
+// Rows per workgroup for the row-slice kernel: the largest R in {64, 32, 16}
+// that still gives at least one workgroup per compute unit (MBOK_GEMV_R
+// overrides, for measurements).
+int rows_per_workgroup(int m) {
+  const char* v = getenv("MBOK_GEMV_R");
+  if (v) {
+    const int r = atoi(v);
+    if (r == 16 || r == 32 || r == 64) return r;
+  }
+  if (m >= 64 * 256) return 64;
+  if (m >= 32 * 256) return 32;
+  return 16;
+}
+
+int rows_waves() {
+  const char* v = getenv("MBOK_GEMV_NW");
+  const int nw = v ? atoi(v) : 8;
+  return (nw == 4 || nw == 8 || nw == 16) ? nw : 8;
+}
+
+template <typename XT, typename AT, int K, int NW, int NS>
+int launch_rows_nw(const Geom& geo, const uint4* bits, const AT* scales, const void* x, float* y,
+                   hipStream_t stream) {
+  constexpr int R = kWave / NS;
+  // slabs of at most 36 groups: 36 * 2112 B = 74 KB of tables (two workgroups
+  // per compute unit)
+  const int nslabs = (geo.G + 35) / 36;
+  const int slab = (geo.G + nslabs - 1) / nslabs;
+  size_t lds = (size_t)slab * kGroupStride;
+  if (lds < NW * R * sizeof(float)) lds = NW * R * sizeof(float);
+  const int blocks = (geo.m + R - 1) / R;
+  hipLaunchKernelGGL((gemv_rows_kernel<XT, AT, K, NW, NS>), dim3(blocks), dim3(NW * kWave), lds,
+                     stream, bits, scales, reinterpret_cast<const XT*>(x), y, geo.m, geo.G, slab);
+  return hipGetLastError() == hipSuccess ? MBOK_OK : MBOK_ERR_HIP;
+}
+
+template <typename XT, typename AT, int K, int NS>
+int launch_rows(const Geom& geo, const uint4* bits, const AT* scales, const void* x, float* y,
+                hipStream_t stream) {
+  switch (rows_waves()) {
+    case 4: return launch_rows_nw<XT, AT, K, 4, NS>(geo, bits, scales, x, y, stream);
+    case 16: return launch_rows_nw<XT, AT, K, 16, NS>(geo, bits, scales, x, y, stream);
+    default: return launch_rows_nw<XT, AT, K, 8, NS>(geo, bits, scales, x, y, stream);
+  }
 }
 
 template <typename XT, typename AT, int K>
-int launch_typed(const Geom& geo, const void* packed, const void* x, float* y,
+int launch_typed(const Geom& geo, const void* packed, const void* x, float* y, void* ws,
                  hipStream_t stream) {
   constexpr int NW = 16;
   const uint4* bits = reinterpret_cast<const uint4*>(packed);
   const AT* scales = reinterpret_cast<const AT*>(reinterpret_cast<const char*>(packed) +
                                                  geo.bits_bytes);
+  const int variant = variant_from_env();
+  if (variant == kRows) {
+    switch (rows_per_workgroup(geo.m)) {
+      case 64: return launch_rows<XT, AT, K, 1>(geo, bits, scales, x, y, stream);
+      case 32: return launch_rows<XT, AT, K, 2>(geo, bits, scales, x, y, stream);
+      default: return launch_rows<XT, AT, K, 4>(geo, bits, scales, x, y, stream);
+    }
+  }
+  if (variant == kSplit) {
+    int gpw, S;
+    gemv_split_shape(geo.RB, geo.G, &gpw, &S);
+    if (S == 1 || ws != nullptr) {
+      switch (gpw) {
+        case 1: return launch_split<XT, AT, K, 1>(geo, S, bits, scales, x, y, ws, stream);
+        case 2: return launch_split<XT, AT, K, 2>(geo, S, bits, scales, x, y, ws, stream);
+        case 3: return launch_split<XT, AT, K, 3>(geo, S, bits, scales, x, y, ws, stream);
+        default: return launch_split<XT, AT, K, 4>(geo, S, bits, scales, x, y, ws, stream);
+      }
+    }
+    // no workspace: whole rows per workgroup
+  }
   const int nslabs = (geo.G + kMaxSlabGroups - 1) / kMaxSlabGroups;
   const int slab = (geo.G + nslabs - 1) / nslabs;
   dim3 grid(geo.RB), block(NW * kWave);
-  if (variant_from_env() == kDirect) {
+  if (variant == kDirect) {
     const size_t lds = (size_t)(slab * kGroup > NW * kWave ? slab * kGroup : NW * kWave) *
                        sizeof(float);
     hipLaunchKernelGGL((gemv_direct_kernel<XT, AT, K, NW>), grid, block, lds, stream, bits,
@@ -279,12 +631,13 @@ int launch_typed(const Geom& geo, const void* packed, const void* x, float* y,
 }
 
 template <typename XT, typename AT>
-int launch_k(const Geom& geo, const void* packed, const void* x, float* y, hipStream_t s) {
+int launch_k(const Geom& geo, const void* packed, const void* x, float* y, void* ws,
+             hipStream_t s) {
   switch (geo.K) {
-    case 1: return launch_typed<XT, AT, 1>(geo, packed, x, y, s);
-    case 2: return launch_typed<XT, AT, 2>(geo, packed, x, y, s);
-    case 3: return launch_typed<XT, AT, 3>(geo, packed, x, y, s);
-    case 4: return launch_typed<XT, AT, 4>(geo, packed, x, y, s);
+    case 1: return launch_typed<XT, AT, 1>(geo, packed, x, y, ws, s);
+    case 2: return launch_typed<XT, AT, 2>(geo, packed, x, y, ws, s);
+    case 3: return launch_typed<XT, AT, 3>(geo, packed, x, y, ws, s);
+    case 4: return launch_typed<XT, AT, 4>(geo, packed, x, y, ws, s);
   }
   return MBOK_ERR_UNSUPPORTED;
 }
@@ -292,14 +645,14 @@ int launch_k(const Geom& geo, const void* packed, const void* x, float* y, hipSt
 }  // namespace
 
 int launch_gemv(const mbok_desc* d, const void* packed, const void* x, int32_t x_dtype,
-                float* y, hipStream_t stream) {
+                float* y, void* ws, hipStream_t stream) {
   const Geom geo = make_geom(d);
   const bool f16a = d->alpha_dtype == MBOK_F16;
   if (x_dtype == MBOK_BF16)
-    return f16a ? launch_k<uint16_t, uint16_t>(geo, packed, x, y, stream)
-                : launch_k<uint16_t, float>(geo, packed, x, y, stream);
-  return f16a ? launch_k<float, uint16_t>(geo, packed, x, y, stream)
-              : launch_k<float, float>(geo, packed, x, y, stream);
+    return f16a ? launch_k<uint16_t, uint16_t>(geo, packed, x, y, ws, stream)
+                : launch_k<uint16_t, float>(geo, packed, x, y, ws, stream);
+  return f16a ? launch_k<float, uint16_t>(geo, packed, x, y, ws, stream)
+              : launch_k<float, float>(geo, packed, x, y, ws, stream);
 }
 
 }  // namespace mbok

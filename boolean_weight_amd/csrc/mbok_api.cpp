@@ -78,14 +78,20 @@ int mbok_pack(const mbok_desc* d, const int8_t* signs, const void* alpha, void* 
   return mbok::launch_pack(d, signs, alpha, packed, (hipStream_t)stream);
 }
 
+size_t mbok_gemv_workspace_bytes(const mbok_desc* d) {
+  if (check_desc(d) != MBOK_OK) return 0;
+  return mbok::gemv_workspace_bytes(d);
+}
+
 int mbok_gemv(const mbok_desc* d, const void* packed, const void* x, int32_t x_dtype, float* y,
-              void* stream) {
+              void* workspace, void* stream) {
   int st = check_desc(d);
   if (st != MBOK_OK) return st;
   if (!packed || !x || !y) return MBOK_ERR_INVALID_ARG;
   if (x_dtype != MBOK_BF16 && x_dtype != MBOK_F32) return MBOK_ERR_DTYPE;
   if (!aligned(packed, 16) || !aligned(x, 16) || !aligned(y, 4)) return MBOK_ERR_ALIGN;
-  return mbok::launch_gemv(d, packed, x, x_dtype, y, (hipStream_t)stream);
+  if (workspace && !aligned(workspace, 256)) return MBOK_ERR_ALIGN;
+  return mbok::launch_gemv(d, packed, x, x_dtype, y, workspace, (hipStream_t)stream);
 }
 
 int mbok_gemm(const mbok_desc* d, const void* packed, const void* X, int32_t x_dtype, int64_t T,

@@ -14,7 +14,8 @@ int launch_residual_binarize(const mbok_desc* d, const float* W, int64_t ldw, in
 int launch_pack(const mbok_desc* d, const int8_t* signs, const void* alpha, void* packed,
                 hipStream_t stream);
 int launch_gemv(const mbok_desc* d, const void* packed, const void* x, int32_t x_dtype,
-                float* y, hipStream_t stream);
+                float* y, void* workspace, hipStream_t stream);
+size_t gemv_workspace_bytes(const mbok_desc* d);
 int launch_gemm(const mbok_desc* d, const void* packed, const void* X, int64_t T, int64_t ldx,
                 float* Y, int64_t ldy, hipStream_t stream);
 

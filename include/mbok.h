@@ -169,20 +169,34 @@ int mbok_pack(const mbok_desc* d, const int8_t* signs, const void* alpha,
               void* packed, void* stream);
 
 /*
+ * Bytes of the workspace mbok_gemv uses for this shape (0 when it needs
+ * none).  Host only; 0 for a NULL or invalid descriptor.
+ */
+size_t mbok_gemv_workspace_bytes(const mbok_desc* d);
+
+/*
  * Decode product for one token ([RN] 关键设计: Wx splits into K Boolean
  * matrix-vector products, so each weight multiply becomes an add or a
  * subtract of an activation; [RN] 局限与展望: activations stay full
  * precision):
  *     y[i] = sum_k sum_g alpha_k[i,g] * sum_{j in group g} b_k[i,j] * x[j]
  * with fp32 accumulation.
- *  packed   device, MBOK_LAYOUT_L64 buffer of this descriptor.
- *  x        device, n values of x_dtype (MBOK_BF16 or MBOK_F32).
- *  y        device fp32 [m]; overwritten (not accumulated).
+ *  packed    device, MBOK_LAYOUT_L64 buffer of this descriptor.
+ *  x         device, n values of x_dtype (MBOK_BF16 or MBOK_F32).
+ *  y         device fp32 [m]; overwritten (not accumulated).
+ *  workspace device, mbok_gemv_workspace_bytes(d) bytes, 256-byte aligned,
+ *            or NULL.  It receives the partial sums of column slices, so that
+ *            a layer is spread over every compute unit; a second small kernel
+ *            on the same stream adds them in a fixed order.  Its contents
+ *            need no initialisation and are meaningless after the call.
+ *            Calls that may run at the same time (other streams) need
+ *            distinct workspaces.  NULL selects whole-row workgroups (no
+ *            workspace, one kernel, fewer workgroups; slower for small m).
  * Errors: INVALID_ARG, SHAPE/UNSUPPORTED, DTYPE (x_dtype), ALIGN (packed and
- * x 16-byte aligned, y 4-byte aligned), HIP.
+ * x 16-byte aligned, y 4-byte aligned, workspace 256-byte aligned), HIP.
  */
 int mbok_gemv(const mbok_desc* d, const void* packed, const void* x,
-              int32_t x_dtype, float* y, void* stream);
+              int32_t x_dtype, float* y, void* workspace, void* stream);
 
 /*
  * The same product for T tokens:  Y[t, i] = sum_j W_hat[i, j] * X[t, j].

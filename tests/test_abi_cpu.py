@@ -106,19 +106,20 @@ def test_compute_calls_validate_before_launch(lib):
     d = _desc()
     R = ctypes.byref
     # NULL pointers
-    assert lib.mbok_gemv(R(d), None, A16, bw.MBOK_BF16, A16, None) == -1
-    assert lib.mbok_gemv(R(d), A16, None, bw.MBOK_BF16, A16, None) == -1
-    assert lib.mbok_gemv(R(d), A16, A16, bw.MBOK_BF16, None, None) == -1
+    assert lib.mbok_gemv(R(d), None, A16, bw.MBOK_BF16, A16, None, None) == -1
+    assert lib.mbok_gemv(R(d), A16, None, bw.MBOK_BF16, A16, None, None) == -1
+    assert lib.mbok_gemv(R(d), A16, A16, bw.MBOK_BF16, None, None, None) == -1
     assert lib.mbok_gemm(R(d), None, A16, bw.MBOK_BF16, 4, 256, A16, 64, None) == -1
     assert lib.mbok_pack(R(d), None, A16, A16, None) == -1
     assert lib.mbok_residual_binarize(R(d), None, 256, A16, A16, None, None) == -1
     # bad dtype
-    assert lib.mbok_gemv(R(d), A16, A16, bw.MBOK_F16, A16, None) == -3
+    assert lib.mbok_gemv(R(d), A16, A16, bw.MBOK_F16, A16, None, None) == -3
     assert lib.mbok_gemm(R(d), A16, A16, bw.MBOK_F32, 4, 256, A16, 64, None) == -3
     # misalignment
-    assert lib.mbok_gemv(R(d), MIS, A16, bw.MBOK_BF16, A16, None) == -4
-    assert lib.mbok_gemv(R(d), A16, MIS, bw.MBOK_BF16, A16, None) == -4
-    assert lib.mbok_gemv(R(d), A16, A16, bw.MBOK_BF16, A16 + 1, None) == -4
+    assert lib.mbok_gemv(R(d), MIS, A16, bw.MBOK_BF16, A16, None, None) == -4
+    assert lib.mbok_gemv(R(d), A16, MIS, bw.MBOK_BF16, A16, None, None) == -4
+    assert lib.mbok_gemv(R(d), A16, A16, bw.MBOK_BF16, A16 + 1, None, None) == -4
+    assert lib.mbok_gemv(R(d), A16, A16, bw.MBOK_BF16, A16, A16 + 16, None) == -4
     assert lib.mbok_gemm(R(d), A16, A16, bw.MBOK_BF16, 4, 260, A16, 64, None) == -4
     assert lib.mbok_pack(R(d), MIS, A16, A16, None) == -4
     assert lib.mbok_residual_binarize(R(d), A16, 258, A16, A16, None, None) == -4
@@ -130,12 +131,12 @@ def test_compute_calls_validate_before_launch(lib):
     assert lib.mbok_gemm(R(d), A16, A16, bw.MBOK_BF16, 4, 256, A16, 63, None) == -1
     assert lib.mbok_residual_binarize(R(d), A16, 128, A16, A16, None, None) == -1
     # descriptors edited by hand
-    assert lib.mbok_gemv(R(_desc(group=64)), A16, A16, bw.MBOK_BF16, A16, None) == -6
-    assert lib.mbok_gemv(R(_desc(layout=2)), A16, A16, bw.MBOK_BF16, A16, None) == -6
-    assert lib.mbok_gemv(R(_desc(K=9)), A16, A16, bw.MBOK_BF16, A16, None) == -6
-    assert lib.mbok_gemv(R(_desc(n=200)), A16, A16, bw.MBOK_BF16, A16, None) == -2
-    assert lib.mbok_gemv(R(_desc(alpha_dtype=2)), A16, A16, bw.MBOK_BF16, A16, None) == -3
-    assert lib.mbok_gemv(None, A16, A16, bw.MBOK_BF16, A16, None) == -1
+    assert lib.mbok_gemv(R(_desc(group=64)), A16, A16, bw.MBOK_BF16, A16, None, None) == -6
+    assert lib.mbok_gemv(R(_desc(layout=2)), A16, A16, bw.MBOK_BF16, A16, None, None) == -6
+    assert lib.mbok_gemv(R(_desc(K=9)), A16, A16, bw.MBOK_BF16, A16, None, None) == -6
+    assert lib.mbok_gemv(R(_desc(n=200)), A16, A16, bw.MBOK_BF16, A16, None, None) == -2
+    assert lib.mbok_gemv(R(_desc(alpha_dtype=2)), A16, A16, bw.MBOK_BF16, A16, None, None) == -3
+    assert lib.mbok_gemv(None, A16, A16, bw.MBOK_BF16, A16, None, None) == -1
 
 
 def test_binding_refuses_host_tensors():

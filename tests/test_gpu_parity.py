@@ -35,15 +35,29 @@ def _gpu():
     torch.cuda.synchronize()
 
 
-@pytest.fixture(params=["lut", "direct"])
+GEMV_VARIANTS = {
+    "rows16": {"MBOK_GEMV_VARIANT": "rows", "MBOK_GEMV_R": "16"},
+    "rows32": {"MBOK_GEMV_VARIANT": "rows", "MBOK_GEMV_R": "32"},
+    "rows64": {"MBOK_GEMV_VARIANT": "rows", "MBOK_GEMV_R": "64", "MBOK_GEMV_NW": "4"},
+    "split": {"MBOK_GEMV_VARIANT": "split"},
+    "fullrow": {"MBOK_GEMV_VARIANT": "fullrow"},
+    "direct": {"MBOK_GEMV_VARIANT": "direct"},
+}
+
+
+@pytest.fixture(params=list(GEMV_VARIANTS))
 def gemv_variant(request):
-    old = os.environ.get("MBOK_GEMV_VARIANT")
-    os.environ["MBOK_GEMV_VARIANT"] = request.param
+    keys = ("MBOK_GEMV_VARIANT", "MBOK_GEMV_R", "MBOK_GEMV_NW")
+    old = {k: os.environ.get(k) for k in keys}
+    for k in keys:
+        os.environ.pop(k, None)
+    os.environ.update(GEMV_VARIANTS[request.param])
     yield request.param
-    if old is None:
-        os.environ.pop("MBOK_GEMV_VARIANT", None)
-    else:
-        os.environ["MBOK_GEMV_VARIANT"] = old
+    for k, v in old.items():
+        if v is None:
+            os.environ.pop(k, None)
+        else:
+            os.environ[k] = v
 
 
 def quantize_on_gpu(W: np.ndarray, K: int, dt: str):
@@ -230,6 +244,37 @@ def test_gemv_k_sweep_first_linear(cfg, K):
     S, A, _ = oracle.residual_binarize(W[rows], K, alpha_dtype=dt)
     ratio = oracle.max_error_ratio(y[rows], oracle.product(S, A, x), oracle.bound(S, A, x))
     assert ratio <= TOL, ratio
+
+
+def test_gemv_workspace_shared_across_shapes_and_garbage():
+    """One workspace serves every shape, whatever it holds beforehand."""
+    say("gemv shared workspace")
+    shapes = [(4096, 4096, 2), (300, 11008, 3), (11008, 4096, 3), (64, 13824, 1)]
+    need = max(bw.mbok_gemv_workspace_bytes(bw.mbok_desc_init(m, n, K, bw.MBOK_F16))
+               for m, n, K in shapes)
+    assert need > 0
+    ws = torch.full((need + 4096,), 0x7f, dtype=torch.uint8, device=DEV)
+    for rep in range(2):
+        for (m, n, K) in shapes:
+            S = syn.random_signs(K, m, n, seed=m + n)
+            A = syn.exact_alpha(K, m, n // 128, seed=K).astype(np.float16)
+            x = syn.exact_activations(1, n, seed=n)[0]
+            d, packed = pack_on_gpu(S, A, "f16")
+            y = torch.empty(m, dtype=torch.float32, device=DEV)
+            bw.mbok_gemv(d, packed, x_to_dev(x, "bf16"), y, workspace=ws)
+            assert np.array_equal(y.cpu().numpy().astype(np.float64), oracle.product(S, A, x)), (m, n, K)
+
+
+def test_gemv_without_workspace_matches():
+    say("gemv without workspace")
+    K, m, n = 3, 500, 4096
+    S = syn.random_signs(K, m, n, seed=3)
+    A = syn.exact_alpha(K, m, n // 128, seed=4).astype(np.float16)
+    x = syn.exact_activations(1, n, seed=5)[0]
+    d, packed = pack_on_gpu(S, A, "f16")
+    y = torch.empty(m, dtype=torch.float32, device=DEV)
+    bw.mbok_gemv(d, packed, x_to_dev(x, "bf16"), y, workspace=None)
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), oracle.product(S, A, x))
 
 
 def test_gemv_config1_full_oracle():
