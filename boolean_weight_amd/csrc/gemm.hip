@@ -1,17 +1,370 @@
-// Multi-token product Y = X . W_hat^T (interim: one decode launch per token).
+// Multi-token product Y = X . W_hat^T on the matrix cores (gfx950).
+//
+// "Highly Efficient and Effective LLMs with Multi-Boolean Architectures",
+// Paper-Notes reading note, 关键设计: W ~ sum_k alpha_k B_k with group-wise
+// scales; with many tokens the product is a dense contraction, so each tile
+// of W_hat = sum_k alpha_k (.) B_k is formed once per workgroup, rounded to
+// bf16 and contracted with the bf16 activations by MFMA with fp32
+// accumulation.
+//
+// Workgroup tile: 256 tokens x 256 output rows, 4 wavefronts of 128 x 128
+// (4 x 4 blocks of v_mfma_f32_32x32x16_bf16, 256 accumulator registers per
+// lane).  The contraction runs in steps of 64 input columns (half a scale
+// group); X and W_hat tiles of a step live in LDS as bf16 rows padded to 144
+// bytes (conflict-free 16-byte fragment reads and writes), double-buffered so
+// that the next step's loads and unpacking overlap this step's MFMAs.
+//
+// Unpacking (one thread per output row): for each (row, group) the 2^K level
+// values sum_k (+-alpha_k) are formed in fp32 and rounded to bf16 once; their
+// low and high bytes are kept "byte-planar" in two registers each (K <= 3).
+// In the L64 word order the K sign bits of 4 consecutive columns 4q..4q+3 sit
+// at bit q of the word's 4 bytes, so the per-byte level indices of a quad are
+// ((W1 >> q) & 0x01010101) | ((W2 >> q) & ..) << 1 | ((W3 >> q) & ..) << 2, and
+// v_perm_b32 turns that selector into 4 low bytes and 4 high bytes of bf16
+// weights at once; two more perms interleave them into natural column order.
 #include "mbok_device.h"
 #include "mbok_launch.h"
 
 namespace mbok {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+constexpr int BT = 256;         // tokens per workgroup tile
+constexpr int BN = 256;         // output rows per workgroup tile
+constexpr int BK = 64;          // input columns per step
+constexpr int LDS_STRIDE = 72;  // bf16 elements per LDS row (64 + 8 padding)
+constexpr int TILE_ELEMS = 256 * LDS_STRIDE;
+constexpr int GEMM_THREADS = 256;
+
+__device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
+  const __bf16 ha = (__bf16)a, hb = (__bf16)b;  // nearest-even
+  return (uint32_t)__builtin_bit_cast(uint16_t, ha) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+
+// Byte-planar bf16 levels of one (row, group): lo_a/hi_a hold the low/high
+// bytes of levels 0..3, lo_b/hi_b of levels 4..7.  Level index bit k-1 is the
+// sign bit of kernel k (1 = +alpha_k).
+struct Levels {
+  uint32_t lo_a, lo_b, hi_a, hi_b;
+};
+
+template <int K>
+__device__ __forceinline__ Levels make_levels(const float* a) {
+  float l[8];
+#pragma unroll
+  for (int idx = 0; idx < 8; ++idx) {
+    float v = (idx & 1) ? a[0] : -a[0];
+    if (K >= 2) v += (idx & 2) ? a[1] : -a[1];
+    if (K >= 3) v += (idx & 4) ? a[2] : -a[2];
+    l[idx] = v;
+  }
+  const uint32_t p01 = bf16_pair(l[0], l[1]), p23 = bf16_pair(l[2], l[3]);
+  const uint32_t p45 = bf16_pair(l[4], l[5]), p67 = bf16_pair(l[6], l[7]);
+  Levels L;
+  // v_perm_b32(s0, s1, sel): selector byte 0..3 picks s1 bytes, 4..7 s0 bytes
+  L.lo_a = __builtin_amdgcn_perm(p23, p01, 0x06040200u);
+  L.hi_a = __builtin_amdgcn_perm(p23, p01, 0x07050301u);
+  L.lo_b = __builtin_amdgcn_perm(p67, p45, 0x06040200u);
+  L.hi_b = __builtin_amdgcn_perm(p67, p45, 0x07050301u);
+  return L;
+}
+
+// Unpack one 32-column sign word per kernel (w[k]) into 32 bf16 weights in
+// natural column order: out[2q], out[2q+1] hold columns 4q..4q+3.
+template <int K>
+__device__ __forceinline__ void unpack_word(const uint32_t* w, const Levels& L, uint32_t* out) {
+  constexpr uint32_t M = 0x11111111u;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    // nibble j = 2e + a of V holds the level index of quad q = 4a + b, element e
+    uint32_t V = (w[0] >> b) & M;
+    if (K >= 2) V |= ((w[1] >> b) & M) << 1;
+    if (K >= 3) V |= ((w[2] >> b) & M) << 2;
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const int q = 4 * a + b;
+      const uint32_t sel = (a ? (V >> 4) : V) & 0x0f0f0f0fu;
+      const uint32_t lo = __builtin_amdgcn_perm(L.lo_b, L.lo_a, sel);
+      const uint32_t hi = __builtin_amdgcn_perm(L.hi_b, L.hi_a, sel);
+      out[2 * q] = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+      out[2 * q + 1] = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+    }
+  }
+}
+
+// K = 4 (16 levels): direct fp32 sums, then bf16.
+__device__ __forceinline__ void unpack_word_k4(const uint32_t* w, const float* a, uint32_t* out) {
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float s = 0.f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) s += ((w[k] >> (8 * e + q)) & 1u) ? a[k] : -a[k];
+      v[e] = s;
+    }
+    out[2 * q] = bf16_pair(v[0], v[1]);
+    out[2 * q + 1] = bf16_pair(v[2], v[3]);
+  }
+}
+
+// Selector words of one 32-column sign word per kernel: V[b] nibble 2e + a is
+// the level index of quad q = 4a + b, element e (see unpack_word).
+template <int K>
+__device__ __forceinline__ void word_selectors(const uint32_t* w, uint32_t* V) {
+  constexpr uint32_t M = 0x11111111u;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    uint32_t v = (w[0] >> b) & M;
+    if (K >= 2) v |= ((w[1] >> b) & M) << 1;
+    if (K >= 3) v |= ((w[2] >> b) & M) << 2;
+    V[b] = v;
+  }
+}
+
+// Quads 4a .. 4a+3 of a word (16 columns 16a .. 16a+15) as 8 bf16 pairs.
+__device__ __forceinline__ void unpack_quads(const uint32_t* V, int a, const Levels& L,
+                                             uint32_t* out) {
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const uint32_t sel = (a ? (V[b] >> 4) : V[b]) & 0x0f0f0f0fu;
+    const uint32_t lo = __builtin_amdgcn_perm(L.lo_b, L.lo_a, sel);
+    const uint32_t hi = __builtin_amdgcn_perm(L.hi_b, L.hi_a, sel);
+    out[2 * b] = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+    out[2 * b + 1] = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+  }
+}
+
+template <typename AT, int K>
+__global__ void __launch_bounds__(GEMM_THREADS) gemm_mfma_kernel(
+    const uint2* __restrict__ bits, const AT* __restrict__ scales, const uint16_t* __restrict__ X,
+    int64_t ldx, float* __restrict__ Y, int64_t ldy, int T, int m, int m_pad, int G) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  // buffer b: activations at smem + 2b * TILE_ELEMS, weights right after
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wt = wave >> 1, wn = wave & 1;
+  const int t0 = blockIdx.y * BT;
+  const int n0 = blockIdx.x * BN;
+  const int S = G * 2;  // steps of 64 columns
+
+  // unpack role: thread = output row n0 + tid; rows past m_pad read row
+  // m_pad - 1 and are zeroed (branch-free)
+  const int row = n0 + tid;
+  const bool row_ok = row < m_pad;
+  const int rowc = row_ok ? row : m_pad - 1;
+  const int rb = rowc / kRowBlock, rr = rowc % kRowBlock;
+  const uint2* bits_row = bits + 2 * ((int64_t)rb * G * K * kRowBlock + rr);
+  const AT* scales_row = scales + (int64_t)rb * G * K * kRowBlock + rr;
+
+  // X copy role: segment j of a step = token tid/8 + 32j, 8 columns (tid%8)*8
+  const int xpart = tid & 7;
+  const uint16_t* xrow[8];
+  bool xok[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int t = t0 + (tid >> 3) + 32 * j;
+    xok[j] = t < T;
+    xrow[j] = X + (int64_t)(xok[j] ? t : T - 1) * ldx + xpart * 8;
+  }
+
+  struct StepRegs {
+    uint4 x[8];
+    uint2 w[K];
+    float a[K];
+  };
+  StepRegs R0, R1;
+
+  auto load_step = [&](int s, StepRegs& R) {
+    const int g = s >> 1, half = s & 1;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) R.x[j] = *reinterpret_cast<const uint4*>(xrow[j] + s * BK);
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const uint32_t c = (uint32_t)(g * K + k) * kRowBlock;
+      R.w[k] = bits_row[2 * c + half];
+      R.a[k] = alpha_to_f32<AT>(scales_row[c]);
+    }
+  };
+  // zero what lies outside the problem (tokens >= T, rows >= m_pad)
+  auto mask_step = [&](StepRegs& R) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (!xok[j]) R.x[j] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      R.w[k] = row_ok ? R.w[k] : make_uint2(0u, 0u);
+      R.a[k] = row_ok ? R.a[k] : 0.f;
+    }
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int lrow = lane & 31, lk = (lane >> 5) * 8;
+  Levels L;
+
+  // One step: MFMAs on buffer cb while the registers R (step sn) are written
+  // to buffer 1-cb, a quarter per 16-column sub-step.  EVEN: sn starts a group
+  // (new levels).
+  auto step = [&](int cb, StepRegs& R, bool even) {
+    mask_step(R);
+    if (K <= 3 && even) L = make_levels<K>(R.a);
+    const uint16_t* xs = smem + 2 * cb * TILE_ELEMS + (wt * 128 + lrow) * LDS_STRIDE + lk;
+    const uint16_t* ws = smem + (2 * cb + 1) * TILE_ELEMS + (wn * 128 + lrow) * LDS_STRIDE + lk;
+    uint16_t* xd = smem + 2 * (cb ^ 1) * TILE_ELEMS + (tid >> 3) * LDS_STRIDE + xpart * 8;
+    uint4* wd = reinterpret_cast<uint4*>(smem + (2 * (cb ^ 1) + 1) * TILE_ELEMS + tid * LDS_STRIDE);
+    uint32_t V[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      bf16x8 av[4], bv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        av[i] = *reinterpret_cast<const bf16x8*>(xs + i * 32 * LDS_STRIDE + 16 * kk);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        bv[j] = *reinterpret_cast<const bf16x8*>(ws + j * 32 * LDS_STRIDE + 16 * kk);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+      // a quarter of the next step: 2 activation segments, 16 weight columns
+      *reinterpret_cast<uint4*>(xd + (2 * kk) * 32 * LDS_STRIDE) = R.x[2 * kk];
+      *reinterpret_cast<uint4*>(xd + (2 * kk + 1) * 32 * LDS_STRIDE) = R.x[2 * kk + 1];
+      uint32_t out[8];
+      if (K <= 3) {
+        if ((kk & 1) == 0) {
+          uint32_t w[K];
+#pragma unroll
+          for (int k = 0; k < K; ++k) w[k] = (kk >> 1) ? R.w[k].y : R.w[k].x;
+          word_selectors<K>(w, V);
+        }
+        unpack_quads(V, kk & 1, L, out);
+      } else {
+        uint32_t w[K], o32[16];
+#pragma unroll
+        for (int k = 0; k < K; ++k) w[k] = (kk >> 1) ? R.w[k].y : R.w[k].x;
+        unpack_word_k4(w, R.a, o32);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) out[q] = o32[8 * (kk & 1) + q];
+      }
+      wd[2 * kk] = make_uint4(out[0], out[1], out[2], out[3]);
+      wd[2 * kk + 1] = make_uint4(out[4], out[5], out[6], out[7]);
+      // interleave: each MFMA followed by a few vector / LDS instructions
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+      }
+    }
+  };
+
+  // prologue: step 0 into buffer 0
+  load_step(0, R0);
+  load_step(1, R1);
+  mask_step(R0);
+  {
+    if (K <= 3) L = make_levels<K>(R0.a);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      *reinterpret_cast<uint4*>(smem + (tid >> 3) * LDS_STRIDE + xpart * 8 + j * 32 * LDS_STRIDE) =
+          R0.x[j];
+    uint4* wd = reinterpret_cast<uint4*>(smem + TILE_ELEMS + tid * LDS_STRIDE);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t w[K], out[16];
+#pragma unroll
+      for (int k = 0; k < K; ++k) w[k] = h ? R0.w[k].y : R0.w[k].x;
+      if (K <= 3)
+        unpack_word<K>(w, L, out);
+      else
+        unpack_word_k4(w, R0.a, out);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        wd[4 * h + j] = make_uint4(out[4 * j], out[4 * j + 1], out[4 * j + 2], out[4 * j + 3]);
+    }
+  }
+  __syncthreads();
+  // steady state, two steps per iteration; loads run two steps ahead (the
+  // step index is clamped at the end, the extra loads are never used)
+  for (int s = 0; s < S; s += 2) {
+    load_step(min(s + 2, S - 1), R0);
+    step(0, R1, false);  // compute step s, store step s+1 (odd)
+    __syncthreads();
+    load_step(min(s + 3, S - 1), R1);
+    step(1, R0, true);  // compute step s+1, store step s+2 (even)
+    __syncthreads();
+  }
+
+  // C layout: lane l, register r -> token 8(r/4) + 4(l/32) + r%4, row l%32
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + wn * 128 + j * 32 + lrow;
+      if (n >= m) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = t0 + wt * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (t < T) Y[(int64_t)t * ldy + n] = acc[i][j][r];
+      }
+    }
+}
+
+template <typename AT>
+int launch_mfma(const Geom& geo, const void* packed, const void* X, int64_t T, int64_t ldx,
+                float* Y, int64_t ldy, hipStream_t stream) {
+  const uint2* bits = reinterpret_cast<const uint2*>(packed);
+  const AT* scales = reinterpret_cast<const AT*>(reinterpret_cast<const char*>(packed) +
+                                                 geo.bits_bytes);
+  const size_t lds = 4 * TILE_ELEMS * sizeof(uint16_t);
+  dim3 grid((geo.m + BN - 1) / BN, (unsigned)((T + BT - 1) / BT));
+  const int m_pad = geo.RB * kRowBlock;
+  const uint16_t* Xb = reinterpret_cast<const uint16_t*>(X);
+  switch (geo.K) {
+    case 1:
+      hipLaunchKernelGGL((gemm_mfma_kernel<AT, 1>), grid, dim3(GEMM_THREADS), lds, stream, bits,
+                         scales, Xb, ldx, Y, ldy, (int)T, geo.m, m_pad, geo.G);
+      break;
+    case 2:
+      hipLaunchKernelGGL((gemm_mfma_kernel<AT, 2>), grid, dim3(GEMM_THREADS), lds, stream, bits,
+                         scales, Xb, ldx, Y, ldy, (int)T, geo.m, m_pad, geo.G);
+      break;
+    case 3:
+      hipLaunchKernelGGL((gemm_mfma_kernel<AT, 3>), grid, dim3(GEMM_THREADS), lds, stream, bits,
+                         scales, Xb, ldx, Y, ldy, (int)T, geo.m, m_pad, geo.G);
+      break;
+    default:
+      hipLaunchKernelGGL((gemm_mfma_kernel<AT, 4>), grid, dim3(GEMM_THREADS), lds, stream, bits,
+                         scales, Xb, ldx, Y, ldy, (int)T, geo.m, m_pad, geo.G);
+      break;
+  }
+  return hipGetLastError() == hipSuccess ? MBOK_OK : MBOK_ERR_HIP;
+}
+
+}  // namespace
 
 int launch_gemm(const mbok_desc* d, const void* packed, const void* X, int64_t T, int64_t ldx,
                 float* Y, int64_t ldy, hipStream_t stream) {
-  const uint16_t* Xb = reinterpret_cast<const uint16_t*>(X);
-  for (int64_t t = 0; t < T; ++t) {
-    const int st = launch_gemv(d, packed, Xb + t * ldx, MBOK_BF16, Y + t * ldy, nullptr, stream);
-    if (st != MBOK_OK) return st;
-  }
-  return MBOK_OK;
+  const Geom geo = make_geom(d);
+  if (T == 1) return launch_gemv(d, packed, X, MBOK_BF16, Y, nullptr, stream);
+  if (T > 65535LL * BT) return MBOK_ERR_SHAPE;
+  if (d->alpha_dtype == MBOK_F16)
+    return launch_mfma<uint16_t>(geo, packed, X, T, ldx, Y, ldy, stream);
+  return launch_mfma<float>(geo, packed, X, T, ldx, Y, ldy, stream);
 }
 
 }  // namespace mbok

@@ -143,31 +143,51 @@ __device__ __forceinline__ float lut_dot128(const uint4 b, uint32_t tab) {
 // likewise, then each entry address is one add of a selected byte to `tab`
 // (any table base works: it is an ordinary register operand).  2.5 VALU
 // operations per 4 weights.
-__device__ __forceinline__ float lut_dot128_sdwa(const uint4 b, uint32_t tab) {
+// 8 table addresses of one sign word (nibbles 0..7), one VOP2 add each.
+__device__ __forceinline__ void word_addresses(uint32_t w, uint32_t tab, uint32_t* a) {
+  const uint32_t ev = (w << 2) & 0x3c3c3c3cu;  // byte k: nibble 2k, times 4
+  const uint32_t od = (w >> 2) & 0x3c3c3c3cu;  // byte k: nibble 2k+1, times 4
+  asm("v_add_u32_sdwa %0, %8, %9 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0\n\t"
+      "v_add_u32_sdwa %1, %8, %10 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0\n\t"
+      "v_add_u32_sdwa %2, %8, %9 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1\n\t"
+      "v_add_u32_sdwa %3, %8, %10 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1\n\t"
+      "v_add_u32_sdwa %4, %8, %9 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2\n\t"
+      "v_add_u32_sdwa %5, %8, %10 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2\n\t"
+      "v_add_u32_sdwa %6, %8, %9 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3\n\t"
+      "v_add_u32_sdwa %7, %8, %10 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3"
+      : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]), "=&v"(a[5]),
+        "=&v"(a[6]), "=&v"(a[7])
+      : "v"(tab), "v"(ev), "v"(od));
+}
+
+// Sum of the 16 lookups of two sign words (w0 = word 2h, w1 = word 2h+1 of
+// the chunk): 16 addresses, then 16 LDS reads in flight, then a tree sum.
+__device__ __forceinline__ float lut_dot64_sdwa(uint32_t w0, uint32_t w1, uint32_t tab, int h) {
   typedef __attribute__((address_space(3))) const float lds_f32;
-  const uint32_t wv[4] = {b.x, b.y, b.z, b.w};
-  float part[4];
+  uint32_t ad[16];
+  word_addresses(w0, tab, ad);
+  word_addresses(w1, tab, ad + 8);
+  float v[16];
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const uint32_t ev = (wv[w] << 2) & 0x3c3c3c3cu;  // byte k: nibble 2k, times 4
-    const uint32_t od = (wv[w] >> 2) & 0x3c3c3c3cu;  // byte k: nibble 2k+1, times 4
-    uint32_t a0, a1, a2, a3, a4, a5, a6, a7;
-    MBOK_ADD_BYTE(a0, tab, ev, 0);
-    MBOK_ADD_BYTE(a1, tab, od, 0);
-    MBOK_ADD_BYTE(a2, tab, ev, 1);
-    MBOK_ADD_BYTE(a3, tab, od, 1);
-    MBOK_ADD_BYTE(a4, tab, ev, 2);
-    MBOK_ADD_BYTE(a5, tab, od, 2);
-    MBOK_ADD_BYTE(a6, tab, ev, 3);
-    MBOK_ADD_BYTE(a7, tab, od, 3);
-    const uint32_t ad[8] = {a0, a1, a2, a3, a4, a5, a6, a7};
-    float s = 0.f;
+  for (int q = 0; q < 16; ++q)
+    v[q] = reinterpret_cast<lds_f32*>((uintptr_t)ad[q])[(16 * h + q) * kTableFloats];
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
-      s += reinterpret_cast<lds_f32*>((uintptr_t)ad[q])[(w * 8 + q) * kTableFloats];
-    part[w] = s;
-  }
-  return (part[0] + part[1]) + (part[2] + part[3]);
+  for (int s = 8; s >= 1; s >>= 1)
+#pragma unroll
+    for (int q = 0; q < s; ++q) v[q] += v[q + s];
+  return v[0];
+}
+
+// The scheduling barriers keep the batches of successive half chunks apart,
+// so at most 16 lookups are in flight per wavefront (about what the LDS
+// counter tracks anyway) and register use stays low enough for 4+ waves per
+// SIMD.
+__device__ __forceinline__ float lut_dot128_sdwa(const uint4 b, uint32_t tab) {
+  const float lo = lut_dot64_sdwa(b.x, b.y, tab, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  const float hi = lut_dot64_sdwa(b.z, b.w, tab, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  return lo + hi;
 }
 
 // LDS byte address of a shared-memory pointer.
@@ -248,40 +268,52 @@ __global__ void __launch_bounds__(NW * kWave) gemv_lut_kernel(
 // next group's sign planes are loaded before the current one is summed.
 constexpr int kGroupStride = 2112;  // bytes between the tables of two groups
 
+// Activations of groups g0 .. g0+sg-1, staged as fp32 in table order: slot
+// 4t + j of group gl holds x[c0(t) + 4j], the column that bit j of table t
+// stands for (t = 8w + a, c0 = 32w + 16(a%2) + a/2).  One thread per 16-column
+// block (two 16-byte loads for bf16); block b of a group holds the columns of
+// tables 8(b/2) + 2e + b%2, e = 0..3, four values each.
 template <typename XT>
-__device__ __forceinline__ float load_x1(const XT* __restrict__ x, int64_t col);
-template <>
-__device__ __forceinline__ float load_x1<float>(const float* __restrict__ x, int64_t col) {
-  return x[col];
-}
-template <>
-__device__ __forceinline__ float load_x1<uint16_t>(const uint16_t* __restrict__ x, int64_t col) {
-  return bf16_bits_to_f32(x[col]);
-}
-
-// Tables of groups g0 .. g0+sg-1.  Work item u = (table t, quarter h) writes
-// entries 4h .. 4h+3 of table t (one float4); consecutive threads write
-// consecutive 16-byte slots, so the stores are free of bank conflicts.
-// Table t = 8w + a of a group covers columns c0 + 4j (j = 0..3) with
-// c0 = 32w + 16(a%2) + a/2; entry p = sum_j (bit j of p ? x : -x), and the
-// quarter h fixes bits 2 and 3 of p.
-template <typename XT>
-__device__ __forceinline__ void build_group_tables(const XT* __restrict__ x, int g0, int sg,
-                                                   float* lds, int tid, int nthreads) {
-  for (int u = tid; u < sg * kChunksPerGroup * 4; u += nthreads) {
-    const int h = u & 3;
-    const int t = (u >> 2) & (kChunksPerGroup - 1);
-    const int gl = u >> 7;
-    const int w = t >> 3, a = t & 7;
-    const int64_t c0 = (int64_t)(g0 + gl) * kGroup + 32 * w + 16 * (a & 1) + (a >> 1);
-    const float x0 = load_x1<XT>(x, c0), x1 = load_x1<XT>(x, c0 + 4);
-    const float x2 = load_x1<XT>(x, c0 + 8), x3 = load_x1<XT>(x, c0 + 12);
-    const float hi = ((h & 1) ? x2 : -x2) + ((h & 2) ? x3 : -x3);
-    float4* dst = reinterpret_cast<float4*>(lds + (gl * kGroupStride) / 4 + t * kTableFloats) + h;
-    *dst = make_float4(-x0 - x1 + hi, x0 - x1 + hi, -x0 + x1 + hi, x0 + x1 + hi);
+__device__ __forceinline__ void stage_x(const XT* __restrict__ x, int g0, int sg,
+                                        float* __restrict__ xs, int tid, int nthreads) {
+  for (int blk = tid; blk < sg * 8; blk += nthreads) {
+    float v[16];
+    load_x16<XT>(x, (int64_t)g0 * kGroup + 16 * blk, v);
+    const int gl = blk >> 3, bb = blk & 7;
+    float4* dst = reinterpret_cast<float4*>(xs + gl * kGroup) + 8 * (bb >> 1) + (bb & 1);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dst[2 * e] = make_float4(v[e], v[4 + e], v[8 + e], v[12 + e]);
   }
 }
 
+// Tables from staged activations: item u = (table t, quarter h) reads the
+// table's four activations with one 16-byte LDS read and writes entries
+// 4h .. 4h+3 (bits 2 and 3 of the entry index fixed by h) as one float4;
+// consecutive items write consecutive 16-byte slots, free of bank conflicts.
+__device__ __forceinline__ void build_tables_from_staged(const float* __restrict__ xs, int sg,
+                                                         float* __restrict__ tabs, int tid,
+                                                         int nthreads) {
+  for (int u = tid; u < sg * kChunksPerGroup * 4; u += nthreads) {
+    const int h = u & 3;
+    const int tg = u >> 2;  // table index within the slab
+    const int gl = tg >> 5, t = tg & 31;
+    const float4 q = reinterpret_cast<const float4*>(xs)[tg];
+    const float hi = ((h & 1) ? q.z : -q.z) + ((h & 2) ? q.w : -q.w);
+    const float sp = q.x + q.y, sm = q.x - q.y;
+    float4* dst = reinterpret_cast<float4*>(tabs + (gl * kGroupStride) / 4 + t * kTableFloats) + h;
+    *dst = make_float4(hi - sp, hi + sm, hi - sm, hi + sp);
+  }
+}
+
+// Row-slice variant: a wavefront covers R = 64/NS rows and NS column slices
+// (lane = c*R + r), a workgroup covers R rows and every column, so no
+// cross-workgroup step is needed and small layers still give m/R workgroups.
+// The NW*NS slices ("streams") of a workgroup take groups p, p+NW*NS, ...;
+// all streams of the workgroup read the same slab of tables.  Group tables
+// are kGroupStride = 2112 bytes apart (33 x 64): the NS slices of a
+// wavefront read consecutive groups, whose tables then start 16 banks apart,
+// so one ds_read of the whole wavefront stays free of bank conflicts.  The
+// sign planes of the next group are loaded while the current one is summed.
 template <typename XT, typename AT, int K, int NW, int NS>
 __global__ void __launch_bounds__(NW * kWave) gemv_rows_kernel(
     const uint4* __restrict__ bits, const AT* __restrict__ scales, const XT* __restrict__ x,
@@ -289,51 +321,63 @@ __global__ void __launch_bounds__(NW * kWave) gemv_rows_kernel(
   constexpr int R = kWave / NS;
   constexpr int NP = NW * NS;
   extern __shared__ float lds[];
+  float* xs = lds + (slab_groups * kGroupStride) / 4;  // staged activations after the tables
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int c = lane / R, r = lane % R;
   const int p = wave * NS + c;
   const int i = blockIdx.x * R + r;  // < m_pad: R divides the 64-row block
   const int rb = i / kRowBlock, rr = i % kRowBlock;
+  // chunk (g, k) of this row: bits_row[(g * K + k) * 64], 32-bit offsets
+  const uint4* bits_row = bits + (int64_t)rb * G * K * kRowBlock + rr;
+  const AT* scales_row = scales + (int64_t)rb * G * K * kRowBlock + rr;
   const uint32_t lbase = lds_addr(lds);
   float yacc = 0.f;
   for (int g0 = 0; g0 < G; g0 += slab_groups) {
     const int sg = min(slab_groups, G - g0);
-    if (g0 > 0) __syncthreads();
-    build_group_tables<XT>(x, g0, sg, lds, threadIdx.x, NW * kWave);
-    __syncthreads();
-    int gl = p;
-    uint4 b[K];
-    float a[K];
-    if (gl < sg) {
+    uint4 bA[K], bB[K];
+    float aA[K], aB[K];
+    if (p < sg) {
 #pragma unroll
       for (int k = 0; k < K; ++k) {
-        const int64_t cidx = (((int64_t)rb * G + g0 + gl) * K + k) * kRowBlock + rr;
-        b[k] = bits[cidx];
-        a[k] = alpha_to_f32<AT>(scales[cidx]);
+        const uint32_t o = (uint32_t)((g0 + p) * K + k) * kRowBlock;
+        bA[k] = bits_row[o];
+        aA[k] = alpha_to_f32<AT>(scales_row[o]);
       }
     }
-    while (gl < sg) {
-      const int gn = gl + NP;
-      uint4 bn[K];
-      float an[K];
-      if (gn < sg) {
+    if (g0 > 0) __syncthreads();
+    stage_x<XT>(x, g0, sg, xs, threadIdx.x, NW * kWave);
+    __syncthreads();
+    build_tables_from_staged(xs, sg, lds, threadIdx.x, NW * kWave);
+    __syncthreads();
+    for (int gl = p; gl < sg; gl += 2 * NP) {
+      const int g1 = gl + NP, g2 = gl + 2 * NP;
+      if (g1 < sg) {
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-          const int64_t cidx = (((int64_t)rb * G + g0 + gn) * K + k) * kRowBlock + rr;
-          bn[k] = bits[cidx];
-          an[k] = alpha_to_f32<AT>(scales[cidx]);
+          const uint32_t o = (uint32_t)((g0 + g1) * K + k) * kRowBlock;
+          bB[k] = bits_row[o];
+          aB[k] = alpha_to_f32<AT>(scales_row[o]);
         }
       }
-      const uint32_t tab = lbase + gl * kGroupStride;
+      {
+        const uint32_t tab = lbase + gl * kGroupStride;
 #pragma unroll
-      for (int k = 0; k < K; ++k) yacc = fmaf(a[k], lut_dot128_sdwa(b[k], tab), yacc);
-#pragma unroll
-      for (int k = 0; k < K; ++k) {
-        b[k] = bn[k];
-        a[k] = an[k];
+        for (int k = 0; k < K; ++k) yacc = fmaf(aA[k], lut_dot128_sdwa(bA[k], tab), yacc);
       }
-      gl = gn;
+      if (g2 < sg) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          const uint32_t o = (uint32_t)((g0 + g2) * K + k) * kRowBlock;
+          bA[k] = bits_row[o];
+          aA[k] = alpha_to_f32<AT>(scales_row[o]);
+        }
+      }
+      if (g1 < sg) {
+        const uint32_t tab = lbase + g1 * kGroupStride;
+#pragma unroll
+        for (int k = 0; k < K; ++k) yacc = fmaf(aB[k], lut_dot128_sdwa(bB[k], tab), yacc);
+      }
     }
   }
   // fixed-order sum over the NS slices of the wavefront, then over wavefronts
@@ -484,12 +528,20 @@ __global__ void __launch_bounds__(NW * kWave) gemv_direct_kernel(
 
 enum Variant { kSplit = 0, kFullRow = 1, kDirect = 2, kRows = 3 };
 
-int variant_from_env() {
+// Kernel choice by shape, from measurements on MI355X (per-launch times in
+// HIP graphs over a rotating pool): row slices of 16 rows for small layers
+// with K <= 2, column slices plus the reduce kernel for wide layers
+// (n >= 2m), whole-row workgroups otherwise.  MBOK_GEMV_VARIANT overrides
+// ("rows", "split", "fullrow", "direct") for measurements.
+int variant_for(const Geom& geo) {
   const char* v = getenv("MBOK_GEMV_VARIANT");
   if (v && strcmp(v, "direct") == 0) return kDirect;
   if (v && strcmp(v, "fullrow") == 0) return kFullRow;
   if (v && strcmp(v, "split") == 0) return kSplit;
-  return kRows;
+  if (v && strcmp(v, "rows") == 0) return kRows;
+  if (geo.n >= 2 * geo.m) return kSplit;
+  if (geo.K <= 2 && geo.m < 16384) return kRows;
+  return kFullRow;
 }
 
 constexpr int kSplitNW = 4;           // wavefronts per split workgroup
@@ -555,19 +607,19 @@ int rows_per_workgroup(int m) {
 
 int rows_waves() {
   const char* v = getenv("MBOK_GEMV_NW");
-  const int nw = v ? atoi(v) : 8;
-  return (nw == 4 || nw == 8 || nw == 16) ? nw : 8;
+  const int nw = v ? atoi(v) : 16;
+  return (nw == 4 || nw == 8 || nw == 16) ? nw : 16;
 }
 
 template <typename XT, typename AT, int K, int NW, int NS>
 int launch_rows_nw(const Geom& geo, const uint4* bits, const AT* scales, const void* x, float* y,
                    hipStream_t stream) {
   constexpr int R = kWave / NS;
-  // slabs of at most 36 groups: 36 * 2112 B = 74 KB of tables (two workgroups
-  // per compute unit)
-  const int nslabs = (geo.G + 35) / 36;
+  // slabs of at most 32 groups: 32 * (2112 + 512) B = 82 KB of tables and
+  // staged activations
+  const int nslabs = (geo.G + 31) / 32;
   const int slab = (geo.G + nslabs - 1) / nslabs;
-  size_t lds = (size_t)slab * kGroupStride;
+  size_t lds = (size_t)slab * kGroupStride + (size_t)slab * kGroup * sizeof(float);
   if (lds < NW * R * sizeof(float)) lds = NW * R * sizeof(float);
   const int blocks = (geo.m + R - 1) / R;
   hipLaunchKernelGGL((gemv_rows_kernel<XT, AT, K, NW, NS>), dim3(blocks), dim3(NW * kWave), lds,
@@ -592,7 +644,7 @@ int launch_typed(const Geom& geo, const void* packed, const void* x, float* y, v
   const uint4* bits = reinterpret_cast<const uint4*>(packed);
   const AT* scales = reinterpret_cast<const AT*>(reinterpret_cast<const char*>(packed) +
                                                  geo.bits_bytes);
-  const int variant = variant_from_env();
+  const int variant = variant_for(geo);
   if (variant == kRows) {
     switch (rows_per_workgroup(geo.m)) {
       case 64: return launch_rows<XT, AT, K, 1>(geo, bits, scales, x, y, stream);

@@ -318,3 +318,48 @@ def test_gemm_config3_tolerance(T):
         S, A, _ = oracle.residual_binarize(W[rows], 3, alpha_dtype="f16")
         ratio = oracle.max_error_ratio(Y[:, rows], oracle.product(S, A, X), oracle.bound(S, A, X))
         assert ratio <= TOL, (name, ratio)
+
+
+@pytest.mark.parametrize("K", [1, 2, 3, 4])
+@pytest.mark.parametrize("T,m,n", [(2, 65, 128), (33, 300, 384), (257, 256, 256), (300, 513, 640)])
+def test_gemm_prefill_exact_ragged(T, m, n, K):
+    say(f"gemm prefill exact T={T} m={m} n={n} K={K}")
+    S = syn.random_signs(K, m, n, seed=T + m + K)
+    A = syn.exact_alpha(K, m, n // 128, seed=T + K).astype(np.float16)
+    X = syn.exact_activations(T, n, seed=T * 3 + K)
+    d, packed = pack_on_gpu(S, A, "f16")
+    Y = gemm(d, packed, X, ldx=n + 16, ldy=m + 5)
+    assert np.array_equal(Y, oracle.product(S, A, X))
+
+
+def test_gemm_identity_activations_give_the_weights():
+    """X = identity rows (T = n) in the exact regime: Y = W_hat^T exactly,
+    which pins the operand orientation, k order and bf16 rounding of W_hat."""
+    say("gemm identity")
+    K, m, n = 3, 200, 384
+    S = syn.random_signs(K, m, n, seed=41)
+    A = syn.exact_alpha(K, m, n // 128, seed=42).astype(np.float16)
+    d, packed = pack_on_gpu(S, A, "f16")
+    Y = gemm(d, packed, np.eye(n, dtype=np.float32))
+    assert np.array_equal(Y, oracle.dequantize(S, A).T)
+
+
+def test_gemm_prefill_config5_tolerance():
+    """Config 5 at full size (11008 x 4096, K = 3, 2048 tokens) on the device;
+    the oracle quantizes and multiplies sampled output rows for every token."""
+    w = syn.WORKLOADS[5]
+    name, m, n = w["linears"][0]
+    T = w["T"][0]
+    say(f"gemm config 5 {m}x{n} T={T}")
+    W = syn.weight(m, n, syn.weight_seed(5))
+    X = syn.activations(T, n, syn.act_seed(5), "bf16")
+    d, signs, alpha, packed, flag = quantize_on_gpu(W, 3, "f16")
+    del signs, alpha
+    Y = gemm(d, packed, X)
+    rows = sample_rows(m, 24, 5)
+    S, A, _ = oracle.residual_binarize(W[rows], 3, alpha_dtype="f16")
+    ratio = oracle.max_error_ratio(Y[:, rows], oracle.product(S, A, X), oracle.bound(S, A, X))
+    assert ratio <= TOL, ratio
+    # determinism
+    Y2 = gemm(d, packed, X)
+    assert np.array_equal(Y, Y2)
