@@ -361,6 +361,7 @@ int launch_gemm(const mbok_desc* d, const void* packed, const void* X, int64_t T
                 float* Y, int64_t ldy, hipStream_t stream) {
   const Geom geo = make_geom(d);
   if (T == 1) return launch_gemv(d, packed, X, MBOK_BF16, Y, nullptr, stream);
+  if (T <= skinny_max_tokens()) return launch_skinny(d, packed, X, T, ldx, Y, ldy, stream);
   if (T > 65535LL * BT) return MBOK_ERR_SHAPE;
   if (d->alpha_dtype == MBOK_F16)
     return launch_mfma<uint16_t>(geo, packed, X, T, ldx, Y, ldy, stream);

@@ -533,6 +533,13 @@ enum Variant { kSplit = 0, kFullRow = 1, kDirect = 2, kRows = 3 };
 // with K <= 2, column slices plus the reduce kernel for wide layers
 // (n >= 2m), whole-row workgroups otherwise.  MBOK_GEMV_VARIANT overrides
 // ("rows", "split", "fullrow", "direct") for measurements.
+// bf16 activations may take the matrix-core kernel of the few-token product
+// (one token); MBOK_GEMV_VARIANT=skinny selects it.
+bool use_skinny_for_gemv(const Geom&) {
+  const char* v = getenv("MBOK_GEMV_VARIANT");
+  return v && strcmp(v, "skinny") == 0;
+}
+
 int variant_for(const Geom& geo) {
   const char* v = getenv("MBOK_GEMV_VARIANT");
   if (v && strcmp(v, "direct") == 0) return kDirect;
@@ -700,6 +707,8 @@ int launch_gemv(const mbok_desc* d, const void* packed, const void* x, int32_t x
                 float* y, void* ws, hipStream_t stream) {
   const Geom geo = make_geom(d);
   const bool f16a = d->alpha_dtype == MBOK_F16;
+  if (x_dtype == MBOK_BF16 && use_skinny_for_gemv(geo))
+    return launch_skinny(d, packed, x, 1, d->n, y, d->m, stream);
   if (x_dtype == MBOK_BF16)
     return f16a ? launch_k<uint16_t, uint16_t>(geo, packed, x, y, ws, stream)
                 : launch_k<uint16_t, float>(geo, packed, x, y, ws, stream);

@@ -16,6 +16,9 @@ int launch_pack(const mbok_desc* d, const int8_t* signs, const void* alpha, void
 int launch_gemv(const mbok_desc* d, const void* packed, const void* x, int32_t x_dtype,
                 float* y, void* workspace, hipStream_t stream);
 size_t gemv_workspace_bytes(const mbok_desc* d);
+int launch_skinny(const mbok_desc* d, const void* packed, const void* X, int64_t T, int64_t ldx,
+                  float* Y, int64_t ldy, hipStream_t stream);
+int skinny_max_tokens();
 int launch_gemm(const mbok_desc* d, const void* packed, const void* X, int64_t T, int64_t ldx,
                 float* Y, int64_t ldy, hipStream_t stream);
 

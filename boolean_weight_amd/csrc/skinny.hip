@@ -1,0 +1,243 @@
+// Few-token product Y = X . W_hat^T, 1..16 tokens, on the matrix cores
+// without rounding W_hat (gfx950).
+//
+// "Highly Efficient and Effective LLMs with Multi-Boolean Architectures",
+// Paper-Notes reading note, 关键设计: W ~ sum_k alpha_k B_k, one scale per
+// (row, 128-column group, kernel).  Per group the product splits exactly as
+//     y[t, row] = sum_g sum_k alpha_k[row, g] * S_k[t, row, g],
+//     S_k[t, row, g] = sum_{c in g} B_k[row, c] * x[t, c],
+// and S_k is a sum of +-x: the signs become bf16 +-1 (exact), the matrix cores
+// add and subtract the bf16 activations with fp32 accumulation, and alpha_k is
+// applied per group in fp32.  Unlike the prefill kernel nothing is rounded to
+// bf16 beyond the activations themselves, so results match the fp64
+// definition to fp32 accumulation error.
+//
+// One v_mfma_f32_16x16x32_bf16 covers 16 tokens x 16 rows x 32 columns:
+//   A (tokens x columns): lane (i, q) = (lane % 16, lane / 16) holds token i,
+//     columns 128g + 32q + 8s + 0..7 at step s (natural order, one 16-byte load);
+//   B (columns x rows): lane (i, q) holds row i of the tile, the same columns;
+//     they are word q of the row's 16-byte chunk for (g, k), where bit 8e + p
+//     is column 32q + 4p + e.  Two byte permutes spread the word into
+//     P01 = [b0, b0, b1, b1] and P23 = [b2, b2, b3, b3]; shifting each left by
+//     7 - p brings the bits of columns 4p + {0, 1} (P01) or 4p + {2, 3} (P23)
+//     to bits 15 and 31, and one v_and_or_b32 per dword makes them the sign
+//     bits of two bf16 ones.  The packed bit is 1 for +1, which gives a set
+//     sign bit, so the kernel accumulates -S_k and subtracts alpha_k * S.
+//   C: lane (i, q), register r = token 4q + r, row i.
+//
+// A workgroup owns 16 rows and all columns; its NW wavefronts take
+// contiguous ranges of groups and walk them 4 groups at a time.  For each
+// kernel, 16-lane block q loads the 16-byte chunks of the 16 rows for group
+// g + q (one 16-byte load per lane, four 256-byte runs per wavefront);
+// v_permlane32_swap + v_permlane16_swap then transpose the 4 x 4 (16-lane
+// block, word) matrix so that register j holds word q of group g + j, the B
+// operand of group g + j.  The scales are spread the same way (3 swaps).  The
+// partial sums of the wavefronts are added in LDS in a fixed wave order, so
+// results are deterministic.
+#include <stdlib.h>
+
+#include "mbok_device.h"
+#include "mbok_launch.h"
+
+namespace mbok {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+
+constexpr int kMaxSkinnyTokens = 16;
+
+// Two bf16 values of magnitude 1 whose sign bits are bits 15 and 31 of src:
+// (src & mask) | ones in one v_and_or_b32, mask = 0x80008000 in an SGPR and
+// ones = 0x3F803F80 in a VGPR (a VOP3 encoding takes no literal constants).
+__device__ __forceinline__ uint32_t signed_ones(uint32_t src, uint32_t mask, uint32_t ones) {
+  uint32_t d;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(src), "s"(mask), "v"(ones));
+  return d;
+}
+
+// Swap the upper 32 lanes of a with the lower 32 lanes of b.
+__device__ __forceinline__ void swap32(uint32_t& a, uint32_t& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+  a = r[0];
+  b = r[1];
+}
+
+// Swap the odd 16-lane rows of a with the even 16-lane rows of b.
+__device__ __forceinline__ void swap16(uint32_t& a, uint32_t& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+  a = r[0];
+  b = r[1];
+}
+
+template <typename AT>
+__device__ __forceinline__ uint32_t scale_bits(AT a);
+template <>
+__device__ __forceinline__ uint32_t scale_bits<float>(float a) { return __float_as_uint(a); }
+template <>
+__device__ __forceinline__ uint32_t scale_bits<uint16_t>(uint16_t a) { return a; }
+
+template <typename AT>
+__device__ __forceinline__ float scale_value(uint32_t b);
+template <>
+__device__ __forceinline__ float scale_value<float>(uint32_t b) { return __uint_as_float(b); }
+template <>
+__device__ __forceinline__ float scale_value<uint16_t>(uint32_t b) {
+  return f16_bits_to_f32((uint16_t)b);
+}
+
+// 4 x 4 transpose of (16-lane block, register): afterwards r[j] in block q is
+// what r[q] held in block j.
+__device__ __forceinline__ void transpose4(uint32_t (&r)[4]) {
+  swap32(r[0], r[2]);
+  swap32(r[1], r[3]);
+  swap16(r[0], r[1]);
+  swap16(r[2], r[3]);
+}
+
+// Broadcast of one value per 16-lane block: afterwards r[j] in every block is
+// the value v held in block j.
+__device__ __forceinline__ void spread4(uint32_t v, uint32_t (&r)[4]) {
+  uint32_t lo = v, hi = v;
+  swap32(lo, hi);  // blocks: lo = [v0 v1 v0 v1], hi = [v2 v3 v2 v3]
+  r[0] = lo, r[1] = lo, r[2] = hi, r[3] = hi;
+  swap16(r[0], r[1]);
+  swap16(r[2], r[3]);
+}
+
+template <typename AT, int K>
+__global__ void __launch_bounds__(1024) gemm_skinny_kernel(
+    const u32x4* __restrict__ bits, const AT* __restrict__ scales,
+    const uint16_t* __restrict__ X, int64_t ldx, float* __restrict__ Y, int64_t ldy, int T,
+    int m, int G) {
+  extern __shared__ float red[];  // [NW][4][64] partial sums
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int NW = blockDim.x >> 6;
+  const int i = lane & 15, q = lane >> 4;
+  const int tile = blockIdx.x;  // rows 16 * tile .. + 15, inside row block tile / 4
+  const int rb = tile >> 2;
+  const int rin = ((tile & 3) << 4) + i;
+  const int g0 = (int)((int64_t)wave * G / NW);
+  const int g1 = (int)((int64_t)(wave + 1) * G / NW);
+  const bool tok_ok = i < T;
+  const uint16_t* xrow = X + (int64_t)(tok_ok ? i : 0) * ldx + 32 * q;
+
+  const uint32_t mask = __builtin_amdgcn_readfirstlane(0x80008000u);
+  uint32_t ones;
+  asm("v_mov_b32 %0, 0x3f803f80" : "=v"(ones));
+
+  f32x4 yacc = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int gb = g0; gb < g1; gb += 4) {
+    const int nj = g1 - gb < 4 ? g1 - gb : 4;  // groups in this block
+    const int gq = gb + (q < nj ? q : nj - 1);  // group loaded by block q
+    const int64_t c = (int64_t)(rb * G + gq) * K * 64 + rin;
+    u32x4 wv[K];
+    AT av[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      wv[k] = bits[c + k * 64];
+      av[k] = scales[c + k * 64];
+    }
+    u32x4 xv[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        xv[j][s] = (tok_ok && j < nj)
+                       ? *reinterpret_cast<const u32x4*>(xrow + (int64_t)kGroup * (gb + j) + 8 * s)
+                       : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      uint32_t w[4] = {wv[k].x, wv[k].y, wv[k].z, wv[k].w};
+      transpose4(w);  // w[j] = word q of row i, group gb + j
+      uint32_t a[4];
+      spread4(scale_bits<AT>(av[k]), a);  // a[j] = scale of row i, group gb + j
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (j >= nj) break;
+        const uint32_t p01 = __builtin_amdgcn_perm(w[j], w[j], 0x01010000u);
+        const uint32_t p23 = __builtin_amdgcn_perm(w[j], w[j], 0x03030202u);
+        f32x4 S = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int se = 7 - 2 * s, so = 6 - 2 * s;  // columns 8s + 0..3, 8s + 4..7
+          const u32x4 b = u32x4{signed_ones(p01 << se, mask, ones),
+                                signed_ones(p23 << se, mask, ones),
+                                signed_ones(p01 << so, mask, ones),
+                                signed_ones(p23 << so, mask, ones)};
+          S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xv[j][s]),
+                                                      __builtin_bit_cast(bf16x8, b), S, 0, 0,
+                                                      0);
+        }
+        const float sc = scale_value<AT>(a[j]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) yacc[r] = __builtin_fmaf(-sc, S[r], yacc[r]);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int r = 0; r < 4; ++r) red[(wave * 4 + r) * 64 + lane] = yacc[r];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < 256; idx += blockDim.x) {
+    float sum = 0.f;
+    for (int w = 0; w < NW; ++w) sum += red[w * 256 + idx];
+    const int l = idx & 63, r = idx >> 6;
+    const int tok = 4 * (l >> 4) + r;
+    const int row = tile * 16 + (l & 15);
+    if (tok < T && row < m) Y[(int64_t)tok * ldy + row] = sum;
+  }
+}
+
+int env_int(const char* name, int fallback) {
+  const char* v = getenv(name);
+  return (v && *v) ? atoi(v) : fallback;
+}
+
+template <typename AT, int K>
+void launch_k(const Geom& geo, const u32x4* bits, const AT* scales, const uint16_t* X,
+              int64_t ldx, float* Y, int64_t ldy, int T, int NW, hipStream_t stream) {
+  const size_t lds = (size_t)NW * 256 * sizeof(float);
+  hipLaunchKernelGGL((gemm_skinny_kernel<AT, K>), dim3(geo.RB * 4), dim3(64 * NW), lds, stream,
+                     bits, scales, X, ldx, Y, ldy, T, geo.m, geo.G);
+}
+
+template <typename AT>
+int launch_at(const Geom& geo, const void* packed, const void* X, int64_t ldx, float* Y,
+              int64_t ldy, int T, hipStream_t stream) {
+  const u32x4* bits = reinterpret_cast<const u32x4*>(packed);
+  const AT* scales = reinterpret_cast<const AT*>(reinterpret_cast<const char*>(packed) +
+                                                 geo.bits_bytes);
+  const uint16_t* Xb = reinterpret_cast<const uint16_t*>(X);
+  // about 4800 wavefronts over the chip (~5 per SIMD), at most 16 per
+  // workgroup; measured best for 4096 to 27648 rows
+  const int tiles = geo.RB * 4;
+  int NW = env_int("MBOK_SKINNY_NW", (4800 + tiles / 2) / tiles);
+  if (NW > 16) NW = 16;
+  if (NW > geo.G) NW = geo.G;
+  if (NW < 1) NW = 1;
+  switch (geo.K) {
+    case 1: launch_k<AT, 1>(geo, bits, scales, Xb, ldx, Y, ldy, T, NW, stream); break;
+    case 2: launch_k<AT, 2>(geo, bits, scales, Xb, ldx, Y, ldy, T, NW, stream); break;
+    case 3: launch_k<AT, 3>(geo, bits, scales, Xb, ldx, Y, ldy, T, NW, stream); break;
+    default: launch_k<AT, 4>(geo, bits, scales, Xb, ldx, Y, ldy, T, NW, stream); break;
+  }
+  return hipGetLastError() == hipSuccess ? MBOK_OK : MBOK_ERR_HIP;
+}
+
+}  // namespace
+
+int skinny_max_tokens() { return kMaxSkinnyTokens; }
+
+int launch_skinny(const mbok_desc* d, const void* packed, const void* X, int64_t T, int64_t ldx,
+                  float* Y, int64_t ldy, hipStream_t stream) {
+  if (T < 1 || T > kMaxSkinnyTokens) return MBOK_ERR_SHAPE;
+  const Geom geo = make_geom(d);
+  if (d->alpha_dtype == MBOK_F16)
+    return launch_at<uint16_t>(geo, packed, X, ldx, Y, ldy, (int)T, stream);
+  return launch_at<float>(geo, packed, X, ldx, Y, ldy, (int)T, stream);
+}
+
+}  // namespace mbok

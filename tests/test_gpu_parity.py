@@ -42,22 +42,53 @@ GEMV_VARIANTS = {
     "split": {"MBOK_GEMV_VARIANT": "split"},
     "fullrow": {"MBOK_GEMV_VARIANT": "fullrow"},
     "direct": {"MBOK_GEMV_VARIANT": "direct"},
+    # matrix-core kernel of the few-token product at one token (bf16 x only;
+    # fp32 x keeps the table kernels)
+    "skinny": {"MBOK_GEMV_VARIANT": "skinny"},
+    "skinny_nw3": {"MBOK_GEMV_VARIANT": "skinny", "MBOK_SKINNY_NW": "3"},
 }
 
+ENV_KEYS = ("MBOK_GEMV_VARIANT", "MBOK_GEMV_R", "MBOK_GEMV_NW", "MBOK_SKINNY_NW")
 
-@pytest.fixture(params=list(GEMV_VARIANTS))
-def gemv_variant(request):
-    keys = ("MBOK_GEMV_VARIANT", "MBOK_GEMV_R", "MBOK_GEMV_NW")
-    old = {k: os.environ.get(k) for k in keys}
-    for k in keys:
+
+def _swap_env(new: dict) -> dict:
+    old = {k: os.environ.get(k) for k in ENV_KEYS}
+    for k in ENV_KEYS:
         os.environ.pop(k, None)
-    os.environ.update(GEMV_VARIANTS[request.param])
-    yield request.param
+    os.environ.update(new)
+    return old
+
+
+def _restore_env(old: dict):
     for k, v in old.items():
         if v is None:
             os.environ.pop(k, None)
         else:
             os.environ[k] = v
+
+
+@pytest.fixture(params=list(GEMV_VARIANTS))
+def gemv_variant(request):
+    old = _swap_env(GEMV_VARIANTS[request.param])
+    yield request.param
+    _restore_env(old)
+
+
+# launch shapes of the few-token kernel: wavefronts per workgroup (uneven
+# group ranges when NW does not divide G, one wavefront doing every group)
+SKINNY_SHAPES = {
+    "default": {},
+    "nw3": {"MBOK_SKINNY_NW": "3"},
+    "nw7": {"MBOK_SKINNY_NW": "7"},
+    "nw1": {"MBOK_SKINNY_NW": "1"},
+}
+
+
+@pytest.fixture(params=list(SKINNY_SHAPES))
+def skinny_shape(request):
+    old = _swap_env(SKINNY_SHAPES[request.param])
+    yield request.param
+    _restore_env(old)
 
 
 def quantize_on_gpu(W: np.ndarray, K: int, dt: str):
@@ -302,6 +333,40 @@ def test_gemm_exact_regime(T, K):
     d, packed = pack_on_gpu(S, A, "f16")
     Y = gemm(d, packed, X, ldx=n + 8, ldy=m + 3)
     assert np.array_equal(Y, oracle.product(S, A, X))
+
+
+@pytest.mark.parametrize("K", [1, 2, 3, 4])
+@pytest.mark.parametrize("T,m,n", [(2, 1, 128), (5, 65, 384), (8, 130, 1152), (16, 200, 640),
+                                   (13, 64, 2048)])
+@pytest.mark.parametrize("dt", ["f16", "f32"])
+def test_gemm_skinny_exact(T, m, n, K, dt, skinny_shape):
+    """Few-token kernel in the exact regime (integer x, power-of-two scales):
+    every launch shape gives the fp64 definition bit for bit, including
+    ragged rows, uneven group ranges and row/column leading dimensions."""
+    say(f"gemm skinny exact T={T} m={m} n={n} K={K} {dt} {skinny_shape}")
+    S = syn.random_signs(K, m, n, seed=T * 7 + m + K)
+    A = syn.exact_alpha(K, m, n // 128, seed=T + 3 * K).astype(np_alpha(dt))
+    X = syn.exact_activations(T, n, seed=T * 5 + K)
+    d, packed = pack_on_gpu(S, A, dt)
+    Y = gemm(d, packed, X, ldx=n + 24, ldy=m + 7)
+    assert np.array_equal(Y, oracle.product(S, A, X))
+
+
+def test_gemm_skinny_matches_fp64_closely():
+    """Random (non-exact) bf16 activations and fp16 scales: the few-token
+    kernel rounds nothing but the fp32 accumulation, so its error stays below
+    1% of the 1e-3 tolerance; rounding W_hat to bf16 (2^-9 relative, random
+    signs over n = 4096 columns) would land near 10% of it."""
+    T, m, n, K = 16, 512, 4096, 3
+    say("gemm skinny closeness")
+    W = syn.weight(m, n, 77)
+    X = syn.activations(T, n, 78, "bf16")
+    d, signs, alpha, packed, flag = quantize_on_gpu(W, K, "f16")
+    del signs, alpha
+    Y = gemm(d, packed, X)
+    S, A, _ = oracle.residual_binarize(W, K, alpha_dtype="f16")
+    ratio = oracle.max_error_ratio(Y, oracle.product(S, A, X), oracle.bound(S, A, X))
+    assert ratio <= 1e-2 * TOL, ratio
 
 
 @pytest.mark.parametrize("T", [4, 16])
