@@ -42,6 +42,18 @@ def parse():
     ap.add_argument("--rotate-bytes", type=float, default=float(2 ** 30))
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after the timed region, one 256 MiB device-to-device copy: the "
+                         "kernel of known size that scales the byte counters")
+    ap.add_argument("--summarize", nargs=3, metavar=("STATS_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU work: turn a rocprofv3 --kernel-trace --stats output and two "
+                         "--pmc outputs (FETCH_SIZE, WRITE_SIZE) of this script into the "
+                         "profile record of the workload given by --config/--K/--T")
+    ap.add_argument("--command", default="", help="with --summarize: the commands that made "
+                                                  "the rocprofv3 outputs, for the record")
+    ap.add_argument("--extra", nargs="*", default=[],
+                    help="with --summarize: more --pmc output dirs of --calibrate-copy runs; "
+                         "every counter in them is reported per dominant call")
     return ap.parse_args()
 
 
@@ -49,8 +61,152 @@ def weight_bytes(m, n, K, alpha_bytes):
     return K * m * n / 8 + K * m * (n // 128) * alpha_bytes
 
 
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "boolean_weight_amd", "csrc")
+COPY_BYTES = 2 ** 28  # calibration copy: 256 MiB read and 256 MiB written
+CAL_CALLS = 8         # dominant calls bracketed by the two calibration copies
+
+
+def kernel_family(T):
+    """Source file and kernel-name prefix of the kernel one call runs."""
+    if T == 1:
+        return "gemv.hip", "gemv_"
+    if T <= 16:
+        return "skinny.hip", "gemm_skinny_kernel"
+    return "gemm.hip", "gemm_mfma_kernel"
+
+
+def source_digest(T):
+    import hashlib
+    h = hashlib.sha256()
+    for f in (kernel_family(T)[0], "mbok_device.h"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def workload_key(config, K, T):
+    return f"config{config}_K{K}_T{T}"
+
+
+def profile_path(config, K, T):
+    return os.path.join(HERE, "profiles", f"pmc_traffic_{kernel_family(T)[0][:-4]}_"
+                        f"{workload_key(config, K, T)}.txt")
+
+
+def stored_traffic(config, K, T):
+    """HBM bytes per launch from the stored counter record of this workload,
+    or None when there is none or the kernel source changed since."""
+    path = profile_path(config, K, T)
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                rec[k.strip()] = v.strip()
+    if rec.get("source_sha256") != source_digest(T):
+        return None
+    try:
+        return float(rec["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def _csv_rows(d, suffix):
+    import csv
+    import glob
+    rows = []
+    for path in glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True):
+        with open(path) as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def bracketed(dispatches, prefix):
+    """dispatches: [(dispatch id, kernel name, value)].  The run ends with
+    [calibration copy][CAL_CALLS calls of the dominant kernel(s)][calibration
+    copy]; returns (values of the first copy's dispatches, values of the
+    calls' dispatches), or None when the pattern is not there."""
+    ds = sorted(dispatches, key=lambda t: t[0])
+    is_copy = lambda nm: "copy" in nm.lower()
+    j = len(ds)
+    while j > 0 and is_copy(ds[j - 1][1]):  # second copy
+        j -= 1
+    end_calls = j
+    while j > 0 and prefix in ds[j - 1][1]:
+        j -= 1
+    calls = [v for _, _, v in ds[j:end_calls]]
+    end_copy = j
+    while j > 0 and is_copy(ds[j - 1][1]):  # first copy
+        j -= 1
+    copy = [v for _, _, v in ds[j:end_copy]]
+    if not calls or not copy or end_calls == len(ds):
+        return None
+    return copy, calls
+
+
+def summarize(args):
+    """Profile record of one workload from rocprofv3 outputs of bench.py."""
+    import mbok_synth as syn
+
+    cfg = syn.WORKLOADS[args.config]
+    K = args.K or cfg["K"]
+    T = args.T or cfg["T"][0]
+    _, prefix = kernel_family(T)
+    stats_dir, fetch_dir, write_dir = args.summarize
+    lines = [f"# rocprofv3 summary, workload {workload_key(args.config, K, T)} "
+             f"({cfg['name']})", f"# commands: {args.command}", ""]
+    stats = _csv_rows(stats_dir, "kernel_stats.csv")
+    lines.append("kernel-trace stats (top kernels by total time):")
+    stats.sort(key=lambda r: -float(r.get("TotalDurationNs", 0)))
+    for r in stats[:6]:
+        lines.append(f"  {r['Name'][:110]} | calls {r['Calls']} | avg {float(r['AverageNs']) / 1e3:.3f} us"
+                     f" | min {float(r['MinNs']) / 1e3:.3f} us | max {float(r['MaxNs']) / 1e3:.3f} us")
+    trace = _csv_rows(stats_dir, "kernel_trace.csv")
+    br = bracketed([(int(r["Dispatch_Id"]), r["Kernel_Name"],
+                     float(r["End_Timestamp"]) - float(r["Start_Timestamp"])) for r in trace], prefix)
+    if br:
+        lines.append(f"dominant_call_kernel_us: {sum(br[1]) / CAL_CALLS / 1e3:.3f} "
+                     f"(sum of kernel durations over {CAL_CALLS} bracketed calls / {CAL_CALLS})")
+    lines.append("")
+    out = {}
+    for tag, d, counter, unit_scale in (("fetch", fetch_dir, "FETCH_SIZE", 1.0),
+                                        ("write", write_dir, "WRITE_SIZE", 1.0)):
+        rows = [r for r in _csv_rows(d, "counter_collection.csv") if r["Counter_Name"] == counter]
+        br = bracketed([(int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"]))
+                        for r in rows], prefix)
+        if not br:
+            lines.append(f"{counter}: calibration pattern not found")
+            continue
+        copy_kib, call_kib = sum(br[0]), sum(br[1])
+        scale = COPY_BYTES / (copy_kib * 1024.0)
+        per_call = call_kib * 1024.0 * scale / CAL_CALLS
+        out[tag] = per_call
+        lines += [f"{counter}_copy_kib: {copy_kib:.1f} over {len(br[0])} dispatches "
+                  f"(256 MiB copied)",
+                  f"{counter}_scale: {scale:.4f}",
+                  f"{counter}_calls_kib: {call_kib:.1f} over {len(br[1])} dispatches",
+                  f"{tag}_bytes_per_launch: {per_call:.0f}"]
+    if len(out) == 2:
+        lines.append(f"traffic_bytes_per_launch: {out['fetch'] + out['write']:.0f}")
+    for d in args.extra:
+        rows = _csv_rows(d, "counter_collection.csv")
+        for counter in sorted({r["Counter_Name"] for r in rows}):
+            br = bracketed([(int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"]))
+                            for r in rows if r["Counter_Name"] == counter], prefix)
+            if br:
+                lines.append(f"{counter}_per_call: {sum(br[1]) / CAL_CALLS:.6g}")
+    lines.append(f"source_sha256: {source_digest(T)}")
+    print("\n".join(lines))
+
+
 def main():
     args = parse()
+    if args.summarize:
+        summarize(args)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer "
               "is measured on one GPU's shard at its full shape.", file=sys.stderr)
@@ -162,23 +318,64 @@ def main():
     ms = t0.elapsed_time(t1)
     ms_per_step = ms / done
 
-    # ---- per-launch durations of the dominant kernel (HIP events on the
-    # launch stream, one pair per launch, plain stream launches)
+    # ---- mean duration of the dominant call: a HIP graph of that call alone
+    # over the pool, replayed back to back and timed with HIP events on the
+    # stream that launches it (graph launches leave no gaps between kernels,
+    # so this is the kernel time rocprofv3 reports)
     dom = max(range(len(layers)), key=lambda li: layers[li][1].m * layers[li][1].n)
     name, d, _ = layers[dom]
-    nk = min(400, ncopy * 2)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(nk)]
-    for i in range(nk):
+
+    def dom_call(i):
         c = i % ncopy
-        evs[i][0].record(stream)
         if T == 1:
             bw.mbok_gemv(d, pools[dom][c], xs[dom], ys[dom])
         else:
             bw.mbok_gemm(d, pools[dom][c], xs[dom], ys[dom])
-        evs[i][1].record(stream)
+
+    s2 = torch.cuda.Stream()
+    s2.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s2):
+        dom_call(0)
+    torch.cuda.current_stream().wait_stream(s2)
     torch.cuda.synchronize()
-    launch_us = float(np.mean([a.elapsed_time(b) for a, b in evs[nk // 4:]]) * 1e3)
+    nrep = max(1, min(200, 2000 // ncopy))
+    if use_graph and ncopy <= 2048:
+        g2 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g2):
+            for i in range(ncopy):
+                dom_call(i)
+        g2.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(nrep):
+            g2.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        launch_us = e0.elapsed_time(e1) * 1e3 / (nrep * ncopy)
+        del g2
+    else:
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(ncopy):
+            dom_call(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        launch_us = e0.elapsed_time(e1) * 1e3 / ncopy
+    if args.calibrate_copy:
+        # [copy] [CAL_CALLS dominant calls on pool copies read longest ago] [copy]:
+        # the profile summary finds this pattern at the end of the dispatch list
+        a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        for i in range(CAL_CALLS):
+            dom_call(i)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
     m, n = d.m, d.n
     alg_bytes = weight_bytes(m, n, K, abytes) + T * n * (2 if xdt == torch.bfloat16 else 4) + T * m * 4
     if T > 16:
@@ -188,9 +385,10 @@ def main():
         roof = {"bound": "hbm", "achieved": alg_bytes / (launch_us * 1e-6) / 1e9,
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = stored_traffic(args.config, K, T)
     roof["kernel"] = name
     roof["launch_us"] = launch_us
+    roof["alg_bytes_per_launch"] = alg_bytes
 
     if T > 16:
         metric, unit = "prefill TFLOP/s", "TFLOP/s"
