@@ -47,6 +47,9 @@ def _compile(src: str, extra: list[str]) -> str:
 def build(verbose: bool = False, extra: list[str] | None = None) -> str:
     """Compile every source and link libmbok.so; returns the library path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
+    # a failed build must not leave an older library behind to be loaded
+    if os.path.exists(LIB):
+        os.remove(LIB)
     extra = list(extra or [])
     with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))

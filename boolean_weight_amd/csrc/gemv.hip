@@ -268,52 +268,9 @@ __global__ void __launch_bounds__(NW * kWave) gemv_lut_kernel(
 // next group's sign planes are loaded before the current one is summed.
 constexpr int kGroupStride = 2112;  // bytes between the tables of two groups
 
-// Activations of groups g0 .. g0+sg-1, staged as fp32 in table order: slot
-// 4t + j of group gl holds x[c0(t) + 4j], the column that bit j of table t
-// stands for (t = 8w + a, c0 = 32w + 16(a%2) + a/2).  One thread per 16-column
-// block (two 16-byte loads for bf16); block b of a group holds the columns of
-// tables 8(b/2) + 2e + b%2, e = 0..3, four values each.
-template <typename XT>
-__device__ __forceinline__ void stage_x(const XT* __restrict__ x, int g0, int sg,
-                                        float* __restrict__ xs, int tid, int nthreads) {
-  for (int blk = tid; blk < sg * 8; blk += nthreads) {
-    float v[16];
-    load_x16<XT>(x, (int64_t)g0 * kGroup + 16 * blk, v);
-    const int gl = blk >> 3, bb = blk & 7;
-    float4* dst = reinterpret_cast<float4*>(xs + gl * kGroup) + 8 * (bb >> 1) + (bb & 1);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) dst[2 * e] = make_float4(v[e], v[4 + e], v[8 + e], v[12 + e]);
-  }
-}
-
-// Tables from staged activations: item u = (table t, quarter h) reads the
-// table's four activations with one 16-byte LDS read and writes entries
-// 4h .. 4h+3 (bits 2 and 3 of the entry index fixed by h) as one float4;
-// consecutive items write consecutive 16-byte slots, free of bank conflicts.
-__device__ __forceinline__ void build_tables_from_staged(const float* __restrict__ xs, int sg,
-                                                         float* __restrict__ tabs, int tid,
-                                                         int nthreads) {
-  for (int u = tid; u < sg * kChunksPerGroup * 4; u += nthreads) {
-    const int h = u & 3;
-    const int tg = u >> 2;  // table index within the slab
-    const int gl = tg >> 5, t = tg & 31;
-    const float4 q = reinterpret_cast<const float4*>(xs)[tg];
-    const float hi = ((h & 1) ? q.z : -q.z) + ((h & 2) ? q.w : -q.w);
-    const float sp = q.x + q.y, sm = q.x - q.y;
-    float4* dst = reinterpret_cast<float4*>(tabs + (gl * kGroupStride) / 4 + t * kTableFloats) + h;
-    *dst = make_float4(hi - sp, hi + sm, hi - sm, hi + sp);
-  }
-}
-
-// Row-slice variant: a wavefront covers R = 64/NS rows and NS column slices
-// (lane = c*R + r), a workgroup covers R rows and every column, so no
-// cross-workgroup step is needed and small layers still give m/R workgroups.
-// The NW*NS slices ("streams") of a workgroup take groups p, p+NW*NS, ...;
-// all streams of the workgroup read the same slab of tables.  Group tables
-// are kGroupStride = 2112 bytes apart (33 x 64): the NS slices of a
-// wavefront read consecutive groups, whose tables then start 16 banks apart,
-// so one ds_read of the whole wavefront stays free of bank conflicts.  The
-// sign planes of the next group are loaded while the current one is summed.
+// Per slab of groups, each thread of the first 8*sg loads one 16-column
+// block of activations, then the sign planes are requested, then the thread
+// builds the four tables of its block straight from registers.
 template <typename XT, typename AT, int K, int NW, int NS>
 __global__ void __launch_bounds__(NW * kWave) gemv_rows_kernel(
     const uint4* __restrict__ bits, const AT* __restrict__ scales, const XT* __restrict__ x,
@@ -321,7 +278,6 @@ __global__ void __launch_bounds__(NW * kWave) gemv_rows_kernel(
   constexpr int R = kWave / NS;
   constexpr int NP = NW * NS;
   extern __shared__ float lds[];
-  float* xs = lds + (slab_groups * kGroupStride) / 4;  // staged activations after the tables
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int c = lane / R, r = lane % R;
@@ -335,6 +291,12 @@ __global__ void __launch_bounds__(NW * kWave) gemv_rows_kernel(
   float yacc = 0.f;
   for (int g0 = 0; g0 < G; g0 += slab_groups) {
     const int sg = min(slab_groups, G - g0);
+    // Activations first: the table build waits only for these (loads return
+    // in order), while the sign planes issued next are still in flight.
+    // Thread b < 8 sg loads the 16-column block b of the slab.
+    const bool hx = (int)threadIdx.x < sg * 8;
+    float v[16];
+    if (hx) load_x16<XT>(x, (int64_t)g0 * kGroup + 16 * threadIdx.x, v);
     uint4 bA[K], bB[K];
     float aA[K], aB[K];
     if (p < sg) {
@@ -345,10 +307,15 @@ __global__ void __launch_bounds__(NW * kWave) gemv_rows_kernel(
         aA[k] = alpha_to_f32<AT>(scales_row[o]);
       }
     }
-    if (g0 > 0) __syncthreads();
-    stage_x<XT>(x, g0, sg, xs, threadIdx.x, NW * kWave);
-    __syncthreads();
-    build_tables_from_staged(xs, sg, lds, threadIdx.x, NW * kWave);
+    if (g0 > 0) __syncthreads();  // the previous slab's tables are no longer read
+    if (hx) {
+      // block bb of group gl holds the columns of tables 8(bb/2) + 2e + bb%2
+      const int gl = threadIdx.x >> 3, bb = threadIdx.x & 7;
+      float* tabs = lds + (gl * kGroupStride) / 4 + (8 * (bb >> 1) + (bb & 1)) * kTableFloats;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        build_table4(v[e], v[4 + e], v[8 + e], v[12 + e], tabs + 2 * e * kTableFloats);
+    }
     __syncthreads();
     for (int gl = p; gl < sg; gl += 2 * NP) {
       const int g1 = gl + NP, g2 = gl + 2 * NP;
@@ -395,6 +362,117 @@ __global__ void __launch_bounds__(NW * kWave) gemv_rows_kernel(
     return;
   }
   if (i < m) y[i] = yacc;
+}
+
+// 16-row tile of work item b.  Workgroup b runs on XCD b % 8, so within each
+// full set of 32 tiles (8 row blocks of 64 rows) the items b = 8j + xcd,
+// j = 4u + quarter, take quarter `quarter` of row block 8u + xcd: the four
+// tiles of a row block share one XCD and its L2 lines of scales.  A trailing
+// partial set keeps b.
+__device__ __forceinline__ int tile16_of(int b, int tiles) {
+  const int full = tiles & ~31;
+  if (b >= full) return b;
+  const int xcd = b & 7, j = b >> 3;
+  return (((j >> 2) << 3) + xcd) * 4 + (j & 3);
+}
+
+// Streaming variant: one persistent workgroup per compute unit.  Wavefront w
+// owns group block w (groups 4w .. 4w+3 of the slab); lane (j, r) =
+// (lane / 16, lane % 16) handles row r of the tile and group 4w + j, so one
+// 16-byte load per lane covers 16 rows x 4 groups (four 256-byte runs of a
+// plane).  The workgroup builds the tables of a slab once and then walks its
+// 16-row tiles (b, b + grid, ... through words_tile), loading tile t + 1 while
+// tile t is summed, so the stream of sign planes overlaps the lookups instead
+// of alternating with them workgroup by workgroup.  Group tables are
+// kGroupStride = 2112 bytes apart, so the 4 groups of one ds_read hit 16-bank
+// windows 16 banks apart.  Partial sums of up to JMAX tiles stay in registers
+// across slabs; each tile is finally summed over the 4 groups of a block and
+// over wavefronts in a fixed order.
+template <typename AT, int K>
+struct BlockLoads {
+  uint4 b[K];
+  float a[K];
+};
+
+template <typename XT, typename AT, int K, int JMAX>
+__global__ void __launch_bounds__(16 * kWave) gemv_stream_kernel(
+    const uint4* __restrict__ bits, const AT* __restrict__ scales, const XT* __restrict__ x,
+    float* __restrict__ y, int m, int G, int slab_groups, int tiles) {
+  extern __shared__ float lds[];
+  const int NW = blockDim.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int r = lane & 15, j = lane >> 4;
+  const int ntl = (tiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;  // <= JMAX
+  float yacc[JMAX];
+#pragma unroll
+  for (int t = 0; t < JMAX; ++t) yacc[t] = 0.f;
+
+  auto load = [&](int t, int g0, int gl, BlockLoads<AT, K>& L) {
+    const int i = tile16_of(blockIdx.x + t * gridDim.x, tiles) * 16 + r;
+    const int64_t ch = (((int64_t)(i / kRowBlock) * G + g0 + gl) * K) * kRowBlock + i % kRowBlock;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      L.b[k] = bits[ch + k * kRowBlock];
+      L.a[k] = alpha_to_f32<AT>(scales[ch + k * kRowBlock]);
+    }
+  };
+
+  for (int g0 = 0; g0 < G; g0 += slab_groups) {
+    const int sg = min(slab_groups, G - g0);
+    const int gl = 4 * wave + j;  // this lane's group within the slab
+    const bool active = gl < sg;
+    const int glc = active ? gl : sg - 1;  // clamped: loads stay in bounds
+    const bool hx = (int)threadIdx.x < sg * 8;
+    float v[16];
+    if (hx) load_x16<XT>(x, (int64_t)g0 * kGroup + 16 * threadIdx.x, v);
+    BlockLoads<AT, K> LA, LB;
+    load(0, g0, glc, LA);
+    if (g0 > 0) __syncthreads();  // the previous slab's tables are no longer read
+    if (hx) {
+      const int tg = threadIdx.x >> 3, bb = threadIdx.x & 7;
+      float* tabs = lds + (tg * kGroupStride) / 4 + (8 * (bb >> 1) + (bb & 1)) * kTableFloats;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        build_table4(v[e], v[4 + e], v[8 + e], v[12 + e], tabs + 2 * e * kTableFloats);
+    }
+    __syncthreads();
+    const uint32_t tab = lds_addr(lds) + glc * kGroupStride;
+    auto sum = [&](const BlockLoads<AT, K>& L, float acc) {
+      float s = 0.f;
+#pragma unroll
+      for (int k = 0; k < K; ++k) s = fmaf(L.a[k], lut_dot128_sdwa(L.b[k], tab), s);
+      return active ? acc + s : acc;
+    };
+#pragma unroll
+    for (int t = 0; t < JMAX; t += 2) {
+      if (t >= ntl) break;
+      if (t + 1 < ntl) load(t + 1, g0, glc, LB);
+      yacc[t] = sum(LA, yacc[t]);
+      if (t + 1 >= ntl) break;
+      if (t + 2 < ntl) load(t + 2, g0, glc, LA);
+      yacc[t + 1] = sum(LB, yacc[t + 1]);
+    }
+  }
+
+  // per tile: fixed-order sum over the 4 groups of a block, then over wavefronts
+  __syncthreads();  // tables are no longer read: reuse LDS
+#pragma unroll
+  for (int t = 0; t < JMAX; ++t) {
+    if (t >= ntl) break;
+    float u = yacc[t];
+    u += __shfl_xor(u, 16, kWave);
+    u += __shfl_xor(u, 32, kWave);
+    if (j == 0) lds[(t * NW + wave) * 16 + r] = u;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < ntl * 16; idx += blockDim.x) {
+    const int t = idx >> 4, rr = idx & 15;
+    float u = lds[(t * NW) * 16 + rr];
+    for (int w = 1; w < NW; ++w) u += lds[(t * NW + w) * 16 + rr];
+    const int i = tile16_of(blockIdx.x + t * gridDim.x, tiles) * 16 + rr;
+    if (i < m) y[i] = u;
+  }
 }
 
 // Column-split variant (the default when a workspace is given): workgroup
@@ -526,7 +604,7 @@ __global__ void __launch_bounds__(NW * kWave) gemv_direct_kernel(
   }
 }
 
-enum Variant { kSplit = 0, kFullRow = 1, kDirect = 2, kRows = 3 };
+enum Variant { kSplit = 0, kFullRow = 1, kDirect = 2, kRows = 3, kStream = 4 };
 
 // Kernel choice by shape, from measurements on MI355X (per-launch times in
 // HIP graphs over a rotating pool): row slices of 16 rows for small layers
@@ -540,15 +618,14 @@ bool use_skinny_for_gemv(const Geom&) {
   return v && strcmp(v, "skinny") == 0;
 }
 
-int variant_for(const Geom& geo) {
+int variant_for(const Geom&) {
   const char* v = getenv("MBOK_GEMV_VARIANT");
   if (v && strcmp(v, "direct") == 0) return kDirect;
   if (v && strcmp(v, "fullrow") == 0) return kFullRow;
   if (v && strcmp(v, "split") == 0) return kSplit;
   if (v && strcmp(v, "rows") == 0) return kRows;
-  if (geo.n >= 2 * geo.m) return kSplit;
-  if (geo.K <= 2 && geo.m < 16384) return kRows;
-  return kFullRow;
+  if (v && strcmp(v, "stream") == 0) return kStream;
+  return kStream;
 }
 
 constexpr int kSplitNW = 4;           // wavefronts per split workgroup
@@ -570,6 +647,7 @@ void gemv_split_shape(int RB, int G, int* gpw, int* S) {
 
 size_t gemv_workspace_bytes(const mbok_desc* d) {
   const Geom geo = make_geom(d);
+  if (variant_for(geo) != kSplit) return 0;
   int gpw, S;
   gemv_split_shape(geo.RB, geo.G, &gpw, &S);
   if (S <= 1) return 0;
@@ -622,11 +700,10 @@ template <typename XT, typename AT, int K, int NW, int NS>
 int launch_rows_nw(const Geom& geo, const uint4* bits, const AT* scales, const void* x, float* y,
                    hipStream_t stream) {
   constexpr int R = kWave / NS;
-  // slabs of at most 32 groups: 32 * (2112 + 512) B = 82 KB of tables and
-  // staged activations
+  // slabs of at most 32 groups: 32 * 2112 B = 66 KB of tables
   const int nslabs = (geo.G + 31) / 32;
   const int slab = (geo.G + nslabs - 1) / nslabs;
-  size_t lds = (size_t)slab * kGroupStride + (size_t)slab * kGroup * sizeof(float);
+  size_t lds = (size_t)slab * kGroupStride;
   if (lds < NW * R * sizeof(float)) lds = NW * R * sizeof(float);
   const int blocks = (geo.m + R - 1) / R;
   hipLaunchKernelGGL((gemv_rows_kernel<XT, AT, K, NW, NS>), dim3(blocks), dim3(NW * kWave), lds,
@@ -634,14 +711,40 @@ int launch_rows_nw(const Geom& geo, const uint4* bits, const AT* scales, const v
   return hipGetLastError() == hipSuccess ? MBOK_OK : MBOK_ERR_HIP;
 }
 
+constexpr int kStreamJ = 8;  // tiles per persistent workgroup (registers)
+
+template <typename XT, typename AT, int K>
+int launch_stream(const Geom& geo, const uint4* bits, const AT* scales, const void* x, float* y,
+                  hipStream_t stream) {
+  // slabs of at most 64 groups (135 KB of tables), one wavefront per block of
+  // 4 groups; one workgroup per compute unit, more when the tiles would not
+  // fit kStreamJ per workgroup
+  const int nslabs = (geo.G + 63) / 64;
+  const int slab = (geo.G + nslabs - 1) / nslabs;
+  const int NW = (slab + 3) / 4;
+  const int tiles = geo.RB * (kRowBlock / 16);
+  int grid = tiles < 256 ? tiles : 256;
+  if (grid * kStreamJ < tiles) grid = (tiles + kStreamJ - 1) / kStreamJ;
+  size_t lds = (size_t)slab * kGroupStride;
+  const size_t red = (size_t)kStreamJ * NW * 16 * sizeof(float);
+  if (lds < red) lds = red;
+  hipLaunchKernelGGL((gemv_stream_kernel<XT, AT, K, kStreamJ>), dim3(grid), dim3(NW * kWave),
+                     lds, stream, bits, scales, reinterpret_cast<const XT*>(x), y, geo.m, geo.G,
+                     slab, tiles);
+  return hipGetLastError() == hipSuccess ? MBOK_OK : MBOK_ERR_HIP;
+}
+
 template <typename XT, typename AT, int K, int NS>
 int launch_rows(const Geom& geo, const uint4* bits, const AT* scales, const void* x, float* y,
                 hipStream_t stream) {
-  switch (rows_waves()) {
-    case 4: return launch_rows_nw<XT, AT, K, 4, NS>(geo, bits, scales, x, y, stream);
-    case 16: return launch_rows_nw<XT, AT, K, 16, NS>(geo, bits, scales, x, y, stream);
-    default: return launch_rows_nw<XT, AT, K, 8, NS>(geo, bits, scales, x, y, stream);
+  // 16 wavefronts leave 128 VGPRs per lane, which K >= 3 exceeds (it would
+  // spill to scratch): those use at most 8
+  const int nw = rows_waves();
+  if (nw == 4) return launch_rows_nw<XT, AT, K, 4, NS>(geo, bits, scales, x, y, stream);
+  if constexpr (K <= 2) {
+    if (nw == 16) return launch_rows_nw<XT, AT, K, 16, NS>(geo, bits, scales, x, y, stream);
   }
+  return launch_rows_nw<XT, AT, K, 8, NS>(geo, bits, scales, x, y, stream);
 }
 
 template <typename XT, typename AT, int K>
@@ -652,6 +755,7 @@ int launch_typed(const Geom& geo, const void* packed, const void* x, float* y, v
   const AT* scales = reinterpret_cast<const AT*>(reinterpret_cast<const char*>(packed) +
                                                  geo.bits_bytes);
   const int variant = variant_for(geo);
+  if (variant == kStream) return launch_stream<XT, AT, K>(geo, bits, scales, x, y, stream);
   if (variant == kRows) {
     switch (rows_per_workgroup(geo.m)) {
       case 64: return launch_rows<XT, AT, K, 1>(geo, bits, scales, x, y, stream);

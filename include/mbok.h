@@ -169,8 +169,11 @@ int mbok_pack(const mbok_desc* d, const int8_t* signs, const void* alpha,
               void* packed, void* stream);
 
 /*
- * Bytes of the workspace mbok_gemv uses for this shape (0 when it needs
- * none).  Host only; 0 for a NULL or invalid descriptor.
+ * Bytes of the workspace mbok_gemv uses for this shape: 0 when the call needs
+ * none, which is the case for every shape with the default kernel (the
+ * column-split kernel, selected for comparison with the environment variable
+ * MBOK_GEMV_VARIANT=split, is the one that uses it).  Host only; 0 for a NULL
+ * or invalid descriptor.
  */
 size_t mbok_gemv_workspace_bytes(const mbok_desc* d);
 
@@ -185,13 +188,14 @@ size_t mbok_gemv_workspace_bytes(const mbok_desc* d);
  *  x         device, n values of x_dtype (MBOK_BF16 or MBOK_F32).
  *  y         device fp32 [m]; overwritten (not accumulated).
  *  workspace device, mbok_gemv_workspace_bytes(d) bytes, 256-byte aligned,
- *            or NULL.  It receives the partial sums of column slices, so that
- *            a layer is spread over every compute unit; a second small kernel
- *            on the same stream adds them in a fixed order.  Its contents
- *            need no initialisation and are meaningless after the call.
- *            Calls that may run at the same time (other streams) need
- *            distinct workspaces.  NULL selects whole-row workgroups (no
- *            workspace, one kernel, fewer workgroups; slower for small m).
+ *            or NULL (always allowed; ignored when the size is 0).  When used
+ *            it receives the partial sums of column slices, which a second
+ *            small kernel on the same stream adds in a fixed order; its
+ *            contents need no initialisation and are meaningless after the
+ *            call, and calls that may run at the same time (other streams)
+ *            need distinct workspaces.
+ * The default kernel keeps one workgroup per compute unit: it builds the
+ * signed-sum tables of x once and streams its 16-row tiles through them.
  * Errors: INVALID_ARG, SHAPE/UNSUPPORTED, DTYPE (x_dtype), ALIGN (packed and
  * x 16-byte aligned, y 4-byte aligned, workspace 256-byte aligned), HIP.
  */

@@ -42,6 +42,7 @@ GEMV_VARIANTS = {
     "split": {"MBOK_GEMV_VARIANT": "split"},
     "fullrow": {"MBOK_GEMV_VARIANT": "fullrow"},
     "direct": {"MBOK_GEMV_VARIANT": "direct"},
+    "stream": {"MBOK_GEMV_VARIANT": "stream"},
     # matrix-core kernel of the few-token product at one token (bf16 x only;
     # fp32 x keeps the table kernels)
     "skinny": {"MBOK_GEMV_VARIANT": "skinny"},
@@ -278,22 +279,30 @@ def test_gemv_k_sweep_first_linear(cfg, K):
 
 
 def test_gemv_workspace_shared_across_shapes_and_garbage():
-    """One workspace serves every shape, whatever it holds beforehand."""
+    """The column-split kernel: one workspace serves every shape, whatever it
+    holds beforehand; the default kernel asks for none."""
     say("gemv shared workspace")
     shapes = [(4096, 4096, 2), (300, 11008, 3), (11008, 4096, 3), (64, 13824, 1)]
-    need = max(bw.mbok_gemv_workspace_bytes(bw.mbok_desc_init(m, n, K, bw.MBOK_F16))
+    assert all(bw.mbok_gemv_workspace_bytes(bw.mbok_desc_init(m, n, K, bw.MBOK_F16)) == 0
                for m, n, K in shapes)
-    assert need > 0
-    ws = torch.full((need + 4096,), 0x7f, dtype=torch.uint8, device=DEV)
-    for rep in range(2):
-        for (m, n, K) in shapes:
-            S = syn.random_signs(K, m, n, seed=m + n)
-            A = syn.exact_alpha(K, m, n // 128, seed=K).astype(np.float16)
-            x = syn.exact_activations(1, n, seed=n)[0]
-            d, packed = pack_on_gpu(S, A, "f16")
-            y = torch.empty(m, dtype=torch.float32, device=DEV)
-            bw.mbok_gemv(d, packed, x_to_dev(x, "bf16"), y, workspace=ws)
-            assert np.array_equal(y.cpu().numpy().astype(np.float64), oracle.product(S, A, x)), (m, n, K)
+    old = _swap_env({"MBOK_GEMV_VARIANT": "split"})
+    try:
+        need = max(bw.mbok_gemv_workspace_bytes(bw.mbok_desc_init(m, n, K, bw.MBOK_F16))
+                   for m, n, K in shapes)
+        assert need > 0
+        ws = torch.full((need + 4096,), 0x7f, dtype=torch.uint8, device=DEV)
+        for rep in range(2):
+            for (m, n, K) in shapes:
+                S = syn.random_signs(K, m, n, seed=m + n)
+                A = syn.exact_alpha(K, m, n // 128, seed=K).astype(np.float16)
+                x = syn.exact_activations(1, n, seed=n)[0]
+                d, packed = pack_on_gpu(S, A, "f16")
+                y = torch.empty(m, dtype=torch.float32, device=DEV)
+                bw.mbok_gemv(d, packed, x_to_dev(x, "bf16"), y, workspace=ws)
+                assert np.array_equal(y.cpu().numpy().astype(np.float64),
+                                      oracle.product(S, A, x)), (m, n, K)
+    finally:
+        _restore_env(old)
 
 
 def test_gemv_without_workspace_matches():
