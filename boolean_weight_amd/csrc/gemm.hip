@@ -22,6 +22,8 @@
 // ((W1 >> q) & 0x01010101) | ((W2 >> q) & ..) << 1 | ((W3 >> q) & ..) << 2, and
 // v_perm_b32 turns that selector into 4 low bytes and 4 high bytes of bf16
 // weights at once; two more perms interleave them into natural column order.
+#include <stdlib.h>
+
 #include "mbok_device.h"
 #include "mbok_launch.h"
 
@@ -226,20 +228,31 @@ __global__ void __launch_bounds__(GEMM_THREADS) gemm_mfma_kernel(
     uint16_t* xd = smem + 2 * (cb ^ 1) * TILE_ELEMS + (tid >> 3) * LDS_STRIDE + xpart * 8;
     uint4* wd = reinterpret_cast<uint4*>(smem + (2 * (cb ^ 1) + 1) * TILE_ELEMS + tid * LDS_STRIDE);
     uint32_t V[4];
+    // fragments of sub-step kk + 1 are read while the MFMAs of kk run
+    bf16x8 av[2][4], bv[2][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) av[0][i] = *reinterpret_cast<const bf16x8*>(xs + i * 32 * LDS_STRIDE);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bv[0][j] = *reinterpret_cast<const bf16x8*>(ws + j * 32 * LDS_STRIDE);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      bf16x8 av[4], bv[4];
+      const int cur = kk & 1;
+      if (kk < 3) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        av[i] = *reinterpret_cast<const bf16x8*>(xs + i * 32 * LDS_STRIDE + 16 * kk);
+        for (int i = 0; i < 4; ++i)
+          av[cur ^ 1][i] =
+              *reinterpret_cast<const bf16x8*>(xs + i * 32 * LDS_STRIDE + 16 * (kk + 1));
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bv[j] = *reinterpret_cast<const bf16x8*>(ws + j * 32 * LDS_STRIDE + 16 * kk);
+        for (int j = 0; j < 4; ++j)
+          bv[cur ^ 1][j] =
+              *reinterpret_cast<const bf16x8*>(ws + j * 32 * LDS_STRIDE + 16 * (kk + 1));
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+          acc[i][j] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[cur][i], bv[cur][j], acc[i][j], 0, 0, 0);
       // a quarter of the next step: 2 activation segments, 16 weight columns
       *reinterpret_cast<uint4*>(xd + (2 * kk) * 32 * LDS_STRIDE) = R.x[2 * kk];
       *reinterpret_cast<uint4*>(xd + (2 * kk + 1) * 32 * LDS_STRIDE) = R.x[2 * kk + 1];
@@ -263,9 +276,11 @@ __global__ void __launch_bounds__(GEMM_THREADS) gemm_mfma_kernel(
       wd[2 * kk] = make_uint4(out[0], out[1], out[2], out[3]);
       wd[2 * kk + 1] = make_uint4(out[4], out[5], out[6], out[7]);
       // interleave: each MFMA followed by a few vector / LDS instructions
+      // (the next sub-step's 8 fragment reads go in between the first MFMAs)
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        if (q < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
         __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
         __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
       }
@@ -324,9 +339,226 @@ __global__ void __launch_bounds__(GEMM_THREADS) gemm_mfma_kernel(
     }
 }
 
+// Two wavefronts per SIMD.  With one wavefront per SIMD the unpacking and
+// LDS traffic of a step sit between its MFMAs (hardware counters: MFMA busy
+// + VALU + LDS + waits add up to the whole wave lifetime), so this variant
+// splits the 256 x 256 tile over 8 wavefronts of 128 tokens x 64 rows
+// (2 x 4 ... 4 x 2 blocks of 32 x 32, 128 accumulator registers): while one
+// wavefront of a SIMD runs MFMAs the other unpacks, copies and reads
+// fragments.  Two threads share a row in the unpack (32 columns each, a
+// quarter of them per 16-column sub-step); each thread copies 4 activation
+// segments per step.
+constexpr int GEMM8_THREADS = 512;
+
+__device__ __forceinline__ void unpack_two_quads(const uint32_t* V, int a, int b0, const Levels& L,
+                                                 uint32_t* out) {
+#pragma unroll
+  for (int bb = 0; bb < 2; ++bb) {
+    const int b = b0 + bb;
+    const uint32_t sel = (a ? (V[b] >> 4) : V[b]) & 0x0f0f0f0fu;
+    const uint32_t lo = __builtin_amdgcn_perm(L.lo_b, L.lo_a, sel);
+    const uint32_t hi = __builtin_amdgcn_perm(L.hi_b, L.hi_a, sel);
+    out[2 * bb] = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+    out[2 * bb + 1] = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+  }
+}
+
+template <typename AT, int K>
+__global__ void __launch_bounds__(GEMM8_THREADS) gemm_mfma8_kernel(
+    const uint32_t* __restrict__ bits, const AT* __restrict__ scales,
+    const uint16_t* __restrict__ X, int64_t ldx, float* __restrict__ Y, int64_t ldy, int T, int m,
+    int m_pad, int G) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  // buffer b: activations at smem + 2b * TILE_ELEMS, weights right after
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wt = wave & 1, wn = wave >> 1;  // 128-token half, 64-row quarter
+  const int t0 = blockIdx.y * BT;
+  const int n0 = blockIdx.x * BN;
+  const int S = G * 2;  // steps of 64 columns
+
+  // unpack role: row n0 + tid/2, columns 32 * (tid % 2) .. + 31 of each step
+  const int urow = tid >> 1, uhalf = tid & 1;
+  const int row = n0 + urow;
+  const bool row_ok = row < m_pad;
+  const int rowc = row_ok ? row : m_pad - 1;
+  const uint32_t row_chunk = (uint32_t)(rowc / kRowBlock) * (uint32_t)(G * K * kRowBlock) +
+                             (uint32_t)(rowc % kRowBlock);
+
+  // X copy role: segment j = token tid/8 + 64 j, columns 8 (tid % 8) .. + 7
+  const int xpart = tid & 7;
+  uint32_t xoff[4];
+  bool xok[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int t = t0 + (tid >> 3) + 64 * j;
+    xok[j] = t < T;
+    xoff[j] = (uint32_t)((int64_t)(xok[j] ? t : T - 1) * ldx) + xpart * 8;
+  }
+
+  struct StepRegs {
+    uint4 x[4];
+    uint32_t w[K];
+    float a[K];
+  };
+  StepRegs R0, R1;
+  auto load_step = [&](int s, StepRegs& R) {
+    const int g = s >> 1;
+    const uint32_t word = 2 * (s & 1) + uhalf;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) R.x[j] = *reinterpret_cast<const uint4*>(X + xoff[j] + s * BK);
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const uint32_t ch = row_chunk + (uint32_t)(g * K + k) * kRowBlock;
+      R.w[k] = bits[ch * 4u + word];
+      R.a[k] = alpha_to_f32<AT>(scales[ch]);
+    }
+  };
+  auto mask_step = [&](StepRegs& R) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (!xok[j]) R.x[j] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      R.w[k] = row_ok ? R.w[k] : 0u;
+      R.a[k] = row_ok ? R.a[k] : 0.f;
+    }
+  };
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int lrow = lane & 31, lk = (lane >> 5) * 8;
+  Levels L;
+
+  // compute step from buffer cb, store the next step (registers R) into cb^1
+  auto step = [&](int cb, StepRegs& R, bool even) {
+    mask_step(R);
+    if (K <= 3 && even) L = make_levels<K>(R.a);
+    const uint16_t* xs = smem + 2 * cb * TILE_ELEMS + (wt * 128 + lrow) * LDS_STRIDE + lk;
+    const uint16_t* ws = smem + (2 * cb + 1) * TILE_ELEMS + (wn * 64 + lrow) * LDS_STRIDE + lk;
+    uint16_t* xd = smem + 2 * (cb ^ 1) * TILE_ELEMS + (tid >> 3) * LDS_STRIDE + xpart * 8;
+    uint4* wd = reinterpret_cast<uint4*>(smem + (2 * (cb ^ 1) + 1) * TILE_ELEMS +
+                                         urow * LDS_STRIDE + uhalf * 32);
+    uint32_t V[4];
+    if (K <= 3) word_selectors<K>(R.w, V);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      bf16x8 av[4], bv[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        av[i] = *reinterpret_cast<const bf16x8*>(xs + i * 32 * LDS_STRIDE + 16 * kk);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        bv[j] = *reinterpret_cast<const bf16x8*>(ws + j * 32 * LDS_STRIDE + 16 * kk);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+      // a quarter of the next step: one activation segment, 8 weight columns
+      *reinterpret_cast<uint4*>(xd + kk * 64 * LDS_STRIDE) = R.x[kk];
+      uint32_t out[4];
+      if (K <= 3) {
+        unpack_two_quads(V, kk >> 1, 2 * (kk & 1), L, out);
+      } else {
+        uint32_t o32[16];
+        unpack_word_k4(R.w, R.a, o32);
+        // columns 8 kk .. 8 kk + 7 are quads 2 kk, 2 kk + 1
+#pragma unroll
+        for (int q = 0; q < 4; ++q) out[q] = o32[4 * kk + q];
+      }
+      wd[kk] = make_uint4(out[0], out[1], out[2], out[3]);
+    }
+  };
+
+  // prologue: step 0 into buffer 0
+  load_step(0, R0);
+  load_step(1, R1);
+  mask_step(R0);
+  {
+    if (K <= 3) L = make_levels<K>(R0.a);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<uint4*>(smem + (tid >> 3) * LDS_STRIDE + xpart * 8 + j * 64 * LDS_STRIDE) =
+          R0.x[j];
+    uint4* wd = reinterpret_cast<uint4*>(smem + TILE_ELEMS + urow * LDS_STRIDE + uhalf * 32);
+    uint32_t out[16];
+    if (K <= 3)
+      unpack_word<K>(R0.w, L, out);
+    else
+      unpack_word_k4(R0.w, R0.a, out);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      wd[j] = make_uint4(out[4 * j], out[4 * j + 1], out[4 * j + 2], out[4 * j + 3]);
+  }
+  __syncthreads();
+  for (int s = 0; s < S; s += 2) {
+    load_step(min(s + 2, S - 1), R0);
+    step(0, R1, false);  // compute step s, store step s+1 (odd)
+    __syncthreads();
+    load_step(min(s + 3, S - 1), R1);
+    step(1, R0, true);  // compute step s+1, store step s+2 (even)
+    __syncthreads();
+  }
+
+  // C layout: lane l, register r -> token 8(r/4) + 4(l/32) + r%4, row l%32
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = n0 + wn * 64 + j * 32 + lrow;
+      if (n >= m) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = t0 + wt * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (t < T) Y[(int64_t)t * ldy + n] = acc[i][j][r];
+      }
+    }
+}
+
+template <typename AT, int K>
+void launch_mfma8_k(const Geom& geo, const uint32_t* bits, const AT* scales, const uint16_t* Xb,
+                    int64_t T, int64_t ldx, float* Y, int64_t ldy, hipStream_t stream) {
+  const size_t lds = 4 * TILE_ELEMS * sizeof(uint16_t);
+  dim3 grid((geo.m + BN - 1) / BN, (unsigned)((T + BT - 1) / BT));
+  hipLaunchKernelGGL((gemm_mfma8_kernel<AT, K>), grid, dim3(GEMM8_THREADS), lds, stream, bits,
+                     scales, Xb, ldx, Y, ldy, (int)T, geo.m, geo.RB * kRowBlock, geo.G);
+}
+
+template <typename AT>
+int launch_mfma8(const Geom& geo, const void* packed, const void* X, int64_t T, int64_t ldx,
+                 float* Y, int64_t ldy, hipStream_t stream) {
+  const uint32_t* bits = reinterpret_cast<const uint32_t*>(packed);
+  const AT* scales = reinterpret_cast<const AT*>(reinterpret_cast<const char*>(packed) +
+                                                 geo.bits_bytes);
+  const uint16_t* Xb = reinterpret_cast<const uint16_t*>(X);
+  switch (geo.K) {
+    case 1: launch_mfma8_k<AT, 1>(geo, bits, scales, Xb, T, ldx, Y, ldy, stream); break;
+    case 2: launch_mfma8_k<AT, 2>(geo, bits, scales, Xb, T, ldx, Y, ldy, stream); break;
+    case 3: launch_mfma8_k<AT, 3>(geo, bits, scales, Xb, T, ldx, Y, ldy, stream); break;
+    default: launch_mfma8_k<AT, 4>(geo, bits, scales, Xb, T, ldx, Y, ldy, stream); break;
+  }
+  return hipGetLastError() == hipSuccess ? MBOK_OK : MBOK_ERR_HIP;
+}
+
+bool use_mfma8() {
+  const char* v = getenv("MBOK_GEMM_WAVES");
+  return !(v && atoi(v) == 4);
+}
+
 template <typename AT>
 int launch_mfma(const Geom& geo, const void* packed, const void* X, int64_t T, int64_t ldx,
                 float* Y, int64_t ldy, hipStream_t stream) {
+  // the 8-wavefront kernel indexes signs and activations with 32-bit offsets
+  const bool fits32 = geo.bits_bytes / 4 < (int64_t(1) << 32) && T * ldx < (int64_t(1) << 32);
+  if (fits32 && use_mfma8()) return launch_mfma8<AT>(geo, packed, X, T, ldx, Y, ldy, stream);
   const uint2* bits = reinterpret_cast<const uint2*>(packed);
   const AT* scales = reinterpret_cast<const AT*>(reinterpret_cast<const char*>(packed) +
                                                  geo.bits_bytes);

@@ -394,9 +394,21 @@ def test_gemm_config3_tolerance(T):
         assert ratio <= TOL, (name, ratio)
 
 
+@pytest.fixture(params=["8", "4"])
+def prefill_waves(request):
+    """Prefill kernel with 8 wavefronts per workgroup (default) or 4."""
+    old = os.environ.get("MBOK_GEMM_WAVES")
+    os.environ["MBOK_GEMM_WAVES"] = request.param
+    yield request.param
+    if old is None:
+        os.environ.pop("MBOK_GEMM_WAVES", None)
+    else:
+        os.environ["MBOK_GEMM_WAVES"] = old
+
+
 @pytest.mark.parametrize("K", [1, 2, 3, 4])
 @pytest.mark.parametrize("T,m,n", [(2, 65, 128), (33, 300, 384), (257, 256, 256), (300, 513, 640)])
-def test_gemm_prefill_exact_ragged(T, m, n, K):
+def test_gemm_prefill_exact_ragged(T, m, n, K, prefill_waves):
     say(f"gemm prefill exact T={T} m={m} n={n} K={K}")
     S = syn.random_signs(K, m, n, seed=T + m + K)
     A = syn.exact_alpha(K, m, n // 128, seed=T + K).astype(np.float16)
