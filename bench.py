@@ -73,7 +73,7 @@ def kernel_family(T):
         return "gemv.hip", "gemv_"
     if T <= 16:
         return "skinny.hip", "gemm_skinny_kernel"
-    return "gemm.hip", "gemm_mfma_kernel"
+    return "gemm.hip", "gemm_mfma"
 
 
 def source_digest(T):

@@ -348,6 +348,11 @@ __global__ void __launch_bounds__(GEMM_THREADS) gemm_mfma_kernel(
 // fragments.  Two threads share a row in the unpack (32 columns each, a
 // quarter of them per 16-column sub-step); each thread copies 4 activation
 // segments per step.
+//
+// Tiles are numbered token tile major (tile = ty * ntx + tx).  The last
+// `ntiles mod #CU` tiles would run as a partial final round, so they are
+// split into two 128-row halves (blocks nfull + 2r + h): each wavefront then
+// covers 32 rows, and the final round takes about half as long.
 constexpr int GEMM8_THREADS = 512;
 
 __device__ __forceinline__ void unpack_two_quads(const uint32_t* V, int a, int b0, const Levels& L,
@@ -367,21 +372,27 @@ template <typename AT, int K>
 __global__ void __launch_bounds__(GEMM8_THREADS) gemm_mfma8_kernel(
     const uint32_t* __restrict__ bits, const AT* __restrict__ scales,
     const uint16_t* __restrict__ X, int64_t ldx, float* __restrict__ Y, int64_t ldy, int T, int m,
-    int m_pad, int G) {
+    int m_pad, int G, int ntx, int nfull) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   // buffer b: activations at smem + 2b * TILE_ELEMS, weights right after
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wt = wave & 1, wn = wave >> 1;  // 128-token half, 64-row quarter
-  const int t0 = blockIdx.y * BT;
-  const int n0 = blockIdx.x * BN;
+  const int b = blockIdx.x;
+  const bool whole = b < nfull;
+  const int tile = whole ? b : nfull + ((b - nfull) >> 1);
+  const int JB = whole ? 2 : 1;              // 32-row blocks per wavefront
+  const int tile_rows = whole ? BN : BN / 2;
+  const int wt = wave & 1, wn = wave >> 1;  // 128-token half, row quarter
+  const int t0 = (tile / ntx) * BT;
+  const int n0 = (tile % ntx) * BN + (whole ? 0 : ((b - nfull) & 1) * (BN / 2));
   const int S = G * 2;  // steps of 64 columns
 
   // unpack role: row n0 + tid/2, columns 32 * (tid % 2) .. + 31 of each step
   const int urow = tid >> 1, uhalf = tid & 1;
+  const bool unpacker = urow < tile_rows;  // uniform per wavefront
   const int row = n0 + urow;
-  const bool row_ok = row < m_pad;
+  const bool row_ok = unpacker && row < m_pad;
   const int rowc = row_ok ? row : m_pad - 1;
   const uint32_t row_chunk = (uint32_t)(rowc / kRowBlock) * (uint32_t)(G * K * kRowBlock) +
                              (uint32_t)(rowc % kRowBlock);
@@ -442,7 +453,8 @@ __global__ void __launch_bounds__(GEMM8_THREADS) gemm_mfma8_kernel(
     mask_step(R);
     if (K <= 3 && even) L = make_levels<K>(R.a);
     const uint16_t* xs = smem + 2 * cb * TILE_ELEMS + (wt * 128 + lrow) * LDS_STRIDE + lk;
-    const uint16_t* ws = smem + (2 * cb + 1) * TILE_ELEMS + (wn * 64 + lrow) * LDS_STRIDE + lk;
+    const uint16_t* ws =
+        smem + (2 * cb + 1) * TILE_ELEMS + (wn * 32 * JB + lrow) * LDS_STRIDE + lk;
     uint16_t* xd = smem + 2 * (cb ^ 1) * TILE_ELEMS + (tid >> 3) * LDS_STRIDE + xpart * 8;
     uint4* wd = reinterpret_cast<uint4*>(smem + (2 * (cb ^ 1) + 1) * TILE_ELEMS +
                                          urow * LDS_STRIDE + uhalf * 32);
@@ -454,14 +466,16 @@ __global__ void __launch_bounds__(GEMM8_THREADS) gemm_mfma8_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         av[i] = *reinterpret_cast<const bf16x8*>(xs + i * 32 * LDS_STRIDE + 16 * kk);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        bv[j] = *reinterpret_cast<const bf16x8*>(ws + j * 32 * LDS_STRIDE + 16 * kk);
+      bv[0] = *reinterpret_cast<const bf16x8*>(ws + 16 * kk);
+      if (JB == 2) bv[1] = *reinterpret_cast<const bf16x8*>(ws + 32 * LDS_STRIDE + 16 * kk);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
+        acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[0], acc[i][0], 0, 0, 0);
+      if (JB == 2) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+        for (int i = 0; i < 4; ++i)
+          acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[1], acc[i][1], 0, 0, 0);
+      }
       // a quarter of the next step: one activation segment, 8 weight columns
       *reinterpret_cast<uint4*>(xd + kk * 64 * LDS_STRIDE) = R.x[kk];
       uint32_t out[4];
@@ -474,7 +488,7 @@ __global__ void __launch_bounds__(GEMM8_THREADS) gemm_mfma8_kernel(
 #pragma unroll
         for (int q = 0; q < 4; ++q) out[q] = o32[4 * kk + q];
       }
-      wd[kk] = make_uint4(out[0], out[1], out[2], out[3]);
+      if (unpacker) wd[kk] = make_uint4(out[0], out[1], out[2], out[3]);
     }
   };
 
@@ -488,15 +502,17 @@ __global__ void __launch_bounds__(GEMM8_THREADS) gemm_mfma8_kernel(
     for (int j = 0; j < 4; ++j)
       *reinterpret_cast<uint4*>(smem + (tid >> 3) * LDS_STRIDE + xpart * 8 + j * 64 * LDS_STRIDE) =
           R0.x[j];
-    uint4* wd = reinterpret_cast<uint4*>(smem + TILE_ELEMS + urow * LDS_STRIDE + uhalf * 32);
-    uint32_t out[16];
-    if (K <= 3)
-      unpack_word<K>(R0.w, L, out);
-    else
-      unpack_word_k4(R0.w, R0.a, out);
+    if (unpacker) {
+      uint4* wd = reinterpret_cast<uint4*>(smem + TILE_ELEMS + urow * LDS_STRIDE + uhalf * 32);
+      uint32_t out[16];
+      if (K <= 3)
+        unpack_word<K>(R0.w, L, out);
+      else
+        unpack_word_k4(R0.w, R0.a, out);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      wd[j] = make_uint4(out[4 * j], out[4 * j + 1], out[4 * j + 2], out[4 * j + 3]);
+      for (int j = 0; j < 4; ++j)
+        wd[j] = make_uint4(out[4 * j], out[4 * j + 1], out[4 * j + 2], out[4 * j + 3]);
+    }
   }
   __syncthreads();
   for (int s = 0; s < S; s += 2) {
@@ -513,8 +529,8 @@ __global__ void __launch_bounds__(GEMM8_THREADS) gemm_mfma8_kernel(
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int n = n0 + wn * 64 + j * 32 + lrow;
-      if (n >= m) continue;
+      const int n = n0 + wn * 32 * JB + j * 32 + lrow;
+      if (j >= JB || n >= m) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int t = t0 + wt * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
@@ -523,13 +539,34 @@ __global__ void __launch_bounds__(GEMM8_THREADS) gemm_mfma8_kernel(
     }
 }
 
+// Compute units of the current device (queried once per device).
+int compute_units() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
 template <typename AT, int K>
 void launch_mfma8_k(const Geom& geo, const uint32_t* bits, const AT* scales, const uint16_t* Xb,
                     int64_t T, int64_t ldx, float* Y, int64_t ldy, hipStream_t stream) {
   const size_t lds = 4 * TILE_ELEMS * sizeof(uint16_t);
-  dim3 grid((geo.m + BN - 1) / BN, (unsigned)((T + BT - 1) / BT));
-  hipLaunchKernelGGL((gemm_mfma8_kernel<AT, K>), grid, dim3(GEMM8_THREADS), lds, stream, bits,
-                     scales, Xb, ldx, Y, ldy, (int)T, geo.m, geo.RB * kRowBlock, geo.G);
+  const int ntx = (geo.m + BN - 1) / BN;
+  const int64_t ntiles = (int64_t)ntx * ((T + BT - 1) / BT);
+  // one workgroup per compute unit at a time (the tiles take 147 KB of LDS)
+  const int ncu = compute_units();
+  const int64_t rem = ntiles % ncu;
+  const int64_t nfull = ntiles - rem;
+  hipLaunchKernelGGL((gemm_mfma8_kernel<AT, K>), dim3((unsigned)(nfull + 2 * rem)),
+                     dim3(GEMM8_THREADS), lds, stream, bits, scales, Xb, ldx, Y, ldy, (int)T,
+                     geo.m, geo.RB * kRowBlock, geo.G, ntx, (int)nfull);
 }
 
 template <typename AT>

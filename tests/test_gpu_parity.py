@@ -418,6 +418,19 @@ def test_gemm_prefill_exact_ragged(T, m, n, K, prefill_waves):
     assert np.array_equal(Y, oracle.product(S, A, X))
 
 
+def test_gemm_prefill_exact_whole_and_half_tiles():
+    """More 256 x 256 tiles than compute units (20 x 13 = 260 tiles on 256):
+    the last round's tiles run as 128-row halves; exact regime, every element."""
+    T, m, n, K = 3328, 5120, 256, 3
+    say("gemm prefill whole and half tiles")
+    S = syn.random_signs(K, m, n, seed=91)
+    A = syn.exact_alpha(K, m, n // 128, seed=92).astype(np.float16)
+    X = syn.exact_activations(T, n, seed=93)
+    d, packed = pack_on_gpu(S, A, "f16")
+    Y = gemm(d, packed, X)
+    assert np.array_equal(Y, oracle.product(S, A, X))
+
+
 def test_gemm_identity_activations_give_the_weights():
     """X = identity rows (T = n) in the exact regime: Y = W_hat^T exactly,
     which pins the operand orientation, k order and bf16 rounding of W_hat."""
