@@ -364,18 +364,6 @@ __global__ void __launch_bounds__(NW * kWave) gemv_rows_kernel(
   if (i < m) y[i] = yacc;
 }
 
-// 16-row tile of work item b.  Workgroup b runs on XCD b % 8, so within each
-// full set of 32 tiles (8 row blocks of 64 rows) the items b = 8j + xcd,
-// j = 4u + quarter, take quarter `quarter` of row block 8u + xcd: the four
-// tiles of a row block share one XCD and its L2 lines of scales.  A trailing
-// partial set keeps b.
-__device__ __forceinline__ int tile16_of(int b, int tiles) {
-  const int full = tiles & ~31;
-  if (b >= full) return b;
-  const int xcd = b & 7, j = b >> 3;
-  return (((j >> 2) << 3) + xcd) * 4 + (j & 3);
-}
-
 // Streaming variant: one persistent workgroup per compute unit.  Wavefront w
 // owns group block w (groups 4w .. 4w+3 of the slab); lane (j, r) =
 // (lane / 16, lane % 16) handles row r of the tile and group 4w + j, so one

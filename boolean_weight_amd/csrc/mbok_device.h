@@ -29,6 +29,18 @@ inline Geom make_geom(const mbok_desc* d) {
   return g;
 }
 
+// 16-row tile of work item b.  Workgroup b runs on XCD b % 8, so within each
+// full set of 32 tiles (8 row blocks of 64 rows) the items b = 8j + xcd,
+// j = 4u + quarter, take quarter `quarter` of row block 8u + xcd: the four
+// tiles of a row block share one XCD and its L2 lines of scales.  A trailing
+// partial set keeps b.
+__device__ __forceinline__ int tile16_of(int b, int tiles) {
+  const int full = tiles & ~31;
+  if (b >= full) return b;
+  const int xcd = b & 7, j = b >> 3;
+  return (((j >> 2) << 3) + xcd) * 4 + (j & 3);
+}
+
 // ----------------------------------------------------------- conversions
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {

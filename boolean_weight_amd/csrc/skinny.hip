@@ -35,6 +35,7 @@
 // partial sums of the wavefronts are added in LDS in a fixed wave order, so
 // results are deterministic.
 #include <stdlib.h>
+#include <string.h>
 
 #include "mbok_device.h"
 #include "mbok_launch.h"
@@ -191,6 +192,127 @@ __global__ void __launch_bounds__(1024) gemm_skinny_kernel(
   }
 }
 
+// Streaming form (the default): one persistent workgroup per compute unit.
+// Wavefront w owns group block w of the slab (groups 4w .. 4w+3, at most 8
+// blocks: slabs of up to 32 groups), loads the activation fragments of its
+// groups once per slab, and walks the workgroup's 16-row tiles (b, b + grid,
+// ... through tile16_of), loading the sign chunks and scales of tile t + 1
+// while tile t is expanded and multiplied.  So the weight stream overlaps the
+// expansion and the MFMAs, and activations are read once per workgroup
+// instead of once per tile.  Partial sums of up to JMAX tiles stay in
+// registers; each tile is summed over wavefronts in a fixed order at the end.
+template <typename AT, int K>
+struct SkinnyLoads {
+  u32x4 w[K];
+  AT a[K];
+};
+
+template <typename AT, int K, int JMAX>
+__global__ void __launch_bounds__(512) gemm_skinny_stream_kernel(
+    const u32x4* __restrict__ bits, const AT* __restrict__ scales,
+    const uint16_t* __restrict__ X, int64_t ldx, float* __restrict__ Y, int64_t ldy, int T,
+    int m, int G, int slab_groups, int tiles) {
+  extern __shared__ float red[];  // [JMAX][NW][4][64] partial sums
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int NW = blockDim.x >> 6;
+  const int i = lane & 15, q = lane >> 4;
+  const int ntl = (tiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;  // <= JMAX
+  const bool tok_ok = i < T;
+  const uint16_t* xrow = X + (int64_t)(tok_ok ? i : 0) * ldx + 32 * q;
+  const uint32_t mask = __builtin_amdgcn_readfirstlane(0x80008000u);
+  uint32_t ones;
+  asm("v_mov_b32 %0, 0x3f803f80" : "=v"(ones));
+
+  f32x4 yacc[JMAX];
+#pragma unroll
+  for (int t = 0; t < JMAX; ++t) yacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int g0 = 0; g0 < G; g0 += slab_groups) {
+    const int sg = min(slab_groups, G - g0);
+    const int nj = min(4, sg - 4 * wave);  // groups of this wavefront's block
+    if (nj <= 0) continue;                 // uniform per wavefront
+    const int gb = g0 + 4 * wave;
+    const int gq = gb + (q < nj ? q : nj - 1);  // group loaded by 16-lane block q
+    u32x4 xv[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        xv[j][s] = (tok_ok && j < nj) ? *reinterpret_cast<const u32x4*>(
+                                            xrow + (int64_t)kGroup * (gb + j) + 8 * s)
+                                      : u32x4{0u, 0u, 0u, 0u};
+    auto load = [&](int t, SkinnyLoads<AT, K>& L) {
+      const int row = tile16_of(blockIdx.x + t * gridDim.x, tiles) * 16 + i;
+      const int64_t c = ((int64_t)(row / kRowBlock) * G + gq) * K * kRowBlock + row % kRowBlock;
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        L.w[k] = bits[c + k * kRowBlock];
+        L.a[k] = scales[c + k * kRowBlock];
+      }
+    };
+    auto compute = [&](const SkinnyLoads<AT, K>& L, f32x4 acc) {
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        uint32_t w[4] = {L.w[k].x, L.w[k].y, L.w[k].z, L.w[k].w};
+        transpose4(w);  // w[j] = word q of row i, group gb + j
+        uint32_t a[4];
+        spread4(scale_bits<AT>(L.a[k]), a);  // a[j] = scale of row i, group gb + j
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (j >= nj) break;
+          const uint32_t p01 = __builtin_amdgcn_perm(w[j], w[j], 0x01010000u);
+          const uint32_t p23 = __builtin_amdgcn_perm(w[j], w[j], 0x03030202u);
+          f32x4 S = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const int se = 7 - 2 * s, so = 6 - 2 * s;
+            const u32x4 bb = u32x4{signed_ones(p01 << se, mask, ones),
+                                   signed_ones(p23 << se, mask, ones),
+                                   signed_ones(p01 << so, mask, ones),
+                                   signed_ones(p23 << so, mask, ones)};
+            S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xv[j][s]),
+                                                        __builtin_bit_cast(bf16x8, bb), S, 0, 0,
+                                                        0);
+          }
+          const float sc = scale_value<AT>(a[j]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(-sc, S[r], acc[r]);
+        }
+      }
+      return acc;
+    };
+    SkinnyLoads<AT, K> LA, LB;
+    load(0, LA);
+#pragma unroll
+    for (int t = 0; t < JMAX; t += 2) {
+      if (t >= ntl) break;
+      if (t + 1 < ntl) load(t + 1, LB);
+      yacc[t] = compute(LA, yacc[t]);
+      if (t + 1 >= ntl) break;
+      if (t + 2 < ntl) load(t + 2, LA);
+      yacc[t + 1] = compute(LB, yacc[t + 1]);
+    }
+  }
+
+#pragma unroll
+  for (int t = 0; t < JMAX; ++t) {
+    if (t >= ntl) break;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[(((t * NW) + wave) * 4 + r) * 64 + lane] = yacc[t][r];
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < ntl * 256; idx += blockDim.x) {
+    const int t = idx >> 8, e = idx & 255;
+    float sum = 0.f;
+    for (int w = 0; w < NW; ++w) sum += red[(t * NW + w) * 256 + e];
+    const int l = e & 63, r = e >> 6;
+    const int tok = 4 * (l >> 4) + r;
+    const int row = tile16_of(blockIdx.x + t * gridDim.x, tiles) * 16 + (l & 15);
+    if (tok < T && row < m) Y[(int64_t)tok * ldy + row] = sum;
+  }
+}
+
 int env_int(const char* name, int fallback) {
   const char* v = getenv(name);
   return (v && *v) ? atoi(v) : fallback;
@@ -204,6 +326,23 @@ void launch_k(const Geom& geo, const u32x4* bits, const AT* scales, const uint16
                      bits, scales, X, ldx, Y, ldy, T, geo.m, geo.G);
 }
 
+constexpr int kSkinnyJ = 8;  // tiles per persistent workgroup (registers)
+
+template <typename AT, int K>
+void launch_stream_k(const Geom& geo, const u32x4* bits, const AT* scales, const uint16_t* X,
+                     int64_t ldx, float* Y, int64_t ldy, int T, hipStream_t stream) {
+  // slabs of at most 32 groups: one wavefront per block of 4 groups, at most 8
+  const int nslabs = (geo.G + 31) / 32;
+  const int slab = (geo.G + nslabs - 1) / nslabs;
+  const int NW = (slab + 3) / 4;
+  const int tiles = geo.RB * 4;
+  int grid = tiles < 256 ? tiles : 256;
+  if (grid * kSkinnyJ < tiles) grid = (tiles + kSkinnyJ - 1) / kSkinnyJ;
+  const size_t lds = (size_t)kSkinnyJ * NW * 256 * sizeof(float);
+  hipLaunchKernelGGL((gemm_skinny_stream_kernel<AT, K, kSkinnyJ>), dim3(grid), dim3(64 * NW), lds,
+                     stream, bits, scales, X, ldx, Y, ldy, T, geo.m, geo.G, slab, tiles);
+}
+
 template <typename AT>
 int launch_at(const Geom& geo, const void* packed, const void* X, int64_t ldx, float* Y,
               int64_t ldy, int T, hipStream_t stream) {
@@ -211,6 +350,22 @@ int launch_at(const Geom& geo, const void* packed, const void* X, int64_t ldx, f
   const AT* scales = reinterpret_cast<const AT*>(reinterpret_cast<const char*>(packed) +
                                                  geo.bits_bytes);
   const uint16_t* Xb = reinterpret_cast<const uint16_t*>(X);
+  // streaming pays off when workgroups get several tiles of one slab (many
+  // rows, at most 32 groups) or when 16 tokens make the activation fragments
+  // worth keeping; MBOK_SKINNY_VARIANT=stream|blocks overrides
+  const char* v = getenv("MBOK_SKINNY_VARIANT");
+  bool streaming = (geo.G <= 32 && geo.m >= 8192) || T >= 16;
+  if (v && strcmp(v, "blocks") == 0) streaming = false;
+  if (v && strcmp(v, "stream") == 0) streaming = true;
+  if (streaming) {
+    switch (geo.K) {
+      case 1: launch_stream_k<AT, 1>(geo, bits, scales, Xb, ldx, Y, ldy, T, stream); break;
+      case 2: launch_stream_k<AT, 2>(geo, bits, scales, Xb, ldx, Y, ldy, T, stream); break;
+      case 3: launch_stream_k<AT, 3>(geo, bits, scales, Xb, ldx, Y, ldy, T, stream); break;
+      default: launch_stream_k<AT, 4>(geo, bits, scales, Xb, ldx, Y, ldy, T, stream); break;
+    }
+    return hipGetLastError() == hipSuccess ? MBOK_OK : MBOK_ERR_HIP;
+  }
   // about 4800 wavefronts over the chip (~5 per SIMD), at most 16 per
   // workgroup; measured best for 4096 to 27648 rows
   const int tiles = geo.RB * 4;

@@ -46,10 +46,12 @@ GEMV_VARIANTS = {
     # matrix-core kernel of the few-token product at one token (bf16 x only;
     # fp32 x keeps the table kernels)
     "skinny": {"MBOK_GEMV_VARIANT": "skinny"},
-    "skinny_nw3": {"MBOK_GEMV_VARIANT": "skinny", "MBOK_SKINNY_NW": "3"},
+    "skinny_blocks_nw3": {"MBOK_GEMV_VARIANT": "skinny", "MBOK_SKINNY_VARIANT": "blocks",
+                          "MBOK_SKINNY_NW": "3"},
 }
 
-ENV_KEYS = ("MBOK_GEMV_VARIANT", "MBOK_GEMV_R", "MBOK_GEMV_NW", "MBOK_SKINNY_NW")
+ENV_KEYS = ("MBOK_GEMV_VARIANT", "MBOK_GEMV_R", "MBOK_GEMV_NW", "MBOK_SKINNY_NW",
+            "MBOK_SKINNY_VARIANT")
 
 
 def _swap_env(new: dict) -> dict:
@@ -75,13 +77,15 @@ def gemv_variant(request):
     _restore_env(old)
 
 
-# launch shapes of the few-token kernel: wavefronts per workgroup (uneven
-# group ranges when NW does not divide G, one wavefront doing every group)
+# the few-token kernels: the streaming default, and the per-tile "blocks"
+# form with several wavefronts per workgroup (uneven group ranges when NW
+# does not divide G, one wavefront doing every group)
 SKINNY_SHAPES = {
     "default": {},
-    "nw3": {"MBOK_SKINNY_NW": "3"},
-    "nw7": {"MBOK_SKINNY_NW": "7"},
-    "nw1": {"MBOK_SKINNY_NW": "1"},
+    "stream": {"MBOK_SKINNY_VARIANT": "stream"},
+    "blocks_nw3": {"MBOK_SKINNY_VARIANT": "blocks", "MBOK_SKINNY_NW": "3"},
+    "blocks_nw7": {"MBOK_SKINNY_VARIANT": "blocks", "MBOK_SKINNY_NW": "7"},
+    "blocks_nw1": {"MBOK_SKINNY_VARIANT": "blocks", "MBOK_SKINNY_NW": "1"},
 }
 
 
@@ -346,7 +350,8 @@ def test_gemm_exact_regime(T, K):
 
 @pytest.mark.parametrize("K", [1, 2, 3, 4])
 @pytest.mark.parametrize("T,m,n", [(2, 1, 128), (5, 65, 384), (8, 130, 1152), (16, 200, 640),
-                                   (13, 64, 2048)])
+                                   (13, 64, 2048), (3, 65, 5120), (16, 70, 11008),
+                                   (5, 4160, 128)])
 @pytest.mark.parametrize("dt", ["f16", "f32"])
 def test_gemm_skinny_exact(T, m, n, K, dt, skinny_shape):
     """Few-token kernel in the exact regime (integer x, power-of-two scales):
