@@ -72,7 +72,7 @@ def kernel_family(T):
     if T == 1:
         return "gemv.hip", "gemv_"
     if T <= 16:
-        return "skinny.hip", "gemm_skinny_kernel"
+        return "skinny.hip", "gemm_skinny"
     return "gemm.hip", "gemm_mfma"
 
 
