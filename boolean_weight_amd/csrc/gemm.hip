@@ -460,14 +460,25 @@ __global__ void __launch_bounds__(GEMM8_THREADS) gemm_mfma8_kernel(
                                          urow * LDS_STRIDE + uhalf * 32);
     uint32_t V[4];
     if (K <= 3) word_selectors<K>(R.w, V);
+    // fragments of sub-step kk + 1 are read while the MFMAs of kk run
+    bf16x8 pa[2][4], pb[2][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pa[0][i] = *reinterpret_cast<const bf16x8*>(xs + i * 32 * LDS_STRIDE);
+    pb[0][0] = *reinterpret_cast<const bf16x8*>(ws);
+    if (JB == 2) pb[0][1] = *reinterpret_cast<const bf16x8*>(ws + 32 * LDS_STRIDE);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      bf16x8 av[4], bv[2];
+      if (kk < 3) {
+        const int nb = (kk + 1) & 1;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        av[i] = *reinterpret_cast<const bf16x8*>(xs + i * 32 * LDS_STRIDE + 16 * kk);
-      bv[0] = *reinterpret_cast<const bf16x8*>(ws + 16 * kk);
-      if (JB == 2) bv[1] = *reinterpret_cast<const bf16x8*>(ws + 32 * LDS_STRIDE + 16 * kk);
+        for (int i = 0; i < 4; ++i)
+          pa[nb][i] = *reinterpret_cast<const bf16x8*>(xs + i * 32 * LDS_STRIDE + 16 * (kk + 1));
+        pb[nb][0] = *reinterpret_cast<const bf16x8*>(ws + 16 * (kk + 1));
+        if (JB == 2)
+          pb[nb][1] = *reinterpret_cast<const bf16x8*>(ws + 32 * LDS_STRIDE + 16 * (kk + 1));
+      }
+      const bf16x8* av = pa[kk & 1];
+      const bf16x8* bv = pb[kk & 1];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[0], acc[i][0], 0, 0, 0);
