@@ -24,7 +24,7 @@ Sources (page title, then the section on that page):
        "Extracción Sucesiva"): each further kernel is fitted to the residual
        error left by the previous ones.
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
   * scale structure: one scale per (kernel k, output row i, group g of 128
     consecutive input columns), as the group-wise strategy of [RN];
   * initialisation: greedy residual binarization, i.e. the residual chain of
@@ -102,6 +102,114 @@ def residual_binarize(W: np.ndarray, K: int, group: int = GROUP,
     if return_chain:
         return S, A, R, chain
     return S, A, R
+
+
+def _ls_scales_exact(w: np.ndarray, b: np.ndarray):
+    """Exact least-squares scales of one group for fixed signs: the solution
+    of the normal equations (B^T B) a = B^T w as Fractions, or None when the
+    integer Gram matrix B^T B is singular.  w: float values (n_g,), b: +-1
+    (K, n_g)."""
+    K = b.shape[0]
+    wf = [Fraction(float(v)) for v in w]
+    G = [[Fraction(int(np.dot(b[k].astype(np.int64), b[l].astype(np.int64)))) for l in range(K)]
+         for k in range(K)]
+    r = [sum((wf[j] if b[k, j] > 0 else -wf[j] for j in range(len(wf))), Fraction(0))
+         for k in range(K)]
+    # Gauss-Jordan elimination on Fractions (exact)
+    M = [G[k] + [r[k]] for k in range(K)]
+    for c in range(K):
+        piv = next((i for i in range(c, K) if M[i][c] != 0), None)
+        if piv is None:
+            return None
+        M[c], M[piv] = M[piv], M[c]
+        for i in range(K):
+            if i != c and M[i][c] != 0:
+                f = M[i][c] / M[c][c]
+                M[i] = [M[i][j] - f * M[c][j] for j in range(K + 1)]
+    return [M[k][K] / M[k][k] for k in range(K)]
+
+
+def _round_fraction(q: Fraction, alpha_dtype: str) -> float:
+    """Nearest-even rounding of an exact rational to the scale dtype."""
+    if alpha_dtype == "f32":
+        dt, mant = np.float32, 24
+    else:
+        dt, mant = np.float16, 11
+    if q == 0:
+        return 0.0
+    sign = -1 if q < 0 else 1
+    a = abs(q)
+    # exponent of the leading bit, clamped to the subnormal range
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    emin = -14 if alpha_dtype == "f16" else -126
+    e = max(e, emin)
+    quantum = Fraction(2) ** (e - mant + 1)
+    t = a / quantum
+    n = t.numerator // t.denominator
+    rem = t - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    v = float(sign * n * quantum)
+    return float(dt(v))  # overflow becomes inf; the value is exact otherwise
+
+
+def _nearest_levels(w: np.ndarray, a: np.ndarray) -> np.ndarray:
+    """Signs (K, n_g) whose level sum_k a_k b_k is nearest to each w, the
+    distance taken in float64; ties go to the larger level, then to the
+    larger pattern index sum_k [b_k = +1] 2^k."""
+    K = a.shape[0]
+    best = np.empty((K, w.shape[0]), dtype=np.int8)
+    for j in range(w.shape[0]):
+        wj = float(w[j])
+        choice = None
+        for idx in range(2 ** K):
+            b = [1 if (idx >> k) & 1 else -1 for k in range(K)]
+            lev = 0.0
+            for k in range(K):  # exact: K <= 4 values of the scale dtype
+                lev += float(a[k]) * b[k]
+            key = (abs(wj - lev), -lev, -idx)
+            if choice is None or key < choice[0]:
+                choice = (key, b)
+        best[:, j] = choice[1]
+    return best
+
+
+def refit(W: np.ndarray, S: np.ndarray, A: np.ndarray, rounds: int = 2,
+          group: int = GROUP, alpha_dtype: str = "f16"):
+    """Alternating refit of the kernels of one layer for the weight itself
+    ([RN] 关键设计, efficient scale optimisation: with the B_k fixed the scales
+    have a closed-form least-squares solution, and B and alpha are optimised
+    in turn, fixing one to update the other).  Per (row, group):
+        repeat `rounds` times: alpha-step, then B-step; finally an alpha-step
+        alpha-step: alpha = exact solution of (B^T B) alpha = B^T w, rounded
+                    once (nearest-even) to the dtype; kept as is when the
+                    integer Gram matrix is singular
+        B-step:     each weight takes the sign pattern of its nearest level
+                    sum_k alpha_k b_k (see _nearest_levels)
+    W: (m, n) float32 values; S: (K, m, n) +-1; A: (K, m, G) scales.
+    Returns new (S, A)."""
+    S = S.copy()
+    A = A.astype(np.float64).copy()
+    K, m, n = S.shape
+    G = n // group
+    for i in range(m):
+        for g in range(G):
+            cols = slice(g * group, (g + 1) * group)
+            w = W[i, cols]
+            b = S[:, i, cols]
+            a = A[:, i, g].copy()
+            for step in range(2 * rounds + 1):
+                if step % 2 == 0:
+                    q = _ls_scales_exact(w, b)
+                    if q is not None:
+                        a = np.array([_round_fraction(v, alpha_dtype) for v in q])
+                else:
+                    b = _nearest_levels(w, a)
+            S[:, i, cols] = b
+            A[:, i, g] = a
+    return S, A.astype(np.float16 if alpha_dtype == "f16" else np.float32)
 
 
 def dequantize(S: np.ndarray, A: np.ndarray, group: int = GROUP) -> np.ndarray:

@@ -62,6 +62,34 @@ MUTATIONS = [
      'axis=-1, bitorder="little")', 'axis=-1, bitorder="big")'),
     ("unpack_bit_means_minus", "unpack",
      "np.where(bits[:, :m, :] == 1, 1, -1)", "np.where(bits[:, :m, :] == 1, -1, 1)"),
+    ("refit_rhs_unsigned", "_ls_scales_exact",
+     "wf[j] if b[k, j] > 0 else -wf[j]", "abs(wf[j])"),
+    ("refit_gram_diagonal_only", "_ls_scales_exact",
+     "Fraction(int(np.dot(b[k].astype(np.int64), b[l].astype(np.int64))))",
+     "Fraction(len(wf) if k == l else 0)"),
+    ("refit_pivot_not_divided", "_ls_scales_exact",
+     "return [M[k][K] / M[k][k] for k in range(K)]", "return [M[k][K] for k in range(K)]"),
+    ("refit_round_ties_odd", "_round_fraction",
+     "(rem == Fraction(1, 2) and n % 2 == 1)", "(rem == Fraction(1, 2) and n % 2 == 0)"),
+    ("refit_round_no_subnormal_clamp", "_round_fraction",
+     "e = max(e, emin)", "e = e"),
+    ("refit_round_truncates", "_round_fraction",
+     "if rem > Fraction(1, 2) or", "if False and"),
+    ("refit_level_tie_to_smaller", "_nearest_levels",
+     "key = (abs(wj - lev), -lev, -idx)", "key = (abs(wj - lev), lev, -idx)"),
+    ("refit_pattern_tie_to_smaller_index", "_nearest_levels",
+     "key = (abs(wj - lev), -lev, -idx)", "key = (abs(wj - lev), -lev, idx)"),
+    ("refit_level_sign_dropped", "_nearest_levels",
+     "lev += float(a[k]) * b[k]", "lev += float(a[k])"),
+    ("refit_steps_swapped", "refit",
+     "if step % 2 == 0:", "if step % 2 == 1:"),
+    ("refit_one_round_short", "refit",
+     "for step in range(2 * rounds + 1):", "for step in range(2 * rounds - 1):"),
+    ("refit_no_final_scale_step", "refit",
+     "for step in range(2 * rounds + 1):", "for step in range(2 * rounds):"),
+    ("refit_singular_zeroes_scales", "refit",
+     "if q is not None:\n                        a = np.array([_round_fraction(v, alpha_dtype) for v in q])",
+     "a = np.array([_round_fraction(v, alpha_dtype) for v in q]) if q is not None else 0 * a"),
 ]
 
 
