@@ -18,6 +18,7 @@ __all__ = [
     "MBOK_F32", "MBOK_F16", "MBOK_BF16", "MBOK_GROUP", "MBOK_MAX_K", "MBOK_MAX_T",
     "MbokError", "mbok_desc", "library_path", "load_library",
     "mbok_desc_init", "mbok_packed_bytes", "mbok_alpha_bytes", "mbok_residual_binarize",
+    "mbok_refit", "MBOK_MAX_REFIT_ROUNDS",
     "mbok_pack", "mbok_gemv", "mbok_gemv_workspace_bytes", "mbok_gemm", "mbok_status_str",
     "mbok_version", "workspace_for",
     "alpha_torch_dtype", "quantize_and_pack",
@@ -29,6 +30,7 @@ MBOK_ROW_BLOCK = 64
 MBOK_MAX_K = 4
 MBOK_MAX_T = 65536
 MBOK_LAYOUT_L64 = 1
+MBOK_MAX_REFIT_ROUNDS = 64
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -71,6 +73,7 @@ def load_library() -> ctypes.CDLL:
         "mbok_packed_bytes": (SZ, [D]),
         "mbok_alpha_bytes": (SZ, [D]),
         "mbok_residual_binarize": (ctypes.c_int, [D, P, I64, P, P, P, P]),
+        "mbok_refit": (ctypes.c_int, [D, P, I64, P, P, I32, P]),
         "mbok_pack": (ctypes.c_int, [D, P, P, P, P]),
         "mbok_gemv_workspace_bytes": (SZ, [D]),
         "mbok_gemv": (ctypes.c_int, [D, P, P, I32, P, P, P]),
@@ -176,6 +179,29 @@ def mbok_residual_binarize(d: mbok_desc, W: torch.Tensor, signs: torch.Tensor,
     _check(load_library().mbok_residual_binarize(
         ctypes.byref(d), W.data_ptr(), ldw, signs.data_ptr(), alpha.data_ptr(), fptr,
         _stream(stream)), "mbok_residual_binarize")
+
+
+def mbok_refit(d: mbok_desc, W: torch.Tensor, signs: torch.Tensor, alpha: torch.Tensor,
+               rounds: int = 2, stream=None) -> None:
+    """Alternating least-squares refit of signs int8 [K, m, n] and alpha
+    [K, m, n/128] (both updated in place) for W fp32 [m, ldw]."""
+    _dev(W, "W"), _dev(signs, "signs"), _dev(alpha, "alpha")
+    if W.dtype != torch.float32 or W.dim() != 2 or W.shape[0] != d.m or W.shape[1] < d.n:
+        raise ValueError("W must be float32 [m, >= n]")
+    if W.stride(1) != 1:
+        raise ValueError("W rows must be contiguous")
+    ldw = W.stride(0)
+    if _nbytes_from(W) < ((d.m - 1) * ldw + d.n) * 4:
+        raise ValueError("W buffer too small")
+    if signs.dtype != torch.int8 or not signs.is_contiguous() or \
+            _nbytes_from(signs) < d.K * d.m * d.n:
+        raise ValueError("signs must be contiguous int8 with K*m*n elements")
+    if alpha.dtype != alpha_torch_dtype(d.alpha_dtype) or not alpha.is_contiguous() \
+            or _nbytes_from(alpha) < mbok_alpha_bytes(d):
+        raise ValueError("alpha has the wrong dtype or size")
+    _check(load_library().mbok_refit(ctypes.byref(d), W.data_ptr(), ldw, signs.data_ptr(),
+                                     alpha.data_ptr(), int(rounds), _stream(stream)),
+           "mbok_refit")
 
 
 def mbok_pack(d: mbok_desc, signs: torch.Tensor, alpha: torch.Tensor, packed: torch.Tensor,

@@ -69,6 +69,19 @@ int mbok_residual_binarize(const mbok_desc* d, const float* W, int64_t ldw, int8
   return mbok::launch_residual_binarize(d, W, ldw, signs, alpha, flag, (hipStream_t)stream);
 }
 
+int mbok_refit(const mbok_desc* d, const float* W, int64_t ldw, int8_t* signs, void* alpha,
+               int32_t rounds, void* stream) {
+  int st = check_desc(d);
+  if (st != MBOK_OK) return st;
+  if (!W || !signs || !alpha) return MBOK_ERR_INVALID_ARG;
+  if (ldw < d->n) return MBOK_ERR_INVALID_ARG;
+  if (rounds < 0 || rounds > MBOK_MAX_REFIT_ROUNDS || rounds > mbok::refit_max_rounds())
+    return MBOK_ERR_INVALID_ARG;
+  if (!aligned(W, 16) || !aligned(signs, 16) || !aligned(alpha, 16) || (ldw % 4) != 0)
+    return MBOK_ERR_ALIGN;
+  return mbok::launch_refit(d, W, ldw, signs, alpha, rounds, (hipStream_t)stream);
+}
+
 int mbok_pack(const mbok_desc* d, const int8_t* signs, const void* alpha, void* packed,
               void* stream) {
   int st = check_desc(d);

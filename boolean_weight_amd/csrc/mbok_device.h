@@ -41,6 +41,45 @@ __device__ __forceinline__ int tile16_of(int b, int tiles) {
   return (((j >> 2) << 3) + xcd) * 4 + (j & 3);
 }
 
+// ------------------------------------------------ error-free float64 sums
+
+// error-free a + b = s + e (Knuth's TwoSum)
+__device__ __forceinline__ void two_sum(double a, double b, double& s, double& e) {
+  s = a + b;
+  double bb = s - a;
+  e = (a - (s - bb)) + (b - bb);
+}
+
+// (hi, lo) += (bhi, blo), renormalised.  Exact whenever the exact sum, and
+// every pair involved, are multiples of one power of two q with magnitudes
+// below about 2^103 q.
+__device__ __forceinline__ void dd_add(double& hi, double& lo, double bhi, double blo) {
+  double s, e;
+  two_sum(hi, bhi, s, e);
+  e += lo + blo;
+  double h2 = s + e;
+  lo = e - (h2 - s);
+  hi = h2;
+}
+
+// Sum of the (hi, lo) pairs of all 64 lanes by a butterfly; every lane ends
+// with the same bits because each combine puts the lower lane's pair first.
+__device__ __forceinline__ void wave_sum_dd(double& hi, double& lo, int lane) {
+#pragma unroll
+  for (int mask = 1; mask < kWave; mask <<= 1) {
+    double ohi = __shfl_xor(hi, mask, kWave);
+    double olo = __shfl_xor(lo, mask, kWave);
+    if (lane & mask) {
+      double th = ohi, tl = olo;
+      dd_add(th, tl, hi, lo);
+      hi = th;
+      lo = tl;
+    } else {
+      dd_add(hi, lo, ohi, olo);
+    }
+  }
+}
+
 // ----------------------------------------------------------- conversions
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {

@@ -11,6 +11,9 @@ namespace mbok {
 
 int launch_residual_binarize(const mbok_desc* d, const float* W, int64_t ldw, int8_t* signs,
                              void* alpha, int32_t* flag, hipStream_t stream);
+int launch_refit(const mbok_desc* d, const float* W, int64_t ldw, int8_t* signs, void* alpha,
+                 int rounds, hipStream_t stream);
+int refit_max_rounds();
 int launch_pack(const mbok_desc* d, const int8_t* signs, const void* alpha, void* packed,
                 hipStream_t stream);
 int launch_gemv(const mbok_desc* d, const void* packed, const void* x, int32_t x_dtype,

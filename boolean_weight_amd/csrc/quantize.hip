@@ -17,27 +17,6 @@
 namespace mbok {
 namespace {
 
-// error-free a + b = s + e (Knuth's TwoSum)
-__device__ __forceinline__ void two_sum(double a, double b, double& s, double& e) {
-  s = a + b;
-  double bb = s - a;
-  e = (a - (s - bb)) + (b - bb);
-}
-
-// (hi, lo) += (bhi, blo), renormalised
-__device__ __forceinline__ void dd_add(double& hi, double& lo, double bhi, double blo) {
-  double s, e;
-  two_sum(hi, bhi, s, e);
-  e += lo + blo;
-  double h2 = s + e;
-  lo = e - (h2 - s);
-  hi = h2;
-}
-
-__device__ __forceinline__ double shfl_xor_d(double v, int mask) {
-  return __shfl_xor(v, mask, kWave);
-}
-
 template <bool F16>
 __global__ void __launch_bounds__(256) residual_binarize_kernel(
     const float* __restrict__ W, int64_t ldw, int m, int n, int K,
@@ -60,20 +39,7 @@ __global__ void __launch_bounds__(256) residual_binarize_kernel(
     const double s1 = (r1 >= 0.0) ? 1.0 : -1.0;
     double hi, lo;
     two_sum(fabs(r0), fabs(r1), hi, lo);
-#pragma unroll
-    for (int mask = 1; mask < kWave; mask <<= 1) {
-      double ohi = shfl_xor_d(hi, mask);
-      double olo = shfl_xor_d(lo, mask);
-      // combine in a lane-independent order so every lane ends with the same bits
-      if (lane & mask) {
-        double th = ohi, tl = olo;
-        dd_add(th, tl, hi, lo);
-        hi = th;
-        lo = tl;
-      } else {
-        dd_add(hi, lo, ohi, olo);
-      }
-    }
+    wave_sum_dd(hi, lo, lane);
     const double a = (hi + lo) / (double)kGroup;  // one rounding, then exact /128
     double a_st;
     const int64_t aidx = ((int64_t)k * m + i) * G + g;

@@ -155,6 +155,45 @@ int mbok_residual_binarize(const mbok_desc* d, const float* W, int64_t ldw,
                            int8_t* signs, void* alpha, int32_t* flag,
                            void* stream);
 
+/* Largest `rounds` accepted by mbok_refit. */
+#define MBOK_MAX_REFIT_ROUNDS 64
+
+/*
+ * Alternating least-squares refit of K Boolean kernels and their scales for
+ * the weight W they approximate ([RN] 关键设计, efficient scale optimisation:
+ * with the Boolean matrices fixed the scales have a closed-form least-squares
+ * solution, and signs and scales are optimised in turn).  Usually run on the
+ * output of mbok_residual_binarize, before mbok_pack.  Per (row i, group g),
+ * with w the 128 weights of the group and b_k its signs:
+ *     repeat `rounds` times: scale step, sign step; then one scale step
+ *     scale step: alpha = exact solution of (B^T B) alpha = B^T w, rounded
+ *                 once to nearest-even in the alpha dtype; when the integer
+ *                 K x K matrix B^T B is singular the scales are kept
+ *     sign step:  each weight takes the signs of its nearest level
+ *                 sum_k alpha_k b_k (float64 levels summed in k order and
+ *                 float64 distances; a tie goes to the larger level, then to
+ *                 the larger pattern index sum_k [b_k = +1] 2^k)
+ * rounds = 0 only re-solves the scales.  With K = 1 nothing changes (the
+ * least-squares scale of sign(w) is mean |w|).  Scales may come out
+ * negative.
+ *  W       device, fp32, row-major [m, ldw], ldw >= n (elements); read only.
+ *  signs   device, int8 [K][m][n], read and overwritten in place with +1 /
+ *          -1; an entry >= 0 is read as +1.
+ *  alpha   device, [K][m][n/128] of d->alpha_dtype (natural order), read
+ *          and overwritten in place.
+ *  rounds  0 .. MBOK_MAX_REFIT_ROUNDS.
+ * The scale step is exact (one rounding of the rational solution) whenever,
+ * within each group, the nonzero weights' magnitudes lie within a factor 2^48
+ * of one another; otherwise the solution is accurate to about 2^-100 before
+ * its rounding.  NaN or Inf weights give unspecified outputs for their
+ * groups (mbok_residual_binarize reports them).
+ * Errors: INVALID_ARG (NULL, ldw < n, rounds out of range),
+ * SHAPE/DTYPE/UNSUPPORTED from d, ALIGN (W, signs or alpha not 16-byte
+ * aligned, ldw % 4 != 0), HIP.
+ */
+int mbok_refit(const mbok_desc* d, const float* W, int64_t ldw, int8_t* signs,
+               void* alpha, int32_t rounds, void* stream);
+
 /*
  * Packs Boolean kernels and their scales into MBOK_LAYOUT_L64 (see the top
  * of this header).  Any +-1 signs are accepted, e.g. those of a finetuned

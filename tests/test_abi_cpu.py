@@ -28,7 +28,7 @@ def lib():
 
 def test_header_declares_the_boundary():
     fns = header_functions()
-    for name in ("mbok_residual_binarize", "mbok_pack", "mbok_gemv", "mbok_gemm"):
+    for name in ("mbok_residual_binarize", "mbok_refit", "mbok_pack", "mbok_gemv", "mbok_gemm"):
         assert name in fns
 
 
@@ -130,6 +130,17 @@ def test_compute_calls_validate_before_launch(lib):
     assert lib.mbok_gemm(R(d), A16, A16, bw.MBOK_BF16, 4, 128, A16, 64, None) == -1
     assert lib.mbok_gemm(R(d), A16, A16, bw.MBOK_BF16, 4, 256, A16, 63, None) == -1
     assert lib.mbok_residual_binarize(R(d), A16, 128, A16, A16, None, None) == -1
+    # the refit: NULLs, leading dimension, rounds, alignment
+    assert lib.mbok_refit(R(d), None, 256, A16, A16, 2, None) == -1
+    assert lib.mbok_refit(R(d), A16, 256, None, A16, 2, None) == -1
+    assert lib.mbok_refit(R(d), A16, 256, A16, None, 2, None) == -1
+    assert lib.mbok_refit(R(d), A16, 128, A16, A16, 2, None) == -1
+    assert lib.mbok_refit(R(d), A16, 256, A16, A16, -1, None) == -1
+    assert lib.mbok_refit(R(d), A16, 256, A16, A16, bw.MBOK_MAX_REFIT_ROUNDS + 1, None) == -1
+    assert lib.mbok_refit(R(d), A16, 258, A16, A16, 2, None) == -4
+    assert lib.mbok_refit(R(d), A16, 256, MIS, A16, 2, None) == -4
+    assert lib.mbok_refit(R(d), A16, 256, A16, MIS, 2, None) == -4
+    assert lib.mbok_refit(R(_desc(K=5)), A16, 256, A16, A16, 2, None) == -6
     # descriptors edited by hand
     assert lib.mbok_gemv(R(_desc(group=64)), A16, A16, bw.MBOK_BF16, A16, None, None) == -6
     assert lib.mbok_gemv(R(_desc(layout=2)), A16, A16, bw.MBOK_BF16, A16, None, None) == -6
