@@ -51,6 +51,10 @@ def parse():
                          "profile record of the workload given by --config/--K/--T")
     ap.add_argument("--command", default="", help="with --summarize: the commands that made "
                                                   "the rocprofv3 outputs, for the record")
+    ap.add_argument("--quantizer", action="store_true",
+                    help="time the setup kernels instead (greedy quantizer, refit, pack) on "
+                         "every linear of the workload; prints one JSON line of its own")
+    ap.add_argument("--refit-rounds", type=int, default=2)
     ap.add_argument("--extra", nargs="*", default=[],
                     help="with --summarize: more --pmc output dirs of --calibrate-copy runs; "
                          "every counter in them is reported per dominant call")
@@ -237,6 +241,9 @@ def main():
                    ("gate_up_proj", 2 * 13824, 5120), ("down_proj", 5120, 13824)]
     if args.config == 3:
         linears = linears[:1] if T == 1 else linears
+    if args.quantizer:
+        quantizer_bench(args, cfg, cfg["linears"], K, adt, abytes)
+        return
 
     # ---- setup: quantize + pack on the device, build the rotating pool
     layers = []
@@ -413,6 +420,75 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args, cfg, linears[dom], K, T, unit)
     print(json.dumps(line), flush=True)
+
+
+def quantizer_bench(args, cfg, linears, K, adt, abytes):
+    """Mean device time of the setup kernels per linear, from HIP events on
+    the launch stream: greedy residual binarization, the alternating refit
+    (--refit-rounds) and packing.  Algorithmic bytes: W fp32 read; signs int8
+    written (greedy), read and written (refit), read (pack); scales likewise;
+    the packed layer written (pack)."""
+    import torch
+
+    import boolean_weight_amd as bw
+    import mbok_synth as syn
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    reps = max(1, args.steps)
+    out = []
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    for li, (name, m, n) in enumerate(linears):
+        W = torch.from_numpy(syn.weight(m, n, syn.weight_seed(args.config, li))).to(dev)
+        d = bw.mbok_desc_init(m, n, K, adt)
+        signs = torch.empty((K, m, n), dtype=torch.int8, device=dev)
+        alpha = torch.empty((K, m, n // 128), dtype=bw.alpha_torch_dtype(adt), device=dev)
+        packed = torch.empty(bw.mbok_packed_bytes(d), dtype=torch.uint8, device=dev)
+        s0 = torch.empty_like(signs)
+        a0 = torch.empty_like(alpha)
+        bw.mbok_residual_binarize(d, W, s0, a0)
+        us_greedy = timed(lambda: bw.mbok_residual_binarize(d, W, signs, alpha))
+
+        def refit_once():
+            # each timed call starts again from the greedy result (two copies
+            # on the same stream, timed apart and subtracted)
+            signs.copy_(s0)
+            alpha.copy_(a0)
+            bw.mbok_refit(d, W, signs, alpha, args.refit_rounds)
+
+        def copies_only():
+            signs.copy_(s0)
+            alpha.copy_(a0)
+
+        us_refit = timed(refit_once) - timed(copies_only)
+        us_pack = timed(lambda: bw.mbok_pack(d, signs, alpha, packed))
+        nw = m * n
+        na = K * m * (n // 128) * abytes
+        b_greedy = 4 * nw + K * nw + na
+        b_refit = 4 * nw + 2 * K * nw + 2 * na
+        b_pack = K * nw + na + bw.mbok_packed_bytes(d)
+        for kern, us, b in (("residual_binarize", us_greedy, b_greedy),
+                            ("refit", us_refit, b_refit), ("pack", us_pack, b_pack)):
+            out.append({"linear": name, "m": m, "n": n, "kernel": kern, "us": round(us, 2),
+                        "alg_bytes": b, "GB/s": round(b / (us * 1e-6) / 1e9, 1),
+                        "frac_hbm": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)})
+        del W, signs, alpha, packed, s0, a0
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "setup kernel time", "unit": "us", "workload": cfg["name"],
+                      "K": K, "refit_rounds": args.refit_rounds, "reps": reps,
+                      "alpha_dtype": cfg["alpha_dtype"], "kernels": out}), flush=True)
 
 
 def cpu_baseline(args, cfg, lin, K, T, unit):
