@@ -7,17 +7,18 @@
 // solution, and the two are optimised in turn, one fixed while the other is
 // updated.
 //
-// One wavefront per (row, group) of 128 columns; lane l holds columns 2l and
-// 2l+1.  Per group:
+// Four lanes per (row, group) of 128 columns, 32 columns each: the weights
+// stay in registers and the signs are kept as one word of bits per kernel
+// and lane.  Per group:
 //   scale step  (B^T B) a = B^T w solved exactly and rounded once.  The Gram
-//               matrix is integer (popcounts of sign ballots); with its
-//               adjugate C and determinant D, a_k = sum_j c_kj w_j / D where
-//               c_kj = sum_l C_kl b_lj is an integer below 2^23, so each
-//               product c_kj w_j is an exact float64 and the sum over the
-//               group is exact as a float64 pair.  The quotient is rounded to
-//               odd in float64 (exact remainder signs), then to nearest-even
-//               in the scale dtype, which equals one rounding of the exact
-//               rational.  A singular Gram matrix keeps the scales.
+//               matrix is integer (popcounts of sign-bit differences); with
+//               its adjugate C and determinant D, a_k = sum_l C_kl r_l / D,
+//               where r_l = sum_j b_lj w_j is summed exactly as a float64
+//               pair and each C_kl r_l is split exactly by fused multiply-
+//               adds.  The quotient is rounded to odd in float64 (exact
+//               remainder signs), then to nearest-even in the scale dtype,
+//               which equals one rounding of the exact rational.  A singular
+//               Gram matrix keeps the scales.
 //   sign step   each weight takes the pattern of its nearest level
 //               sum_k a_k b_k (levels and distances in float64; ties go to
 //               the larger level, then to the larger pattern index
@@ -32,6 +33,7 @@ namespace mbok {
 namespace {
 
 constexpr int kMaxRefitRounds = 64;
+constexpr int kRefitBlock = 256;  // threads per workgroup, four per (row, group)
 
 // Exact sign (-1, 0, +1) of a + b + c + d (no overflow): the terms are merged
 // into a nonoverlapping expansion of increasing magnitude with error-free
@@ -104,8 +106,8 @@ __device__ double div_round_odd(double nh, double nl, double D) {
 
 // Determinant of the 3x3 matrix formed by rows r0, r1, r2 and columns c0, c1,
 // c2 of the 4x4 integer matrix A.
-__device__ __forceinline__ int64_t det3(const int64_t A[4][4], int r0, int r1, int r2, int c0,
-                                        int c1, int c2) {
+__device__ __forceinline__ int det3(const int A[4][4], int r0, int r1, int r2, int c0, int c1,
+                                    int c2) {
   return A[r0][c0] * (A[r1][c1] * A[r2][c2] - A[r1][c2] * A[r2][c1]) -
          A[r0][c1] * (A[r1][c0] * A[r2][c2] - A[r1][c2] * A[r2][c0]) +
          A[r0][c2] * (A[r1][c0] * A[r2][c1] - A[r1][c1] * A[r2][c0]);
@@ -114,14 +116,18 @@ __device__ __forceinline__ int64_t det3(const int64_t A[4][4], int r0, int r1, i
 // Adjugate and determinant of the K x K Gram matrix, taken as the 4x4 matrix
 // diag(Gram, I): its determinant is det(Gram) and the top-left K x K block
 // of its adjugate is adj(Gram).  adj[k][l] = (-1)^(k+l) * minor(l, k).
+// 32-bit integers suffice: a Gram matrix of +-1 vectors of length 128 is
+// positive semidefinite with diagonal 128, so (Hadamard) its determinant is
+// at most 2^28, every cofactor at most 2^21 in magnitude, and each product
+// formed here stays below 2^31.
 template <int K>
-__device__ __forceinline__ int64_t adjugate(const int Gm[K][K], int64_t adj[K][K]) {
-  int64_t A[4][4];
+__device__ __forceinline__ int adjugate(const int Gm[K][K], int adj[K][K]) {
+  int A[4][4];
 #pragma unroll
   for (int r = 0; r < 4; ++r)
 #pragma unroll
     for (int c = 0; c < 4; ++c) A[r][c] = (r < K && c < K) ? Gm[r < K ? r : 0][c < K ? c : 0] : (r == c);
-  int64_t cof[4][4];
+  int cof[4][4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
 #pragma unroll
@@ -132,11 +138,11 @@ __device__ __forceinline__ int64_t adjugate(const int Gm[K][K], int64_t adj[K][K
         if (t != r) rs[nr++] = t;
         if (t != c) cs[nc++] = t;
       }
-      const int64_t mnr = det3(A, rs[0], rs[1], rs[2], cs[0], cs[1], cs[2]);
+      const int mnr = det3(A, rs[0], rs[1], rs[2], cs[0], cs[1], cs[2]);
       cof[r][c] = ((r + c) & 1) ? -mnr : mnr;
     }
   }
-  int64_t det = 0;
+  int det = 0;
 #pragma unroll
   for (int c = 0; c < 4; ++c) det += A[0][c] * cof[0][c];
 #pragma unroll
@@ -152,108 +158,175 @@ __device__ __forceinline__ double load_alpha(const void* alpha, int64_t idx) {
   return (double)reinterpret_cast<const float*>(alpha)[idx];
 }
 
+// Lanes 4t .. 4t+3 (a quad) share one (row, group): lane q holds columns
+// 32q .. 32q+31.
+
+// Exact pair sum over the lane's 32 columns of b_j w_j (bit j of `bits`),
+// in two chains.
+__device__ __forceinline__ void signed_sum32(const float w[32], uint32_t bits, double& hi,
+                                             double& lo) {
+  double h0 = 0.0, l0 = 0.0, h1 = 0.0, l1 = 0.0;
+#pragma unroll
+  for (int j = 0; j < 32; j += 2) {
+    const float v0 = ((bits >> j) & 1u) ? w[j] : -w[j];
+    const float v1 = ((bits >> (j + 1)) & 1u) ? w[j + 1] : -w[j + 1];
+    dd_acc(h0, l0, (double)v0);
+    dd_acc(h1, l1, (double)v1);
+  }
+  two_sum(h0, l0, h0, l0);
+  two_sum(h1, l1, h1, l1);
+  dd_add(h0, l0, h1, l1);
+  hi = h0;
+  lo = l0;
+}
+
 template <bool F16, int K>
 __global__ void __launch_bounds__(256) refit_kernel(const float* __restrict__ W, int64_t ldw,
                                                     int m, int n, int8_t* __restrict__ signs,
                                                     void* __restrict__ alpha, int rounds) {
-  const int lane = threadIdx.x & (kWave - 1);
+  constexpr int M = 1 << K;  // levels
   const int G = n / kGroup;
-  const int64_t task = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
-  if (task >= (int64_t)m * G) return;  // whole wave exits together
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t task = tid >> 2;
+  const int q = (int)(tid & 3);
+  if (task >= (int64_t)m * G) return;  // whole quads exit together
   const int i = (int)(task / G);
   const int g = (int)(task % G);
-  const int64_t col = (int64_t)g * kGroup + 2 * lane;
+  const int64_t col = (int64_t)g * kGroup + 32 * q;
 
-  const float2 w2 = *reinterpret_cast<const float2*>(W + (int64_t)i * ldw + col);
-  const double w0 = (double)w2.x, w1 = (double)w2.y;
-  bool p0[K], p1[K];  // current signs of the lane's two columns (true = +1)
-  double a[K];        // current scales, values of the scale dtype
+  float w[32];
+  load_weights32(W + (int64_t)i * ldw + col, w);
+  uint32_t bits[K];  // bit j: column 32q + j is +1
+  double a[K];
 #pragma unroll
   for (int k = 0; k < K; ++k) {
-    const char2 sv = *reinterpret_cast<const char2*>(signs + ((int64_t)k * m + i) * n + col);
-    p0[k] = sv.x >= 0;
-    p1[k] = sv.y >= 0;
+    bits[k] = load_sign_bits32(signs + ((int64_t)k * m + i) * n + col);
     a[k] = load_alpha<F16>(alpha, ((int64_t)k * m + i) * G + g);
   }
 
   for (int step = 0; step < 2 * rounds + 1; ++step) {
     if ((step & 1) == 0) {
-      // ---- scale step
-      uint64_t ev[K], od[K];
-#pragma unroll
-      for (int k = 0; k < K; ++k) {
-        ev[k] = __ballot(p0[k]);
-        od[k] = __ballot(p1[k]);
-      }
+      // ---- scale step.  Gram matrix: 128 - 2 * (differing signs), the
+      // differences of the K(K-1)/2 pairs packed 8 bits each for the quad sum
       int Gm[K][K];
+      {
+        int packed[2] = {0, 0};
+        int slot = 0;
 #pragma unroll
-      for (int k = 0; k < K; ++k)
+        for (int k = 0; k < K; ++k)
 #pragma unroll
-        for (int l = 0; l < K; ++l)
-          Gm[k][l] = kGroup - 2 * (__popcll(ev[k] ^ ev[l]) + __popcll(od[k] ^ od[l]));
-      int64_t adj[K][K];
-      const int64_t det = adjugate<K>(Gm, adj);
+          for (int l = k + 1; l < K; ++l, ++slot)
+            packed[slot >> 2] |= __popc(bits[k] ^ bits[l]) << (8 * (slot & 3));
+        packed[0] = quad_sum_i(packed[0]);
+        if (K * (K - 1) / 2 > 4) packed[1] = quad_sum_i(packed[1]);
+        slot = 0;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          Gm[k][k] = kGroup;
+#pragma unroll
+          for (int l = k + 1; l < K; ++l, ++slot) {
+            const int diff = (packed[slot >> 2] >> (8 * (slot & 3))) & 0xff;
+            Gm[k][l] = Gm[l][k] = kGroup - 2 * diff;
+          }
+        }
+      }
+      int adj[K][K];
+      const int det = adjugate<K>(Gm, adj);
       if (det == 0) continue;  // singular: the scales stay
-      const double D = (double)det;
+      double rh[K], rl[K];
 #pragma unroll
-      for (int k = 0; k < K; ++k) {
-        int64_t c0 = 0, c1 = 0;
-#pragma unroll
-        for (int l = 0; l < K; ++l) {
-          c0 += p0[l] ? adj[k][l] : -adj[k][l];
-          c1 += p1[l] ? adj[k][l] : -adj[k][l];
-        }
-        double hi, lo;
-        two_sum((double)c0 * w0, (double)c1 * w1, hi, lo);  // both products exact
-        wave_sum_dd(hi, lo, lane);
-        const double q = div_round_odd(hi, lo, D);
-        if (F16)
-          a[k] = (double)f16_bits_to_f32(f64_to_f16_rne(q));
-        else
-          a[k] = (double)(float)q;  // v_cvt_f32_f64: nearest-even
+      for (int l = 0; l < K; ++l) {
+        signed_sum32(w, bits[l], rh[l], rl[l]);
+        quad_sum_dd(rh[l], rl[l], q);
       }
+      // lane q solves for scale k = q (lanes beyond K repeat the last one)
+      const int kq = q < K ? q : K - 1;
+      double nh = 0.0, nl = 0.0;
+#pragma unroll
+      for (int l = 0; l < K; ++l) {
+        int cq = adj[0][l];
+#pragma unroll
+        for (int k = 1; k < K; ++k) cq = (kq == k) ? adj[k][l] : cq;
+        const double c = (double)cq;  // |c| < 2^22: exact
+        const double p = c * rh[l], pe = __fma_rn(c, rh[l], -p);
+        const double pl = c * rl[l], ple = __fma_rn(c, rl[l], -pl);
+        dd_add(nh, nl, p, pe);
+        dd_add(nh, nl, pl, ple);
+      }
+      const double qt = div_round_odd(nh, nl, (double)det);
+      const double aq = F16 ? (double)f16_bits_to_f32(f64_to_f16_rne(qt))
+                            : (double)(float)qt;  // v_cvt_f32_f64: nearest-even
+      a[0] = quad_perm_d<0x00>(aq);
+      if (K > 1) a[1 < K ? 1 : 0] = quad_perm_d<0x55>(aq);
+      if (K > 2) a[2 < K ? 2 : 0] = quad_perm_d<0xaa>(aq);
+      if (K > 3) a[3 < K ? 3 : 0] = quad_perm_d<0xff>(aq);
     } else {
-      // ---- sign step: nearest of the 2^K levels, scanned in pattern order
-      double b0d = 0.0, b0l = 0.0, b1d = 0.0, b1l = 0.0;
-      int b0i = -1, b1i = -1;
+      // ---- sign step.  The levels, each summed in kernel order, are sorted
+      // ascending by (level, pattern); scanning them in that order and
+      // taking every level whose distance is <= the best so far ends on the
+      // nearest level, the larger one on a tie, the larger pattern on equal
+      // levels.
+      double lev[M];
+      int pat[M];
 #pragma unroll
-      for (int idx = 0; idx < (1 << K); ++idx) {
-        double lev = 0.0;
+      for (int idx = 0; idx < M; ++idx) {
+        double v = 0.0;
 #pragma unroll
-        for (int k = 0; k < K; ++k) lev = lev + (((idx >> k) & 1) ? a[k] : -a[k]);
-        const double d0 = fabs(w0 - lev), d1 = fabs(w1 - lev);
-        if (b0i < 0 || d0 < b0d || (d0 == b0d && lev >= b0l)) {
-          b0d = d0;
-          b0l = lev;
-          b0i = idx;
-        }
-        if (b1i < 0 || d1 < b1d || (d1 == b1d && lev >= b1l)) {
-          b1d = d1;
-          b1l = lev;
-          b1i = idx;
+        for (int k = 0; k < K; ++k) v = v + (((idx >> k) & 1) ? a[k] : -a[k]);
+        lev[idx] = v;
+        pat[idx] = idx;
+      }
+      // odd-even transposition sort: M passes of compare-exchange
+#pragma unroll
+      for (int pass = 0; pass < M; ++pass) {
+#pragma unroll
+        for (int x = pass & 1; x + 1 < M; x += 2) {
+          const bool swap = lev[x] > lev[x + 1] || (lev[x] == lev[x + 1] && pat[x] > pat[x + 1]);
+          const double l0 = lev[x], l1 = lev[x + 1];
+          const int p0 = pat[x], p1 = pat[x + 1];
+          lev[x] = swap ? l1 : l0;
+          lev[x + 1] = swap ? l0 : l1;
+          pat[x] = swap ? p1 : p0;
+          pat[x + 1] = swap ? p0 : p1;
         }
       }
+      uint32_t nb[K];
 #pragma unroll
-      for (int k = 0; k < K; ++k) {
-        p0[k] = (b0i >> k) & 1;
-        p1[k] = (b1i >> k) & 1;
+      for (int k = 0; k < K; ++k) nb[k] = 0;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        const double wj = (double)w[j];
+        double bd = fabs(wj - lev[0]);
+        int bp = pat[0];
+#pragma unroll
+        for (int x = 1; x < M; ++x) {
+          const double dx = fabs(wj - lev[x]);
+          const bool take = dx <= bd;
+          bd = take ? dx : bd;
+          bp = take ? pat[x] : bp;
+        }
+#pragma unroll
+        for (int k = 0; k < K; ++k) nb[k] |= (uint32_t)((bp >> k) & 1) << j;
       }
+#pragma unroll
+      for (int k = 0; k < K; ++k) bits[k] = nb[k];
     }
   }
 
 #pragma unroll
   for (int k = 0; k < K; ++k) {
-    char2 sv;
-    sv.x = p0[k] ? 1 : -1;
-    sv.y = p1[k] ? 1 : -1;
-    *reinterpret_cast<char2*>(signs + ((int64_t)k * m + i) * n + col) = sv;
-    const int64_t aidx = ((int64_t)k * m + i) * G + g;
-    if (lane == 0) {
-      if (F16)
-        reinterpret_cast<uint16_t*>(alpha)[aidx] = f64_to_f16_rne(a[k]);  // exact: a is fp16
-      else
-        reinterpret_cast<float*>(alpha)[aidx] = (float)a[k];
-    }
+    store_sign_bits32(signs + ((int64_t)k * m + i) * n + col, bits[k]);
+  }
+  if (q < K) {
+    // lane q stores scale q (its value is bit-identical in every lane)
+    double aq = a[0];
+#pragma unroll
+    for (int k = 1; k < K; ++k) aq = (q == k) ? a[k] : aq;
+    const int64_t aidx = ((int64_t)q * m + i) * G + g;
+    if (F16)
+      reinterpret_cast<uint16_t*>(alpha)[aidx] = f64_to_f16_rne(aq);  // exact: aq is fp16
+    else
+      reinterpret_cast<float*>(alpha)[aidx] = (float)aq;
   }
 }
 
@@ -262,10 +335,9 @@ int launch_refit_dt(const mbok_desc* d, const float* W, int64_t ldw, int8_t* sig
                     int rounds, hipStream_t stream) {
   const int G = d->n / kGroup;
   const int64_t tasks = (int64_t)d->m * G;
-  const int waves_per_block = 4;
-  const int64_t blocks = (tasks + waves_per_block - 1) / waves_per_block;
+  const int64_t blocks = (4 * tasks + kRefitBlock - 1) / kRefitBlock;
   if (blocks > 0x7fffffff) return MBOK_ERR_SHAPE;
-  dim3 grid((unsigned)blocks), block(waves_per_block * kWave);
+  dim3 grid((unsigned)blocks), block(kRefitBlock);
   switch (d->K) {
     case 1:
       hipLaunchKernelGGL((refit_kernel<F16, 1>), grid, block, 0, stream, W, ldw, d->m, d->n,
