@@ -22,7 +22,10 @@ Sources (page title, then the section on that page):
            or greedy search.
   [GS] gist.science summaries of the same paper ("Successive SVID",
        "Extracción Sucesiva"): each further kernel is fitted to the residual
-       error left by the previous ones.
+       error left by the previous ones.  The Italian summary, section "D.
+       Allocazione Automatica dei Kernel": the number of kernels per weight
+       is allocated for an average bit budget from residual error,
+       importance and size.
 
 Readings taken where the pages are silent:
   * scale structure: one scale per (kernel k, output row i, group g of 128
@@ -34,7 +37,15 @@ Readings taken where the pages are silent:
   * the scale is the exact float64 group mean of |R| (math.fsum, one
     rounding) rounded once, nearest-even, to the storage dtype, and the
     residual update uses that rounded scale, so W = W_hat + R_K exactly;
-  * y is produced in fp32 by the device; the oracle keeps float64.
+  * y is produced in fp32 by the device; the oracle keeps float64;
+  * refit: the scale step solves the normal equations exactly and rounds
+    once; the sign step takes each weight's nearest level (ties: larger
+    level, then larger pattern index); a singular Gram matrix keeps the
+    scales; rounds alternate (scale, sign) and end with a scale step;
+  * allocation: residual energy = exact squared Frobenius norm of R_K, one
+    rounding per row and one fsum over rows; importance is 1 for every
+    weight (it needs data); the budget is a total of kernel-bits; ties go to
+    fewer bits, then to the first K vector in lexicographic order.
 
 parity pins: every function here is pinned in tests/test_oracle_pins.py
 against closed forms, constructed examples, brute force (Fraction,
@@ -210,6 +221,55 @@ def refit(W: np.ndarray, S: np.ndarray, A: np.ndarray, rounds: int = 2,
             S[:, i, cols] = b
             A[:, i, g] = a
     return S, A.astype(np.float16 if alpha_dtype == "f16" else np.float32)
+
+
+def residual_energies(W: np.ndarray, K: int, group: int = GROUP, alpha_dtype: str = "f16"):
+    """Residual energy of the greedy decomposition after k = 0..K kernels
+    ([GS-it] "Allocazione Automatica dei Kernel": the allocation weighs the
+    residual approximation error of each weight).
+        rows[k, i] = the float64 nearest to the exact sum over row i of
+                     R_k[i, j]^2 (R_0 = W; R_k as in residual_binarize)
+        layer[k]   = fsum over i of rows[k, i]  (exact sum, one rounding)
+    Returns rows float64 [K+1, m] and layer float64 [K+1]."""
+    _, _, _, chain = residual_binarize(W, K, group, alpha_dtype, return_chain=True)
+    m = np.asarray(W).shape[0]
+    rows = np.empty((K + 1, m), dtype=np.float64)
+    for k in range(K + 1):
+        Rk = chain[k]
+        for i in range(m):
+            rows[k, i] = float(sum((Fraction(float(v)) ** 2 for v in Rk[i]), Fraction(0)))
+    layer = np.array([math.fsum(rows[k].tolist()) for k in range(K + 1)])
+    return rows, layer
+
+
+def allocate_kernels(errors, sizes, budget: int, kmax: int):
+    """Kernels per weight under a bit budget ([GS-it] "Allocazione Automatica
+    dei Kernel": the number of kernels of each weight is chosen for an
+    average bit budget, trading residual error against the weight's size;
+    the importance term needs data and is left out, i.e. every weight counts
+    the same).
+        errors[l][K-1]  residual energy of weight l with K kernels
+        sizes[l]        entries of weight l (bits per kernel)
+        budget          largest total sum_l K_l * sizes[l]
+    Every K vector in {1..kmax}^L is tried in lexicographic order; the total
+    error is summed in float64 in layer order.  The least error wins, then the
+    fewest bits, then the first vector in that order.  Returns the tuple of
+    K_l, or None when even K = 1 everywhere exceeds the budget."""
+    from itertools import product as cartesian
+
+    L = len(sizes)
+    best = None
+    for ks in cartesian(range(1, kmax + 1), repeat=L):
+        bits = sum(int(k) * int(sz) for k, sz in zip(ks, sizes))
+        if bits > budget:
+            continue
+        err = 0.0
+        for l in range(L):
+            err = err + float(errors[l][ks[l] - 1])
+        key = (err, bits)
+        if best is None or key < best[0]:
+            best = (key, ks)
+    return None if best is None else tuple(best[1])
 
 
 def dequantize(S: np.ndarray, A: np.ndarray, group: int = GROUP) -> np.ndarray:

@@ -672,6 +672,177 @@ def pin_refit_lowers_error(o):
         assert tot < {2: Fraction(95, 100), 3: Fraction(85, 100)}[K] * tot0, (K, float(tot / tot0))
 
 
+# ------------------------------------------------ residual energy, allocation
+
+def pin_energy_walsh(o):
+    """E1: the constructed exact decomposition of I6 has closed-form
+    residual energies: 128 G (c1^2 + c2^2 + c3^2), 128 G (c2^2 + c3^2),
+    128 G c3^2 and 0 per row (orthogonal patterns), and m times that for the
+    layer."""
+    H = walsh_hadamard(128)
+    rng = np.random.default_rng(41)
+    m, G, K = 3, 2, 3
+    c = [2.0 ** -5 + 2.0 ** -8, 2.0 ** -7 + 2.0 ** -9, 2.0 ** -8 + 2.0 ** -10]
+    W = np.zeros((m, 128 * G))
+    for i in range(m):
+        for g in range(G):
+            rows = rng.choice(128, size=K, replace=False)
+            d = rng.choice([-1, 1], size=128)
+            for k in range(K):
+                W[i, 128 * g:128 * g + 128] += c[k] * H[rows[k]] * d
+    W = W.astype(np.float32)
+    rows, layer = o.residual_energies(W, K, alpha_dtype="f16")
+    want = [128 * G * sum(Fraction(ck) ** 2 for ck in c[k:]) for k in range(K + 1)]
+    for k in range(K + 1):
+        assert all(Fraction(float(v)) == want[k] for v in rows[k]), (k, rows[k], float(want[k]))
+        assert Fraction(float(layer[k])) == m * want[k], (k, layer[k])
+
+
+def pin_energy_single_kernel(o):
+    """E2: with one kernel the residual energy of a group has the closed form
+    |w|^2 - 128 (2 alpha a - alpha^2) with a = |w|_1 / 128 and alpha the
+    stored scale; a row sums its groups exactly and rounds once, the layer
+    adds the rounded rows exactly and rounds once."""
+    rng = np.random.default_rng(42)
+    W = rng.normal(0, 0.02, size=(5, 384)).astype(np.float32)
+    S, A, _ = o.residual_binarize(W, 1, alpha_dtype="f16")
+    rows, layer = o.residual_energies(W, 1, alpha_dtype="f16")
+    total = Fraction(0)
+    for i in range(5):
+        e0 = Fraction(0)
+        e1 = Fraction(0)
+        for g in range(3):
+            wg = [Fraction(float(v)) for v in W[i, 128 * g:128 * g + 128]]
+            sq = sum(v * v for v in wg)
+            a = sum(abs(v) for v in wg) / 128
+            al = Fraction(float(A[0, i, g]))
+            e0 += sq
+            e1 += sq - 128 * (2 * al * a - al * al)
+        assert rows[0, i] == float(e0) and rows[1, i] == float(e1), i
+        total += Fraction(float(rows[1, i]))
+    assert layer[1] == float(total)
+
+
+def pin_energy_decreases(o):
+    """E3: greedy kernels never raise the residual energy of a row (each step
+    subtracts a least-squares fit), for K up to 4 and both scale dtypes."""
+    rng = np.random.default_rng(43)
+    W = rng.normal(0, 0.02, size=(4, 256)).astype(np.float32)
+    for dt in ("f16", "f32"):
+        rows, layer = o.residual_energies(W, 4, alpha_dtype=dt)
+        assert np.all(np.diff(rows, axis=0) <= 0) and np.all(np.diff(layer) < 0), dt
+
+
+def _read_allocations():
+    cases = []
+    for name, ex in read_golden("allocation.txt").items():
+        sizes = [int(v) for v in ex["sizes"]]
+        kmax = int(ex["kmax"][0])
+        errors = [ex[f"errors_{l}"] for l in range(len(sizes))]
+        for key, val in ex.items():
+            if key.startswith("budget_"):
+                want = tuple(int(v) for v in val)
+                cases.append((name, sizes, kmax, errors, int(key[7:]),
+                              None if not any(want) else want))
+    return cases
+
+
+def pin_allocation_hand_worked(o):
+    """A1: the hand-worked allocations of tests/golden/allocation.txt,
+    including the two tie rules and an infeasible budget."""
+    for name, sizes, kmax, errors, budget, want in _read_allocations():
+        got = o.allocate_kernels(errors, sizes, budget, kmax)
+        assert got == want, (name, budget, got, want)
+
+
+def _knapsack_best(errors, sizes, budget, kmax):
+    """Least (error, bits) by dynamic programming over used bits (integers):
+    best[b] = least error of the first l weights using exactly b bits."""
+    INF = float("inf")
+    best = {0: 0.0}
+    for l, sz in enumerate(sizes):
+        nxt = {}
+        for b, e in best.items():
+            for K in range(1, kmax + 1):
+                nb = b + K * sz
+                if nb > budget:
+                    continue
+                ne = e + float(errors[l][K - 1])
+                if ne < nxt.get(nb, INF):
+                    nxt[nb] = ne
+        best = nxt
+    if not best:
+        return None
+    return min((e, b) for b, e in best.items())
+
+
+def pin_allocation_knapsack(o):
+    """A2: on random instances (unequal sizes, dyadic errors so that every
+    sum is exact) the allocation reaches the least (error, bits) that a
+    dynamic program over used bits finds, and stays within the budget."""
+    rng = np.random.default_rng(44)
+    for trial in range(40):
+        L = int(rng.integers(1, 6))
+        kmax = int(rng.integers(1, 5))
+        sizes = [int(v) for v in rng.integers(1, 9, size=L)]
+        errors = []
+        for l in range(L):
+            e = np.sort(rng.integers(0, 4096, size=kmax))[::-1] / 1024.0
+            errors.append(e.tolist())
+        budget = int(rng.integers(0, kmax * sum(sizes) + 3))
+        got = o.allocate_kernels(errors, sizes, budget, kmax)
+        want = _knapsack_best(errors, sizes, budget, kmax)
+        if want is None:
+            assert got is None, (trial, got)
+            continue
+        bits = sum(k * s for k, s in zip(got, sizes))
+        err = sum(errors[l][got[l] - 1] for l in range(L))
+        assert bits <= budget and (err, bits) == want, (trial, got, want)
+
+
+def pin_allocation_greedy_convex(o):
+    """A3: with equal sizes and convex, decreasing errors, adding one kernel
+    at a time where it lowers the error most is optimal (separable convex
+    allocation), so both reach the same least error."""
+    rng = np.random.default_rng(45)
+    for trial in range(30):
+        L, kmax = int(rng.integers(2, 6)), 4
+        errors = []
+        for l in range(L):
+            steps = np.sort(rng.integers(1, 512, size=kmax - 1))[::-1]  # shrinking gains
+            e = [4096.0]
+            for st in steps:
+                e.append(e[-1] - float(st))
+            errors.append([v / 1024.0 for v in e])
+        budget = int(rng.integers(L, kmax * L + 1))
+        K = [1] * L
+        for _ in range(budget - L):
+            gains = [(errors[l][K[l] - 1] - errors[l][K[l]]) if K[l] < kmax else -1.0
+                     for l in range(L)]
+            lbest = int(np.argmax(gains))
+            if gains[lbest] <= 0:
+                break
+            K[lbest] += 1
+        got = o.allocate_kernels(errors, [1] * L, budget, kmax)
+        assert sum(errors[l][got[l] - 1] for l in range(L)) == \
+            sum(errors[l][K[l] - 1] for l in range(L)), (trial, got, K)
+
+
+def pin_allocation_monotone(o):
+    """A4: a larger budget never gives a larger least error."""
+    rng = np.random.default_rng(46)
+    sizes = [3, 5, 2, 7]
+    errors = [sorted(rng.random(4).tolist(), reverse=True) for _ in sizes]
+    prev = None
+    for budget in range(sum(sizes), 4 * sum(sizes) + 1):
+        got = o.allocate_kernels(errors, sizes, budget, 4)
+        err = 0.0
+        for l in range(4):
+            err = err + errors[l][got[l] - 1]
+        assert prev is None or err <= prev, budget
+        prev = err
+
+
 ALL_PINS = [
     pin_round_alpha_rne, pin_hand_worked, pin_sign_step, pin_scale_is_least_squares,
     pin_residual_chain, pin_levels, pin_single_kernel_textbook, pin_constructed_walsh,
@@ -681,4 +852,7 @@ ALL_PINS = [
     pin_refit_hand_worked, pin_refit_scale_step, pin_refit_sign_step, pin_refit_ties,
     pin_refit_single_kernel, pin_refit_walsh_fixed_point, pin_refit_singular_gram,
     pin_refit_lowers_error,
+    pin_energy_walsh, pin_energy_single_kernel, pin_energy_decreases,
+    pin_allocation_hand_worked, pin_allocation_knapsack, pin_allocation_greedy_convex,
+    pin_allocation_monotone,
 ]

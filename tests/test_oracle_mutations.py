@@ -90,6 +90,22 @@ MUTATIONS = [
     ("refit_singular_zeroes_scales", "refit",
      "if q is not None:\n                        a = np.array([_round_fraction(v, alpha_dtype) for v in q])",
      "a = np.array([_round_fraction(v, alpha_dtype) for v in q]) if q is not None else 0 * a"),
+    ("energy_of_abs_not_square", "residual_energies",
+     "(Fraction(float(v)) ** 2 for v in Rk[i])", "(abs(Fraction(float(v))) for v in Rk[i])"),
+    ("energy_one_kernel_late", "residual_energies",
+     "Rk = chain[k]", "Rk = chain[min(k + 1, K)]"),
+    ("energy_layer_drops_last_row", "residual_energies",
+     "math.fsum(rows[k].tolist())", "math.fsum(rows[k][:-1].tolist())"),
+    ("allocation_ignores_budget", "allocate_kernels",
+     "if bits > budget:", "if False:"),
+    ("allocation_ties_to_more_bits", "allocate_kernels",
+     "key = (err, bits)", "key = (err, -bits)"),
+    ("allocation_ties_to_last_vector", "allocate_kernels",
+     "if best is None or key < best[0]:", "if best is None or key <= best[0]:"),
+    ("allocation_size_ignored", "allocate_kernels",
+     "bits = sum(int(k) * int(sz) for k, sz in zip(ks, sizes))", "bits = sum(int(k) for k in ks)"),
+    ("allocation_error_of_wrong_kernel", "allocate_kernels",
+     "err = err + float(errors[l][ks[l] - 1])", "err = err + float(errors[l][min(ks[l], kmax - 1)])"),
 ]
 
 
