@@ -44,8 +44,9 @@ Readings taken where the pages are silent:
     scales; rounds alternate (scale, sign) and end with a scale step;
   * allocation: residual energy = exact squared Frobenius norm of R_K, one
     rounding per row and one fsum over rows; importance is 1 for every
-    weight (it needs data); the budget is a total of kernel-bits; ties go to
-    fewer bits, then to the first K vector in lexicographic order.
+    weight (it needs data); the budget is a total of kernel-bits; total
+    errors are compared exactly; ties go to fewer bits, then to the first K
+    vector in lexicographic order.
 
 parity pins: every function here is pinned in tests/test_oracle_pins.py
 against closed forms, constructed examples, brute force (Fraction,
@@ -252,9 +253,9 @@ def allocate_kernels(errors, sizes, budget: int, kmax: int):
         sizes[l]        entries of weight l (bits per kernel)
         budget          largest total sum_l K_l * sizes[l]
     Every K vector in {1..kmax}^L is tried in lexicographic order; the total
-    error is summed in float64 in layer order.  The least error wins, then the
-    fewest bits, then the first vector in that order.  Returns the tuple of
-    K_l, or None when even K = 1 everywhere exceeds the budget."""
+    error is the exact (rational) sum of the float64 errors.  The least error
+    wins, then the fewest bits, then the first vector in that order.  Returns
+    the tuple of K_l, or None when even K = 1 everywhere exceeds the budget."""
     from itertools import product as cartesian
 
     L = len(sizes)
@@ -263,9 +264,9 @@ def allocate_kernels(errors, sizes, budget: int, kmax: int):
         bits = sum(int(k) * int(sz) for k, sz in zip(ks, sizes))
         if bits > budget:
             continue
-        err = 0.0
+        err = Fraction(0)
         for l in range(L):
-            err = err + float(errors[l][ks[l] - 1])
+            err = err + Fraction(float(errors[l][ks[l] - 1]))
         key = (err, bits)
         if best is None or key < best[0]:
             best = (key, ks)

@@ -777,8 +777,8 @@ def _knapsack_best(errors, sizes, budget, kmax):
 
 
 def pin_allocation_knapsack(o):
-    """A2: on random instances (unequal sizes, dyadic errors so that every
-    sum is exact) the allocation reaches the least (error, bits) that a
+    """A2: on random instances (unequal sizes, dyadic errors so that float
+    sums are exact too) the allocation reaches the least (error, bits) that a
     dynamic program over used bits finds, and stays within the budget."""
     rng = np.random.default_rng(44)
     for trial in range(40):
@@ -836,9 +836,7 @@ def pin_allocation_monotone(o):
     prev = None
     for budget in range(sum(sizes), 4 * sum(sizes) + 1):
         got = o.allocate_kernels(errors, sizes, budget, 4)
-        err = 0.0
-        for l in range(4):
-            err = err + errors[l][got[l] - 1]
+        err = sum((Fraction(errors[l][got[l] - 1]) for l in range(4)), Fraction(0))
         assert prev is None or err <= prev, budget
         prev = err
 

@@ -105,7 +105,8 @@ MUTATIONS = [
     ("allocation_size_ignored", "allocate_kernels",
      "bits = sum(int(k) * int(sz) for k, sz in zip(ks, sizes))", "bits = sum(int(k) for k in ks)"),
     ("allocation_error_of_wrong_kernel", "allocate_kernels",
-     "err = err + float(errors[l][ks[l] - 1])", "err = err + float(errors[l][min(ks[l], kmax - 1)])"),
+     "err = err + Fraction(float(errors[l][ks[l] - 1]))",
+     "err = err + Fraction(float(errors[l][min(ks[l], kmax - 1)]))"),
 ]
 
 
