@@ -18,10 +18,10 @@ __all__ = [
     "MBOK_F32", "MBOK_F16", "MBOK_BF16", "MBOK_GROUP", "MBOK_MAX_K", "MBOK_MAX_T",
     "MbokError", "mbok_desc", "library_path", "load_library",
     "mbok_desc_init", "mbok_packed_bytes", "mbok_alpha_bytes", "mbok_residual_binarize",
-    "mbok_refit", "MBOK_MAX_REFIT_ROUNDS",
+    "mbok_refit", "MBOK_MAX_REFIT_ROUNDS", "mbok_residual_energy", "mbok_allocate_kernels",
     "mbok_pack", "mbok_gemv", "mbok_gemv_workspace_bytes", "mbok_gemm", "mbok_status_str",
     "mbok_version", "workspace_for",
-    "alpha_torch_dtype", "quantize_and_pack",
+    "alpha_torch_dtype", "quantize_and_pack", "allocate_for_budget",
 ]
 
 MBOK_F32, MBOK_F16, MBOK_BF16 = 0, 1, 2
@@ -74,6 +74,8 @@ def load_library() -> ctypes.CDLL:
         "mbok_alpha_bytes": (SZ, [D]),
         "mbok_residual_binarize": (ctypes.c_int, [D, P, I64, P, P, P, P]),
         "mbok_refit": (ctypes.c_int, [D, P, I64, P, P, I32, P]),
+        "mbok_residual_energy": (ctypes.c_int, [D, P, I64, P, P, P]),
+        "mbok_allocate_kernels": (ctypes.c_int, [I32, P, P, I32, I64, P]),
         "mbok_pack": (ctypes.c_int, [D, P, P, P, P]),
         "mbok_gemv_workspace_bytes": (SZ, [D]),
         "mbok_gemv": (ctypes.c_int, [D, P, P, I32, P, P, P]),
@@ -204,6 +206,43 @@ def mbok_refit(d: mbok_desc, W: torch.Tensor, signs: torch.Tensor, alpha: torch.
            "mbok_refit")
 
 
+def mbok_residual_energy(d: mbok_desc, W: torch.Tensor, row_energy: torch.Tensor,
+                         layer_energy: torch.Tensor, stream=None) -> None:
+    """Residual energies of the greedy chain after 0..K kernels: row_energy
+    float64 [K+1, m] and layer_energy float64 [K+1] (both overwritten)."""
+    _dev(W, "W"), _dev(row_energy, "row_energy"), _dev(layer_energy, "layer_energy")
+    if W.dtype != torch.float32 or W.dim() != 2 or W.shape[0] != d.m or W.shape[1] < d.n:
+        raise ValueError("W must be float32 [m, >= n]")
+    if W.stride(1) != 1:
+        raise ValueError("W rows must be contiguous")
+    ldw = W.stride(0)
+    if _nbytes_from(W) < ((d.m - 1) * ldw + d.n) * 4:
+        raise ValueError("W buffer too small")
+    for t, cnt, nm in ((row_energy, (d.K + 1) * d.m, "row_energy"),
+                       (layer_energy, d.K + 1, "layer_energy")):
+        if t.dtype != torch.float64 or not t.is_contiguous() or t.numel() < cnt:
+            raise ValueError(f"{nm} must be contiguous float64 with {cnt} elements")
+    _check(load_library().mbok_residual_energy(ctypes.byref(d), W.data_ptr(), ldw,
+                                               row_energy.data_ptr(), layer_energy.data_ptr(),
+                                               _stream(stream)), "mbok_residual_energy")
+
+
+def mbok_allocate_kernels(sizes, errors, budget: int) -> list:
+    """Kernels per weight under a total bit budget (host only).  sizes: L
+    entry counts; errors: L rows of kmax residual energies (K = 1..kmax)."""
+    import numpy as np
+
+    sz = np.ascontiguousarray(np.asarray(sizes, dtype=np.int64).reshape(-1))
+    er = np.ascontiguousarray(np.asarray(errors, dtype=np.float64))
+    if er.ndim != 2 or er.shape[0] != sz.shape[0]:
+        raise ValueError("errors must be [L, kmax] with one row per size")
+    out = np.zeros(sz.shape[0], dtype=np.int32)
+    _check(load_library().mbok_allocate_kernels(
+        int(sz.shape[0]), sz.ctypes.data, er.ctypes.data, int(er.shape[1]), int(budget),
+        out.ctypes.data), "mbok_allocate_kernels")
+    return out.tolist()
+
+
 def mbok_pack(d: mbok_desc, signs: torch.Tensor, alpha: torch.Tensor, packed: torch.Tensor,
               stream=None) -> None:
     """signs int8 [K, m, n] + alpha [K, m, n/128] -> packed uint8 [mbok_packed_bytes]."""
@@ -310,3 +349,25 @@ def quantize_and_pack(W: torch.Tensor, K: int, alpha_dtype: int = MBOK_F16, stre
     if int(flag.item()) != 0:
         raise ValueError("W holds NaN or Inf")
     return d, packed, signs, alpha
+
+
+def allocate_for_budget(weights, avg_kernels: float, kmax: int = MBOK_MAX_K,
+                        alpha_dtype: int = MBOK_F16, stream=None):
+    """Kernels per weight for a set of device fp32 weights under an average
+    budget of `avg_kernels` kernels per entry: the residual energies of each
+    weight's greedy chain (mbok_residual_energy, K = 1..kmax) feed
+    mbok_allocate_kernels with budget floor(avg_kernels * total entries).
+    Returns (K list, layer energies [L][kmax + 1] as nested lists)."""
+    errors, sizes, energies = [], [], []
+    for W in weights:
+        m, n = W.shape
+        d = mbok_desc_init(m, n, kmax, alpha_dtype)
+        rows = torch.empty((kmax + 1, m), dtype=torch.float64, device=W.device)
+        layer = torch.empty(kmax + 1, dtype=torch.float64, device=W.device)
+        mbok_residual_energy(d, W, rows, layer, stream)
+        e = layer.cpu().tolist()
+        energies.append(e)
+        errors.append(e[1:])
+        sizes.append(m * n)
+    budget = int(avg_kernels * sum(sizes))
+    return mbok_allocate_kernels(sizes, errors, budget), energies

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cmath>
+
 #include "../../include/mbok.h"
 #include "mbok_launch.h"
 
@@ -69,6 +71,31 @@ int mbok_residual_binarize(const mbok_desc* d, const float* W, int64_t ldw, int8
   return mbok::launch_residual_binarize(d, W, ldw, signs, alpha, flag, (hipStream_t)stream);
 }
 
+int mbok_residual_energy(const mbok_desc* d, const float* W, int64_t ldw, double* row_energy,
+                         double* layer_energy, void* stream) {
+  int st = check_desc(d);
+  if (st != MBOK_OK) return st;
+  if (!W || !row_energy || !layer_energy) return MBOK_ERR_INVALID_ARG;
+  if (ldw < d->n) return MBOK_ERR_INVALID_ARG;
+  if (!aligned(W, 16) || (ldw % 4) != 0 || !aligned(row_energy, 8) || !aligned(layer_energy, 8))
+    return MBOK_ERR_ALIGN;
+  return mbok::launch_residual_energy(d, W, ldw, row_energy, layer_energy, (hipStream_t)stream);
+}
+
+int mbok_allocate_kernels(int32_t L, const int64_t* sizes, const double* errors, int32_t kmax,
+                          int64_t budget, int32_t* K_out) {
+  if (!sizes || !errors || !K_out || L < 1 || kmax < 1 || kmax > MBOK_MAX_K || budget < 0)
+    return MBOK_ERR_INVALID_ARG;
+  for (int32_t l = 0; l < L; ++l) {
+    if (sizes[l] < 1 || sizes[l] > (int64_t(1) << 44)) return MBOK_ERR_INVALID_ARG;
+    for (int32_t k = 0; k < kmax; ++k) {
+      const double e = errors[(size_t)l * kmax + k];
+      if (!std::isfinite(e) || e < 0.0) return MBOK_ERR_INVALID_ARG;
+    }
+  }
+  return mbok::allocate_kernels(L, sizes, errors, kmax, budget, K_out);
+}
+
 int mbok_refit(const mbok_desc* d, const float* W, int64_t ldw, int8_t* signs, void* alpha,
                int32_t rounds, void* stream) {
   int st = check_desc(d);
@@ -129,6 +156,7 @@ const char* mbok_status_str(int status) {
     case MBOK_ERR_ALIGN: return "MBOK_ERR_ALIGN: pointer or leading dimension misaligned";
     case MBOK_ERR_HIP: return "MBOK_ERR_HIP: the HIP runtime rejected a launch";
     case MBOK_ERR_UNSUPPORTED: return "MBOK_ERR_UNSUPPORTED: K, group or layout outside what the library runs";
+    case MBOK_ERR_INFEASIBLE: return "MBOK_ERR_INFEASIBLE: no kernel allocation fits the bit budget";
   }
   return "unknown status";
 }

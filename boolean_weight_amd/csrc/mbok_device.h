@@ -43,8 +43,11 @@ __device__ __forceinline__ int tile16_of(int b, int tiles) {
 
 // ------------------------------------------------ error-free float64 sums
 
-// error-free a + b = s + e (Knuth's TwoSum)
+// error-free a + b = s + e (Knuth's TwoSum).  The helpers below hold only
+// when each add is rounded on its own: with contraction a caller's product
+// could be fused into them, so it is switched off inside them.
 __device__ __forceinline__ void two_sum(double a, double b, double& s, double& e) {
+#pragma clang fp contract(off)
   s = a + b;
   double bb = s - a;
   e = (a - (s - bb)) + (b - bb);
@@ -56,6 +59,7 @@ __device__ __forceinline__ void two_sum(double a, double b, double& s, double& e
 // final renormalisation is a full TwoSum, so cancellation between hi and bhi
 // (a small s next to a larger e) stays exact.
 __device__ __forceinline__ void dd_add(double& hi, double& lo, double bhi, double blo) {
+#pragma clang fp contract(off)
   double s, e;
   two_sum(hi, bhi, s, e);
   e += lo + blo;
@@ -172,6 +176,7 @@ __device__ __forceinline__ void store_sign_bits32(int8_t* __restrict__ dst, uint
 // (hi, lo) += v for a float64 v, error-free; exact under the same condition
 // as dd_add.  The pair is renormalised only by the caller (dd_add).
 __device__ __forceinline__ void dd_acc(double& hi, double& lo, double v) {
+#pragma clang fp contract(off)
   double s, e;
   two_sum(hi, v, s, e);
   hi = s;

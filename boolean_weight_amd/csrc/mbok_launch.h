@@ -11,6 +11,8 @@ namespace mbok {
 
 int launch_residual_binarize(const mbok_desc* d, const float* W, int64_t ldw, int8_t* signs,
                              void* alpha, int32_t* flag, hipStream_t stream);
+int launch_residual_energy(const mbok_desc* d, const float* W, int64_t ldw, double* rows,
+                           double* layer, hipStream_t stream);
 int launch_refit(const mbok_desc* d, const float* W, int64_t ldw, int8_t* signs, void* alpha,
                  int rounds, hipStream_t stream);
 int refit_max_rounds();
@@ -22,6 +24,8 @@ size_t gemv_workspace_bytes(const mbok_desc* d);
 int launch_skinny(const mbok_desc* d, const void* packed, const void* X, int64_t T, int64_t ldx,
                   float* Y, int64_t ldy, hipStream_t stream);
 int skinny_max_tokens();
+int allocate_kernels(int L, const int64_t* sizes, const double* errors, int kmax, int64_t budget,
+                     int32_t* K_out);
 int launch_gemm(const mbok_desc* d, const void* packed, const void* X, int64_t T, int64_t ldx,
                 float* Y, int64_t ldy, hipStream_t stream);
 

@@ -15,6 +15,11 @@
 // is exact when the group's residual magnitudes lie within about 2^48 of
 // one another; the residuals of a group share the scales' quantum, so this
 // holds for any trained layer.)
+// Every float64 operation in this file is an exact or a once-rounded IEEE
+// operation: no multiply may be fused into a following add (that would
+// break the error-free sums), so contraction is off for the whole file.
+#pragma clang fp contract(off)
+
 #include "mbok_device.h"
 #include "mbok_launch.h"
 
@@ -118,12 +123,157 @@ int launch_dt(const mbok_desc* d, const float* W, int64_t ldw, int8_t* signs, vo
   return hipGetLastError() == hipSuccess ? MBOK_OK : MBOK_ERR_HIP;
 }
 
+// Residual energies of the greedy chain, per row: rows[k * m + i] = the
+// float64 nearest to sum_j R_k[i, j]^2 for k = 0..K (R_0 = W).  One
+// workgroup per row; quad t of the workgroup takes the row's groups t, t + Q,
+// ...  Each lane recomputes R_0..R_K of its 32 columns in the quantizer's
+// order (the scales come out bit-identical to residual_binarize_kernel's)
+// and accumulates the exact squares (a product and its fused-multiply-add
+// error) into float64 pairs; the quads' pairs are then added in quad order.
+constexpr int kEnergyMaxQuads = 64;
+
+template <bool F16, int K>
+__global__ void __launch_bounds__(256) residual_energy_kernel(const float* __restrict__ W,
+                                                              int64_t ldw, int m, int n,
+                                                              double* __restrict__ rows) {
+  __shared__ double sh_hi[kEnergyMaxQuads][K + 1];
+  __shared__ double sh_lo[kEnergyMaxQuads][K + 1];
+  const int i = blockIdx.x;
+  const int G = n / kGroup;
+  const int nquads = blockDim.x >> 2;
+  const int quad = threadIdx.x >> 2;
+  const int q = threadIdx.x & 3;
+  double eh[K + 1], el[K + 1];
+#pragma unroll
+  for (int k = 0; k <= K; ++k) eh[k] = el[k] = 0.0;
+
+  for (int g = quad; g < G; g += nquads) {  // the same trip count in a quad
+    float w[32];
+    load_weights32(W + (int64_t)i * ldw + (int64_t)g * kGroup + 32 * q, w);
+    uint32_t bits[K];
+    double a_st[K];
+#pragma unroll
+    for (int k = 0; k <= K; ++k) {
+      double h0 = 0.0, l0 = 0.0, h1 = 0.0, l1 = 0.0;
+      uint32_t b = 0;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        double r = (double)w[j];
+#pragma unroll
+        for (int p = 0; p < k; ++p) r = ((bits[p] >> j) & 1u) ? r - a_st[p] : r + a_st[p];
+        const double sq = r * r, sqe = __fma_rn(r, r, -sq);
+        dd_acc(eh[k], el[k], sq);
+        el[k] += sqe;
+        if (k < K) {
+          b |= (uint32_t)(r >= 0.0) << j;
+          if (j & 1)
+            dd_acc(h1, l1, fabs(r));
+          else
+            dd_acc(h0, l0, fabs(r));
+        }
+      }
+      if (k < K) {
+        bits[k] = b;
+        two_sum(h0, l0, h0, l0);
+        two_sum(h1, l1, h1, l1);
+        dd_add(h0, l0, h1, l1);
+        quad_sum_dd(h0, l0, q);
+        const double a = (h0 + l0) / (double)kGroup;
+        a_st[k] = F16 ? (double)f16_bits_to_f32(f64_to_f16_rne(a)) : (double)(float)a;
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k <= K; ++k) {
+    two_sum(eh[k], el[k], eh[k], el[k]);
+    quad_sum_dd(eh[k], el[k], q);
+    if (q == 0) {
+      sh_hi[quad][k] = eh[k];
+      sh_lo[quad][k] = el[k];
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x <= K) {
+    const int k = threadIdx.x;
+    double h = sh_hi[0][k], l = sh_lo[0][k];
+    for (int t = 1; t < nquads; ++t) dd_add(h, l, sh_hi[t][k], sh_lo[t][k]);
+    rows[(int64_t)k * m + i] = h;  // h = RN(h + l)
+  }
+}
+
+// layer[k] = the float64 nearest to sum_i rows[k * m + i]: per thread a
+// strided pair sum, then a fixed tree over the workgroup.
+__global__ void __launch_bounds__(256) energy_layer_kernel(const double* __restrict__ rows, int m,
+                                                           int kcount,
+                                                           double* __restrict__ layer) {
+  __shared__ double sh_hi[256], sh_lo[256];
+  const int t = threadIdx.x;
+  for (int k = 0; k < kcount; ++k) {
+    double h = 0.0, l = 0.0;
+    for (int i = t; i < m; i += 256) dd_acc(h, l, rows[(int64_t)k * m + i]);
+    two_sum(h, l, h, l);
+    sh_hi[t] = h;
+    sh_lo[t] = l;
+    __syncthreads();
+    for (int s = 128; s > 0; s >>= 1) {
+      if (t < s) {
+        double a = sh_hi[t], b = sh_lo[t];
+        dd_add(a, b, sh_hi[t + s], sh_lo[t + s]);
+        sh_hi[t] = a;
+        sh_lo[t] = b;
+      }
+      __syncthreads();
+    }
+    if (t == 0) layer[k] = sh_hi[0];
+    __syncthreads();
+  }
+}
+
+template <bool F16>
+int launch_energy_dt(const mbok_desc* d, const float* W, int64_t ldw, double* rows, double* layer,
+                     hipStream_t stream) {
+  const int G = d->n / kGroup;
+  const int nquads = G < kEnergyMaxQuads ? G : kEnergyMaxQuads;
+  const int threads = (4 * nquads + kWave - 1) / kWave * kWave;
+  dim3 grid((unsigned)d->m), block(threads);
+  switch (d->K) {
+    case 1:
+      hipLaunchKernelGGL((residual_energy_kernel<F16, 1>), grid, block, 0, stream, W, ldw, d->m,
+                         d->n, rows);
+      break;
+    case 2:
+      hipLaunchKernelGGL((residual_energy_kernel<F16, 2>), grid, block, 0, stream, W, ldw, d->m,
+                         d->n, rows);
+      break;
+    case 3:
+      hipLaunchKernelGGL((residual_energy_kernel<F16, 3>), grid, block, 0, stream, W, ldw, d->m,
+                         d->n, rows);
+      break;
+    case 4:
+      hipLaunchKernelGGL((residual_energy_kernel<F16, 4>), grid, block, 0, stream, W, ldw, d->m,
+                         d->n, rows);
+      break;
+    default:
+      return MBOK_ERR_UNSUPPORTED;
+  }
+  if (hipGetLastError() != hipSuccess) return MBOK_ERR_HIP;
+  hipLaunchKernelGGL(energy_layer_kernel, dim3(1), dim3(256), 0, stream, rows, d->m, d->K + 1,
+                     layer);
+  return hipGetLastError() == hipSuccess ? MBOK_OK : MBOK_ERR_HIP;
+}
+
 }  // namespace
 
 int launch_residual_binarize(const mbok_desc* d, const float* W, int64_t ldw, int8_t* signs,
                              void* alpha, int32_t* flag, hipStream_t stream) {
   if (d->alpha_dtype == MBOK_F16) return launch_dt<true>(d, W, ldw, signs, alpha, flag, stream);
   return launch_dt<false>(d, W, ldw, signs, alpha, flag, stream);
+}
+
+int launch_residual_energy(const mbok_desc* d, const float* W, int64_t ldw, double* rows,
+                           double* layer, hipStream_t stream) {
+  if (d->alpha_dtype == MBOK_F16) return launch_energy_dt<true>(d, W, ldw, rows, layer, stream);
+  return launch_energy_dt<false>(d, W, ldw, rows, layer, stream);
 }
 
 }  // namespace mbok

@@ -26,6 +26,11 @@
 // The pair sums are exact when, within a group, the nonzero weights'
 // magnitudes lie within a factor 2^48 of one another (any trained layer);
 // beyond that the quotient before its rounding is accurate to about 2^-100.
+// Every float64 operation in this file is an exact or a once-rounded IEEE
+// operation: no multiply may be fused into a following add (that would
+// break the error-free sums), so contraction is off for the whole file.
+#pragma clang fp contract(off)
+
 #include "mbok_device.h"
 #include "mbok_launch.h"
 

@@ -92,7 +92,8 @@ enum {
   MBOK_ERR_DTYPE = -3,       /* dtype not accepted by this call */
   MBOK_ERR_ALIGN = -4,       /* pointer or leading dimension misaligned */
   MBOK_ERR_HIP = -5,         /* the HIP runtime rejected a launch */
-  MBOK_ERR_UNSUPPORTED = -6  /* K or group outside what the library runs */
+  MBOK_ERR_UNSUPPORTED = -6, /* K or group outside what the library runs */
+  MBOK_ERR_INFEASIBLE = -7   /* no kernel allocation fits the bit budget */
 };
 
 /* Element types. */
@@ -193,6 +194,54 @@ int mbok_residual_binarize(const mbok_desc* d, const float* W, int64_t ldw,
  */
 int mbok_refit(const mbok_desc* d, const float* W, int64_t ldw, int8_t* signs,
                void* alpha, int32_t rounds, void* stream);
+
+/*
+ * Residual energy of the greedy decomposition (the chain of
+ * mbok_residual_binarize with d->K kernels) after k = 0..K kernels: the
+ * residual approximation error that the kernel allocation weighs ([GS]
+ * Italian summary, section "D. Allocazione Automatica dei Kernel").
+ *     row_energy[k * m + i] = float64 nearest to sum_j R_k[i, j]^2
+ *     layer_energy[k]       = float64 nearest to sum_i row_energy[k * m + i]
+ * with R_0 = W and R_k the float64 residual after k kernels (the scales
+ * rounded to d->alpha_dtype exactly as mbok_residual_binarize rounds them).
+ * Because the greedy chain does not depend on how many kernels follow,
+ * layer_energy[K'] is the error of the K'-kernel decomposition for every
+ * K' <= K.  The sums are exact pair sums before their one rounding when a
+ * row's squared residuals (and the layer's row energies) lie within a factor
+ * of about 2^90 (2^48) of one another.
+ *  W             device, fp32, row-major [m, ldw], ldw >= n; read only.
+ *  row_energy    device, float64 [K + 1][m]; overwritten.
+ *  layer_energy  device, float64 [K + 1]; overwritten.
+ * Errors: INVALID_ARG (NULL, ldw < n), SHAPE/DTYPE/UNSUPPORTED from d, ALIGN
+ * (W 16 bytes, ldw % 4, energies 8 bytes), HIP.
+ */
+int mbok_residual_energy(const mbok_desc* d, const float* W, int64_t ldw,
+                         double* row_energy, double* layer_energy, void* stream);
+
+/*
+ * Number of kernels for each of L weights under a bit budget ([GS] Italian
+ * summary, section "D. Allocazione Automatica dei Kernel": kernels per
+ * weight chosen for an average bit budget from residual error and weight
+ * size; the importance term needs data and is left out, so every weight
+ * counts the same).  Host only, no GPU work.  Chooses K_l in 1..kmax with
+ *     sum_l K_l * sizes[l] <= budget
+ * minimising the exact sum of errors[l * kmax + K_l - 1]; among equal
+ * errors the fewest bits, then the first K vector in lexicographic order.
+ * The answer is exact (dynamic programming over exact error sums).
+ *  L       number of weights, >= 1.
+ *  sizes   host int64 [L], entries per weight (bits per kernel), each >= 1.
+ *  errors  host float64 [L][kmax], errors[l * kmax + K - 1] = residual energy
+ *          of weight l with K kernels (e.g. layer_energy[K] of
+ *          mbok_residual_energy); finite and >= 0.
+ *  kmax    1 .. MBOK_MAX_K.
+ *  budget  total kernel-bits, e.g. floor(average kernels * sum of sizes).
+ *  K_out   host int32 [L], written on success only.
+ * Errors: INVALID_ARG (NULL, L < 1, kmax, sizes < 1, errors negative or not
+ * finite, budget < 0), INFEASIBLE (sum of sizes > budget), UNSUPPORTED (more
+ * than 2^22 partial allocations would be compared).
+ */
+int mbok_allocate_kernels(int32_t L, const int64_t* sizes, const double* errors,
+                          int32_t kmax, int64_t budget, int32_t* K_out);
 
 /*
  * Packs Boolean kernels and their scales into MBOK_LAYOUT_L64 (see the top

@@ -51,7 +51,7 @@ def test_header_compiles_as_c(tmp_path):
 
 def test_version_and_status_strings(lib):
     assert "mbok" in bw.mbok_version()
-    for code in (0, -1, -2, -3, -4, -5, -6):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7):
         s = bw.mbok_status_str(code)
         assert s.startswith("MBOK_"), s
     assert bw.mbok_status_str(-99) == "unknown status"
@@ -130,6 +130,15 @@ def test_compute_calls_validate_before_launch(lib):
     assert lib.mbok_gemm(R(d), A16, A16, bw.MBOK_BF16, 4, 128, A16, 64, None) == -1
     assert lib.mbok_gemm(R(d), A16, A16, bw.MBOK_BF16, 4, 256, A16, 63, None) == -1
     assert lib.mbok_residual_binarize(R(d), A16, 128, A16, A16, None, None) == -1
+    # residual energies: NULLs, leading dimension, alignment
+    assert lib.mbok_residual_energy(R(d), None, 256, A16, A16, None) == -1
+    assert lib.mbok_residual_energy(R(d), A16, 256, None, A16, None) == -1
+    assert lib.mbok_residual_energy(R(d), A16, 256, A16, None, None) == -1
+    assert lib.mbok_residual_energy(R(d), A16, 128, A16, A16, None) == -1
+    assert lib.mbok_residual_energy(R(d), MIS, 256, A16, A16, None) == -4
+    assert lib.mbok_residual_energy(R(d), A16, 258, A16, A16, None) == -4
+    assert lib.mbok_residual_energy(R(d), A16, 256, A16 + 4, A16, None) == -4
+    assert lib.mbok_residual_energy(R(_desc(K=5)), A16, 256, A16, A16, None) == -6
     # the refit: NULLs, leading dimension, rounds, alignment
     assert lib.mbok_refit(R(d), None, 256, A16, A16, 2, None) == -1
     assert lib.mbok_refit(R(d), A16, 256, None, A16, 2, None) == -1
@@ -156,3 +165,89 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(ValueError):
         bw.mbok_gemv(d, torch.zeros(10, dtype=torch.uint8), torch.zeros(256),
                      torch.zeros(64))
+
+
+# ------------------------------------------------ kernel allocation (host)
+
+def _alloc(sizes, errors, budget):
+    return bw.mbok_allocate_kernels(sizes, errors, budget)
+
+
+def test_allocation_matches_oracle_hand_worked():
+    import oracle_pins as P
+    for name, sizes, kmax, errors, budget, want in P._read_allocations():
+        if want is None:
+            with pytest.raises(bw.MbokError) as e:
+                _alloc(sizes, errors, budget)
+            assert e.value.status == -7
+        else:
+            assert tuple(_alloc(sizes, errors, budget)) == want, (name, budget)
+
+
+def test_allocation_matches_oracle_random():
+    """The library's dynamic program against the oracle's search over every
+    K vector, on oracle-side random instances with many exact ties."""
+    import numpy as np
+    rng = np.random.default_rng(51)
+    for trial in range(150):
+        L = int(rng.integers(1, 6))
+        kmax = int(rng.integers(1, 5))
+        sizes = [int(v) for v in rng.integers(1, 6, size=L)]
+        # small dyadic values: many equal totals, so the tie rules matter
+        errors = [sorted((rng.integers(0, 6, size=kmax) / 4.0).tolist(), reverse=True)
+                  for _ in range(L)]
+        budget = int(rng.integers(sum(sizes), kmax * sum(sizes) + 2))
+        want = oracle.allocate_kernels(errors, sizes, budget, kmax)
+        assert tuple(_alloc(sizes, errors, budget)) == want, (trial, sizes, errors, budget)
+
+
+def test_allocation_exact_sums_beat_float_rounding():
+    """Errors whose float64 sums would tie are still ordered by their exact
+    sums: 1 + 2^-60 beats 1 in total once 2^-60 is added elsewhere."""
+    sizes = [1, 1]
+    errors = [[1.0, 2.0 ** -60], [2.0 ** -60, 0.0]]
+    # budget 3: (1,2): 1 + 0 = 1; (2,1): 2^-60 + 2^-60 = 2^-59 <- smaller
+    assert _alloc(sizes, errors, 3) == [2, 1]
+    assert oracle.allocate_kernels(errors, sizes, 3, 2) == (2, 1)
+
+
+def test_allocation_rejects_bad_arguments(lib):
+    import numpy as np
+    sz = np.array([4, 4], dtype=np.int64)
+    er = np.array([[1.0, 0.5], [1.0, 0.5]])
+    out = np.zeros(2, dtype=np.int32)
+    A = lambda L, s, e, k, b, o: lib.mbok_allocate_kernels(L, s, e, k, b, o)
+    assert A(2, sz.ctypes.data, er.ctypes.data, 2, 16, out.ctypes.data) == 0
+    assert list(out) == [2, 2]
+    assert A(0, sz.ctypes.data, er.ctypes.data, 2, 16, out.ctypes.data) == -1
+    assert A(2, None, er.ctypes.data, 2, 16, out.ctypes.data) == -1
+    assert A(2, sz.ctypes.data, er.ctypes.data, 5, 16, out.ctypes.data) == -1
+    assert A(2, sz.ctypes.data, er.ctypes.data, 2, -1, out.ctypes.data) == -1
+    assert A(2, sz.ctypes.data, er.ctypes.data, 2, 7, out.ctypes.data) == -7
+    bad = er.copy()
+    bad[1, 1] = np.nan
+    assert A(2, sz.ctypes.data, bad.ctypes.data, 2, 16, out.ctypes.data) == -1
+    bad[1, 1] = -1.0
+    assert A(2, sz.ctypes.data, bad.ctypes.data, 2, 16, out.ctypes.data) == -1
+    zs = sz.copy()
+    zs[0] = 0
+    assert A(2, zs.ctypes.data, er.ctypes.data, 2, 16, out.ctypes.data) == -1
+
+
+def test_allocation_many_weights_is_fast():
+    """A whole 32-layer model of seven linears each (224 weights, config-4
+    sizes in units of 5120 x 512 entries) allocates in well under a second."""
+    import time
+    import numpy as np
+    rng = np.random.default_rng(52)
+    sizes = [10, 10, 10, 10, 27, 27, 27] * 32
+    errors = []
+    for sz in sizes:
+        e0 = sz * (1.0 + 0.2 * rng.random())
+        errors.append([e0 * 0.36, e0 * 0.13, e0 * 0.057, e0 * 0.024])
+    budget = int(2.5 * sum(sizes))
+    t0 = time.perf_counter()
+    K = _alloc(sizes, errors, budget)
+    assert time.perf_counter() - t0 < 5.0
+    assert sum(k * s for k, s in zip(K, sizes)) <= budget
+    assert min(K) >= 1 and max(K) <= 4
