@@ -55,6 +55,9 @@ def parse():
                     help="time the setup kernels instead (greedy quantizer, refit, pack) on "
                          "every linear of the workload; prints one JSON line of its own")
     ap.add_argument("--refit-rounds", type=int, default=2)
+    ap.add_argument("--avg-k", type=float, default=None,
+                    help="LLaMA-13B-shaped layer only: allocate K per linear (1..4) from the "
+                         "residual energies for this average number of kernels per weight")
     ap.add_argument("--extra", nargs="*", default=[],
                     help="with --summarize: more --pmc output dirs of --calibrate-copy runs; "
                          "every counter in them is reported per dominant call")
@@ -245,17 +248,45 @@ def main():
         quantizer_bench(args, cfg, cfg["linears"], K, adt, abytes)
         return
 
+    # weights of each launch: (name, W on the device, K)
+    allocation = None
+    if args.avg_k is not None:
+        if args.config != 4:
+            print("--avg-k applies to the LLaMA-13B-shaped layer (--config 4)", file=sys.stderr)
+            sys.exit(2)
+        Ws = [torch.from_numpy(syn.weight(m, n, syn.weight_seed(4, li))).to(dev)
+              for li, (name, m, n) in enumerate(cfg["linears"])]
+        Ks, _ = bw.allocate_for_budget(Ws, args.avg_k, kmax=4, alpha_dtype=adt)
+        allocation = {nm: k for (nm, _, _), k in zip(cfg["linears"], Ks)}
+        names = [nm for nm, _, _ in cfg["linears"]]
+        launches = []
+        # q|k|v and gate|up share their input: fused when their K agree
+        for group in (["q_proj", "k_proj", "v_proj"], ["o_proj"], ["gate_proj", "up_proj"],
+                      ["down_proj"]):
+            idx = [names.index(g) for g in group]
+            if len({Ks[t] for t in idx}) == 1 and len(idx) > 1:
+                launches.append(("|".join(group), torch.cat([Ws[t] for t in idx]), Ks[idx[0]]))
+            else:
+                launches.extend((names[t], Ws[t], Ks[t]) for t in idx)
+        del Ws
+        K = max(Ks)
+    else:
+        launches = [(name, None, K) for name, m, n in linears]
+
     # ---- setup: quantize + pack on the device, build the rotating pool
     layers = []
     per_step_wbytes = 0.0
     per_step_bytes = 0.0
     per_step_flops = 0.0
-    for li, (name, m, n) in enumerate(linears):
-        W = torch.from_numpy(syn.weight(m, n, syn.weight_seed(args.config, li))).to(dev)
-        d, packed, signs, alpha = bw.quantize_and_pack(W, K, adt)
-        del W, signs, alpha
+    for li, (name, Wl, Kl) in enumerate(launches):
+        if Wl is None:
+            _, m, n = linears[li]
+            Wl = torch.from_numpy(syn.weight(m, n, syn.weight_seed(args.config, li))).to(dev)
+        m, n = Wl.shape
+        d, packed, signs, alpha = bw.quantize_and_pack(Wl, Kl, adt)
+        del Wl, signs, alpha
         layers.append((name, d, packed))
-        wb = weight_bytes(m, n, K, abytes)
+        wb = weight_bytes(m, n, Kl, abytes)
         per_step_wbytes += wb
         per_step_bytes += wb + T * n * (2 if xdt == torch.bfloat16 else 4) + T * m * 4
         per_step_flops += 2.0 * m * n * T
@@ -384,7 +415,7 @@ def main():
         torch.cuda.synchronize()
         del a, b
     m, n = d.m, d.n
-    alg_bytes = weight_bytes(m, n, K, abytes) + T * n * (2 if xdt == torch.bfloat16 else 4) + T * m * 4
+    alg_bytes = weight_bytes(m, n, d.K, abytes) + T * n * (2 if xdt == torch.bfloat16 else 4) + T * m * 4
     if T > 16:
         roof = {"bound": "mfma", "achieved": 2.0 * m * n * T / (launch_us * 1e-6) / 1e12,
                 "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s"}
@@ -392,7 +423,7 @@ def main():
         roof = {"bound": "hbm", "achieved": alg_bytes / (launch_us * 1e-6) / 1e9,
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = stored_traffic(args.config, K, T)
+    roof["traffic"] = stored_traffic(args.config, K, T) if allocation is None else None
     roof["kernel"] = name
     roof["launch_us"] = launch_us
     roof["alg_bytes_per_launch"] = alg_bytes
@@ -410,7 +441,8 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic (seeded N(0,0.02) weights via greedy residual binarization, N(0,1) activations)",
         "config": {"workload": cfg["name"], "linears": [[nm, dd.m, dd.n] for nm, dd, _ in layers],
-                   "K": K, "group": 128, "T": T, "alpha_dtype": cfg["alpha_dtype"],
+                   "K": K if allocation is None else allocation, "group": 128, "T": T,
+                   "alpha_dtype": cfg["alpha_dtype"],
                    "x_dtype": cfg["x_dtype"], "rotating_pool_MB": round(ncopy * per_step_wbytes / 2**20),
                    "launch": "hip graph" if use_graph else "stream",
                    "pct_hbm_peak_of_value": round(100 * value / HBM_PEAK_GBPS, 1) if unit == "GB/s" else None,
@@ -418,7 +450,8 @@ def main():
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(args, cfg, linears[dom], K, T, unit)
+        dname, dd = layers[dom][0], layers[dom][1]
+        line["cpu_baseline"] = cpu_baseline(args, cfg, (dname, dd.m, dd.n), dd.K, T, unit)
     print(json.dumps(line), flush=True)
 
 
