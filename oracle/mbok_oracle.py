@@ -306,6 +306,30 @@ def bound(S: np.ndarray, A: np.ndarray, X: np.ndarray,
     return E[0] if one else E
 
 
+def product_transposed(S: np.ndarray, A: np.ndarray, Gr: np.ndarray,
+                       group: int = GROUP) -> np.ndarray:
+    """DX = Gr . W_hat in float64: DX[t, j] = sum_i W_hat[i, j] Gr[t, i], the
+    activation gradient of the layer (the Boolean-domain training of [GS]
+    propagates gradients through the same weights; [RN] 关键设计: the product
+    splits into K Boolean products).  Gr is [T, m]; a 1-D g gives a 1-D dx."""
+    Gr = np.asarray(Gr, dtype=np.float64)
+    one = Gr.ndim == 1
+    G2 = Gr[None, :] if one else Gr
+    D = G2 @ dequantize(S, A, group)
+    return D[0] if one else D
+
+
+def bound_transposed(S: np.ndarray, A: np.ndarray, Gr: np.ndarray,
+                     group: int = GROUP) -> np.ndarray:
+    """E[t, j] = sum_i |W_hat[i, j]| |Gr[t, i]|: the scale of the accepted
+    error of the transposed product."""
+    Gr = np.asarray(Gr, dtype=np.float64)
+    one = Gr.ndim == 1
+    G2 = Gr[None, :] if one else Gr
+    E = np.abs(G2) @ np.abs(dequantize(S, A, group))
+    return E[0] if one else E
+
+
 def product_rows(S: np.ndarray, A: np.ndarray, X: np.ndarray, rows,
                  group: int = GROUP):
     """Y[:, rows] and E[:, rows] for a subset of output rows only, so that very

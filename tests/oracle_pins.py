@@ -841,6 +841,56 @@ def pin_allocation_monotone(o):
         prev = err
 
 
+# ------------------------------------------------------- transposed product
+
+def pin_transposed_integer(o):
+    """T1: K = 1 and alpha = 1 reduce the transposed product to an exact
+    int64 matmul g^T B; one-hot g gives a row of W_hat."""
+    rng = np.random.default_rng(61)
+    S = rng.choice(np.array([-1, 1], dtype=np.int8), size=(1, 45, 256))
+    A = np.ones((1, 45, 2), dtype=np.float32)
+    g = rng.integers(-8, 9, size=45)
+    want = g.astype(np.int64) @ S[0].astype(np.int64)
+    assert np.array_equal(o.product_transposed(S, A, g), want.astype(np.float64))
+    S3 = rng.choice(np.array([-1, 1], dtype=np.int8), size=(3, 7, 384))
+    A3 = (2.0 ** -rng.integers(3, 9, size=(3, 7, 3))).astype(np.float16)
+    for i in (0, 6):
+        e = np.zeros(7)
+        e[i] = 1.0
+        row = sum(np.repeat(A3[k, i].astype(np.float64), 128) * S3[k, i] for k in range(3))
+        assert np.array_equal(o.product_transposed(S3, A3, e), row), i
+
+
+def pin_transposed_adjoint(o):
+    """T2: <W_hat x, g> = <x, W_hat^T g> exactly (rationals): the transposed
+    product is the adjoint of the (pinned) forward product; and it is linear
+    in g."""
+    rng = np.random.default_rng(62)
+    K, m, n = 2, 5, 256
+    S = rng.choice(np.array([-1, 1], dtype=np.int8), size=(K, m, n))
+    A = (2.0 ** -rng.integers(2, 7, size=(K, m, 2))).astype(np.float16)
+    x = rng.integers(-8, 9, size=n).astype(np.float64)
+    g = rng.integers(-8, 9, size=m).astype(np.float64)
+    y = o.product(S, A, x)
+    dx = o.product_transposed(S, A, g)
+    lhs = sum(Fraction(float(a)) * Fraction(float(b)) for a, b in zip(y, g))
+    rhs = sum(Fraction(float(a)) * Fraction(float(b)) for a, b in zip(x, dx))
+    assert lhs == rhs
+    g2 = rng.integers(-8, 9, size=m).astype(np.float64)
+    assert np.array_equal(o.product_transposed(S, A, g + 2 * g2),
+                          o.product_transposed(S, A, g) + 2 * o.product_transposed(S, A, g2))
+    G = np.stack([g, g2])
+    assert np.array_equal(o.product_transposed(S, A, G)[1], o.product_transposed(S, A, g2))
+    E = o.bound_transposed(S, A, G)
+    assert np.all(np.abs(o.product_transposed(S, A, G)) <= E) and E.shape == (2, n)
+    # with every term nonnegative the bound is the product itself; flipping
+    # the signs of g or of the kernels leaves it unchanged
+    Sp = np.ones_like(S)
+    gp = np.abs(g)
+    assert np.array_equal(o.bound_transposed(Sp, A, gp), o.product_transposed(Sp, A, gp))
+    assert np.array_equal(o.bound_transposed(-S, A, -g), o.bound_transposed(S, A, g))
+
+
 ALL_PINS = [
     pin_round_alpha_rne, pin_hand_worked, pin_sign_step, pin_scale_is_least_squares,
     pin_residual_chain, pin_levels, pin_single_kernel_textbook, pin_constructed_walsh,
@@ -853,4 +903,5 @@ ALL_PINS = [
     pin_energy_walsh, pin_energy_single_kernel, pin_energy_decreases,
     pin_allocation_hand_worked, pin_allocation_knapsack, pin_allocation_greedy_convex,
     pin_allocation_monotone,
+    pin_transposed_integer, pin_transposed_adjoint,
 ]

@@ -107,6 +107,10 @@ MUTATIONS = [
     ("allocation_error_of_wrong_kernel", "allocate_kernels",
      "err = err + Fraction(float(errors[l][ks[l] - 1]))",
      "err = err + Fraction(float(errors[l][min(ks[l], kmax - 1)]))"),
+    ("transposed_uses_forward_orientation", "product_transposed",
+     "D = G2 @ dequantize(S, A, group)", "D = (dequantize(S, A, group) @ G2.T).T"),
+    ("transposed_bound_without_abs_g", "bound_transposed",
+     "E = np.abs(G2) @", "E = G2 @"),
 ]
 
 
