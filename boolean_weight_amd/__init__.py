@@ -20,6 +20,7 @@ __all__ = [
     "mbok_desc_init", "mbok_packed_bytes", "mbok_alpha_bytes", "mbok_residual_binarize",
     "mbok_refit", "MBOK_MAX_REFIT_ROUNDS", "mbok_residual_energy", "mbok_allocate_kernels",
     "mbok_pack", "mbok_gemv", "mbok_gemv_workspace_bytes", "mbok_gemm", "mbok_status_str",
+    "mbok_gemvt", "mbok_gemvt_workspace_bytes",
     "mbok_version", "workspace_for",
     "alpha_torch_dtype", "quantize_and_pack", "allocate_for_budget",
 ]
@@ -80,6 +81,8 @@ def load_library() -> ctypes.CDLL:
         "mbok_gemv_workspace_bytes": (SZ, [D]),
         "mbok_gemv": (ctypes.c_int, [D, P, P, I32, P, P, P]),
         "mbok_gemm": (ctypes.c_int, [D, P, P, I32, I64, I64, P, I64, P]),
+        "mbok_gemvt_workspace_bytes": (SZ, [D]),
+        "mbok_gemvt": (ctypes.c_int, [D, P, P, I32, P, P, P]),
         "mbok_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "mbok_version": (ctypes.c_char_p, []),
     }
@@ -306,6 +309,39 @@ def mbok_gemv(d: mbok_desc, packed: torch.Tensor, x: torch.Tensor, y: torch.Tens
         wptr = workspace.data_ptr()
     _check(load_library().mbok_gemv(ctypes.byref(d), packed.data_ptr(), x.data_ptr(), xd,
                                     y.data_ptr(), wptr, _stream(stream)), "mbok_gemv")
+
+
+def mbok_gemvt_workspace_bytes(d: mbok_desc) -> int:
+    return int(load_library().mbok_gemvt_workspace_bytes(ctypes.byref(d)))
+
+
+def mbok_gemvt(d: mbok_desc, packed: torch.Tensor, g: torch.Tensor, dx: torch.Tensor,
+               workspace: torch.Tensor | None | bool = True, stream=None) -> None:
+    """dx[n] (fp32, overwritten) = W_hat^T g for g bf16 / fp32 [m].
+
+    workspace: True (default) uses a cached workspace for this device and
+    stream; a tensor is used as given; None/False runs without one."""
+    _dev(packed, "packed"), _dev(g, "g"), _dev(dx, "dx")
+    if _nbytes_from(packed) < mbok_packed_bytes(d):
+        raise ValueError("packed buffer too small")
+    gd = _x_dtype(g)
+    if g.numel() < d.m or not g.is_contiguous():
+        raise ValueError("g must be contiguous with m elements")
+    if dx.dtype != torch.float32 or dx.numel() < d.n or not dx.is_contiguous():
+        raise ValueError("dx must be contiguous float32 with n elements")
+    need = mbok_gemvt_workspace_bytes(d)
+    if workspace is True:
+        workspace = workspace_for(need, dx.device, stream)
+    elif workspace is False:
+        workspace = None
+    wptr = None
+    if workspace is not None and need > 0:
+        _dev(workspace, "workspace")
+        if _nbytes_from(workspace) < need:
+            raise ValueError("workspace too small")
+        wptr = workspace.data_ptr()
+    _check(load_library().mbok_gemvt(ctypes.byref(d), packed.data_ptr(), g.data_ptr(), gd,
+                                     dx.data_ptr(), wptr, _stream(stream)), "mbok_gemvt")
 
 
 def mbok_gemm(d: mbok_desc, packed: torch.Tensor, X: torch.Tensor, Y: torch.Tensor,

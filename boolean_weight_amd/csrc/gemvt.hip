@@ -1,0 +1,230 @@
+// Transposed decode product dx = W_hat^T g for one gradient vector g: the
+// activation gradient through the Boolean weights.
+//
+// "Highly Efficient and Effective LLMs with Multi-Boolean Architectures":
+// the gist.science summaries' Boolean-domain training propagates gradients
+// through the Boolean weights; the Paper-Notes reading note, 关键设计, splits
+// the product into K Boolean products of signs.  Here
+//     dx[j] = sum_i sum_k (alpha_k[i, g(j)] * g[i]) * b_k[i, j],
+// i.e. per (row, kernel) the scaled gradient c = alpha * g (fp32) is added to
+// or subtracted from every column of the row's group.
+//
+// Table form, transposed from the decode kernels: the signs of one byte
+// position (8 columns spaced 4 apart) in 4 consecutive rows form a 4 x 8 bit
+// block; a two-step delta-swap transpose turns it into 8 nibbles, one per
+// column, whose bit t is row t.  A 16-entry table of the signed sums of the 4
+// rows' c values (entry p = sum_t (bit t of p ? c_t : -c_t)) then gives each
+// column's contribution with one lookup.
+//
+// Work split: workgroup (g, s) is one wavefront for column group g and the
+// s-th slice of row blocks.  It stages each (row block, group, kernel) plane
+// (64 rows x 16 bytes) in LDS and walks it in 4 steps of 16 rows: lane
+// 16 rq + p takes byte position p of rows 4 rq .. 4 rq + 3 of the step, and
+// keeps 8 column sums across all its planes.  The 4 row-quad lanes of a byte
+// position are added at the end; with several slices each one writes its 128
+// partial sums to the workspace and a second kernel adds the slices in order.
+#include "mbok_device.h"
+#include "mbok_launch.h"
+
+namespace mbok {
+namespace {
+
+constexpr int kTargetWaves = 2048;  // ~8 single-wave workgroups per compute unit
+constexpr int kMaxSlices = 64;
+
+template <typename GT>
+__device__ __forceinline__ float load_grad(const GT* g, int64_t i);
+template <>
+__device__ __forceinline__ float load_grad<float>(const float* g, int64_t i) { return g[i]; }
+template <>
+__device__ __forceinline__ float load_grad<uint16_t>(const uint16_t* g, int64_t i) {
+  return bf16_bits_to_f32(g[i]);
+}
+
+// 4 x 8 bit transpose inside a word.  In: bit 8t + q = (row t, column q).
+// Out: column q < 4 at bits 8q .. 8q+3, column 4 + c at bits 8c+4 .. 8c+7,
+// bit t of each nibble = row t.  Two delta swaps: the off-diagonal 2 x 2
+// blocks of each 4 x 4 half (distance 14), then the off-diagonal entries of
+// each 2 x 2 block (distance 7).
+__device__ __forceinline__ uint32_t transpose4x8(uint32_t x) {
+  uint32_t t = ((x >> 14) ^ x) & 0x0000cccc;
+  x ^= t ^ (t << 14);
+  t = ((x >> 7) ^ x) & 0x00aa00aa;
+  x ^= t ^ (t << 7);
+  return x;
+}
+
+__device__ __forceinline__ int nibble_shift(int q) { return 8 * (q & 3) + 4 * (q >> 2); }
+
+template <typename GT, typename AT, int K>
+__global__ void __launch_bounds__(kWave) gemvt_kernel(const uint4* __restrict__ bits,
+                                                      const AT* __restrict__ scales,
+                                                      const GT* __restrict__ grad,
+                                                      float* __restrict__ out, int m, int G,
+                                                      int RB, int rbs, int64_t slice_stride) {
+  __shared__ uint4 plane[2][kRowBlock];
+  __shared__ float csh[2][kRowBlock];
+  __shared__ float tab[2][kRowBlock];
+  const int g = blockIdx.x;
+  const int slice = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int rq = lane >> 4, p = lane & 15;
+  const int rb0 = slice * rbs;
+  const int rb1 = min(rb0 + rbs, RB);
+  float acc[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+
+  const int np = (rb1 > rb0 ? rb1 - rb0 : 0) * K;  // planes of this slice
+  auto chunk = [&](int t) -> int64_t {
+    const int rb = rb0 + t / K, k = t % K;
+    return ((int64_t)(rb * G + g) * K + k) * kRowBlock + lane;
+  };
+  uint4 nb = make_uint4(0, 0, 0, 0);
+  AT na = AT(0);
+  if (np > 0) {
+    nb = bits[chunk(0)];
+    na = scales[chunk(0)];
+  }
+  float gv = 0.f;
+  for (int t = 0; t < np; ++t) {
+    const uint4 cb = nb;
+    const AT ca = na;
+    if (t % K == 0) {
+      const int64_t row = (int64_t)(rb0 + t / K) * kRowBlock + lane;
+      gv = row < m ? load_grad<GT>(grad, row) : 0.f;
+    }
+    if (t + 1 < np) {
+      nb = bits[chunk(t + 1)];
+      na = scales[chunk(t + 1)];
+    }
+    const int pb = t & 1;
+    plane[pb][lane] = cb;
+    csh[pb][lane] = alpha_to_f32(ca) * gv;  // padding rows: alpha = 0 and g = 0
+    __syncthreads();
+    const uint32_t* pl = reinterpret_cast<const uint32_t*>(plane[pb]);
+    const int w = p >> 2, e = p & 3;
+    // v_perm selectors: byte e of the low word, byte e of the high word
+    const uint32_t sel = (uint32_t)e | ((uint32_t)(4 + e) << 8) | 0x0c0c0000u;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int r0 = 16 * s + 4 * rq;
+      // table entry p of row quad rq: sum_t (bit t of p ? c_t : -c_t)
+      const float c0 = csh[pb][r0], c1 = csh[pb][r0 + 1];
+      const float c2 = csh[pb][r0 + 2], c3 = csh[pb][r0 + 3];
+      float ent = (p & 1) ? c0 : -c0;
+      ent += (p & 2) ? c1 : -c1;
+      ent += (p & 4) ? c2 : -c2;
+      ent += (p & 8) ? c3 : -c3;
+      const int tb = s & 1;
+      tab[tb][lane] = ent;
+      // byte p of rows r0 .. r0+3 -> one word, row t in byte t
+      const uint32_t d0 = pl[4 * r0 + w], d1 = pl[4 * (r0 + 1) + w];
+      const uint32_t d2 = pl[4 * (r0 + 2) + w], d3 = pl[4 * (r0 + 3) + w];
+      const uint32_t lo = __builtin_amdgcn_perm(d1, d0, sel);  // bytes: b0, b1, 0, 0
+      const uint32_t hi = __builtin_amdgcn_perm(d3, d2, sel);  // bytes: b2, b3, 0, 0
+      const uint32_t X = transpose4x8(lo | (hi << 16));
+      __syncthreads();
+      const float* tq = &tab[tb][16 * rq];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] += tq[(X >> nibble_shift(q)) & 0xfu];
+    }
+  }
+  // the four row-quad lanes of a byte position hold the same columns
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    acc[q] += __shfl_xor(acc[q], 16, kWave);
+    acc[q] += __shfl_xor(acc[q], 32, kWave);
+  }
+  if (rq == 0) {
+    float* dst = out + slice * slice_stride + (int64_t)g * kGroup + 32 * (p >> 2) + (p & 3);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) dst[4 * q] = acc[q];
+  }
+}
+
+// dx[j] = sum over slices s (in order) of partial[s * n + j]
+__global__ void __launch_bounds__(256) gemvt_reduce_kernel(const float* __restrict__ partial,
+                                                           int S, int n, float* __restrict__ dx) {
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= n) return;
+  float v = partial[j];
+  for (int s = 1; s < S; ++s) v += partial[(int64_t)s * n + j];
+  dx[j] = v;
+}
+
+// Row-block slices per column group: enough single-wave workgroups to fill
+// the chip, at most kMaxSlices.
+void slicing(const Geom& geo, int& S, int& rbs) {
+  int want = (kTargetWaves + geo.G - 1) / geo.G;
+  want = want < 1 ? 1 : (want > kMaxSlices ? kMaxSlices : want);
+  if (want > geo.RB) want = geo.RB;
+  rbs = (geo.RB + want - 1) / want;
+  S = (geo.RB + rbs - 1) / rbs;
+}
+
+template <typename GT, typename AT>
+int launch_t(const Geom& geo, const void* packed, const void* grad, float* dx, void* ws,
+             hipStream_t stream) {
+  const uint4* bits = reinterpret_cast<const uint4*>(packed);
+  const AT* scales =
+      reinterpret_cast<const AT*>(reinterpret_cast<const char*>(packed) + geo.bits_bytes);
+  int S, rbs;
+  slicing(geo, S, rbs);
+  if (!ws) {  // one slice per group writes dx directly
+    S = 1;
+    rbs = geo.RB;
+  }
+  float* out = S > 1 ? reinterpret_cast<float*>(ws) : dx;
+  const GT* gr = reinterpret_cast<const GT*>(grad);
+  dim3 grid((unsigned)geo.G, (unsigned)S), block(kWave);
+  switch (geo.K) {
+    case 1:
+      hipLaunchKernelGGL((gemvt_kernel<GT, AT, 1>), grid, block, 0, stream, bits, scales, gr, out,
+                         geo.m, geo.G, geo.RB, rbs, (int64_t)geo.n);
+      break;
+    case 2:
+      hipLaunchKernelGGL((gemvt_kernel<GT, AT, 2>), grid, block, 0, stream, bits, scales, gr, out,
+                         geo.m, geo.G, geo.RB, rbs, (int64_t)geo.n);
+      break;
+    case 3:
+      hipLaunchKernelGGL((gemvt_kernel<GT, AT, 3>), grid, block, 0, stream, bits, scales, gr, out,
+                         geo.m, geo.G, geo.RB, rbs, (int64_t)geo.n);
+      break;
+    case 4:
+      hipLaunchKernelGGL((gemvt_kernel<GT, AT, 4>), grid, block, 0, stream, bits, scales, gr, out,
+                         geo.m, geo.G, geo.RB, rbs, (int64_t)geo.n);
+      break;
+    default:
+      return MBOK_ERR_UNSUPPORTED;
+  }
+  if (hipGetLastError() != hipSuccess) return MBOK_ERR_HIP;
+  if (S > 1) {
+    hipLaunchKernelGGL(gemvt_reduce_kernel, dim3((geo.n + 255) / 256), dim3(256), 0, stream, out,
+                       S, geo.n, dx);
+    if (hipGetLastError() != hipSuccess) return MBOK_ERR_HIP;
+  }
+  return MBOK_OK;
+}
+
+}  // namespace
+
+size_t gemvt_workspace_bytes(const mbok_desc* d) {
+  const Geom geo = make_geom(d);
+  int S, rbs;
+  slicing(geo, S, rbs);
+  return S > 1 ? (size_t)S * (size_t)geo.n * sizeof(float) : 0;
+}
+
+int launch_gemvt(const mbok_desc* d, const void* packed, const void* grad, int32_t g_dtype,
+                 float* dx, void* ws, hipStream_t stream) {
+  const Geom geo = make_geom(d);
+  const bool f16a = d->alpha_dtype == MBOK_F16;
+  if (g_dtype == MBOK_BF16)
+    return f16a ? launch_t<uint16_t, uint16_t>(geo, packed, grad, dx, ws, stream)
+                : launch_t<uint16_t, float>(geo, packed, grad, dx, ws, stream);
+  return f16a ? launch_t<float, uint16_t>(geo, packed, grad, dx, ws, stream)
+              : launch_t<float, float>(geo, packed, grad, dx, ws, stream);
+}
+
+}  // namespace mbok

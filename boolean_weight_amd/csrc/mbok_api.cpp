@@ -134,6 +134,23 @@ int mbok_gemv(const mbok_desc* d, const void* packed, const void* x, int32_t x_d
   return mbok::launch_gemv(d, packed, x, x_dtype, y, workspace, (hipStream_t)stream);
 }
 
+size_t mbok_gemvt_workspace_bytes(const mbok_desc* d) {
+  if (check_desc(d) != MBOK_OK) return 0;
+  return mbok::gemvt_workspace_bytes(d);
+}
+
+int mbok_gemvt(const mbok_desc* d, const void* packed, const void* g, int32_t g_dtype, float* dx,
+               void* workspace, void* stream) {
+  int st = check_desc(d);
+  if (st != MBOK_OK) return st;
+  if (!packed || !g || !dx) return MBOK_ERR_INVALID_ARG;
+  if (g_dtype != MBOK_BF16 && g_dtype != MBOK_F32) return MBOK_ERR_DTYPE;
+  if (!aligned(packed, 16) || !aligned(g, g_dtype == MBOK_BF16 ? 2 : 4) || !aligned(dx, 4))
+    return MBOK_ERR_ALIGN;
+  if (workspace && !aligned(workspace, 256)) return MBOK_ERR_ALIGN;
+  return mbok::launch_gemvt(d, packed, g, g_dtype, dx, workspace, (hipStream_t)stream);
+}
+
 int mbok_gemm(const mbok_desc* d, const void* packed, const void* X, int32_t x_dtype, int64_t T,
               int64_t ldx, float* Y, int64_t ldy, void* stream) {
   int st = check_desc(d);

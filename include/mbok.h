@@ -291,6 +291,36 @@ int mbok_gemv(const mbok_desc* d, const void* packed, const void* x,
               int32_t x_dtype, float* y, void* workspace, void* stream);
 
 /*
+ * Bytes of the workspace mbok_gemvt uses for this shape (the partial column
+ * sums of its row slices), 0 when it needs none.  Host only; 0 for a NULL or
+ * invalid descriptor.
+ */
+size_t mbok_gemvt_workspace_bytes(const mbok_desc* d);
+
+/*
+ * Transposed decode product for one gradient vector, the activation gradient
+ * of the layer (the [GS] summaries' Boolean-domain training propagates
+ * gradients through the Boolean weights; [RN] 关键设计: the product splits
+ * into K Boolean products):
+ *     dx[j] = sum_i sum_k alpha_k[i, j/128] * b_k[i, j] * g[i]
+ * Each term alpha_k[i, .] * g[i] is formed in fp32; the sums are fp32.
+ *  packed    device, MBOK_LAYOUT_L64 buffer of this descriptor (the same
+ *            buffer mbok_gemv reads).
+ *  g         device, m values of g_dtype (MBOK_BF16 or MBOK_F32).
+ *  dx        device fp32 [n]; overwritten (not accumulated).
+ *  workspace device, mbok_gemvt_workspace_bytes(d) bytes, 256-byte aligned,
+ *            or NULL.  With NULL one workgroup per column group walks all
+ *            rows (correct, slower); with the workspace the rows are split
+ *            into slices whose partial sums a second kernel adds in a fixed
+ *            order.  Its contents need no initialisation; calls that may run
+ *            at the same time need distinct workspaces.
+ * Errors: INVALID_ARG (NULL), SHAPE/UNSUPPORTED from d, DTYPE (g_dtype),
+ * ALIGN (packed 16 bytes, g and dx 4 bytes, workspace 256 bytes), HIP.
+ */
+int mbok_gemvt(const mbok_desc* d, const void* packed, const void* g,
+               int32_t g_dtype, float* dx, void* workspace, void* stream);
+
+/*
  * The same product for T tokens:  Y[t, i] = sum_j W_hat[i, j] * X[t, j].
  * T <= 16 runs the weight-streaming skinny kernel (exact fp32 scaling of
  * +-1 products).  T > 16 is the prefill GEMM: each tile of W_hat is formed

@@ -130,6 +130,18 @@ def test_compute_calls_validate_before_launch(lib):
     assert lib.mbok_gemm(R(d), A16, A16, bw.MBOK_BF16, 4, 128, A16, 64, None) == -1
     assert lib.mbok_gemm(R(d), A16, A16, bw.MBOK_BF16, 4, 256, A16, 63, None) == -1
     assert lib.mbok_residual_binarize(R(d), A16, 128, A16, A16, None, None) == -1
+    # transposed product
+    assert lib.mbok_gemvt(R(d), None, A16, bw.MBOK_BF16, A16, None, None) == -1
+    assert lib.mbok_gemvt(R(d), A16, None, bw.MBOK_BF16, A16, None, None) == -1
+    assert lib.mbok_gemvt(R(d), A16, A16, bw.MBOK_BF16, None, None, None) == -1
+    assert lib.mbok_gemvt(R(d), A16, A16, bw.MBOK_F16, A16, None, None) == -3
+    assert lib.mbok_gemvt(R(d), MIS, A16, bw.MBOK_BF16, A16, None, None) == -4
+    assert lib.mbok_gemvt(R(d), A16, A16 + 1, bw.MBOK_BF16, A16, None, None) == -4
+    assert lib.mbok_gemvt(R(d), A16, A16 + 2, bw.MBOK_F32, A16, None, None) == -4
+    assert lib.mbok_gemvt(R(d), A16, A16, bw.MBOK_F32, A16 + 2, None, None) == -4
+    assert lib.mbok_gemvt(R(d), A16, A16, bw.MBOK_F32, A16, A16 + 16, None) == -4
+    assert lib.mbok_gemvt(R(_desc(K=9)), A16, A16, bw.MBOK_F32, A16, None, None) == -6
+    assert lib.mbok_gemvt_workspace_bytes(None) == 0
     # residual energies: NULLs, leading dimension, alignment
     assert lib.mbok_residual_energy(R(d), None, 256, A16, A16, None) == -1
     assert lib.mbok_residual_energy(R(d), A16, 256, None, A16, None) == -1
