@@ -55,6 +55,8 @@ def parse():
                     help="time the setup kernels instead (greedy quantizer, refit, pack) on "
                          "every linear of the workload; prints one JSON line of its own")
     ap.add_argument("--refit-rounds", type=int, default=2)
+    ap.add_argument("--transposed", action="store_true",
+                    help="one token: time the transposed product dx = W_hat^T g instead")
     ap.add_argument("--avg-k", type=float, default=None,
                     help="LLaMA-13B-shaped layer only: allocate K per linear (1..4) from the "
                          "residual energies for this average number of kernels per weight")
@@ -244,6 +246,9 @@ def main():
                    ("gate_up_proj", 2 * 13824, 5120), ("down_proj", 5120, 13824)]
     if args.config == 3:
         linears = linears[:1] if T == 1 else linears
+    if args.transposed and T != 1:
+        print("--transposed runs one gradient vector (T = 1)", file=sys.stderr)
+        sys.exit(2)
     if args.quantizer:
         quantizer_bench(args, cfg, cfg["linears"], K, adt, abytes)
         return
@@ -299,18 +304,30 @@ def main():
     torch.cuda.empty_cache()
     xs, ys = [], []
     for li, (name, d, _) in enumerate(layers):
+        if args.transposed:  # gradient g [m] in, dx [n] out
+            x = torch.from_numpy(syn.activations(1, d.m, syn.act_seed(args.config, li) + 500,
+                                                 cfg["x_dtype"])).to(dev).to(xdt)
+            xs.append(x[0].contiguous())
+            ys.append(torch.empty((d.n,), dtype=torch.float32, device=dev))
+            continue
         x = torch.from_numpy(syn.activations(T, d.n, syn.act_seed(args.config, li),
                                              cfg["x_dtype"])).to(dev).to(xdt)
         xs.append(x if T > 1 else x[0].contiguous())
         ys.append(torch.empty((T, d.m) if T > 1 else (d.m,), dtype=torch.float32, device=dev))
 
+    def call(li, c):
+        d = layers[li][1]
+        if args.transposed:
+            bw.mbok_gemvt(d, pools[li][c], xs[li], ys[li])
+        elif T == 1:
+            bw.mbok_gemv(d, pools[li][c], xs[li], ys[li])
+        else:
+            bw.mbok_gemm(d, pools[li][c], xs[li], ys[li])
+
     def step(i):
         c = i % ncopy
-        for li, (name, d, _) in enumerate(layers):
-            if T == 1:
-                bw.mbok_gemv(d, pools[li][c], xs[li], ys[li])
-            else:
-                bw.mbok_gemm(d, pools[li][c], xs[li], ys[li])
+        for li in range(len(layers)):
+            call(li, c)
 
     # A HIP graph of one pass over the whole pool (>= 1 GiB of distinct
     # weights): replays stream cold weights and save per-launch CPU work.
@@ -364,11 +381,7 @@ def main():
     name, d, _ = layers[dom]
 
     def dom_call(i):
-        c = i % ncopy
-        if T == 1:
-            bw.mbok_gemv(d, pools[dom][c], xs[dom], ys[dom])
-        else:
-            bw.mbok_gemm(d, pools[dom][c], xs[dom], ys[dom])
+        call(dom, i % ncopy)
 
     s2 = torch.cuda.Stream()
     s2.wait_stream(torch.cuda.current_stream())
@@ -415,7 +428,10 @@ def main():
         torch.cuda.synchronize()
         del a, b
     m, n = d.m, d.n
-    alg_bytes = weight_bytes(m, n, d.K, abytes) + T * n * (2 if xdt == torch.bfloat16 else 4) + T * m * 4
+    if args.transposed:  # g in, dx out
+        alg_bytes = weight_bytes(m, n, d.K, abytes) + m * (2 if xdt == torch.bfloat16 else 4) + n * 4
+    else:
+        alg_bytes = weight_bytes(m, n, d.K, abytes) + T * n * (2 if xdt == torch.bfloat16 else 4) + T * m * 4
     if T > 16:
         roof = {"bound": "mfma", "achieved": 2.0 * m * n * T / (launch_us * 1e-6) / 1e12,
                 "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s"}
@@ -423,12 +439,16 @@ def main():
         roof = {"bound": "hbm", "achieved": alg_bytes / (launch_us * 1e-6) / 1e9,
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = stored_traffic(args.config, K, T) if allocation is None else None
+    roof["traffic"] = (stored_traffic(args.config, K, T)
+                       if allocation is None and not args.transposed else None)
     roof["kernel"] = name
     roof["launch_us"] = launch_us
     roof["alg_bytes_per_launch"] = alg_bytes
 
-    if T > 16:
+    if args.transposed:
+        metric, unit = "transposed weight GB/s", "GB/s"
+        value = per_step_wbytes / (ms_per_step * 1e-3) / 1e9
+    elif T > 16:
         metric, unit = "prefill TFLOP/s", "TFLOP/s"
         value = per_step_flops / (ms_per_step * 1e-3) / 1e12
     else:
@@ -449,6 +469,8 @@ def main():
                    "wall_s": round(wall, 3)},
         "roofline": roof,
     }
+    if args.transposed:
+        line["config"]["product"] = "dx = W_hat^T g"
     if not args.no_cpu_baseline:
         dname, dd = layers[dom][0], layers[dom][1]
         line["cpu_baseline"] = cpu_baseline(args, cfg, (dname, dd.m, dd.n), dd.K, T, unit)
@@ -539,10 +561,14 @@ def cpu_baseline(args, cfg, lin, K, T, unit):
         rows = m if T == 1 else min(m, 512)
         S, A, _ = oracle.residual_binarize(W[:rows], K, alpha_dtype=cfg["alpha_dtype"])
         X = syn.activations(T, n, syn.act_seed(args.config, 0), cfg["x_dtype"])
+        Gr = syn.activations(1, rows, syn.act_seed(args.config, 0) + 500, cfg["x_dtype"])[0]
         t0 = time.perf_counter()
         reps = 0
         while True:
-            oracle.product(S, A, X if T > 1 else X[0])
+            if args.transposed:
+                oracle.product_transposed(S, A, Gr)
+            else:
+                oracle.product(S, A, X if T > 1 else X[0])
             reps += 1
             if time.perf_counter() - t0 > args.cpu_seconds:
                 break
@@ -553,7 +579,8 @@ def cpu_baseline(args, cfg, lin, K, T, unit):
     else:
         value = 2.0 * rows * n * T * reps / dt / 1e12
     return {"value": value, "unit": unit, "cores": cores, "kind": "oracle",
-            "sample": f"{reps} oracle products (fp64 dequantize + matmul) of {name} "
+            "sample": f"{reps} oracle {'transposed ' if args.transposed else ''}products "
+                      f"(fp64 dequantize + matmul) of {name} "
                       f"rows 0..{rows - 1} x {n}, K={K}, T={T}, in {dt:.1f} s"}
 
 

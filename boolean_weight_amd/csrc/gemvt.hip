@@ -16,21 +16,27 @@
 // rows' c values (entry p = sum_t (bit t of p ? c_t : -c_t)) then gives each
 // column's contribution with one lookup.
 //
-// Work split: workgroup (g, s) is one wavefront for column group g and the
-// s-th slice of row blocks.  It stages each (row block, group, kernel) plane
-// (64 rows x 16 bytes) in LDS and walks it in 4 steps of 16 rows: lane
+// Work split: each wavefront takes one column group g and one slice of its
+// row blocks, stages each (row block, group, kernel) plane (64 rows x 16
+// bytes) in its own LDS region and walks it in 4 steps of 16 rows: lane
 // 16 rq + p takes byte position p of rows 4 rq .. 4 rq + 3 of the step, and
-// keeps 8 column sums across all its planes.  The 4 row-quad lanes of a byte
-// position are added at the end; with several slices each one writes its 128
-// partial sums to the workspace and a second kernel adds the slices in order.
+// keeps 8 column sums across all its planes.  The lane of row r builds a
+// quarter of its row quad's table from the quad's four c values (quad
+// permutations), so a plane's 16 tables and its bits reach LDS together.  The
+// 4 row-quad lanes of a byte position are added at the end, then the 4
+// wavefronts (slices) of a workgroup in order; with several workgroups per
+// column group each writes its 128 partial sums to the workspace and a
+// second kernel adds them in order.
 #include "mbok_device.h"
 #include "mbok_launch.h"
 
 namespace mbok {
 namespace {
 
-constexpr int kTargetWaves = 2048;  // ~8 single-wave workgroups per compute unit
-constexpr int kMaxSlices = 64;
+constexpr int kTargetWaves = 2048;    // ~8 wavefronts per compute unit
+constexpr int kSlicesPerBlock = 4;    // wavefronts (row-block slices) per workgroup
+constexpr int kMaxBlocksY = 16;       // workgroups along the rows of a column group
+constexpr int kMaxSlices = kSlicesPerBlock * kMaxBlocksY;
 
 template <typename GT>
 __device__ __forceinline__ float load_grad(const GT* g, int64_t i);
@@ -56,19 +62,26 @@ __device__ __forceinline__ uint32_t transpose4x8(uint32_t x) {
 
 __device__ __forceinline__ int nibble_shift(int q) { return 8 * (q & 3) + 4 * (q >> 2); }
 
+// Each wavefront's LDS region is its own, and a wavefront's LDS operations
+// complete in order: waiting for them (and keeping the compiler from moving
+// memory accesses across) is all the ordering needed.  A workgroup barrier
+// would also wait for the next plane's global loads, meant to stay in flight.
+__device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 template <typename GT, typename AT, int K>
-__global__ void __launch_bounds__(kWave) gemvt_kernel(const uint4* __restrict__ bits,
-                                                      const AT* __restrict__ scales,
-                                                      const GT* __restrict__ grad,
-                                                      float* __restrict__ out, int m, int G,
-                                                      int RB, int rbs, int64_t slice_stride) {
-  __shared__ uint4 plane[2][kRowBlock];
-  __shared__ float csh[2][kRowBlock];
-  __shared__ float tab[2][kRowBlock];
+__global__ void __launch_bounds__(kSlicesPerBlock * kWave) gemvt_kernel(
+    const uint4* __restrict__ bits, const AT* __restrict__ scales, const GT* __restrict__ grad,
+    float* __restrict__ out, int m, int G, int RB, int rbs, int64_t slice_stride) {
+  __shared__ uint4 plane[kSlicesPerBlock][2][kRowBlock];
+  // the 16 tables of a plane (one per row quad), 16 entries each
+  __shared__ float4 tab[kSlicesPerBlock][2][kRowBlock];
+  __shared__ float red[kSlicesPerBlock][kGroup];
   const int g = blockIdx.x;
-  const int slice = blockIdx.y;
-  const int lane = threadIdx.x;
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int slice = blockIdx.y * kSlicesPerBlock + wave;
   const int rq = lane >> 4, p = lane & 15;
+  const int u = lane & 3;  // this lane's quarter of its own row quad's table
   const int rb0 = slice * rbs;
   const int rb1 = min(rb0 + rbs, RB);
   float acc[8];
@@ -87,6 +100,9 @@ __global__ void __launch_bounds__(kWave) gemvt_kernel(const uint4* __restrict__ 
     na = scales[chunk(0)];
   }
   float gv = 0.f;
+  const int w = p >> 2, e = p & 3;
+  // v_perm selector: byte e of the low word, byte e of the high word
+  const uint32_t sel = (uint32_t)e | ((uint32_t)(4 + e) << 8) | 0x0c0c0000u;
   for (int t = 0; t < np; ++t) {
     const uint4 cb = nb;
     const AT ca = na;
@@ -98,34 +114,37 @@ __global__ void __launch_bounds__(kWave) gemvt_kernel(const uint4* __restrict__ 
       nb = bits[chunk(t + 1)];
       na = scales[chunk(t + 1)];
     }
+    // c of this lane's row (padding rows: alpha = 0 and g = 0), then the c of
+    // all four rows of the lane's row quad by quad permutations
+    const float c = alpha_to_f32(ca) * gv;
+    const float c0 = __int_as_float(quad_perm_i<0x00>(__float_as_int(c)));
+    const float c1 = __int_as_float(quad_perm_i<0x55>(__float_as_int(c)));
+    const float c2 = __int_as_float(quad_perm_i<0xaa>(__float_as_int(c)));
+    const float c3 = __int_as_float(quad_perm_i<0xff>(__float_as_int(c)));
+    // entries 4u + v, v = 0..3: bits 0, 1 of the entry come from v, bits 2, 3
+    // from u; entry = (+-c0 +-c1) + (+-c2 +-c3)
+    const float hiq = ((u & 1) ? c2 : -c2) + ((u & 2) ? c3 : -c3);
+    float4 ent;
+    ent.x = (-c0 - c1) + hiq;
+    ent.y = (c0 - c1) + hiq;
+    ent.z = (-c0 + c1) + hiq;
+    ent.w = (c0 + c1) + hiq;
     const int pb = t & 1;
-    plane[pb][lane] = cb;
-    csh[pb][lane] = alpha_to_f32(ca) * gv;  // padding rows: alpha = 0 and g = 0
-    __syncthreads();
-    const uint32_t* pl = reinterpret_cast<const uint32_t*>(plane[pb]);
-    const int w = p >> 2, e = p & 3;
-    // v_perm selectors: byte e of the low word, byte e of the high word
-    const uint32_t sel = (uint32_t)e | ((uint32_t)(4 + e) << 8) | 0x0c0c0000u;
+    plane[wave][pb][lane] = cb;
+    tab[wave][pb][lane] = ent;  // row quad lane / 4, entries 4u .. 4u+3
+    lds_sync();
+    const uint32_t* pl = reinterpret_cast<const uint32_t*>(plane[wave][pb]);
+    const float* tb = reinterpret_cast<const float*>(tab[wave][pb]);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int r0 = 16 * s + 4 * rq;
-      // table entry p of row quad rq: sum_t (bit t of p ? c_t : -c_t)
-      const float c0 = csh[pb][r0], c1 = csh[pb][r0 + 1];
-      const float c2 = csh[pb][r0 + 2], c3 = csh[pb][r0 + 3];
-      float ent = (p & 1) ? c0 : -c0;
-      ent += (p & 2) ? c1 : -c1;
-      ent += (p & 4) ? c2 : -c2;
-      ent += (p & 8) ? c3 : -c3;
-      const int tb = s & 1;
-      tab[tb][lane] = ent;
       // byte p of rows r0 .. r0+3 -> one word, row t in byte t
       const uint32_t d0 = pl[4 * r0 + w], d1 = pl[4 * (r0 + 1) + w];
       const uint32_t d2 = pl[4 * (r0 + 2) + w], d3 = pl[4 * (r0 + 3) + w];
       const uint32_t lo = __builtin_amdgcn_perm(d1, d0, sel);  // bytes: b0, b1, 0, 0
       const uint32_t hi = __builtin_amdgcn_perm(d3, d2, sel);  // bytes: b2, b3, 0, 0
       const uint32_t X = transpose4x8(lo | (hi << 16));
-      __syncthreads();
-      const float* tq = &tab[tb][16 * rq];
+      const float* tq = tb + 16 * (r0 >> 2);  // table of row quad r0 / 4
 #pragma unroll
       for (int q = 0; q < 8; ++q) acc[q] += tq[(X >> nibble_shift(q)) & 0xfu];
     }
@@ -137,30 +156,45 @@ __global__ void __launch_bounds__(kWave) gemvt_kernel(const uint4* __restrict__ 
     acc[q] += __shfl_xor(acc[q], 32, kWave);
   }
   if (rq == 0) {
-    float* dst = out + slice * slice_stride + (int64_t)g * kGroup + 32 * (p >> 2) + (p & 3);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) dst[4 * q] = acc[q];
+    for (int q = 0; q < 8; ++q) red[wave][32 * w + 4 * q + e] = acc[q];
+  }
+  __syncthreads();
+  // the workgroup's slices, added in order
+  if (threadIdx.x < kGroup) {
+    float v = red[0][threadIdx.x];
+#pragma unroll
+    for (int sv = 1; sv < kSlicesPerBlock; ++sv) v += red[sv][threadIdx.x];
+    out[blockIdx.y * slice_stride + (int64_t)g * kGroup + threadIdx.x] = v;
   }
 }
 
-// dx[j] = sum over slices s (in order) of partial[s * n + j]
+// dx[j] = the sum over slice groups s of partial[s * n + j], in order, all
+// loads of a thread issued together.
 __global__ void __launch_bounds__(256) gemvt_reduce_kernel(const float* __restrict__ partial,
                                                            int S, int n, float* __restrict__ dx) {
   const int j = blockIdx.x * blockDim.x + threadIdx.x;
   if (j >= n) return;
-  float v = partial[j];
-  for (int s = 1; s < S; ++s) v += partial[(int64_t)s * n + j];
+  float buf[kMaxBlocksY];
+#pragma unroll
+  for (int s = 0; s < kMaxBlocksY; ++s) buf[s] = s < S ? partial[(int64_t)s * n + j] : 0.f;
+  float v = buf[0];
+#pragma unroll
+  for (int s = 1; s < kMaxBlocksY; ++s) v += buf[s];
   dx[j] = v;
 }
 
-// Row-block slices per column group: enough single-wave workgroups to fill
-// the chip, at most kMaxSlices.
-void slicing(const Geom& geo, int& S, int& rbs) {
-  int want = (kTargetWaves + geo.G - 1) / geo.G;
+// Row-block slices per column group: enough wavefronts to fill the chip,
+// kSlicesPerBlock per workgroup, at most kMaxBlocksY workgroups per group
+// (SY).  Without a workspace SY = 1.
+void slicing(const Geom& geo, bool have_ws, int& SY, int& rbs) {
+  int want = (kTargetWaves + geo.G - 1) / geo.G;  // wavefront slices
   want = want < 1 ? 1 : (want > kMaxSlices ? kMaxSlices : want);
+  if (!have_ws && want > kSlicesPerBlock) want = kSlicesPerBlock;
   if (want > geo.RB) want = geo.RB;
   rbs = (geo.RB + want - 1) / want;
-  S = (geo.RB + rbs - 1) / rbs;
+  const int S = (geo.RB + rbs - 1) / rbs;
+  SY = (S + kSlicesPerBlock - 1) / kSlicesPerBlock;
 }
 
 template <typename GT, typename AT>
@@ -169,15 +203,11 @@ int launch_t(const Geom& geo, const void* packed, const void* grad, float* dx, v
   const uint4* bits = reinterpret_cast<const uint4*>(packed);
   const AT* scales =
       reinterpret_cast<const AT*>(reinterpret_cast<const char*>(packed) + geo.bits_bytes);
-  int S, rbs;
-  slicing(geo, S, rbs);
-  if (!ws) {  // one slice per group writes dx directly
-    S = 1;
-    rbs = geo.RB;
-  }
-  float* out = S > 1 ? reinterpret_cast<float*>(ws) : dx;
+  int SY, rbs;
+  slicing(geo, ws != nullptr, SY, rbs);
+  float* out = SY > 1 ? reinterpret_cast<float*>(ws) : dx;
   const GT* gr = reinterpret_cast<const GT*>(grad);
-  dim3 grid((unsigned)geo.G, (unsigned)S), block(kWave);
+  dim3 grid((unsigned)geo.G, (unsigned)SY), block(kSlicesPerBlock * kWave);
   switch (geo.K) {
     case 1:
       hipLaunchKernelGGL((gemvt_kernel<GT, AT, 1>), grid, block, 0, stream, bits, scales, gr, out,
@@ -199,9 +229,9 @@ int launch_t(const Geom& geo, const void* packed, const void* grad, float* dx, v
       return MBOK_ERR_UNSUPPORTED;
   }
   if (hipGetLastError() != hipSuccess) return MBOK_ERR_HIP;
-  if (S > 1) {
+  if (SY > 1) {
     hipLaunchKernelGGL(gemvt_reduce_kernel, dim3((geo.n + 255) / 256), dim3(256), 0, stream, out,
-                       S, geo.n, dx);
+                       SY, geo.n, dx);
     if (hipGetLastError() != hipSuccess) return MBOK_ERR_HIP;
   }
   return MBOK_OK;
@@ -211,9 +241,9 @@ int launch_t(const Geom& geo, const void* packed, const void* grad, float* dx, v
 
 size_t gemvt_workspace_bytes(const mbok_desc* d) {
   const Geom geo = make_geom(d);
-  int S, rbs;
-  slicing(geo, S, rbs);
-  return S > 1 ? (size_t)S * (size_t)geo.n * sizeof(float) : 0;
+  int SY, rbs;
+  slicing(geo, true, SY, rbs);
+  return SY > 1 ? (size_t)SY * (size_t)geo.n * sizeof(float) : 0;
 }
 
 int launch_gemvt(const mbok_desc* d, const void* packed, const void* grad, int32_t g_dtype,
