@@ -22,7 +22,10 @@ Sources (page title, then the section on that page):
            or greedy search.
   [GS] gist.science summaries of the same paper ("Successive SVID",
        "Extracción Sucesiva"): each further kernel is fitted to the residual
-       error left by the previous ones.  The Italian summary, section "D.
+       error left by the previous ones; SVID approximates a weight by
+       sign(W) (.) (s_out s_in^T), s_out s_in^T the rank-1 SVD of |W|
+       ("Riformulazione Booleana e SVID", "Descomposición SVID").  The
+       Italian summary, section "D.
        Allocazione Automatica dei Kernel": the number of kernels per weight
        is allocated for an average bit budget from residual error,
        importance and size.
@@ -271,6 +274,88 @@ def allocate_kernels(errors, sizes, budget: int, kmax: int):
         if best is None or key < best[0]:
             best = (key, ks)
     return None if best is None else tuple(best[1])
+
+
+def _top_singular(M: np.ndarray):
+    """Largest singular value of a nonnegative float64 matrix M and its unit
+    singular vectors (u, v), signed so that each sums to >= 0.  A library
+    SVD: numpy's dense LAPACK SVD up to 2^22 entries, above that scipy's
+    ARPACK (scipy.sparse.linalg.svds, one triple, tol=0, a start vector of
+    ones, so the result is reproducible)."""
+    if M.size <= (1 << 22):
+        U, sv, Vt = np.linalg.svd(M, full_matrices=False)
+        sigma, u, v = float(sv[0]), U[:, 0], Vt[0]
+    else:
+        from scipy.sparse.linalg import svds
+        U, sv, Vt = svds(M, k=1, tol=0, v0=np.ones(min(M.shape)))
+        sigma, u, v = float(sv[0]), U[:, 0], Vt[0]
+    if u.sum() < 0:
+        u = -u
+    if v.sum() < 0:
+        v = -v
+    return sigma, u, v
+
+
+def svid_decompose(W: np.ndarray, K: int, alpha_dtype: str = "f16"):
+    """Successive sign-value-independent decomposition (gist.science
+    summaries, "Riformulazione Booleana e SVID" / "Successive SVID" /
+    "Descomposición SVID"): a weight is approximated by sign(W) (.) (s_out
+    s_in^T) with s_out s_in^T the rank-1 SVD of |W|, and every further kernel
+    is fitted the same way to the residual left by the previous ones.  For
+    k = 1..K, in float64:
+        S_k   = sign(R_{k-1})  (sign(0) = +1),   R_0 = W
+        sigma, u, v = the top singular triple of |R_{k-1}|
+        s_out = sqrt(sigma) u,  s_in = sqrt(sigma) v, each rounded once to
+                alpha_dtype (nearest-even)
+        R_k   = R_{k-1} - S_k (.) (s_out s_in^T)   (rounded s, one rounding
+                per entry)
+    Returns S int8 [K, m, n], s_out [K, m] and s_in [K, n] (alpha dtype) and
+    R_K float64 [m, n]."""
+    W = np.asarray(W)
+    m, n = W.shape
+    R = W.astype(np.float64)
+    S = np.empty((K, m, n), dtype=np.int8)
+    SO = np.empty((K, m), dtype=_ALPHA_NP[alpha_dtype])
+    SI = np.empty((K, n), dtype=_ALPHA_NP[alpha_dtype])
+    for k in range(K):
+        Sk = np.where(R >= 0.0, 1, -1).astype(np.int8)
+        sigma, u, v = _top_singular(np.abs(R))
+        root = math.sqrt(sigma)
+        SO[k] = round_alpha(root * u, alpha_dtype)
+        SI[k] = round_alpha(root * v, alpha_dtype)
+        outer = SO[k].astype(np.float64)[:, None] * SI[k].astype(np.float64)[None, :]
+        R = R - Sk.astype(np.float64) * outer
+        S[k] = Sk
+    return S, SO, SI, R
+
+
+def svid_dequantize(S: np.ndarray, SO: np.ndarray, SI: np.ndarray) -> np.ndarray:
+    """W_hat = sum_k S_k (.) (s_out^k s_in^k^T) in float64."""
+    K, m, n = S.shape
+    What = np.zeros((m, n), dtype=np.float64)
+    for k in range(K):
+        What += S[k].astype(np.float64) * (SO[k].astype(np.float64)[:, None] *
+                                           SI[k].astype(np.float64)[None, :])
+    return What
+
+
+def svid_product(S, SO, SI, X):
+    """Y = X . W_hat^T for the SVID representation, i.e. y = sum_k s_out^k
+    (.) (S_k (s_in^k (.) x)), in float64; a 1-D x gives a 1-D y."""
+    X = np.asarray(X, dtype=np.float64)
+    one = X.ndim == 1
+    X2 = X[None, :] if one else X
+    Y = X2 @ svid_dequantize(S, SO, SI).T
+    return Y[0] if one else Y
+
+
+def svid_bound(S, SO, SI, X):
+    """E[t, i] = sum_j |W_hat[i, j]| |X[t, j]| for the SVID representation."""
+    X = np.asarray(X, dtype=np.float64)
+    one = X.ndim == 1
+    X2 = X[None, :] if one else X
+    E = np.abs(X2) @ np.abs(svid_dequantize(S, SO, SI)).T
+    return E[0] if one else E
 
 
 def dequantize(S: np.ndarray, A: np.ndarray, group: int = GROUP) -> np.ndarray:

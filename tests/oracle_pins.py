@@ -891,6 +891,80 @@ def pin_transposed_adjoint(o):
     assert np.array_equal(o.bound_transposed(-S, A, -g), o.bound_transposed(S, A, g))
 
 
+# ---------------------------------------------------------------- SVID
+
+def pin_svid_exact_rank1(o):
+    """V1: W = S (.) (a b^T) with positive fp16 vectors a, b of equal norm (b a
+    permutation of a; m = n) is recovered exactly by one SVID kernel: |W| is
+    the rank-1 a b^T, so sqrt(sigma) u = a and sqrt(sigma) v = b.  A zero row
+    and a zero column (a 0 in a and in b) get s = 0 and signs +1."""
+    rng = np.random.default_rng(71)
+    n = 96
+    a = (rng.integers(16, 64, size=n) / 256.0).astype(np.float16)
+    a[5] = 0.0
+    b = a[rng.permutation(n)]
+    S = rng.choice(np.array([-1, 1], dtype=np.int8), size=(n, n))
+    W = (S.astype(np.float64) * (a.astype(np.float64)[:, None] * b.astype(np.float64)[None, :]))
+    W = W.astype(np.float32)
+    zero_col = int(np.flatnonzero(b == 0)[0])
+    Sg, SO, SI, R = o.svid_decompose(W, 1, alpha_dtype="f16")
+    want_S = S.copy()
+    want_S[5, :] = 1
+    want_S[:, zero_col] = 1
+    assert np.array_equal(Sg[0], want_S)
+    assert np.array_equal(SO[0], a) and np.array_equal(SI[0], b)
+    assert np.all(R == 0)
+
+
+def _power_top(M, iters=200):
+    """Top singular value of M by plain power iteration on M^T M."""
+    v = np.ones(M.shape[1]) / np.sqrt(M.shape[1])
+    for _ in range(iters):
+        u = M @ v
+        v = M.T @ u
+        v /= np.linalg.norm(v)
+    return float(np.linalg.norm(M @ v))
+
+
+def pin_svid_eckart_young(o):
+    """V2: the sign-value split makes W - S (.) (s_out s_in^T) = S (.) (|W| -
+    s_out s_in^T), so with the rank-1 SVD of |W| the residual energy is
+    |W|_F^2 - sigma_1^2 (Eckart-Young), sigma_1 found here by a plain power
+    iteration; the scale vectors are nonnegative (Perron); later kernels
+    lower the residual further."""
+    rng = np.random.default_rng(72)
+    W = rng.normal(0, 0.02, size=(40, 256)).astype(np.float32)
+    S, SO, SI, R = o.svid_decompose(W, 3, alpha_dtype="f32")
+    W64 = W.astype(np.float64)
+    sigma = _power_top(np.abs(W64))
+    S1, SO1, SI1, R1 = o.svid_decompose(W, 1, alpha_dtype="f32")
+    e1 = float(np.sum(R1 ** 2))
+    assert abs(e1 - (np.sum(W64 ** 2) - sigma ** 2)) <= 1e-5 * np.sum(W64 ** 2), e1
+    assert np.all(SO >= 0) and np.all(SI >= 0)
+    # the successive kernels: each fit lowers the residual
+    norms = [np.linalg.norm(W64)]
+    for K in (1, 2, 3):
+        norms.append(np.linalg.norm(o.svid_decompose(W, K, alpha_dtype="f32")[3]))
+    assert norms[0] > norms[1] > norms[2] > norms[3]
+    assert np.array_equal(S[:1], S1) and np.array_equal(SO[:1], SO1)
+
+
+def pin_svid_product_grouped(o):
+    """V3: when every s_in^k is constant on each 128-column group, the SVID
+    product equals the group-scaled product with alpha_k[i, g] = s_out^k[i]
+    * c_g (the pinned product), and the SVID bound matches too."""
+    rng = np.random.default_rng(73)
+    K, m, n = 2, 9, 384
+    S = rng.choice(np.array([-1, 1], dtype=np.int8), size=(K, m, n))
+    SO = (2.0 ** -rng.integers(1, 4, size=(K, m))).astype(np.float32)
+    cg = (2.0 ** -rng.integers(1, 4, size=(K, 3))).astype(np.float32)
+    SI = np.repeat(cg, 128, axis=1)
+    A = (SO[:, :, None].astype(np.float64) * cg[:, None, :]).astype(np.float32)
+    x = rng.integers(-8, 9, size=n).astype(np.float64)
+    assert np.array_equal(o.svid_product(S, SO, SI, x), o.product(S, A, x))
+    assert np.array_equal(o.svid_bound(S, SO, SI, x), o.bound(S, A, x))
+
+
 ALL_PINS = [
     pin_round_alpha_rne, pin_hand_worked, pin_sign_step, pin_scale_is_least_squares,
     pin_residual_chain, pin_levels, pin_single_kernel_textbook, pin_constructed_walsh,
@@ -904,4 +978,5 @@ ALL_PINS = [
     pin_allocation_hand_worked, pin_allocation_knapsack, pin_allocation_greedy_convex,
     pin_allocation_monotone,
     pin_transposed_integer, pin_transposed_adjoint,
+    pin_svid_exact_rank1, pin_svid_eckart_young, pin_svid_product_grouped,
 ]

@@ -111,6 +111,21 @@ MUTATIONS = [
      "D = G2 @ dequantize(S, A, group)", "D = (dequantize(S, A, group) @ G2.T).T"),
     ("transposed_bound_without_abs_g", "bound_transposed",
      "E = np.abs(G2) @", "E = G2 @"),
+    ("svid_sign_tie_to_minus_one", "svid_decompose",
+     "np.where(R >= 0.0, 1, -1)", "np.where(R > 0.0, 1, -1)"),
+    ("svid_of_signed_residual", "svid_decompose",
+     "_top_singular(np.abs(R))", "_top_singular(R)"),
+    ("svid_sigma_not_split", "svid_decompose",
+     "root = math.sqrt(sigma)", "root = sigma"),
+    ("svid_in_vector_misordered", "svid_decompose",
+     "SI[k] = round_alpha(root * v, alpha_dtype)", "SI[k] = round_alpha(root * v[::-1], alpha_dtype)"),
+    ("svid_vectors_swapped", "svid_decompose",
+     "SO[k] = round_alpha(root * u, alpha_dtype)\n        SI[k] = round_alpha(root * v, alpha_dtype)",
+     "SO[k] = round_alpha(root * v, alpha_dtype)\n        SI[k] = round_alpha(root * u, alpha_dtype)"),
+    ("svid_residual_not_updated", "svid_decompose",
+     "R = R - Sk.astype(np.float64) * outer", "R = R"),
+    ("svid_product_transposed_scales", "svid_dequantize",
+     "SO[k].astype(np.float64)[:, None] *", "SO[k].astype(np.float64)[::-1, None] *"),
 ]
 
 
