@@ -21,6 +21,8 @@ __all__ = [
     "mbok_refit", "MBOK_MAX_REFIT_ROUNDS", "mbok_residual_energy", "mbok_allocate_kernels",
     "mbok_pack", "mbok_gemv", "mbok_gemv_workspace_bytes", "mbok_gemm", "mbok_status_str",
     "mbok_gemvt", "mbok_gemvt_workspace_bytes",
+    "mbok_svid_workspace_bytes", "mbok_svid_decompose", "mbok_svid_pack",
+    "mbok_svid_gemv_workspace_bytes", "mbok_svid_gemv", "MBOK_MAX_SVID_ITERS",
     "mbok_version", "workspace_for",
     "alpha_torch_dtype", "quantize_and_pack", "allocate_for_budget",
 ]
@@ -32,6 +34,7 @@ MBOK_MAX_K = 4
 MBOK_MAX_T = 65536
 MBOK_LAYOUT_L64 = 1
 MBOK_MAX_REFIT_ROUNDS = 64
+MBOK_MAX_SVID_ITERS = 1000
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -83,6 +86,11 @@ def load_library() -> ctypes.CDLL:
         "mbok_gemm": (ctypes.c_int, [D, P, P, I32, I64, I64, P, I64, P]),
         "mbok_gemvt_workspace_bytes": (SZ, [D]),
         "mbok_gemvt": (ctypes.c_int, [D, P, P, I32, P, P, P]),
+        "mbok_svid_workspace_bytes": (SZ, [D]),
+        "mbok_svid_decompose": (ctypes.c_int, [D, P, I64, P, P, P, I32, P, P]),
+        "mbok_svid_pack": (ctypes.c_int, [D, P, P, P, P]),
+        "mbok_svid_gemv_workspace_bytes": (SZ, [D]),
+        "mbok_svid_gemv": (ctypes.c_int, [D, P, P, P, I32, P, P, P]),
         "mbok_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "mbok_version": (ctypes.c_char_p, []),
     }
@@ -342,6 +350,93 @@ def mbok_gemvt(d: mbok_desc, packed: torch.Tensor, g: torch.Tensor, dx: torch.Te
         wptr = workspace.data_ptr()
     _check(load_library().mbok_gemvt(ctypes.byref(d), packed.data_ptr(), g.data_ptr(), gd,
                                      dx.data_ptr(), wptr, _stream(stream)), "mbok_gemvt")
+
+
+def mbok_svid_workspace_bytes(d: mbok_desc) -> int:
+    return int(load_library().mbok_svid_workspace_bytes(ctypes.byref(d)))
+
+
+def mbok_svid_gemv_workspace_bytes(d: mbok_desc) -> int:
+    return int(load_library().mbok_svid_gemv_workspace_bytes(ctypes.byref(d)))
+
+
+def mbok_svid_decompose(d: mbok_desc, W: torch.Tensor, signs: torch.Tensor, s_out: torch.Tensor,
+                        s_in: torch.Tensor, iters: int = 32, workspace: torch.Tensor | None = None,
+                        stream=None) -> None:
+    """Successive SVID of W fp32 [m, ldw] into signs int8 [K, m, n], s_out
+    [K, m] and s_in [K, n] (scale dtype).  A workspace is allocated when none
+    is given."""
+    _dev(W, "W"), _dev(signs, "signs"), _dev(s_out, "s_out"), _dev(s_in, "s_in")
+    if W.dtype != torch.float32 or W.dim() != 2 or W.shape[0] != d.m or W.shape[1] < d.n:
+        raise ValueError("W must be float32 [m, >= n]")
+    if W.stride(1) != 1:
+        raise ValueError("W rows must be contiguous")
+    ldw = W.stride(0)
+    if _nbytes_from(W) < ((d.m - 1) * ldw + d.n) * 4:
+        raise ValueError("W buffer too small")
+    at = alpha_torch_dtype(d.alpha_dtype)
+    if signs.dtype != torch.int8 or not signs.is_contiguous() or signs.numel() < d.K * d.m * d.n:
+        raise ValueError("signs must be contiguous int8 with K*m*n elements")
+    for t, cnt, nm in ((s_out, d.K * d.m, "s_out"), (s_in, d.K * d.n, "s_in")):
+        if t.dtype != at or not t.is_contiguous() or t.numel() < cnt:
+            raise ValueError(f"{nm} must be contiguous {at} with {cnt} elements")
+    need = mbok_svid_workspace_bytes(d)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=W.device)
+    _dev(workspace, "workspace")
+    if _nbytes_from(workspace) < need:
+        raise ValueError("workspace too small")
+    _check(load_library().mbok_svid_decompose(
+        ctypes.byref(d), W.data_ptr(), ldw, signs.data_ptr(), s_out.data_ptr(), s_in.data_ptr(),
+        int(iters), workspace.data_ptr(), _stream(stream)), "mbok_svid_decompose")
+
+
+def mbok_svid_pack(d: mbok_desc, signs: torch.Tensor, s_out: torch.Tensor, packed: torch.Tensor,
+                   stream=None) -> None:
+    """signs int8 [K, m, n] + s_out [K, m] -> packed uint8 [mbok_packed_bytes]."""
+    _dev(signs, "signs"), _dev(s_out, "s_out"), _dev(packed, "packed")
+    if signs.dtype != torch.int8 or not signs.is_contiguous() or signs.numel() < d.K * d.m * d.n:
+        raise ValueError("signs must be contiguous int8 with K*m*n elements")
+    if s_out.dtype != alpha_torch_dtype(d.alpha_dtype) or not s_out.is_contiguous() or \
+            s_out.numel() < d.K * d.m:
+        raise ValueError("s_out has the wrong dtype or size")
+    if _nbytes_from(packed) < mbok_packed_bytes(d):
+        raise ValueError("packed buffer too small")
+    _check(load_library().mbok_svid_pack(ctypes.byref(d), signs.data_ptr(), s_out.data_ptr(),
+                                         packed.data_ptr(), _stream(stream)), "mbok_svid_pack")
+
+
+_SVID_WS: dict = {}
+
+
+def mbok_svid_gemv(d: mbok_desc, packed: torch.Tensor, s_in: torch.Tensor, x: torch.Tensor,
+                   y: torch.Tensor, workspace: torch.Tensor | None = None, stream=None) -> None:
+    """y[m] (fp32, overwritten) = sum_k s_out^k (.) (B_k (s_in^k (.) x)) for x bf16 / fp32 [n].
+    Without a workspace one is kept per (device, stream)."""
+    _dev(packed, "packed"), _dev(s_in, "s_in"), _dev(x, "x"), _dev(y, "y")
+    if _nbytes_from(packed) < mbok_packed_bytes(d):
+        raise ValueError("packed buffer too small")
+    if s_in.dtype != alpha_torch_dtype(d.alpha_dtype) or not s_in.is_contiguous() or \
+            s_in.numel() < d.K * d.n:
+        raise ValueError("s_in has the wrong dtype or size")
+    xd = _x_dtype(x)
+    if x.numel() < d.n or not x.is_contiguous():
+        raise ValueError("x must be contiguous with n elements")
+    if y.dtype != torch.float32 or y.numel() < d.m or not y.is_contiguous():
+        raise ValueError("y must be contiguous float32 with m elements")
+    need = mbok_svid_gemv_workspace_bytes(d)
+    if workspace is None:
+        key = (y.device.index, _stream(stream))
+        workspace = _SVID_WS.get(key)
+        if workspace is None or workspace.numel() < need:
+            workspace = torch.empty(max(need, 1 << 20), dtype=torch.uint8, device=y.device)
+            _SVID_WS[key] = workspace
+    _dev(workspace, "workspace")
+    if _nbytes_from(workspace) < need:
+        raise ValueError("workspace too small")
+    _check(load_library().mbok_svid_gemv(ctypes.byref(d), packed.data_ptr(), s_in.data_ptr(),
+                                         x.data_ptr(), xd, y.data_ptr(), workspace.data_ptr(),
+                                         _stream(stream)), "mbok_svid_gemv")
 
 
 def mbok_gemm(d: mbok_desc, packed: torch.Tensor, X: torch.Tensor, Y: torch.Tensor,

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmbok.so")
 
-SOURCES = ["mbok_api.cpp", "allocate.cpp", "quantize.hip", "refit.hip", "pack.hip", "gemv.hip", "gemvt.hip", "gemm.hip", "skinny.hip"]
+SOURCES = ["mbok_api.cpp", "allocate.cpp", "quantize.hip", "refit.hip", "svid.hip", "pack.hip", "gemv.hip", "gemvt.hip", "gemm.hip", "skinny.hip"]
 ARCH = "gfx950"
 
 COMMON = [

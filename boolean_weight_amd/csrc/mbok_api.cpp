@@ -96,6 +96,54 @@ int mbok_allocate_kernels(int32_t L, const int64_t* sizes, const double* errors,
   return mbok::allocate_kernels(L, sizes, errors, kmax, budget, K_out);
 }
 
+size_t mbok_svid_workspace_bytes(const mbok_desc* d) {
+  if (check_desc(d) != MBOK_OK) return 0;
+  return mbok::svid_workspace_bytes(d);
+}
+
+int mbok_svid_decompose(const mbok_desc* d, const float* W, int64_t ldw, int8_t* signs,
+                        void* s_out, void* s_in, int32_t iters, void* workspace, void* stream) {
+  int st = check_desc(d);
+  if (st != MBOK_OK) return st;
+  if (!W || !signs || !s_out || !s_in || !workspace) return MBOK_ERR_INVALID_ARG;
+  if (ldw < d->n || iters < 1 || iters > MBOK_MAX_SVID_ITERS) return MBOK_ERR_INVALID_ARG;
+  if (!aligned(W, 16) || (ldw % 4) != 0 || !aligned(signs, 16) || !aligned(s_out, 4) ||
+      !aligned(s_in, 4) || !aligned(workspace, 256))
+    return MBOK_ERR_ALIGN;
+  return mbok::launch_svid_decompose(d, W, ldw, signs, s_out, s_in, iters, workspace,
+                                     (hipStream_t)stream);
+}
+
+int mbok_svid_pack(const mbok_desc* d, const int8_t* signs, const void* s_out, void* packed,
+                   void* stream) {
+  int st = check_desc(d);
+  if (st != MBOK_OK) return st;
+  if (!signs || !s_out || !packed) return MBOK_ERR_INVALID_ARG;
+  if (!aligned(signs, 16) || !aligned(s_out, 4) || !aligned(packed, 16)) return MBOK_ERR_ALIGN;
+  return mbok::launch_svid_pack(d, signs, s_out, packed, (hipStream_t)stream);
+}
+
+size_t mbok_svid_gemv_workspace_bytes(const mbok_desc* d) {
+  if (check_desc(d) != MBOK_OK) return 0;
+  return mbok::svid_gemv_workspace_bytes(d);
+}
+
+int mbok_svid_gemv(const mbok_desc* d, const void* packed, const void* s_in, const void* x,
+                   int32_t x_dtype, float* y, void* workspace, void* stream) {
+  int st = check_desc(d);
+  if (st != MBOK_OK) return st;
+  if (!packed || !s_in || !x || !y || !workspace) return MBOK_ERR_INVALID_ARG;
+  if (x_dtype != MBOK_BF16 && x_dtype != MBOK_F32) return MBOK_ERR_DTYPE;
+  if (!aligned(packed, 16) || !aligned(s_in, 4) || !aligned(x, 4) || !aligned(y, 4) ||
+      !aligned(workspace, 256))
+    return MBOK_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  uint16_t* xs = reinterpret_cast<uint16_t*>(workspace);
+  st = mbok::launch_svid_prep(d, x, x_dtype, s_in, xs, s);
+  if (st != MBOK_OK) return st;
+  return mbok::launch_svid_skinny(d, packed, xs, y, s);
+}
+
 int mbok_refit(const mbok_desc* d, const float* W, int64_t ldw, int8_t* signs, void* alpha,
                int32_t rounds, void* stream) {
   int st = check_desc(d);

@@ -189,6 +189,12 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
   return __uint_as_float(b << 16);
 }
 
+// float32 -> bf16 bits, one rounding to nearest-even (the compiler's
+// conversion, as the prefill unpack uses)
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
+  return __builtin_bit_cast(uint16_t, (__bf16)v);
+}
+
 __device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
   return (float)__builtin_bit_cast(_Float16, h);
 }

@@ -13,7 +13,8 @@ namespace {
 template <typename AT>
 __global__ void __launch_bounds__(256) pack_kernel(const int8_t* __restrict__ signs,
                                                    const AT* __restrict__ alpha, int m, int n,
-                                                   int K, int RB, uint4* __restrict__ bits,
+                                                   int K, int RB, int row_stride, int group_stride,
+                                                   uint4* __restrict__ bits,
                                                    AT* __restrict__ scales) {
   const int G = n / kGroup;
   const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -46,16 +47,17 @@ __global__ void __launch_bounds__(256) pack_kernel(const int8_t* __restrict__ si
         }
       }
     }
-    a = alpha[((int64_t)k * m + i) * G + g];
+    a = alpha[((int64_t)k * m + i) * row_stride + (int64_t)g * group_stride];
   }
   bits[c] = make_uint4(w[0], w[1], w[2], w[3]);
   scales[c] = a;
 }
 
-}  // namespace
-
-int launch_pack(const mbok_desc* d, const int8_t* signs, const void* alpha, void* packed,
-                hipStream_t stream) {
+// alpha[(k m + i) * row_stride + g * group_stride] is the scale of chunk
+// (row i, group g, kernel k): (G, 1) for per-group scales, (1, 0) for one
+// scale per row (the SVID s_out).
+int pack_strided(const mbok_desc* d, const int8_t* signs, const void* alpha, void* packed,
+                 int row_stride, int group_stride, hipStream_t stream) {
   const Geom geo = make_geom(d);
   const int64_t total = (int64_t)geo.RB * geo.G * geo.K * kRowBlock;
   const int block = 256;
@@ -66,12 +68,25 @@ int launch_pack(const mbok_desc* d, const int8_t* signs, const void* alpha, void
   if (d->alpha_dtype == MBOK_F16)
     hipLaunchKernelGGL(pack_kernel<uint16_t>, dim3((unsigned)blocks), dim3(block), 0, stream,
                        signs, reinterpret_cast<const uint16_t*>(alpha), geo.m, geo.n, geo.K,
-                       geo.RB, bits, reinterpret_cast<uint16_t*>(scales));
+                       geo.RB, row_stride, group_stride, bits,
+                       reinterpret_cast<uint16_t*>(scales));
   else
     hipLaunchKernelGGL(pack_kernel<float>, dim3((unsigned)blocks), dim3(block), 0, stream,
                        signs, reinterpret_cast<const float*>(alpha), geo.m, geo.n, geo.K,
-                       geo.RB, bits, reinterpret_cast<float*>(scales));
+                       geo.RB, row_stride, group_stride, bits, reinterpret_cast<float*>(scales));
   return hipGetLastError() == hipSuccess ? MBOK_OK : MBOK_ERR_HIP;
+}
+
+}  // namespace
+
+int launch_pack(const mbok_desc* d, const int8_t* signs, const void* alpha, void* packed,
+                hipStream_t stream) {
+  return pack_strided(d, signs, alpha, packed, d->n / kGroup, 1, stream);
+}
+
+int launch_svid_pack(const mbok_desc* d, const int8_t* signs, const void* s_out, void* packed,
+                     hipStream_t stream) {
+  return pack_strided(d, signs, s_out, packed, 1, 0, stream);
 }
 
 }  // namespace mbok

@@ -207,7 +207,11 @@ struct SkinnyLoads {
   AT a[K];
 };
 
-template <typename AT, int K, int JMAX>
+// SV: the SVID product.  Token rows 2k and 2k+1 of X hold the hi and lo bf16
+// parts of s_in^k (.) x, the scale slots hold s_out^k of the row (the same in
+// every group), so kernel k is applied to its two token rows only and the
+// output is the sum of all token rows: y = sum_k s_out^k (.) (B_k (s_in^k (.) x)).
+template <typename AT, int K, int JMAX, bool SV>
 __global__ void __launch_bounds__(512) gemm_skinny_stream_kernel(
     const u32x4* __restrict__ bits, const AT* __restrict__ scales,
     const uint16_t* __restrict__ X, int64_t ldx, float* __restrict__ Y, int64_t ldy, int T,
@@ -276,8 +280,17 @@ __global__ void __launch_bounds__(512) gemm_skinny_stream_kernel(
                                                         0);
           }
           const float sc = scale_value<AT>(a[j]);
+          if constexpr (SV) {
+            // token 4q + r belongs to kernel (4q + r) / 2
+            const float sc0 = (2 * q == k) ? sc : 0.f, sc1 = (2 * q + 1 == k) ? sc : 0.f;
+            acc[0] = __builtin_fmaf(-sc0, S[0], acc[0]);
+            acc[1] = __builtin_fmaf(-sc0, S[1], acc[1]);
+            acc[2] = __builtin_fmaf(-sc1, S[2], acc[2]);
+            acc[3] = __builtin_fmaf(-sc1, S[3], acc[3]);
+          } else {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(-sc, S[r], acc[r]);
+            for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(-sc, S[r], acc[r]);
+          }
         }
       }
       return acc;
@@ -302,14 +315,30 @@ __global__ void __launch_bounds__(512) gemm_skinny_stream_kernel(
     for (int r = 0; r < 4; ++r) red[(((t * NW) + wave) * 4 + r) * 64 + lane] = yacc[t][r];
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < ntl * 256; idx += blockDim.x) {
-    const int t = idx >> 8, e = idx & 255;
-    float sum = 0.f;
-    for (int w = 0; w < NW; ++w) sum += red[(t * NW + w) * 256 + e];
-    const int l = e & 63, r = e >> 6;
-    const int tok = 4 * (l >> 4) + r;
-    const int row = tile16_of(blockIdx.x + t * gridDim.x, tiles) * 16 + (l & 15);
-    if (tok < T && row < m) Y[(int64_t)tok * ldy + row] = sum;
+  if constexpr (SV) {
+    // one output per row: the token rows in order, each summed over wavefronts
+    for (int idx = threadIdx.x; idx < ntl * 16; idx += blockDim.x) {
+      const int t = idx >> 4, ri = idx & 15;
+      float sum = 0.f;
+      for (int tok = 0; tok < T; ++tok) {
+        const int e = (tok & 3) * 64 + (tok >> 2) * 16 + ri;
+        float part = 0.f;
+        for (int w = 0; w < NW; ++w) part += red[(t * NW + w) * 256 + e];
+        sum += part;
+      }
+      const int row = tile16_of(blockIdx.x + t * gridDim.x, tiles) * 16 + ri;
+      if (row < m) Y[row] = sum;
+    }
+  } else {
+    for (int idx = threadIdx.x; idx < ntl * 256; idx += blockDim.x) {
+      const int t = idx >> 8, e = idx & 255;
+      float sum = 0.f;
+      for (int w = 0; w < NW; ++w) sum += red[(t * NW + w) * 256 + e];
+      const int l = e & 63, r = e >> 6;
+      const int tok = 4 * (l >> 4) + r;
+      const int row = tile16_of(blockIdx.x + t * gridDim.x, tiles) * 16 + (l & 15);
+      if (tok < T && row < m) Y[(int64_t)tok * ldy + row] = sum;
+    }
   }
 }
 
@@ -328,7 +357,7 @@ void launch_k(const Geom& geo, const u32x4* bits, const AT* scales, const uint16
 
 constexpr int kSkinnyJ = 8;  // tiles per persistent workgroup (registers)
 
-template <typename AT, int K>
+template <typename AT, int K, bool SV = false>
 void launch_stream_k(const Geom& geo, const u32x4* bits, const AT* scales, const uint16_t* X,
                      int64_t ldx, float* Y, int64_t ldy, int T, hipStream_t stream) {
   // slabs of at most 32 groups: one wavefront per block of 4 groups, at most 8
@@ -339,7 +368,7 @@ void launch_stream_k(const Geom& geo, const u32x4* bits, const AT* scales, const
   int grid = tiles < 256 ? tiles : 256;
   if (grid * kSkinnyJ < tiles) grid = (tiles + kSkinnyJ - 1) / kSkinnyJ;
   const size_t lds = (size_t)kSkinnyJ * NW * 256 * sizeof(float);
-  hipLaunchKernelGGL((gemm_skinny_stream_kernel<AT, K, kSkinnyJ>), dim3(grid), dim3(64 * NW), lds,
+  hipLaunchKernelGGL((gemm_skinny_stream_kernel<AT, K, kSkinnyJ, SV>), dim3(grid), dim3(64 * NW), lds,
                      stream, bits, scales, X, ldx, Y, ldy, T, geo.m, geo.G, slab, tiles);
 }
 
@@ -385,6 +414,34 @@ int launch_at(const Geom& geo, const void* packed, const void* X, int64_t ldx, f
 }  // namespace
 
 int skinny_max_tokens() { return kMaxSkinnyTokens; }
+
+// The SVID product on prepared activations (svid_prep_kernel): 2K token rows.
+int launch_svid_skinny(const mbok_desc* d, const void* packed, const uint16_t* xs, float* y,
+                       hipStream_t stream) {
+  const Geom geo = make_geom(d);
+  const u32x4* bits = reinterpret_cast<const u32x4*>(packed);
+  const int T = 2 * geo.K;
+  if (d->alpha_dtype == MBOK_F16) {
+    const uint16_t* sc = reinterpret_cast<const uint16_t*>(
+        reinterpret_cast<const char*>(packed) + geo.bits_bytes);
+    switch (geo.K) {
+      case 1: launch_stream_k<uint16_t, 1, true>(geo, bits, sc, xs, geo.n, y, geo.m, T, stream); break;
+      case 2: launch_stream_k<uint16_t, 2, true>(geo, bits, sc, xs, geo.n, y, geo.m, T, stream); break;
+      case 3: launch_stream_k<uint16_t, 3, true>(geo, bits, sc, xs, geo.n, y, geo.m, T, stream); break;
+      default: launch_stream_k<uint16_t, 4, true>(geo, bits, sc, xs, geo.n, y, geo.m, T, stream); break;
+    }
+  } else {
+    const float* sc =
+        reinterpret_cast<const float*>(reinterpret_cast<const char*>(packed) + geo.bits_bytes);
+    switch (geo.K) {
+      case 1: launch_stream_k<float, 1, true>(geo, bits, sc, xs, geo.n, y, geo.m, T, stream); break;
+      case 2: launch_stream_k<float, 2, true>(geo, bits, sc, xs, geo.n, y, geo.m, T, stream); break;
+      case 3: launch_stream_k<float, 3, true>(geo, bits, sc, xs, geo.n, y, geo.m, T, stream); break;
+      default: launch_stream_k<float, 4, true>(geo, bits, sc, xs, geo.n, y, geo.m, T, stream); break;
+    }
+  }
+  return hipGetLastError() == hipSuccess ? MBOK_OK : MBOK_ERR_HIP;
+}
 
 int launch_skinny(const mbok_desc* d, const void* packed, const void* X, int64_t T, int64_t ldx,
                   float* Y, int64_t ldy, hipStream_t stream) {

@@ -243,6 +243,83 @@ int mbok_residual_energy(const mbok_desc* d, const float* W, int64_t ldw,
 int mbok_allocate_kernels(int32_t L, const int64_t* sizes, const double* errors,
                           int32_t kmax, int64_t budget, int32_t* K_out);
 
+/* Largest number of power-iteration rounds accepted by mbok_svid_decompose. */
+#define MBOK_MAX_SVID_ITERS 1000
+
+/* Bytes of the workspace mbok_svid_decompose needs (float64 iterates and
+ * partial sums).  Host only; 0 for a NULL or invalid descriptor. */
+size_t mbok_svid_workspace_bytes(const mbok_desc* d);
+
+/*
+ * Successive sign-value-independent decomposition (SVID), the scale variant
+ * of the [GS] summaries ("Riformulazione Booleana e SVID", "Successive
+ * SVID", "Descomposición SVID"): W ~ sum_k B_k (.) (s_out^k s_in^k^T), where
+ * for k = 1..K, with R_0 = W:
+ *     B_k          = sign(R_{k-1})            (0 and -0.0 give +1)
+ *     sigma, u, v  = the top singular triple of |R_{k-1}|, by `iters` rounds
+ *                    of float64 power iteration from v = 1/sqrt(n)
+ *     s_out^k      = sqrt(sigma) u, s_in^k = sqrt(sigma) v, each rounded once
+ *                    to nearest-even in d->alpha_dtype
+ *     R_k          = R_{k-1} - B_k (.) (s_out^k s_in^k^T)  (float64, with the
+ *                    rounded vectors)
+ * The residual is recomputed from W on every pass (never stored).  Power
+ * iteration reaches the SVD's vectors when the ratio of the two largest
+ * singular values of |R| is well below 1 (about 0.03 for trained-like
+ * weights, so 16-32 rounds give float64 accuracy).  Sums run in a fixed
+ * order: results are bit-reproducible.
+ *  W          device, fp32, row-major [m, ldw], ldw >= n; read only.
+ *  signs      device, int8 [K][m][n]; written with +1 / -1.
+ *  s_out      device, [K][m] of d->alpha_dtype; written.
+ *  s_in       device, [K][n] of d->alpha_dtype; written.
+ *  iters      1 .. MBOK_MAX_SVID_ITERS.
+ *  workspace  device, mbok_svid_workspace_bytes(d) bytes, 256-byte aligned;
+ *             needs no initialisation; calls that may overlap need distinct
+ *             workspaces.
+ * Errors: INVALID_ARG (NULL, ldw < n, iters), SHAPE/DTYPE/UNSUPPORTED from
+ * d, ALIGN (W and signs 16 bytes, ldw % 4, vectors 4 bytes, workspace 256
+ * bytes), HIP.
+ */
+int mbok_svid_decompose(const mbok_desc* d, const float* W, int64_t ldw,
+                        int8_t* signs, void* s_out, void* s_in, int32_t iters,
+                        void* workspace, void* stream);
+
+/*
+ * Packs SVID kernels into MBOK_LAYOUT_L64: the sign bits as mbok_pack writes
+ * them, and s_out^k[i] in the scale slot of every group of row i, kernel k.
+ * (s_in is passed to mbok_svid_gemv separately.)
+ *  signs   device int8 [K][m][n];  s_out  device [K][m] of d->alpha_dtype;
+ *  packed  device, mbok_packed_bytes(d) bytes, fully overwritten.
+ * Errors: INVALID_ARG, SHAPE/DTYPE/UNSUPPORTED, ALIGN (signs and packed 16
+ * bytes, s_out 4 bytes), HIP.
+ */
+int mbok_svid_pack(const mbok_desc* d, const int8_t* signs, const void* s_out,
+                   void* packed, void* stream);
+
+/* Bytes of the workspace mbok_svid_gemv needs: 2 K n bf16 activation rows.
+ * Host only; 0 for a NULL or invalid descriptor. */
+size_t mbok_svid_gemv_workspace_bytes(const mbok_desc* d);
+
+/*
+ * Decode product of the SVID representation ([GS] summaries: the product is
+ * the Boolean one with x scaled per kernel and the output scaled per row):
+ *     y[i] = sum_k s_out^k[i] * sum_j b_k[i, j] * s_in^k[j] * x[j]
+ * s_in^k (.) x is formed in fp32 (exact for fp16 scales and bf16 x) and
+ * split into bf16 hi + lo parts, so the matrix cores see it to about 2^-17
+ * relative; the +-1 contractions accumulate in fp32 and s_out applies in
+ * fp32.
+ *  packed     device, the buffer of mbok_svid_pack.
+ *  s_in       device [K][n] of d->alpha_dtype.
+ *  x          device, n values of x_dtype (MBOK_BF16 or MBOK_F32).
+ *  y          device fp32 [m]; overwritten.
+ *  workspace  device, mbok_svid_gemv_workspace_bytes(d) bytes, 256-byte
+ *             aligned; overwritten (the prepared activations).
+ * Errors: INVALID_ARG (NULL), SHAPE/UNSUPPORTED from d, DTYPE (x_dtype),
+ * ALIGN (packed 16 bytes, s_in, x, y 4 bytes, workspace 256 bytes), HIP.
+ */
+int mbok_svid_gemv(const mbok_desc* d, const void* packed, const void* s_in,
+                   const void* x, int32_t x_dtype, float* y, void* workspace,
+                   void* stream);
+
 /*
  * Packs Boolean kernels and their scales into MBOK_LAYOUT_L64 (see the top
  * of this header).  Any +-1 signs are accepted, e.g. those of a finetuned
