@@ -55,6 +55,10 @@ def parse():
                     help="time the setup kernels instead (greedy quantizer, refit, pack) on "
                          "every linear of the workload; prints one JSON line of its own")
     ap.add_argument("--refit-rounds", type=int, default=2)
+    ap.add_argument("--svid", action="store_true",
+                    help="one token: the SVID scale variant (successive SVID decomposition, "
+                         "then y = sum_k s_out^k (.) (B_k (s_in^k (.) x)))")
+    ap.add_argument("--svid-iters", type=int, default=32)
     ap.add_argument("--transposed", action="store_true",
                     help="one token: time the transposed product dx = W_hat^T g instead")
     ap.add_argument("--avg-k", type=float, default=None,
@@ -246,6 +250,9 @@ def main():
                    ("gate_up_proj", 2 * 13824, 5120), ("down_proj", 5120, 13824)]
     if args.config == 3:
         linears = linears[:1] if T == 1 else linears
+    if args.svid and (T != 1 or args.transposed or args.avg_k is not None):
+        print("--svid runs one token on its own", file=sys.stderr)
+        sys.exit(2)
     if args.transposed and T != 1:
         print("--transposed runs one gradient vector (T = 1)", file=sys.stderr)
         sys.exit(2)
@@ -280,6 +287,7 @@ def main():
 
     # ---- setup: quantize + pack on the device, build the rotating pool
     layers = []
+    svid_in = []  # s_in of each layer (SVID)
     per_step_wbytes = 0.0
     per_step_bytes = 0.0
     per_step_flops = 0.0
@@ -288,8 +296,21 @@ def main():
             _, m, n = linears[li]
             Wl = torch.from_numpy(syn.weight(m, n, syn.weight_seed(args.config, li))).to(dev)
         m, n = Wl.shape
-        d, packed, signs, alpha = bw.quantize_and_pack(Wl, Kl, adt)
-        del Wl, signs, alpha
+        if args.svid:
+            d = bw.mbok_desc_init(m, n, Kl, adt)
+            at = bw.alpha_torch_dtype(adt)
+            signs = torch.empty((Kl, m, n), dtype=torch.int8, device=dev)
+            s_out = torch.empty((Kl, m), dtype=at, device=dev)
+            s_in = torch.empty((Kl, n), dtype=at, device=dev)
+            bw.mbok_svid_decompose(d, Wl, signs, s_out, s_in, args.svid_iters)
+            packed = torch.empty(bw.mbok_packed_bytes(d), dtype=torch.uint8, device=dev)
+            bw.mbok_svid_pack(d, signs, s_out, packed)
+            svid_in.append(s_in)
+            del signs, s_out
+        else:
+            d, packed, signs, alpha = bw.quantize_and_pack(Wl, Kl, adt)
+            del signs, alpha
+        del Wl
         layers.append((name, d, packed))
         wb = weight_bytes(m, n, Kl, abytes)
         per_step_wbytes += wb
@@ -317,7 +338,9 @@ def main():
 
     def call(li, c):
         d = layers[li][1]
-        if args.transposed:
+        if args.svid:
+            bw.mbok_svid_gemv(d, pools[li][c], svid_in[li], xs[li], ys[li])
+        elif args.transposed:
             bw.mbok_gemvt(d, pools[li][c], xs[li], ys[li])
         elif T == 1:
             bw.mbok_gemv(d, pools[li][c], xs[li], ys[li])
@@ -428,7 +451,10 @@ def main():
         torch.cuda.synchronize()
         del a, b
     m, n = d.m, d.n
-    if args.transposed:  # g in, dx out
+    if args.svid:  # packed layer, s_in, x in; y out
+        alg_bytes = (weight_bytes(m, n, d.K, abytes) + d.K * n * abytes
+                     + n * (2 if xdt == torch.bfloat16 else 4) + m * 4)
+    elif args.transposed:  # g in, dx out
         alg_bytes = weight_bytes(m, n, d.K, abytes) + m * (2 if xdt == torch.bfloat16 else 4) + n * 4
     else:
         alg_bytes = weight_bytes(m, n, d.K, abytes) + T * n * (2 if xdt == torch.bfloat16 else 4) + T * m * 4
@@ -440,12 +466,15 @@ def main():
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = (stored_traffic(args.config, K, T)
-                       if allocation is None and not args.transposed else None)
+                       if allocation is None and not args.transposed and not args.svid else None)
     roof["kernel"] = name
     roof["launch_us"] = launch_us
     roof["alg_bytes_per_launch"] = alg_bytes
 
-    if args.transposed:
+    if args.svid:
+        metric, unit = "svid weight GB/s", "GB/s"
+        value = per_step_wbytes / (ms_per_step * 1e-3) / 1e9
+    elif args.transposed:
         metric, unit = "transposed weight GB/s", "GB/s"
         value = per_step_wbytes / (ms_per_step * 1e-3) / 1e9
     elif T > 16:
@@ -471,6 +500,9 @@ def main():
     }
     if args.transposed:
         line["config"]["product"] = "dx = W_hat^T g"
+    if args.svid:
+        line["config"]["product"] = "y = sum_k s_out^k (.) (B_k (s_in^k (.) x)) (successive SVID)"
+        line["config"]["svid_iters"] = args.svid_iters
     if not args.no_cpu_baseline:
         dname, dd = layers[dom][0], layers[dom][1]
         line["cpu_baseline"] = cpu_baseline(args, cfg, (dname, dd.m, dd.n), dd.K, T, unit)
@@ -529,13 +561,22 @@ def quantizer_bench(args, cfg, linears, K, adt, abytes):
 
         us_refit = timed(refit_once) - timed(copies_only)
         us_pack = timed(lambda: bw.mbok_pack(d, signs, alpha, packed))
+        at = bw.alpha_torch_dtype(adt)
+        so = torch.empty((K, m), dtype=at, device=dev)
+        si = torch.empty((K, n), dtype=at, device=dev)
+        svws = torch.empty(bw.mbok_svid_workspace_bytes(d), dtype=torch.uint8, device=dev)
+        us_svid = timed(lambda: bw.mbok_svid_decompose(d, W, signs, so, si, args.svid_iters, svws))
         nw = m * n
         na = K * m * (n // 128) * abytes
         b_greedy = 4 * nw + K * nw + na
         b_refit = 4 * nw + 2 * K * nw + 2 * na
         b_pack = K * nw + na + bw.mbok_packed_bytes(d)
+        # SVID: per kernel, per power-iteration round two passes over W and the
+        # earlier kernels' signs, plus the sign pass
+        b_svid = sum((2 * args.svid_iters + 1) * (4 * nw + kk * nw) + nw for kk in range(K))
         for kern, us, b in (("residual_binarize", us_greedy, b_greedy),
-                            ("refit", us_refit, b_refit), ("pack", us_pack, b_pack)):
+                            ("refit", us_refit, b_refit), ("pack", us_pack, b_pack),
+                            ("svid_decompose", us_svid, b_svid)):
             out.append({"linear": name, "m": m, "n": n, "kernel": kern, "us": round(us, 2),
                         "alg_bytes": b, "GB/s": round(b / (us * 1e-6) / 1e9, 1),
                         "frac_hbm": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)})
@@ -565,7 +606,9 @@ def cpu_baseline(args, cfg, lin, K, T, unit):
         t0 = time.perf_counter()
         reps = 0
         while True:
-            if args.transposed:
+            if args.svid:
+                oracle.svid_product(S, A[:, :, 0], np.ones((K, n)), X[0])
+            elif args.transposed:
                 oracle.product_transposed(S, A, Gr)
             else:
                 oracle.product(S, A, X if T > 1 else X[0])

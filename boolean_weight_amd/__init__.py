@@ -406,13 +406,9 @@ def mbok_svid_pack(d: mbok_desc, signs: torch.Tensor, s_out: torch.Tensor, packe
                                          packed.data_ptr(), _stream(stream)), "mbok_svid_pack")
 
 
-_SVID_WS: dict = {}
-
-
 def mbok_svid_gemv(d: mbok_desc, packed: torch.Tensor, s_in: torch.Tensor, x: torch.Tensor,
-                   y: torch.Tensor, workspace: torch.Tensor | None = None, stream=None) -> None:
-    """y[m] (fp32, overwritten) = sum_k s_out^k (.) (B_k (s_in^k (.) x)) for x bf16 / fp32 [n].
-    Without a workspace one is kept per (device, stream)."""
+                   y: torch.Tensor, stream=None) -> None:
+    """y[m] (fp32, overwritten) = sum_k s_out^k (.) (B_k (s_in^k (.) x)) for x bf16 / fp32 [n]."""
     _dev(packed, "packed"), _dev(s_in, "s_in"), _dev(x, "x"), _dev(y, "y")
     if _nbytes_from(packed) < mbok_packed_bytes(d):
         raise ValueError("packed buffer too small")
@@ -424,19 +420,9 @@ def mbok_svid_gemv(d: mbok_desc, packed: torch.Tensor, s_in: torch.Tensor, x: to
         raise ValueError("x must be contiguous with n elements")
     if y.dtype != torch.float32 or y.numel() < d.m or not y.is_contiguous():
         raise ValueError("y must be contiguous float32 with m elements")
-    need = mbok_svid_gemv_workspace_bytes(d)
-    if workspace is None:
-        key = (y.device.index, _stream(stream))
-        workspace = _SVID_WS.get(key)
-        if workspace is None or workspace.numel() < need:
-            workspace = torch.empty(max(need, 1 << 20), dtype=torch.uint8, device=y.device)
-            _SVID_WS[key] = workspace
-    _dev(workspace, "workspace")
-    if _nbytes_from(workspace) < need:
-        raise ValueError("workspace too small")
     _check(load_library().mbok_svid_gemv(ctypes.byref(d), packed.data_ptr(), s_in.data_ptr(),
-                                         x.data_ptr(), xd, y.data_ptr(), workspace.data_ptr(),
-                                         _stream(stream)), "mbok_svid_gemv")
+                                         x.data_ptr(), xd, y.data_ptr(), None, _stream(stream)),
+           "mbok_svid_gemv")
 
 
 def mbok_gemm(d: mbok_desc, packed: torch.Tensor, X: torch.Tensor, Y: torch.Tensor,

@@ -124,24 +124,20 @@ int mbok_svid_pack(const mbok_desc* d, const int8_t* signs, const void* s_out, v
 }
 
 size_t mbok_svid_gemv_workspace_bytes(const mbok_desc* d) {
-  if (check_desc(d) != MBOK_OK) return 0;
-  return mbok::svid_gemv_workspace_bytes(d);
+  (void)d;
+  return 0;
 }
 
 int mbok_svid_gemv(const mbok_desc* d, const void* packed, const void* s_in, const void* x,
                    int32_t x_dtype, float* y, void* workspace, void* stream) {
   int st = check_desc(d);
   if (st != MBOK_OK) return st;
-  if (!packed || !s_in || !x || !y || !workspace) return MBOK_ERR_INVALID_ARG;
+  if (!packed || !s_in || !x || !y) return MBOK_ERR_INVALID_ARG;
   if (x_dtype != MBOK_BF16 && x_dtype != MBOK_F32) return MBOK_ERR_DTYPE;
-  if (!aligned(packed, 16) || !aligned(s_in, 4) || !aligned(x, 4) || !aligned(y, 4) ||
-      !aligned(workspace, 256))
+  if (!aligned(packed, 16) || !aligned(s_in, 16) || !aligned(x, 16) || !aligned(y, 4) ||
+      (workspace && !aligned(workspace, 256)))
     return MBOK_ERR_ALIGN;
-  hipStream_t s = (hipStream_t)stream;
-  uint16_t* xs = reinterpret_cast<uint16_t*>(workspace);
-  st = mbok::launch_svid_prep(d, x, x_dtype, s_in, xs, s);
-  if (st != MBOK_OK) return st;
-  return mbok::launch_svid_skinny(d, packed, xs, y, s);
+  return mbok::launch_svid_skinny(d, packed, x, x_dtype, s_in, y, (hipStream_t)stream);
 }
 
 int mbok_refit(const mbok_desc* d, const float* W, int64_t ldw, int8_t* signs, void* alpha,

@@ -32,11 +32,8 @@ int launch_svid_decompose(const mbok_desc* d, const float* W, int64_t ldw, int8_
                           void* s_out, void* s_in, int iters, void* ws, hipStream_t stream);
 int launch_svid_pack(const mbok_desc* d, const int8_t* signs, const void* s_out, void* packed,
                      hipStream_t stream);
-size_t svid_gemv_workspace_bytes(const mbok_desc* d);
-int launch_svid_prep(const mbok_desc* d, const void* x, int32_t x_dtype, const void* s_in,
-                     uint16_t* xs, hipStream_t stream);
-int launch_svid_skinny(const mbok_desc* d, const void* packed, const uint16_t* xs, float* y,
-                       hipStream_t stream);
+int launch_svid_skinny(const mbok_desc* d, const void* packed, const void* x, int32_t x_dtype,
+                       const void* s_in, float* y, hipStream_t stream);
 int allocate_kernels(int L, const int64_t* sizes, const double* errors, int kmax, int64_t budget,
                      int32_t* K_out);
 int launch_gemm(const mbok_desc* d, const void* packed, const void* X, int64_t T, int64_t ldx,

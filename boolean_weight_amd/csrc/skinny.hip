@@ -207,15 +207,57 @@ struct SkinnyLoads {
   AT a[K];
 };
 
-// SV: the SVID product.  Token rows 2k and 2k+1 of X hold the hi and lo bf16
-// parts of s_in^k (.) x, the scale slots hold s_out^k of the row (the same in
-// every group), so kernel k is applied to its two token rows only and the
-// output is the sum of all token rows: y = sum_k s_out^k (.) (B_k (s_in^k (.) x)).
+// The SVID product's activations for one wavefront's block of 4 groups:
+// frag[((j * K + k) * 2 + part) * 128 + c] (bf16) is the hi (part 0) or lo
+// (part 1) part of v = s_in^k[col] * x[col], col = 128 (gb + j) + c, formed
+// in fp32 (exact for fp16 scales and bf16 x); hi = RNE(v), lo = RNE(v - hi),
+// so hi + lo is v to about 2^-17 relative.  The 64 lanes share the values.
+template <typename AT, int K>
+__device__ __forceinline__ void svid_block_fragments(const void* __restrict__ x, int x_f32,
+                                                     const AT* __restrict__ s_in, int n, int gb,
+                                                     int nj, int lane,
+                                                     uint16_t* __restrict__ frag) {
+  // lane takes columns c = lane and lane + 64 of each group; all loads first
+  float xv[4][2];
+  AT sv[4][K][2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int64_t col = (int64_t)kGroup * (gb + (j < nj ? j : 0)) + lane + 64 * h;
+      xv[j][h] = x_f32 ? reinterpret_cast<const float*>(x)[col]
+                       : bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(x)[col]);
+#pragma unroll
+      for (int k = 0; k < K; ++k) sv[j][k][h] = s_in[(int64_t)k * n + col];
+    }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (j >= nj) break;
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int c = lane + 64 * h;
+        const float v = alpha_to_f32<AT>(sv[j][k][h]) * xv[j][h];
+        const uint16_t hi = f32_to_bf16_rne(v);
+        frag[((j * K + k) * 2) * kGroup + c] = hi;
+        frag[((j * K + k) * 2 + 1) * kGroup + c] = f32_to_bf16_rne(v - bf16_bits_to_f32(hi));
+      }
+  }
+}
+
+// SV: the SVID product.  Token row 2k + part holds the hi / lo bf16 part of
+// s_in^k (.) x (svid_block_fragments, formed by each wavefront for its own
+// groups in a private LDS area after the partial-sum area), the scale slots hold
+// s_out^k of the row (the same in every group), so kernel k is applied to its
+// two token rows only and the output is the sum of all token rows:
+// y = sum_k s_out^k (.) (B_k (s_in^k (.) x)).  X and ldx are unused then.
 template <typename AT, int K, int JMAX, bool SV>
 __global__ void __launch_bounds__(512) gemm_skinny_stream_kernel(
     const u32x4* __restrict__ bits, const AT* __restrict__ scales,
     const uint16_t* __restrict__ X, int64_t ldx, float* __restrict__ Y, int64_t ldy, int T,
-    int m, int G, int slab_groups, int tiles) {
+    int m, int G, int slab_groups, int tiles, const void* __restrict__ sv_x, int sv_xf32,
+    const AT* __restrict__ sv_sin) {
   extern __shared__ float red[];  // [JMAX][NW][4][64] partial sums
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -223,7 +265,10 @@ __global__ void __launch_bounds__(512) gemm_skinny_stream_kernel(
   const int i = lane & 15, q = lane >> 4;
   const int ntl = (tiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;  // <= JMAX
   const bool tok_ok = i < T;
-  const uint16_t* xrow = X + (int64_t)(tok_ok ? i : 0) * ldx + 32 * q;
+  const uint16_t* xrow = SV ? nullptr : X + (int64_t)(tok_ok ? i : 0) * ldx + 32 * q;
+  uint16_t* frag = SV ? reinterpret_cast<uint16_t*>(red + JMAX * NW * 256) +
+                            wave * (4 * K * 2 * kGroup)
+                      : nullptr;
   const uint32_t mask = __builtin_amdgcn_readfirstlane(0x80008000u);
   uint32_t ones;
   asm("v_mov_b32 %0, 0x3f803f80" : "=v"(ones));
@@ -239,13 +284,27 @@ __global__ void __launch_bounds__(512) gemm_skinny_stream_kernel(
     const int gb = g0 + 4 * wave;
     const int gq = gb + (q < nj ? q : nj - 1);  // group loaded by 16-lane block q
     u32x4 xv[4][4];
+    if constexpr (SV) {
+      svid_block_fragments<AT, K>(sv_x, sv_xf32, sv_sin, G * kGroup, gb, nj, lane, frag);
+      // the area is this wavefront's own, and its LDS operations complete in order
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        xv[j][s] = (tok_ok && j < nj) ? *reinterpret_cast<const u32x4*>(
-                                            xrow + (int64_t)kGroup * (gb + j) + 8 * s)
-                                      : u32x4{0u, 0u, 0u, 0u};
+        for (int s = 0; s < 4; ++s)
+          xv[j][s] = (tok_ok && j < nj)
+                         ? *reinterpret_cast<const u32x4*>(
+                               frag + ((j * K + (i >> 1)) * 2 + (i & 1)) * kGroup + 32 * q + 8 * s)
+                         : u32x4{0u, 0u, 0u, 0u};
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          xv[j][s] = (tok_ok && j < nj) ? *reinterpret_cast<const u32x4*>(
+                                              xrow + (int64_t)kGroup * (gb + j) + 8 * s)
+                                        : u32x4{0u, 0u, 0u, 0u};
+    }
     auto load = [&](int t, SkinnyLoads<AT, K>& L) {
       const int row = tile16_of(blockIdx.x + t * gridDim.x, tiles) * 16 + i;
       const int64_t c = ((int64_t)(row / kRowBlock) * G + gq) * K * kRowBlock + row % kRowBlock;
@@ -359,7 +418,8 @@ constexpr int kSkinnyJ = 8;  // tiles per persistent workgroup (registers)
 
 template <typename AT, int K, bool SV = false>
 void launch_stream_k(const Geom& geo, const u32x4* bits, const AT* scales, const uint16_t* X,
-                     int64_t ldx, float* Y, int64_t ldy, int T, hipStream_t stream) {
+                     int64_t ldx, float* Y, int64_t ldy, int T, hipStream_t stream,
+                     const void* sv_x = nullptr, int sv_xf32 = 0, const AT* sv_sin = nullptr) {
   // slabs of at most 32 groups: one wavefront per block of 4 groups, at most 8
   const int nslabs = (geo.G + 31) / 32;
   const int slab = (geo.G + nslabs - 1) / nslabs;
@@ -367,9 +427,11 @@ void launch_stream_k(const Geom& geo, const u32x4* bits, const AT* scales, const
   const int tiles = geo.RB * 4;
   int grid = tiles < 256 ? tiles : 256;
   if (grid * kSkinnyJ < tiles) grid = (tiles + kSkinnyJ - 1) / kSkinnyJ;
-  const size_t lds = (size_t)kSkinnyJ * NW * 256 * sizeof(float);
+  size_t lds = (size_t)kSkinnyJ * NW * 256 * sizeof(float);
+  if (SV) lds += (size_t)NW * 4 * K * 2 * kGroup * sizeof(uint16_t);
   hipLaunchKernelGGL((gemm_skinny_stream_kernel<AT, K, kSkinnyJ, SV>), dim3(grid), dim3(64 * NW), lds,
-                     stream, bits, scales, X, ldx, Y, ldy, T, geo.m, geo.G, slab, tiles);
+                     stream, bits, scales, X, ldx, Y, ldy, T, geo.m, geo.G, slab, tiles, sv_x,
+                     sv_xf32, sv_sin);
 }
 
 template <typename AT>
@@ -415,29 +477,32 @@ int launch_at(const Geom& geo, const void* packed, const void* X, int64_t ldx, f
 
 int skinny_max_tokens() { return kMaxSkinnyTokens; }
 
-// The SVID product on prepared activations (svid_prep_kernel): 2K token rows.
-int launch_svid_skinny(const mbok_desc* d, const void* packed, const uint16_t* xs, float* y,
-                       hipStream_t stream) {
+// The SVID product: 2K token rows formed from x and s_in in the kernel.
+int launch_svid_skinny(const mbok_desc* d, const void* packed, const void* x, int32_t x_dtype,
+                       const void* s_in, float* y, hipStream_t stream) {
   const Geom geo = make_geom(d);
   const u32x4* bits = reinterpret_cast<const u32x4*>(packed);
   const int T = 2 * geo.K;
+  const int xf = x_dtype == MBOK_F32 ? 1 : 0;
   if (d->alpha_dtype == MBOK_F16) {
     const uint16_t* sc = reinterpret_cast<const uint16_t*>(
         reinterpret_cast<const char*>(packed) + geo.bits_bytes);
+    const uint16_t* si = reinterpret_cast<const uint16_t*>(s_in);
     switch (geo.K) {
-      case 1: launch_stream_k<uint16_t, 1, true>(geo, bits, sc, xs, geo.n, y, geo.m, T, stream); break;
-      case 2: launch_stream_k<uint16_t, 2, true>(geo, bits, sc, xs, geo.n, y, geo.m, T, stream); break;
-      case 3: launch_stream_k<uint16_t, 3, true>(geo, bits, sc, xs, geo.n, y, geo.m, T, stream); break;
-      default: launch_stream_k<uint16_t, 4, true>(geo, bits, sc, xs, geo.n, y, geo.m, T, stream); break;
+      case 1: launch_stream_k<uint16_t, 1, true>(geo, bits, sc, nullptr, 0, y, geo.m, T, stream, x, xf, si); break;
+      case 2: launch_stream_k<uint16_t, 2, true>(geo, bits, sc, nullptr, 0, y, geo.m, T, stream, x, xf, si); break;
+      case 3: launch_stream_k<uint16_t, 3, true>(geo, bits, sc, nullptr, 0, y, geo.m, T, stream, x, xf, si); break;
+      default: launch_stream_k<uint16_t, 4, true>(geo, bits, sc, nullptr, 0, y, geo.m, T, stream, x, xf, si); break;
     }
   } else {
     const float* sc =
         reinterpret_cast<const float*>(reinterpret_cast<const char*>(packed) + geo.bits_bytes);
+    const float* si = reinterpret_cast<const float*>(s_in);
     switch (geo.K) {
-      case 1: launch_stream_k<float, 1, true>(geo, bits, sc, xs, geo.n, y, geo.m, T, stream); break;
-      case 2: launch_stream_k<float, 2, true>(geo, bits, sc, xs, geo.n, y, geo.m, T, stream); break;
-      case 3: launch_stream_k<float, 3, true>(geo, bits, sc, xs, geo.n, y, geo.m, T, stream); break;
-      default: launch_stream_k<float, 4, true>(geo, bits, sc, xs, geo.n, y, geo.m, T, stream); break;
+      case 1: launch_stream_k<float, 1, true>(geo, bits, sc, nullptr, 0, y, geo.m, T, stream, x, xf, si); break;
+      case 2: launch_stream_k<float, 2, true>(geo, bits, sc, nullptr, 0, y, geo.m, T, stream, x, xf, si); break;
+      case 3: launch_stream_k<float, 3, true>(geo, bits, sc, nullptr, 0, y, geo.m, T, stream, x, xf, si); break;
+      default: launch_stream_k<float, 4, true>(geo, bits, sc, nullptr, 0, y, geo.m, T, stream, x, xf, si); break;
     }
   }
   return hipGetLastError() == hipSuccess ? MBOK_OK : MBOK_ERR_HIP;

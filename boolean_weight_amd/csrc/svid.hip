@@ -1,5 +1,5 @@
-// Successive sign-value-independent decomposition (SVID) on the GPU, and the
-// activation preparation of its product.
+// Successive sign-value-independent decomposition (SVID) on the GPU.  (Its
+// product runs in the few-token kernel, skinny.hip.)
 //
 // "Highly Efficient and Effective LLMs with Multi-Boolean Architectures",
 // gist.science summaries, "Riformulazione Booleana e SVID" (Italian),
@@ -216,33 +216,6 @@ int decompose(const mbok_desc* d, const float* W, int64_t ldw, int8_t* signs, AT
   return MBOK_OK;
 }
 
-// ---------------------------------------------------------------- product
-
-// Activation rows of the SVID product for the few-token kernel: for kernel k,
-// v = s_in^k[j] * x[j] in fp32 (exact for fp16 scales and bf16 x), split into
-// bf16 hi = RNE(v) and lo = RNE(v - hi); row 2k gets hi and row 2k+1 lo, so
-// the matrix cores see v to about 2^-17 relative.
-template <typename XT, typename AT>
-__global__ void __launch_bounds__(kSvidBlock) svid_prep_kernel(const XT* __restrict__ x,
-                                                               const AT* __restrict__ s_in,
-                                                               int n, int K,
-                                                               uint16_t* __restrict__ xs) {
-  const int j = blockIdx.x * kSvidBlock + threadIdx.x;
-  if (j >= n) return;
-  float xv;
-  if constexpr (sizeof(XT) == 2)
-    xv = bf16_bits_to_f32(x[j]);
-  else
-    xv = x[j];
-  for (int k = 0; k < K; ++k) {
-    const float v = alpha_to_f32<AT>(s_in[(int64_t)k * n + j]) * xv;
-    const uint16_t hi = f32_to_bf16_rne(v);
-    const float rest = v - bf16_bits_to_f32(hi);
-    xs[(int64_t)(2 * k) * n + j] = hi;
-    xs[(int64_t)(2 * k + 1) * n + j] = f32_to_bf16_rne(rest);
-  }
-}
-
 }  // namespace
 
 size_t svid_workspace_bytes(const mbok_desc* d) {
@@ -258,36 +231,6 @@ int launch_svid_decompose(const mbok_desc* d, const float* W, int64_t ldw, int8_
                                reinterpret_cast<uint16_t*>(s_in), iters, w, stream);
   return decompose<float>(d, W, ldw, signs, reinterpret_cast<float*>(s_out),
                           reinterpret_cast<float*>(s_in), iters, w, stream);
-}
-
-size_t svid_gemv_workspace_bytes(const mbok_desc* d) {
-  return (size_t)2 * d->K * (size_t)d->n * sizeof(uint16_t);
-}
-
-int launch_svid_prep(const mbok_desc* d, const void* x, int32_t x_dtype, const void* s_in,
-                     uint16_t* xs, hipStream_t stream) {
-  const dim3 grid((unsigned)((d->n + kSvidBlock - 1) / kSvidBlock)), blk(kSvidBlock);
-  const bool f16a = d->alpha_dtype == MBOK_F16;
-  if (x_dtype == MBOK_BF16) {
-    if (f16a)
-      hipLaunchKernelGGL((svid_prep_kernel<uint16_t, uint16_t>), grid, blk, 0, stream,
-                         reinterpret_cast<const uint16_t*>(x),
-                         reinterpret_cast<const uint16_t*>(s_in), d->n, d->K, xs);
-    else
-      hipLaunchKernelGGL((svid_prep_kernel<uint16_t, float>), grid, blk, 0, stream,
-                         reinterpret_cast<const uint16_t*>(x), reinterpret_cast<const float*>(s_in),
-                         d->n, d->K, xs);
-  } else {
-    if (f16a)
-      hipLaunchKernelGGL((svid_prep_kernel<float, uint16_t>), grid, blk, 0, stream,
-                         reinterpret_cast<const float*>(x),
-                         reinterpret_cast<const uint16_t*>(s_in), d->n, d->K, xs);
-    else
-      hipLaunchKernelGGL((svid_prep_kernel<float, float>), grid, blk, 0, stream,
-                         reinterpret_cast<const float*>(x), reinterpret_cast<const float*>(s_in),
-                         d->n, d->K, xs);
-  }
-  return hipGetLastError() == hipSuccess ? MBOK_OK : MBOK_ERR_HIP;
 }
 
 }  // namespace mbok

@@ -295,8 +295,8 @@ int mbok_svid_decompose(const mbok_desc* d, const float* W, int64_t ldw,
 int mbok_svid_pack(const mbok_desc* d, const int8_t* signs, const void* s_out,
                    void* packed, void* stream);
 
-/* Bytes of the workspace mbok_svid_gemv needs: 2 K n bf16 activation rows.
- * Host only; 0 for a NULL or invalid descriptor. */
+/* Bytes of the workspace mbok_svid_gemv uses: 0 (the argument is kept for a
+ * form that stages activations).  Host only. */
 size_t mbok_svid_gemv_workspace_bytes(const mbok_desc* d);
 
 /*
@@ -306,15 +306,16 @@ size_t mbok_svid_gemv_workspace_bytes(const mbok_desc* d);
  * s_in^k (.) x is formed in fp32 (exact for fp16 scales and bf16 x) and
  * split into bf16 hi + lo parts, so the matrix cores see it to about 2^-17
  * relative; the +-1 contractions accumulate in fp32 and s_out applies in
- * fp32.
+ * fp32.  Results are bit-reproducible.
  *  packed     device, the buffer of mbok_svid_pack.
- *  s_in       device [K][n] of d->alpha_dtype.
- *  x          device, n values of x_dtype (MBOK_BF16 or MBOK_F32).
+ *  s_in       device [K][n] of d->alpha_dtype, 16-byte aligned.
+ *  x          device, n values of x_dtype (MBOK_BF16 or MBOK_F32), 16-byte
+ *             aligned.
  *  y          device fp32 [m]; overwritten.
- *  workspace  device, mbok_svid_gemv_workspace_bytes(d) bytes, 256-byte
- *             aligned; overwritten (the prepared activations).
+ *  workspace  device pointer or NULL; unused (checked for 256-byte alignment
+ *             when given).
  * Errors: INVALID_ARG (NULL), SHAPE/UNSUPPORTED from d, DTYPE (x_dtype),
- * ALIGN (packed 16 bytes, s_in, x, y 4 bytes, workspace 256 bytes), HIP.
+ * ALIGN (packed, s_in, x 16 bytes, y 4 bytes, workspace 256 bytes), HIP.
  */
 int mbok_svid_gemv(const mbok_desc* d, const void* packed, const void* s_in,
                    const void* x, int32_t x_dtype, float* y, void* workspace,

@@ -140,10 +140,12 @@ def test_compute_calls_validate_before_launch(lib):
     assert lib.mbok_svid_decompose(R(d), A16, 256, MIS, A16, A16, 8, A16, None) == -4
     assert lib.mbok_svid_pack(R(d), None, A16, A16, None) == -1
     assert lib.mbok_svid_pack(R(d), A16, A16 + 2, A16, None) == -4
-    assert lib.mbok_svid_gemv(R(d), A16, A16, A16, bw.MBOK_BF16, A16, None, None) == -1
-    assert lib.mbok_svid_gemv(R(d), A16, A16, A16, bw.MBOK_F16, A16, A16, None) == -3
+    assert lib.mbok_svid_gemv(R(d), A16, None, A16, bw.MBOK_BF16, A16, None, None) == -1
+    assert lib.mbok_svid_gemv(R(d), A16, A16, A16, bw.MBOK_F16, A16, None, None) == -3
     assert lib.mbok_svid_gemv(R(d), A16, A16, A16, bw.MBOK_BF16, A16, A16 + 64, None) == -4
-    assert lib.mbok_svid_gemv_workspace_bytes(R(d)) == 2 * 2 * 256 * 2
+    assert lib.mbok_svid_gemv(R(d), A16, A16 + 8, A16, bw.MBOK_BF16, A16, None, None) == -4
+    assert lib.mbok_svid_gemv(R(d), A16, A16, A16 + 8, bw.MBOK_BF16, A16, None, None) == -4
+    assert lib.mbok_svid_gemv_workspace_bytes(R(d)) == 0
     assert lib.mbok_svid_workspace_bytes(R(d)) > 0 and lib.mbok_svid_workspace_bytes(None) == 0
     # transposed product
     assert lib.mbok_gemvt(R(d), None, A16, bw.MBOK_BF16, A16, None, None) == -1
