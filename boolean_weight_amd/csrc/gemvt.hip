@@ -27,7 +27,7 @@
 // wavefronts (slices) of a workgroup in order; with several workgroups per
 // column group each writes its 128 partial sums to the workspace and a
 // second kernel adds them in order.
-#include "mbok_device.h"
+#include "mbok_exact.h"
 #include "mbok_launch.h"
 
 namespace mbok {

@@ -20,7 +20,7 @@
 // break the error-free sums), so contraction is off for the whole file.
 #pragma clang fp contract(off)
 
-#include "mbok_device.h"
+#include "mbok_exact.h"
 #include "mbok_launch.h"
 
 namespace mbok {

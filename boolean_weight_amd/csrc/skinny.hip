@@ -37,7 +37,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-#include "mbok_device.h"
+#include "mbok_exact.h"
 #include "mbok_launch.h"
 
 namespace mbok {

@@ -26,7 +26,7 @@
 // multiply may be fused into an add, so contraction is off for the file.
 #pragma clang fp contract(off)
 
-#include "mbok_device.h"
+#include "mbok_exact.h"
 #include "mbok_launch.h"
 
 namespace mbok {
