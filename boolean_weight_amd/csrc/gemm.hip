@@ -368,29 +368,29 @@ __device__ __forceinline__ void unpack_two_quads(const uint32_t* V, int a, int b
   }
 }
 
-template <typename AT, int K>
-__global__ void __launch_bounds__(GEMM8_THREADS) gemm_mfma8_kernel(
-    const uint32_t* __restrict__ bits, const AT* __restrict__ scales,
-    const uint16_t* __restrict__ X, int64_t ldx, float* __restrict__ Y, int64_t ldy, int T, int m,
-    int m_pad, int G, int ntx, int nfull) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+// The body of one workgroup: JB = 2 for a whole 256-row tile, 1 for one
+// 128-row half of a tile of the partial final round (a compile-time constant,
+// so the loop has no branches on it).
+template <typename AT, int K, int JB>
+__device__ __forceinline__ void mfma8_tile(const uint32_t* __restrict__ bits,
+                                           const AT* __restrict__ scales,
+                                           const uint16_t* __restrict__ X, int64_t ldx,
+                                           float* __restrict__ Y, int64_t ldy, int T, int m,
+                                           int m_pad, int G, int ntx, int tile, int half,
+                                           uint16_t* smem) {
   // buffer b: activations at smem + 2b * TILE_ELEMS, weights right after
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int b = blockIdx.x;
-  const bool whole = b < nfull;
-  const int tile = whole ? b : nfull + ((b - nfull) >> 1);
-  const int JB = whole ? 2 : 1;              // 32-row blocks per wavefront
-  const int tile_rows = whole ? BN : BN / 2;
+  constexpr int tile_rows = JB == 2 ? BN : BN / 2;
   const int wt = wave & 1, wn = wave >> 1;  // 128-token half, row quarter
   const int t0 = (tile / ntx) * BT;
-  const int n0 = (tile % ntx) * BN + (whole ? 0 : ((b - nfull) & 1) * (BN / 2));
+  const int n0 = (tile % ntx) * BN + half * (BN / 2);
   const int S = G * 2;  // steps of 64 columns
 
   // unpack role: row n0 + tid/2, columns 32 * (tid % 2) .. + 31 of each step
   const int urow = tid >> 1, uhalf = tid & 1;
-  const bool unpacker = urow < tile_rows;  // uniform per wavefront
+  const bool unpacker = JB == 2 || urow < tile_rows;  // uniform per wavefront
   const int row = n0 + urow;
   const bool row_ok = unpacker && row < m_pad;
   const int rowc = row_ok ? row : m_pad - 1;
@@ -426,10 +426,16 @@ __global__ void __launch_bounds__(GEMM8_THREADS) gemm_mfma8_kernel(
       R.a[k] = alpha_to_f32<AT>(scales[ch]);
     }
   };
+  // selects, not branches: the step stays one basic block
   auto mask_step = [&](StepRegs& R) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (!xok[j]) R.x[j] = make_uint4(0u, 0u, 0u, 0u);
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t keep = xok[j] ? 0xffffffffu : 0u;
+      R.x[j].x &= keep;
+      R.x[j].y &= keep;
+      R.x[j].z &= keep;
+      R.x[j].w &= keep;
+    }
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       R.w[k] = row_ok ? R.w[k] : 0u;
@@ -539,15 +545,29 @@ __global__ void __launch_bounds__(GEMM8_THREADS) gemm_mfma8_kernel(
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < JB; ++j) {
       const int n = n0 + wn * 32 * JB + j * 32 + lrow;
-      if (j >= JB || n >= m) continue;
+      if (n >= m) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int t = t0 + wt * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         if (t < T) Y[(int64_t)t * ldy + n] = acc[i][j][r];
       }
     }
+}
+
+template <typename AT, int K>
+__global__ void __launch_bounds__(GEMM8_THREADS) gemm_mfma8_kernel(
+    const uint32_t* __restrict__ bits, const AT* __restrict__ scales,
+    const uint16_t* __restrict__ X, int64_t ldx, float* __restrict__ Y, int64_t ldy, int T, int m,
+    int m_pad, int G, int ntx, int nfull) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  const int b = blockIdx.x;
+  if (b < nfull)
+    mfma8_tile<AT, K, 2>(bits, scales, X, ldx, Y, ldy, T, m, m_pad, G, ntx, b, 0, smem);
+  else
+    mfma8_tile<AT, K, 1>(bits, scales, X, ldx, Y, ldy, T, m, m_pad, G, ntx,
+                         nfull + ((b - nfull) >> 1), (b - nfull) & 1, smem);
 }
 
 // Compute units of the current device (queried once per device).
