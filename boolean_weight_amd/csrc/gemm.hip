@@ -32,6 +32,9 @@ namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+// a native vector type keeps the activation staging in registers (a uint4
+// struct member went through scratch memory)
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 
 constexpr int BT = 256;         // tokens per workgroup tile
 constexpr int BN = 256;         // output rows per workgroup tile
@@ -392,24 +395,25 @@ __device__ __forceinline__ void mfma8_tile(const uint32_t* __restrict__ bits,
   const int urow = tid >> 1, uhalf = tid & 1;
   const bool unpacker = JB == 2 || urow < tile_rows;  // uniform per wavefront
   const int row = n0 + urow;
-  const bool row_ok = unpacker && row < m_pad;
-  const int rowc = row_ok ? row : m_pad - 1;
+  const int rowc = row < m_pad ? row : m_pad - 1;
   const uint32_t row_chunk = (uint32_t)(rowc / kRowBlock) * (uint32_t)(G * K * kRowBlock) +
                              (uint32_t)(rowc % kRowBlock);
 
-  // X copy role: segment j = token tid/8 + 64 j, columns 8 (tid % 8) .. + 7
+  // X copy role: segment j = token tid/8 + 64 j, columns 8 (tid % 8) .. + 7.
+  // Tokens past T read token T - 1 and rows past the padded row count read
+  // the last padded row: every load stays inside the buffers, and the
+  // products of those tokens and rows are never stored (each output element
+  // depends only on its own token and row), so nothing needs masking.
   const int xpart = tid & 7;
   uint32_t xoff[4];
-  bool xok[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int t = t0 + (tid >> 3) + 64 * j;
-    xok[j] = t < T;
-    xoff[j] = (uint32_t)((int64_t)(xok[j] ? t : T - 1) * ldx) + xpart * 8;
+    xoff[j] = (uint32_t)((int64_t)(t < T ? t : T - 1) * ldx) + xpart * 8;
   }
 
   struct StepRegs {
-    uint4 x[4];
+    u32x4 x[4];
     uint32_t w[K];
     float a[K];
   };
@@ -418,7 +422,7 @@ __device__ __forceinline__ void mfma8_tile(const uint32_t* __restrict__ bits,
     const int g = s >> 1;
     const uint32_t word = 2 * (s & 1) + uhalf;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) R.x[j] = *reinterpret_cast<const uint4*>(X + xoff[j] + s * BK);
+    for (int j = 0; j < 4; ++j) R.x[j] = *reinterpret_cast<const u32x4*>(X + xoff[j] + s * BK);
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       const uint32_t ch = row_chunk + (uint32_t)(g * K + k) * kRowBlock;
@@ -426,23 +430,6 @@ __device__ __forceinline__ void mfma8_tile(const uint32_t* __restrict__ bits,
       R.a[k] = alpha_to_f32<AT>(scales[ch]);
     }
   };
-  // selects, not branches: the step stays one basic block
-  auto mask_step = [&](StepRegs& R) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t keep = xok[j] ? 0xffffffffu : 0u;
-      R.x[j].x &= keep;
-      R.x[j].y &= keep;
-      R.x[j].z &= keep;
-      R.x[j].w &= keep;
-    }
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-      R.w[k] = row_ok ? R.w[k] : 0u;
-      R.a[k] = row_ok ? R.a[k] : 0.f;
-    }
-  };
-
   f32x16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -456,7 +443,6 @@ __device__ __forceinline__ void mfma8_tile(const uint32_t* __restrict__ bits,
 
   // compute step from buffer cb, store the next step (registers R) into cb^1
   auto step = [&](int cb, StepRegs& R, bool even) {
-    mask_step(R);
     if (K <= 3 && even) L = make_levels<K>(R.a);
     const uint16_t* xs = smem + 2 * cb * TILE_ELEMS + (wt * 128 + lrow) * LDS_STRIDE + lk;
     const uint16_t* ws =
@@ -494,7 +480,7 @@ __device__ __forceinline__ void mfma8_tile(const uint32_t* __restrict__ bits,
           acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[1], acc[i][1], 0, 0, 0);
       }
       // a quarter of the next step: one activation segment, 8 weight columns
-      *reinterpret_cast<uint4*>(xd + kk * 64 * LDS_STRIDE) = R.x[kk];
+      *reinterpret_cast<u32x4*>(xd + kk * 64 * LDS_STRIDE) = R.x[kk];
       uint32_t out[4];
       if (K <= 3) {
         unpack_two_quads(V, kk >> 1, 2 * (kk & 1), L, out);
@@ -512,12 +498,11 @@ __device__ __forceinline__ void mfma8_tile(const uint32_t* __restrict__ bits,
   // prologue: step 0 into buffer 0
   load_step(0, R0);
   load_step(1, R1);
-  mask_step(R0);
   {
     if (K <= 3) L = make_levels<K>(R0.a);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<uint4*>(smem + (tid >> 3) * LDS_STRIDE + xpart * 8 + j * 64 * LDS_STRIDE) =
+      *reinterpret_cast<u32x4*>(smem + (tid >> 3) * LDS_STRIDE + xpart * 8 + j * 64 * LDS_STRIDE) =
           R0.x[j];
     if (unpacker) {
       uint4* wd = reinterpret_cast<uint4*>(smem + TILE_ELEMS + urow * LDS_STRIDE + uhalf * 32);

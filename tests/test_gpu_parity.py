@@ -423,7 +423,7 @@ def test_gemm_prefill_exact_ragged(T, m, n, K, prefill_waves):
     assert np.array_equal(Y, oracle.product(S, A, X))
 
 
-def test_gemm_prefill_exact_whole_and_half_tiles():
+def test_gemm_prefill_exact_whole_and_half_tiles(prefill_waves):
     """More 256 x 256 tiles than compute units (20 x 13 = 260 tiles on 256):
     the last round's tiles run as 128-row halves; exact regime, every element."""
     T, m, n, K = 3328, 5120, 256, 3
@@ -436,7 +436,7 @@ def test_gemm_prefill_exact_whole_and_half_tiles():
     assert np.array_equal(Y, oracle.product(S, A, X))
 
 
-def test_gemm_identity_activations_give_the_weights():
+def test_gemm_identity_activations_give_the_weights(prefill_waves):
     """X = identity rows (T = n) in the exact regime: Y = W_hat^T exactly,
     which pins the operand orientation, k order and bf16 rounding of W_hat."""
     say("gemm identity")
@@ -448,7 +448,7 @@ def test_gemm_identity_activations_give_the_weights():
     assert np.array_equal(Y, oracle.dequantize(S, A).T)
 
 
-def test_gemm_prefill_config5_tolerance():
+def test_gemm_prefill_config5_tolerance(prefill_waves):
     """Config 5 at full size (11008 x 4096, K = 3, 2048 tokens) on the device;
     the oracle quantizes and multiplies sampled output rows for every token."""
     w = syn.WORKLOADS[5]
