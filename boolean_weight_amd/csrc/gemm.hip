@@ -23,6 +23,7 @@
 // v_perm_b32 turns that selector into 4 low bytes and 4 high bytes of bf16
 // weights at once; two more perms interleave them into natural column order.
 #include <stdlib.h>
+#include <string.h>
 
 #include "mbok_device.h"
 #include "mbok_launch.h"
@@ -415,7 +416,12 @@ __device__ __forceinline__ void mfma8_tile(const uint32_t* __restrict__ bits,
   struct StepRegs {
     u32x4 x[4];
     uint32_t w[K];
-    float a[K];
+    AT a[K];  // raw scales: converted where they are used, so that nothing
+              // waits on these loads in the step that issues them
+  };
+  auto scales_f32 = [](const StepRegs& R, float* f) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) f[k] = alpha_to_f32<AT>(R.a[k]);
   };
   StepRegs R0, R1;
   auto load_step = [&](int s, StepRegs& R) {
@@ -427,7 +433,7 @@ __device__ __forceinline__ void mfma8_tile(const uint32_t* __restrict__ bits,
     for (int k = 0; k < K; ++k) {
       const uint32_t ch = row_chunk + (uint32_t)(g * K + k) * kRowBlock;
       R.w[k] = bits[ch * 4u + word];
-      R.a[k] = alpha_to_f32<AT>(scales[ch]);
+      R.a[k] = scales[ch];
     }
   };
   f32x16 acc[4][2];
@@ -443,7 +449,11 @@ __device__ __forceinline__ void mfma8_tile(const uint32_t* __restrict__ bits,
 
   // compute step from buffer cb, store the next step (registers R) into cb^1
   auto step = [&](int cb, StepRegs& R, bool even) {
-    if (K <= 3 && even) L = make_levels<K>(R.a);
+    if (K <= 3 && even) {
+      float af[K];
+      scales_f32(R, af);
+      L = make_levels<K>(af);
+    }
     const uint16_t* xs = smem + 2 * cb * TILE_ELEMS + (wt * 128 + lrow) * LDS_STRIDE + lk;
     const uint16_t* ws =
         smem + (2 * cb + 1) * TILE_ELEMS + (wn * 32 * JB + lrow) * LDS_STRIDE + lk;
@@ -486,7 +496,9 @@ __device__ __forceinline__ void mfma8_tile(const uint32_t* __restrict__ bits,
         unpack_two_quads(V, kk >> 1, 2 * (kk & 1), L, out);
       } else {
         uint32_t o32[16];
-        unpack_word_k4(R.w, R.a, o32);
+        float af[K];
+        scales_f32(R, af);
+        unpack_word_k4(R.w, af, o32);
         // columns 8 kk .. 8 kk + 7 are quads 2 kk, 2 kk + 1
 #pragma unroll
         for (int q = 0; q < 4; ++q) out[q] = o32[4 * kk + q];
@@ -499,7 +511,9 @@ __device__ __forceinline__ void mfma8_tile(const uint32_t* __restrict__ bits,
   load_step(0, R0);
   load_step(1, R1);
   {
-    if (K <= 3) L = make_levels<K>(R0.a);
+    float af0[K];
+    scales_f32(R0, af0);
+    if (K <= 3) L = make_levels<K>(af0);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       *reinterpret_cast<u32x4*>(smem + (tid >> 3) * LDS_STRIDE + xpart * 8 + j * 64 * LDS_STRIDE) =
@@ -510,13 +524,15 @@ __device__ __forceinline__ void mfma8_tile(const uint32_t* __restrict__ bits,
       if (K <= 3)
         unpack_word<K>(R0.w, L, out);
       else
-        unpack_word_k4(R0.w, R0.a, out);
+        unpack_word_k4(R0.w, af0, out);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         wd[j] = make_uint4(out[4 * j], out[4 * j + 1], out[4 * j + 2], out[4 * j + 3]);
     }
   }
   __syncthreads();
+  // (Pinning these loads to the top of the step with a scheduling barrier
+  // was measured slower: it also keeps the first fragment reads below them.)
   for (int s = 0; s < S; s += 2) {
     load_step(min(s + 2, S - 1), R0);
     step(0, R1, false);  // compute step s, store step s+1 (odd)
@@ -541,18 +557,38 @@ __device__ __forceinline__ void mfma8_tile(const uint32_t* __restrict__ bits,
     }
 }
 
+// Tile at position p of the XCD-blocked order: pairs of token tiles, sweeping
+// the row tiles (p -> token tile 2q + d, row tile tx), the last token tile
+// alone when their count is odd.  Workgroup b runs on XCD b % 8, so giving
+// XCD x the positions x * nfull / 8 .. of the full round puts ~16 row tiles
+// x 2 token tiles on each XCD: its L2 holds those activations and weights
+// instead of every XCD streaming every token tile.
+__device__ __forceinline__ int tile_at(int p, int ntx, int nty) {
+  const int q = p / (2 * ntx);
+  const int rem = p - q * 2 * ntx;
+  if (2 * q + 1 < nty) return (2 * q + (rem & 1)) * ntx + (rem >> 1);
+  return 2 * q * ntx + rem;
+}
+
 template <typename AT, int K>
 __global__ void __launch_bounds__(GEMM8_THREADS) gemm_mfma8_kernel(
     const uint32_t* __restrict__ bits, const AT* __restrict__ scales,
     const uint16_t* __restrict__ X, int64_t ldx, float* __restrict__ Y, int64_t ldy, int T, int m,
-    int m_pad, int G, int ntx, int nfull) {
+    int m_pad, int G, int ntx, int nfull, int xcd_order) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   const int b = blockIdx.x;
-  if (b < nfull)
-    mfma8_tile<AT, K, 2>(bits, scales, X, ldx, Y, ldy, T, m, m_pad, G, ntx, b, 0, smem);
-  else
-    mfma8_tile<AT, K, 1>(bits, scales, X, ldx, Y, ldy, T, m, m_pad, G, ntx,
-                         nfull + ((b - nfull) >> 1), (b - nfull) & 1, smem);
+  const int nty = (T + BT - 1) / BT;
+  if (b < nfull) {
+    int p = b;
+    if (xcd_order && (nfull & 7) == 0) p = (b & 7) * (nfull >> 3) + (b >> 3);
+    const int tile = xcd_order ? tile_at(p, ntx, nty) : p;
+    mfma8_tile<AT, K, 2>(bits, scales, X, ldx, Y, ldy, T, m, m_pad, G, ntx, tile, 0, smem);
+  } else {
+    const int p = nfull + ((b - nfull) >> 1);
+    const int tile = xcd_order ? tile_at(p, ntx, nty) : p;
+    mfma8_tile<AT, K, 1>(bits, scales, X, ldx, Y, ldy, T, m, m_pad, G, ntx, tile,
+                         (b - nfull) & 1, smem);
+  }
 }
 
 // Compute units of the current device (queried once per device).
@@ -570,6 +606,13 @@ int compute_units() {
   return cache[dev];
 }
 
+// MBOK_GEMM_ORDER=token keeps the plain token-major tile order (for
+// measurements); the default is the XCD-blocked order.
+int gemm_xcd_order() {
+  const char* v = getenv("MBOK_GEMM_ORDER");
+  return v && strcmp(v, "token") == 0 ? 0 : 1;
+}
+
 template <typename AT, int K>
 void launch_mfma8_k(const Geom& geo, const uint32_t* bits, const AT* scales, const uint16_t* Xb,
                     int64_t T, int64_t ldx, float* Y, int64_t ldy, hipStream_t stream) {
@@ -582,7 +625,7 @@ void launch_mfma8_k(const Geom& geo, const uint32_t* bits, const AT* scales, con
   const int64_t nfull = ntiles - rem;
   hipLaunchKernelGGL((gemm_mfma8_kernel<AT, K>), dim3((unsigned)(nfull + 2 * rem)),
                      dim3(GEMM8_THREADS), lds, stream, bits, scales, Xb, ldx, Y, ldy, (int)T,
-                     geo.m, geo.RB * kRowBlock, geo.G, ntx, (int)nfull);
+                     geo.m, geo.RB * kRowBlock, geo.G, ntx, (int)nfull, gemm_xcd_order());
 }
 
 template <typename AT>

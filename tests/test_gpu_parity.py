@@ -399,16 +399,28 @@ def test_gemm_config3_tolerance(T):
         assert ratio <= TOL, (name, ratio)
 
 
-@pytest.fixture(params=["8", "4"])
+PREFILL_VARIANTS = {
+    "8": {"MBOK_GEMM_WAVES": "8"},
+    "8_token_order": {"MBOK_GEMM_WAVES": "8", "MBOK_GEMM_ORDER": "token"},
+    "4": {"MBOK_GEMM_WAVES": "4"},
+}
+
+
+@pytest.fixture(params=list(PREFILL_VARIANTS))
 def prefill_waves(request):
-    """Prefill kernel with 8 wavefronts per workgroup (default) or 4."""
-    old = os.environ.get("MBOK_GEMM_WAVES")
-    os.environ["MBOK_GEMM_WAVES"] = request.param
+    """Prefill kernel with 8 wavefronts per workgroup (default; XCD-blocked
+    or token-major tile order) or 4."""
+    keys = ("MBOK_GEMM_WAVES", "MBOK_GEMM_ORDER")
+    old = {k: os.environ.get(k) for k in keys}
+    for k in keys:
+        os.environ.pop(k, None)
+    os.environ.update(PREFILL_VARIANTS[request.param])
     yield request.param
-    if old is None:
-        os.environ.pop("MBOK_GEMM_WAVES", None)
-    else:
-        os.environ["MBOK_GEMM_WAVES"] = old
+    for k, v in old.items():
+        if v is None:
+            os.environ.pop(k, None)
+        else:
+            os.environ[k] = v
 
 
 @pytest.mark.parametrize("K", [1, 2, 3, 4])
