@@ -353,8 +353,11 @@ def main():
             call(li, c)
 
     # A HIP graph of one pass over the whole pool (>= 1 GiB of distinct
-    # weights): replays stream cold weights and save per-launch CPU work.
-    use_graph = not args.no_graph and ncopy * len(layers) <= 2048
+    # weights), or of the timed steps when they are fewer: replays stream
+    # cold weights and save per-launch CPU work (and the timed region never
+    # mixes graph replays with plain launches when steps <= the pool).
+    glen = min(ncopy, max(1, args.steps))
+    use_graph = not args.no_graph and glen * len(layers) <= 2048
     graph = None
     if use_graph:
         s = torch.cuda.Stream()
@@ -365,16 +368,18 @@ def main():
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            for i in range(ncopy):
+            for i in range(glen):
                 step(i)
+        graph.replay()  # the first replay uploads the graph: keep it untimed
+        torch.cuda.synchronize()
 
     def run(nsteps):
         """Exactly nsteps steps: whole graph replays, then single launches."""
         i = 0
         if use_graph:
-            for _ in range(nsteps // ncopy):
+            for _ in range(nsteps // glen):
                 graph.replay()
-            i = (nsteps // ncopy) * ncopy
+            i = (nsteps // glen) * glen
         while i < nsteps:
             step(i)
             i += 1
