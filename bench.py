@@ -366,20 +366,30 @@ def main():
             step(0)
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for i in range(glen):
-                step(i)
-        graph.replay()  # the first replay uploads the graph: keep it untimed
-        torch.cuda.synchronize()
+        def capture(count):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(count):
+                    step(i)
+            g.replay()  # the first replay uploads the graph: keep it untimed
+            torch.cuda.synchronize()
+            return g
+
+        graph = capture(glen)
+        # the steps past the last whole replay (warm-up and timed counts) run
+        # as graphs of their own too, captured here, outside the timed region
+        rest = {r: capture(r) for r in {args.warmup % glen, args.steps % glen} if r}
 
     def run(nsteps):
-        """Exactly nsteps steps: whole graph replays, then single launches."""
+        """Exactly nsteps steps: whole graph replays, then the remainder."""
         i = 0
         if use_graph:
             for _ in range(nsteps // glen):
                 graph.replay()
             i = (nsteps // glen) * glen
+            if nsteps > i:
+                rest[nsteps - i].replay()
+                i = nsteps
         while i < nsteps:
             step(i)
             i += 1
