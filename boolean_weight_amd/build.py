@@ -25,6 +25,11 @@ COMMON = [
     "-Wall", "-Wno-unused-function",
     # no packed fp32 instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the first kernel arguments arrive preloaded in SGPRs at wave launch,
+    # so the address arithmetic does not wait for a kernarg load (about
+    # 0.45 us of a 4096 x 4096 decode call); code objects keep the loading
+    # prologue for firmware without preload
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
 ]
 
 
