@@ -383,9 +383,14 @@ struct BlockLoads {
 };
 
 template <typename XT, typename AT, int K, int JMAX>
+// The arguments the first loads need come first, so that they are among
+// the ones preloaded into SGPRs at launch; the scales are found from the
+// packed buffer (they follow the 4 G K tiles 16-byte sign chunks).
 __global__ void __launch_bounds__(16 * kWave) gemv_stream_kernel(
-    const uint4* __restrict__ bits, const AT* __restrict__ scales, const XT* __restrict__ x,
-    float* __restrict__ y, int m, int G, int slab_groups, int tiles) {
+    const uint4* __restrict__ bits, const XT* __restrict__ x, int G, int tiles, int slab_groups,
+    float* __restrict__ y, int m) {
+  const AT* __restrict__ scales =
+      reinterpret_cast<const AT*>(bits + (int64_t)tiles * 16 * G * K);
   extern __shared__ float lds[];
   const int NW = blockDim.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
@@ -716,9 +721,11 @@ int launch_stream(const Geom& geo, const uint4* bits, const AT* scales, const vo
   size_t lds = (size_t)slab * kGroupStride;
   const size_t red = (size_t)kStreamJ * NW * 16 * sizeof(float);
   if (lds < red) lds = red;
+  if ((const void*)(bits + (int64_t)tiles * 16 * geo.G * K) != (const void*)scales)
+    return MBOK_ERR_UNSUPPORTED;  // the kernel finds the scales after the signs
   hipLaunchKernelGGL((gemv_stream_kernel<XT, AT, K, kStreamJ>), dim3(grid), dim3(NW * kWave),
-                     lds, stream, bits, scales, reinterpret_cast<const XT*>(x), y, geo.m, geo.G,
-                     slab, tiles);
+                     lds, stream, bits, reinterpret_cast<const XT*>(x), geo.G, tiles, slab, y,
+                     geo.m);
   return hipGetLastError() == hipSuccess ? MBOK_OK : MBOK_ERR_HIP;
 }
 
