@@ -217,6 +217,25 @@ def test_gemv_exact_regime(m, n, K, gemv_variant):
         assert np.array_equal(y, want), np.max(np.abs(y - want))
 
 
+# The streaming kernel walks 16-row tiles (up to 8 per persistent workgroup)
+# over column slabs of at most 64 groups, loading a slab's first tile during
+# the previous slab's last one.  These layers take two or three slabs with 1
+# to 4 tiles per workgroup (odd and even counts); K = 4 keeps one slab at a
+# time.  Sampled rows include the whole last row block.
+@pytest.mark.parametrize("K,m,n", [(2, 4200, 8320), (3, 8400, 8320), (1, 12400, 16512),
+                                   (4, 4300, 8320)])
+def test_gemv_stream_slabs_exact(K, m, n):
+    say(f"gemv stream slabs m={m} n={n} K={K}")
+    S = syn.random_signs(K, m, n, seed=m + n + K)
+    A = syn.exact_alpha(K, m, n // 128, seed=m + 3 * K).astype(np.float16)
+    x = syn.exact_activations(1, n, seed=n + 5 * K)[0]
+    d, packed = pack_on_gpu(S, A, "f16")
+    y = gemv(d, packed, x, "bf16", guard=17)
+    rows = np.unique(np.r_[np.arange(0, m, 13), np.arange(m - 70, m)])
+    want = oracle.product(S[:, rows], A[:, rows], x)
+    assert np.array_equal(y[rows], want), np.max(np.abs(y[rows] - want))
+
+
 def test_gemv_one_hot_and_all_ones(gemv_variant):
     say(f"gemv one-hot {gemv_variant}")
     K, m, n = 3, 70, 384
