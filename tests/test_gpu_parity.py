@@ -467,6 +467,34 @@ def test_gemm_prefill_exact_whole_and_half_tiles(prefill_waves):
     assert np.array_equal(Y, oracle.product(S, A, X))
 
 
+def test_gemm_maximum_tokens():
+    """T = MBOK_MAX_T tokens, every element (exact regime).  With ldx = n the
+    activation offsets fit in 32 bits and the 8-wavefront kernel runs; with
+    ldx = 65536, T * ldx reaches 2^32 elements (an 8 GiB activation buffer)
+    and the kernel with 64-bit offsets runs instead."""
+    K, m, n = 2, 70, 256
+    T = bw.MBOK_MAX_T
+    say(f"gemm maximum tokens T={T} m={m} n={n} K={K}")
+    S = syn.random_signs(K, m, n, seed=61)
+    A = syn.exact_alpha(K, m, n // 128, seed=62).astype(np.float16)
+    X = syn.exact_activations(T, n, seed=63)
+    want = oracle.product(S, A, X)
+    d, packed = pack_on_gpu(S, A, "f16")
+    Xn = x_to_dev(X, "bf16")
+    for ldx in (n, 65536):
+        say(f"gemm maximum tokens ldx={ldx}")
+        if ldx == n:
+            Xd = Xn
+        else:
+            Xd = torch.zeros((T, ldx), dtype=torch.bfloat16, device=DEV)
+            Xd[:, :n] = Xn
+        Y = torch.full((T, m), -777.25, dtype=torch.float32, device=DEV)
+        bw.mbok_gemm(d, packed, Xd, Y)
+        assert np.array_equal(Y.cpu().numpy().astype(np.float64), want), ldx
+        del Xd, Y
+    torch.cuda.empty_cache()
+
+
 def test_gemm_identity_activations_give_the_weights(prefill_waves):
     """X = identity rows (T = n) in the exact regime: Y = W_hat^T exactly,
     which pins the operand orientation, k order and bf16 rounding of W_hat."""
