@@ -495,6 +495,38 @@ def test_gemm_maximum_tokens():
     torch.cuda.empty_cache()
 
 
+def test_maximum_rows():
+    """m = 2^24 rows (the maximum), n = 128, K = 1, exact regime, through the
+    decode (T = 1), few-token (T = 4) and prefill (T = 17) kernels: sampled
+    rows (every 4099th and the last 70) against the oracle, and no output
+    left unwritten.  This runs the tile and chunk index arithmetic over its
+    whole range."""
+    K, m, n = 1, 1 << 24, 128
+    say(f"maximum rows m={m} n={n} K={K}")
+    S = syn.random_signs(K, m, n, seed=71)
+    A = syn.exact_alpha(K, m, n // 128, seed=72).astype(np.float16)
+    d, packed = pack_on_gpu(S, A, "f16")
+    rows = np.unique(np.r_[np.arange(0, m, 4099), np.arange(m - 70, m)])
+    Ss, As = S[:, rows].copy(), A[:, rows].copy()
+    del S
+    rows_t = torch.from_numpy(rows).to(DEV)
+    canary = -777.25  # |y| <= 128 * 8 * 2^-4 in this regime, so never equal
+    for T in (1, 4, 17):
+        say(f"maximum rows T={T}")
+        X = syn.exact_activations(T, n, seed=73 + T)
+        Xd = x_to_dev(X, "bf16")
+        Y = torch.full((T, m), canary, dtype=torch.float32, device=DEV)
+        if T == 1:
+            bw.mbok_gemv(d, packed, Xd[0], Y[0])
+        else:
+            bw.mbok_gemm(d, packed, Xd, Y)
+        assert not bool((Y == canary).any()), T
+        got = Y[:, rows_t].cpu().numpy().astype(np.float64)
+        assert np.array_equal(got, oracle.product(Ss, As, X)), T
+        del Y
+    torch.cuda.empty_cache()
+
+
 def test_gemm_identity_activations_give_the_weights(prefill_waves):
     """X = identity rows (T = n) in the exact regime: Y = W_hat^T exactly,
     which pins the operand orientation, k order and bf16 rounding of W_hat."""
