@@ -25,6 +25,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "mbok_device.h"
 #include "mbok_launch.h"
 
@@ -591,19 +593,20 @@ __global__ void __launch_bounds__(GEMM8_THREADS) gemm_mfma8_kernel(
   }
 }
 
-// Compute units of the current device (queried once per device).
+// Compute units of the current device (queried once per device; host
+// threads that race on the first query store the same value).
 int compute_units() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int n = 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         n <= 0)
       n = 256;
-    cache[dev] = n;
+    cache[dev].store(n, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return n;
 }
 
 // MBOK_GEMM_ORDER=token keeps the plain token-major tile order (for
