@@ -64,6 +64,9 @@ def parse():
     ap.add_argument("--avg-k", type=float, default=None,
                     help="LLaMA-13B-shaped layer only: allocate K per linear (1..4) from the "
                          "residual energies for this average number of kernels per weight")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="time the vendor library's plain bf16 GEMM (torch.matmul) at the "
+                         "workload's product shape, as a yardstick for the prefill kernel")
     ap.add_argument("--extra", nargs="*", default=[],
                     help="with --summarize: more --pmc output dirs of --calibrate-copy runs; "
                          "every counter in them is reported per dominant call")
@@ -258,6 +261,9 @@ def main():
         sys.exit(2)
     if args.quantizer:
         quantizer_bench(args, cfg, cfg["linears"], K, adt, abytes)
+        return
+    if args.library_gemm:
+        library_gemm_bench(args, cfg, linears, T)
         return
 
     # weights of each launch: (name, W on the device, K)
@@ -600,6 +606,51 @@ def quantizer_bench(args, cfg, linears, K, adt, abytes):
     print(json.dumps({"metric": "setup kernel time", "unit": "us", "workload": cfg["name"],
                       "K": K, "refit_rounds": args.refit_rounds, "reps": reps,
                       "alpha_dtype": cfg["alpha_dtype"], "kernels": out}), flush=True)
+
+
+def library_gemm_bench(args, cfg, linears, T):
+    """A yardstick, not the product: the vendor library's dense bf16 GEMM
+    (torch.matmul, hipBLASLt on ROCm) at the first linear's shape, with
+    weights already in bf16 (no unpacking) and a bf16 output.  Both operand
+    orders are timed, each as a HIP graph of repeated calls."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    name, m, n = linears[0]
+    X = torch.randn(T, n, device=dev, dtype=torch.bfloat16)
+    W = torch.randn(m, n, device=dev, dtype=torch.bfloat16)
+    reps = 50
+    out = []
+    for order, a, b in (("X W^T", X, W.t().contiguous()), ("W X^T", W, X.t().contiguous())):
+        C = torch.empty(a.shape[0], b.shape[1], device=dev, dtype=torch.bfloat16)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(3):
+                torch.matmul(a, b, out=C)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                torch.matmul(a, b, out=C)
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        tf = 2.0 * T * n * m / (us * 1e-6) / 1e12
+        out.append({"order": order, "us": round(us, 1), "TFLOP/s": round(tf, 1),
+                    "frac_bf16_peak": round(tf / BF16_MFMA_PEAK_TFLOPS, 4)})
+        del C, g
+    print(json.dumps({"metric": "library bf16 GEMM TFLOP/s", "kind": "comparison",
+                      "library": "torch.matmul (hipBLASLt), bf16 in and out, weights pre-unpacked",
+                      "workload": cfg["name"], "linear": [name, m, n], "T": T, "runs": out}),
+          flush=True)
 
 
 def cpu_baseline(args, cfg, lin, K, T, unit):
