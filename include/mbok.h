@@ -400,8 +400,9 @@ int mbok_gemvt(const mbok_desc* d, const void* packed, const void* g,
 
 /*
  * The same product for T tokens:  Y[t, i] = sum_j W_hat[i, j] * X[t, j].
- * T <= 16 runs the weight-streaming skinny kernel (exact fp32 scaling of
- * +-1 products).  T > 16 is the prefill GEMM: each tile of W_hat is formed
+ * T = 1 runs the decode kernel of mbok_gemv (without a workspace).  T = 2..16
+ * runs the weight-streaming few-token kernel (exact fp32 scaling of +-1
+ * products).  T > 16 is the prefill GEMM: each tile of W_hat is formed
  * as sum_k alpha_k * b_k in fp32, rounded to bf16 (nearest-even) in LDS, and
  * contracted with the bf16 X tile on the matrix cores with fp32 accumulation.
  *  X        device bf16 [T, ldx], ldx >= n, ldx % 8 == 0.
