@@ -218,12 +218,13 @@ def test_gemv_exact_regime(m, n, K, gemv_variant):
 
 
 # The streaming kernel walks 16-row tiles (up to 8 per persistent workgroup)
-# over column slabs of at most 64 groups, loading a slab's first tile during
-# the previous slab's last one.  These layers take two or three slabs with 1
-# to 4 tiles per workgroup (odd and even counts); K = 4 keeps one slab at a
-# time.  Sampled rows include the whole last row block.
+# over column slabs of at most 64 groups.  These layers take two or three
+# slabs with 1 to 4 tiles per workgroup (odd and even counts), or one slab
+# (n <= 4096) with 2 to 5 tiles per workgroup.  Sampled rows include the
+# whole last row block.
 @pytest.mark.parametrize("K,m,n", [(2, 4200, 8320), (3, 8400, 8320), (1, 12400, 16512),
-                                   (4, 4300, 8320)])
+                                   (4, 4300, 8320), (2, 12000, 4096), (3, 16384, 4096),
+                                   (3, 16400, 4096), (1, 5000, 2048)])
 def test_gemv_stream_slabs_exact(K, m, n):
     say(f"gemv stream slabs m={m} n={n} K={K}")
     S = syn.random_signs(K, m, n, seed=m + n + K)
