@@ -1,0 +1,97 @@
+"""Products enqueued on two streams at once.
+
+The library keeps no device state between calls: scratch memory is a
+workspace the caller passes in (the binding keeps one per stream), and the
+kernels use no atomics.  So the decode, transposed, few-token and prefill
+products enqueued on two streams at the same time must give the same bits as
+the same calls run one after another on one stream.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import boolean_weight_amd as bw
+import mbok_synth as syn
+from gpu_util import DEV, pack_on_gpu, say, x_to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    bw.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def _layer(K, m, n, seed):
+    S = syn.random_signs(K, m, n, seed=seed)
+    A = syn.exact_alpha(K, m, n // 128, seed=seed + 1).astype(np.float16)
+    return pack_on_gpu(S, A, "f16")
+
+
+def _jobs(tag):
+    """The calls of one stream: (name, output tensor, function enqueuing it)."""
+    seed = 700 if tag == "a" else 800
+    d1, p1 = _layer(2, 4096, 4096, seed)
+    d2, p2 = _layer(3, 1000, 2048, seed + 10)
+    x = x_to_dev(syn.activations(1, 4096, seed + 20, "bf16")[0], "bf16")
+    g = x_to_dev(syn.activations(1, 4096, seed + 21, "bf16")[0], "bf16")
+    X5 = x_to_dev(syn.activations(5, 2048, seed + 22, "bf16"), "bf16")
+    X300 = x_to_dev(syn.activations(300, 2048, seed + 23, "bf16"), "bf16")
+    y = torch.empty(4096, dtype=torch.float32, device=DEV)
+    dx = torch.empty(4096, dtype=torch.float32, device=DEV)
+    Y5 = torch.empty((5, 1000), dtype=torch.float32, device=DEV)
+    Y300 = torch.empty((300, 1000), dtype=torch.float32, device=DEV)
+    keep = (d1, p1, d2, p2, x, g, X5, X300)  # keep the inputs alive
+    return keep, [
+        ("gemv", y, lambda: bw.mbok_gemv(d1, p1, x, y)),
+        ("gemvt", dx, lambda: bw.mbok_gemvt(d1, p1, g, dx)),
+        ("gemm5", Y5, lambda: bw.mbok_gemm(d2, p2, X5, Y5)),
+        ("gemm300", Y300, lambda: bw.mbok_gemm(d2, p2, X300, Y300)),
+    ]
+
+
+@pytest.mark.parametrize("variant", ["stream", "split"])
+def test_two_streams_give_the_sequential_bits(variant):
+    say(f"two streams, decode variant {variant}")
+    old = os.environ.get("MBOK_GEMV_VARIANT")
+    os.environ["MBOK_GEMV_VARIANT"] = variant
+    try:
+        keep_a, jobs_a = _jobs("a")
+        keep_b, jobs_b = _jobs("b")
+        torch.cuda.synchronize()
+        # one after another on the current stream
+        want = {}
+        for tag, jobs in (("a", jobs_a), ("b", jobs_b)):
+            for name, out, fn in jobs:
+                out.fill_(-1.0)
+                fn()
+                torch.cuda.synchronize()
+                want[(tag, name)] = out.clone()
+        # both streams at once, several rounds, calls interleaved on the host
+        s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+        for rnd in range(3):
+            for _, out, _ in jobs_a + jobs_b:
+                out.fill_(-2.0)
+            s1.wait_stream(torch.cuda.current_stream())
+            s2.wait_stream(torch.cuda.current_stream())
+            for (_, _, fa), (_, _, fb) in zip(jobs_a, jobs_b):
+                with torch.cuda.stream(s1):
+                    fa()
+                with torch.cuda.stream(s2):
+                    fb()
+            torch.cuda.synchronize()
+            for tag, jobs in (("a", jobs_a), ("b", jobs_b)):
+                for name, out, _ in jobs:
+                    assert torch.equal(out, want[(tag, name)]), (rnd, tag, name)
+        del keep_a, keep_b
+    finally:
+        if old is None:
+            os.environ.pop("MBOK_GEMV_VARIANT", None)
+        else:
+            os.environ["MBOK_GEMV_VARIANT"] = old
