@@ -188,6 +188,23 @@ def test_compute_calls_validate_before_launch(lib):
     assert lib.mbok_gemv(None, A16, A16, bw.MBOK_BF16, A16, None, None) == -1
 
 
+def test_missing_library_fails_loudly(tmp_path):
+    """Without the built HIP library the binding raises; there is no CPU path."""
+    import sys
+    code = ("import boolean_weight_amd as bw\n"
+            "try:\n"
+            "    bw.load_library()\n"
+            "except RuntimeError as e:\n"
+            "    print('RAISED', e)\n"
+            "else:\n"
+            "    print('LOADED')\n")
+    env = dict(os.environ, MBOK_LIBRARY=str(tmp_path / "absent" / "libmbok.so"))
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert "RAISED" in r.stdout and "not built" in r.stdout, r.stdout
+
+
 def test_binding_refuses_host_tensors():
     import torch
     d = bw.mbok_desc_init(64, 256, 2, bw.MBOK_F16)
