@@ -33,7 +33,9 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 2000; with --quantizer, timed calls per "
+                         "kernel, default 5)")
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--K", type=int, default=None, help="override the workload's K")
@@ -220,6 +222,8 @@ def summarize(args):
 
 def main():
     args = parse()
+    if args.steps is None:
+        args.steps = 5 if args.quantizer else 2000
     if args.summarize:
         summarize(args)
         return
@@ -603,6 +607,7 @@ def quantizer_bench(args, cfg, linears, K, adt, abytes):
                         "frac_hbm": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)})
         del W, signs, alpha, packed, s0, a0
         torch.cuda.empty_cache()
+        print(f"quantizer bench: {name} {m}x{n} done", file=sys.stderr, flush=True)
     print(json.dumps({"metric": "setup kernel time", "unit": "us", "workload": cfg["name"],
                       "K": K, "refit_rounds": args.refit_rounds, "reps": reps,
                       "alpha_dtype": cfg["alpha_dtype"], "kernels": out}), flush=True)
