@@ -394,9 +394,13 @@ __device__ __forceinline__ void mfma8_tile(const uint32_t* __restrict__ bits,
   const int n0 = (tile % ntx) * BN + half * (BN / 2);
   const int S = G * 2;  // steps of 64 columns
 
-  // unpack role: row n0 + tid/2, columns 32 * (tid % 2) .. + 31 of each step
-  const int urow = tid >> 1, uhalf = tid & 1;
-  const bool unpacker = JB == 2 || urow < tile_rows;  // uniform per wavefront
+  // unpack role: TPR threads per row, each 64 / TPR columns of a step (a
+  // whole tile: row n0 + tid/2, columns 32 (tid % 2) ..; a half tile: row
+  // n0 + tid/4, columns 16 (tid % 4) .., so that every wavefront unpacks)
+  constexpr int TPR = JB == 2 ? 2 : 4;
+  static_assert(GEMM8_THREADS / TPR == tile_rows, "one row per TPR threads");
+  const int urow = tid / TPR, upart = tid % TPR;
+  const int uword = JB == 2 ? upart : upart >> 1;  // 32-column word of the step
   const int row = n0 + urow;
   const int rowc = row < m_pad ? row : m_pad - 1;
   const uint32_t row_chunk = (uint32_t)(rowc / kRowBlock) * (uint32_t)(G * K * kRowBlock) +
@@ -428,7 +432,7 @@ __device__ __forceinline__ void mfma8_tile(const uint32_t* __restrict__ bits,
   StepRegs R0, R1;
   auto load_step = [&](int s, StepRegs& R) {
     const int g = s >> 1;
-    const uint32_t word = 2 * (s & 1) + uhalf;
+    const uint32_t word = 2 * (s & 1) + uword;
 #pragma unroll
     for (int j = 0; j < 4; ++j) R.x[j] = *reinterpret_cast<const u32x4*>(X + xoff[j] + s * BK);
 #pragma unroll
@@ -461,7 +465,7 @@ __device__ __forceinline__ void mfma8_tile(const uint32_t* __restrict__ bits,
         smem + (2 * cb + 1) * TILE_ELEMS + (wn * 32 * JB + lrow) * LDS_STRIDE + lk;
     uint16_t* xd = smem + 2 * (cb ^ 1) * TILE_ELEMS + (tid >> 3) * LDS_STRIDE + xpart * 8;
     uint4* wd = reinterpret_cast<uint4*>(smem + (2 * (cb ^ 1) + 1) * TILE_ELEMS +
-                                         urow * LDS_STRIDE + uhalf * 32);
+                                         urow * LDS_STRIDE + upart * (64 / TPR));
     uint32_t V[4];
     if (K <= 3) word_selectors<K>(R.w, V);
     // fragments of sub-step kk + 1 are read while the MFMAs of kk run
@@ -493,19 +497,29 @@ __device__ __forceinline__ void mfma8_tile(const uint32_t* __restrict__ bits,
       }
       // a quarter of the next step: one activation segment, 8 weight columns
       *reinterpret_cast<u32x4*>(xd + kk * 64 * LDS_STRIDE) = R.x[kk];
-      uint32_t out[4];
-      if (K <= 3) {
-        unpack_two_quads(V, kk >> 1, 2 * (kk & 1), L, out);
-      } else {
-        uint32_t o32[16];
-        float af[K];
-        scales_f32(R, af);
-        unpack_word_k4(R.w, af, o32);
-        // columns 8 kk .. 8 kk + 7 are quads 2 kk, 2 kk + 1
+      // 8 weight columns per sub-step (a half tile: in the first two only).
+      // The thread's 8-column piece of its word is kk (a whole tile), or
+      // 2 h + kk with h = upart % 2 (a half tile); piece q is quads 2q, 2q+1.
+      // Register arrays are indexed with constants only (h selects).
+      if (JB == 2 || kk < 2) {
+        const bool h = (upart & 1) != 0;
+        uint32_t out[4];
+        if (K <= 3) {
+          if (JB == 2)
+            unpack_two_quads(V, kk >> 1, 2 * (kk & 1), L, out);
+          else
+            unpack_two_quads(V, h, 2 * kk, L, out);
+        } else {
+          uint32_t o32[16];
+          float af[K];
+          scales_f32(R, af);
+          unpack_word_k4(R.w, af, o32);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) out[q] = o32[4 * kk + q];
+          for (int e = 0; e < 4; ++e)
+            out[e] = JB == 2 ? o32[4 * kk + e] : (h ? o32[8 + 4 * kk + e] : o32[4 * kk + e]);
+        }
+        wd[kk] = make_uint4(out[0], out[1], out[2], out[3]);
       }
-      if (unpacker) wd[kk] = make_uint4(out[0], out[1], out[2], out[3]);
     }
   };
 
@@ -520,16 +534,26 @@ __device__ __forceinline__ void mfma8_tile(const uint32_t* __restrict__ bits,
     for (int j = 0; j < 4; ++j)
       *reinterpret_cast<u32x4*>(smem + (tid >> 3) * LDS_STRIDE + xpart * 8 + j * 64 * LDS_STRIDE) =
           R0.x[j];
-    if (unpacker) {
-      uint4* wd = reinterpret_cast<uint4*>(smem + TILE_ELEMS + urow * LDS_STRIDE + uhalf * 32);
+    {
+      uint4* wd = reinterpret_cast<uint4*>(smem + TILE_ELEMS + urow * LDS_STRIDE +
+                                           upart * (64 / TPR));
       uint32_t out[16];
       if (K <= 3)
         unpack_word<K>(R0.w, L, out);
       else
         unpack_word_k4(R0.w, af0, out);
+      // out[4 p .. 4 p + 3]: 8-column piece p of the word (a half tile's
+      // thread takes pieces 2 h, 2 h + 1; constant indices, h selects)
+      constexpr int NP = 4 / (TPR / 2);  // pieces per thread: 4 or 2
+      const bool h = (upart & 1) != 0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        wd[j] = make_uint4(out[4 * j], out[4 * j + 1], out[4 * j + 2], out[4 * j + 3]);
+      for (int j = 0; j < NP; ++j) {
+        uint32_t o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          o[e] = JB == 2 ? out[4 * j + e] : (h ? out[8 + 4 * j + e] : out[4 * j + e]);
+        wd[j] = make_uint4(o[0], o[1], o[2], o[3]);
+      }
     }
   }
   __syncthreads();
