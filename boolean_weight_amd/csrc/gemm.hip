@@ -389,7 +389,12 @@ __device__ __forceinline__ void mfma8_tile(const uint32_t* __restrict__ bits,
   const int lane = tid & 63;
   const int wave = tid >> 6;
   constexpr int tile_rows = JB == 2 ? BN : BN / 2;
-  const int wt = wave & 1, wn = wave >> 1;  // 128-token half, row quarter
+  // wavefront tile: TI blocks of 32 tokens x TJ blocks of 32 rows; a whole
+  // tile takes 2 x 4 wavefronts of 128 x 64, a half tile 4 x 2 of 64 x 64
+  // (4 fragment reads per 4 MFMAs instead of 5 for 128 x 32)
+  constexpr int TI = JB == 2 ? 4 : 2, TJ = 2;
+  const int wt = JB == 2 ? (wave & 1) : (wave & 3);    // token block of the wavefront
+  const int wn = JB == 2 ? (wave >> 1) : (wave >> 2);  // row block of the wavefront
   const int t0 = (tile / ntx) * BT;
   const int n0 = (tile % ntx) * BN + half * (BN / 2);
   const int S = G * 2;  // steps of 64 columns
@@ -442,11 +447,11 @@ __device__ __forceinline__ void mfma8_tile(const uint32_t* __restrict__ bits,
       R.a[k] = scales[ch];
     }
   };
-  f32x16 acc[4][2];
+  f32x16 acc[TI][TJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < TJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
@@ -460,41 +465,41 @@ __device__ __forceinline__ void mfma8_tile(const uint32_t* __restrict__ bits,
       scales_f32(R, af);
       L = make_levels<K>(af);
     }
-    const uint16_t* xs = smem + 2 * cb * TILE_ELEMS + (wt * 128 + lrow) * LDS_STRIDE + lk;
+    const uint16_t* xs =
+        smem + 2 * cb * TILE_ELEMS + (wt * 32 * TI + lrow) * LDS_STRIDE + lk;
     const uint16_t* ws =
-        smem + (2 * cb + 1) * TILE_ELEMS + (wn * 32 * JB + lrow) * LDS_STRIDE + lk;
+        smem + (2 * cb + 1) * TILE_ELEMS + (wn * 32 * TJ + lrow) * LDS_STRIDE + lk;
     uint16_t* xd = smem + 2 * (cb ^ 1) * TILE_ELEMS + (tid >> 3) * LDS_STRIDE + xpart * 8;
     uint4* wd = reinterpret_cast<uint4*>(smem + (2 * (cb ^ 1) + 1) * TILE_ELEMS +
                                          urow * LDS_STRIDE + upart * (64 / TPR));
     uint32_t V[4];
     if (K <= 3) word_selectors<K>(R.w, V);
     // fragments of sub-step kk + 1 are read while the MFMAs of kk run
-    bf16x8 pa[2][4], pb[2][2];
+    bf16x8 pa[2][TI], pb[2][TJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pa[0][i] = *reinterpret_cast<const bf16x8*>(xs + i * 32 * LDS_STRIDE);
-    pb[0][0] = *reinterpret_cast<const bf16x8*>(ws);
-    if (JB == 2) pb[0][1] = *reinterpret_cast<const bf16x8*>(ws + 32 * LDS_STRIDE);
+    for (int i = 0; i < TI; ++i)
+      pa[0][i] = *reinterpret_cast<const bf16x8*>(xs + i * 32 * LDS_STRIDE);
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+      pb[0][j] = *reinterpret_cast<const bf16x8*>(ws + j * 32 * LDS_STRIDE);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       if (kk < 3) {
         const int nb = (kk + 1) & 1;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < TI; ++i)
           pa[nb][i] = *reinterpret_cast<const bf16x8*>(xs + i * 32 * LDS_STRIDE + 16 * (kk + 1));
-        pb[nb][0] = *reinterpret_cast<const bf16x8*>(ws + 16 * (kk + 1));
-        if (JB == 2)
-          pb[nb][1] = *reinterpret_cast<const bf16x8*>(ws + 32 * LDS_STRIDE + 16 * (kk + 1));
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+          pb[nb][j] = *reinterpret_cast<const bf16x8*>(ws + j * 32 * LDS_STRIDE + 16 * (kk + 1));
       }
       const bf16x8* av = pa[kk & 1];
       const bf16x8* bv = pb[kk & 1];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[0], acc[i][0], 0, 0, 0);
-      if (JB == 2) {
+      for (int j = 0; j < TJ; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[1], acc[i][1], 0, 0, 0);
-      }
+        for (int i = 0; i < TI; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
       // a quarter of the next step: one activation segment, 8 weight columns
       *reinterpret_cast<u32x4*>(xd + kk * 64 * LDS_STRIDE) = R.x[kk];
       // 8 weight columns per sub-step (a half tile: in the first two only).
@@ -570,14 +575,14 @@ __device__ __forceinline__ void mfma8_tile(const uint32_t* __restrict__ bits,
 
   // C layout: lane l, register r -> token 8(r/4) + 4(l/32) + r%4, row l%32
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < JB; ++j) {
-      const int n = n0 + wn * 32 * JB + j * 32 + lrow;
+    for (int j = 0; j < TJ; ++j) {
+      const int n = n0 + wn * 32 * TJ + j * 32 + lrow;
       if (n >= m) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int t = t0 + wt * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int t = t0 + wt * 32 * TI + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         if (t < T) Y[(int64_t)t * ldy + n] = acc[i][j][r];
       }
     }
