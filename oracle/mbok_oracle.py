@@ -276,19 +276,27 @@ def allocate_kernels(errors, sizes, budget: int, kmax: int):
     return None if best is None else tuple(best[1])
 
 
-def _top_singular(M: np.ndarray):
+# Matrices with at most this many entries take the dense LAPACK SVD; larger
+# ones take ARPACK.  Read at call time, so a pin can lower it and drive the
+# ARPACK branch on a small matrix.
+DENSE_SVD_LIMIT = 1 << 22
+
+
+def _top_singular(M: np.ndarray, dense_limit: int | None = None):
     """Largest singular value of a nonnegative float64 matrix M and its unit
     singular vectors (u, v), signed so that each sums to >= 0.  A library
-    SVD: numpy's dense LAPACK SVD up to 2^22 entries, above that scipy's
-    ARPACK (scipy.sparse.linalg.svds, one triple, tol=0, a start vector of
-    ones, so the result is reproducible)."""
-    if M.size <= (1 << 22):
+    SVD: numpy's dense LAPACK SVD up to `dense_limit` entries (default
+    DENSE_SVD_LIMIT), above that scipy's ARPACK (scipy.sparse.linalg.svds,
+    one triple, tol=0, a start vector of ones, so the result is
+    reproducible)."""
+    limit = DENSE_SVD_LIMIT if dense_limit is None else dense_limit
+    if M.size <= limit:
         U, sv, Vt = np.linalg.svd(M, full_matrices=False)
         sigma, u, v = float(sv[0]), U[:, 0], Vt[0]
     else:
         from scipy.sparse.linalg import svds
-        U, sv, Vt = svds(M, k=1, tol=0, v0=np.ones(min(M.shape)))
-        sigma, u, v = float(sv[0]), U[:, 0], Vt[0]
+        Ua, sa, Vta = svds(M, k=1, tol=0, v0=np.ones(min(M.shape)))
+        sigma, u, v = float(sa[0]), Ua[:, 0], Vta[0, :]
     if u.sum() < 0:
         u = -u
     if v.sum() < 0:
@@ -415,15 +423,6 @@ def bound_transposed(S: np.ndarray, A: np.ndarray, Gr: np.ndarray,
     return E[0] if one else E
 
 
-def product_rows(S: np.ndarray, A: np.ndarray, X: np.ndarray, rows,
-                 group: int = GROUP):
-    """Y[:, rows] and E[:, rows] for a subset of output rows only, so that very
-    large layers can be checked on sampled outputs."""
-    rows = np.asarray(rows)
-    return (product(S[:, rows], A[:, rows], X, group),
-            bound(S[:, rows], A[:, rows], X, group))
-
-
 def product_fraction(S: np.ndarray, A: np.ndarray, X: np.ndarray,
                      group: int = GROUP):
     """Exact rational Y[t][i] by the triple loop (tiny shapes only)."""
@@ -447,9 +446,17 @@ def product_fraction(S: np.ndarray, A: np.ndarray, X: np.ndarray,
 
 
 def max_error_ratio(Y_dev: np.ndarray, Y_ref: np.ndarray, E: np.ndarray) -> float:
-    """max |Y_dev - Y_ref| / E (entries with E == 0 must match exactly)."""
+    """The acceptance figure of the tolerance: max over entries of
+    |Y_dev - Y_ref| / E, where E is the bound sum_j |W_hat_ij| |x_j|; a result
+    is accepted when this is at most 1e-3.  An entry with E == 0 must match
+    exactly (+0 equals -0), else the figure is inf; a non-finite difference
+    (NaN or inf in Y_dev) satisfies no bound and also gives inf."""
     Y_dev = np.asarray(Y_dev, dtype=np.float64)
+    Y_ref = np.asarray(Y_ref, dtype=np.float64)
+    E = np.asarray(E, dtype=np.float64)
     diff = np.abs(Y_dev - Y_ref)
+    if not np.all(np.isfinite(diff)):
+        return math.inf
     zero = E == 0
     if np.any(diff[zero] != 0):
         return math.inf

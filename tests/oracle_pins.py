@@ -64,7 +64,10 @@ def read_golden(name: str = "hand_worked.txt"):
                 cur = out.setdefault(line.strip("[]"), {})
                 continue
             key, val = (s.strip() for s in line.split("=", 1))
-            cur[key] = [float(v) for v in val.split()]
+            if "|" in val:
+                cur[key] = [[float(v) for v in r.split()] for r in val.split("|")]
+            else:
+                cur[key] = [float(v) for v in val.split()]
     return out
 
 
@@ -388,6 +391,58 @@ def pin_bound(o):
     for i in range(m):
         w = sum(float(A[k, i, 1]) * int(S[k, i, 130]) for k in range(K))
         assert e[i] == 2.0 * abs(w)
+
+
+def pin_error_ratio_hand_worked(o):
+    """The tolerance's acceptance figure on the hand-worked cases of
+    tests/golden/error_ratio.txt: the largest |y_dev - y_ref| / E, exact
+    equality required where E = 0, and inf for a mismatch there or for a
+    non-finite result."""
+    cases = read_golden("error_ratio.txt")
+    assert sorted(cases) == ["A", "B", "C", "D", "E", "F"]
+    for name, c in cases.items():
+        got = o.max_error_ratio(np.array(c["y_dev"]), np.array(c["y_ref"]), np.array(c["E"]))
+        want = c["figure"][0]
+        if np.isinf(want):
+            assert got == np.inf, (name, got)
+        else:
+            assert got == want, (name, got, want)
+
+
+def pin_error_ratio_decides_tolerance(o):
+    """Against the tolerance written out element by element: a device result
+    made from the reference plus a perturbation of exactly r * E (r drawn per
+    entry, either sign) has figure max(r); the figure is <= 1e-3 exactly when
+    every entry meets |diff| <= 1e-3 E; scaling y_dev - y_ref and E together
+    leaves it unchanged."""
+    rng = np.random.default_rng(27)
+    for _ in range(20):
+        T, m = rng.integers(1, 4), rng.integers(1, 40)
+        E = rng.uniform(0.5, 4.0, size=(T, m)).round(3)
+        E[rng.random(size=(T, m)) < 0.2] = 0.0
+        Y_ref = rng.normal(size=(T, m)).round(3)
+        r = rng.uniform(0.0, 2e-3, size=(T, m))
+        sgn = rng.choice([-1.0, 1.0], size=(T, m))
+        # powers of two keep Y_ref + sgn r E - Y_ref = sgn r E exact
+        E = np.ldexp(1.0, np.round(np.log2(np.maximum(E, 1e-9))).astype(int)) * (E > 0)
+        r = np.ldexp(np.floor(r * 2.0 ** 20), -20)
+        Y_ref = np.ldexp(np.round(Y_ref * 2.0 ** 10), -10)
+        Y_dev = Y_ref + sgn * r * E
+        got = o.max_error_ratio(Y_dev, Y_ref, E)
+        pos = E > 0
+        want = float(np.max(r[pos])) if np.any(pos) else 0.0
+        assert got == want, (got, want)
+        ok = all(abs(Y_dev[t, i] - Y_ref[t, i]) <= 1e-3 * E[t, i]
+                 for t in range(T) for i in range(m))
+        assert (got <= 1e-3) == ok
+        assert o.max_error_ratio(Y_ref + 4 * (Y_dev - Y_ref), Y_ref, 4 * E) == got
+    # a single bad entry anywhere is found
+    Y_ref = np.zeros((3, 50))
+    E = np.ones((3, 50))
+    for t, i in ((0, 0), (2, 49), (1, 17)):
+        Y_dev = Y_ref.copy()
+        Y_dev[t, i] = -0.5
+        assert o.max_error_ratio(Y_dev, Y_ref, E) == 0.5
 
 
 # ----------------------------------------------------------------- layout
@@ -926,6 +981,32 @@ def _power_top(M, iters=200):
     return float(np.linalg.norm(M @ v))
 
 
+def pin_top_singular_arpack(o):
+    """The iterative (ARPACK) branch of the library SVD, forced on small
+    matrices by a size limit of 0, agrees with the dense LAPACK branch and
+    with a plain power iteration: sigma to 1e-12, the unit vectors to 1e-9,
+    both signed to a nonnegative sum; the exact rank-1 SVID recovery (V1)
+    holds through that branch too."""
+    rng = np.random.default_rng(74)
+    for shape in ((120, 300), (300, 120), (64, 64)):
+        M = np.abs(rng.normal(size=shape))
+        s_it, u_it, v_it = o._top_singular(M, dense_limit=0)
+        s_de, u_de, v_de = o._top_singular(M, dense_limit=M.size)
+        assert u_it.shape == (shape[0],) and v_it.shape == (shape[1],)
+        assert abs(s_it - s_de) <= 1e-12 * s_de
+        assert abs(s_it - _power_top(M)) <= 1e-10 * s_de
+        assert np.max(np.abs(u_it - u_de)) <= 1e-9 and np.max(np.abs(v_it - v_de)) <= 1e-9
+        assert u_it.sum() >= 0 and v_it.sum() >= 0
+        assert abs(np.linalg.norm(M @ v_it) - s_de) <= 1e-10 * s_de
+        assert np.max(np.abs(M.T @ u_it - s_de * v_it)) <= 1e-9 * s_de
+    saved = o.DENSE_SVD_LIMIT
+    try:
+        o.DENSE_SVD_LIMIT = 0
+        pin_svid_exact_rank1(o)
+    finally:
+        o.DENSE_SVD_LIMIT = saved
+
+
 def pin_svid_eckart_young(o):
     """V2: the sign-value split makes W - S (.) (s_out s_in^T) = S (.) (|W| -
     s_out s_in^T), so with the rank-1 SVD of |W| the residual energy is
@@ -970,6 +1051,7 @@ ALL_PINS = [
     pin_residual_chain, pin_levels, pin_single_kernel_textbook, pin_constructed_walsh,
     pin_exhaustive_search, pin_gaussian_statistics, pin_integer_matmul,
     pin_fraction_bruteforce, pin_one_hot_and_all_ones, pin_linearity, pin_bound,
+    pin_error_ratio_hand_worked, pin_error_ratio_decides_tolerance,
     pin_pack_roundtrip, pin_layout_single_bit,
     pin_refit_hand_worked, pin_refit_scale_step, pin_refit_sign_step, pin_refit_ties,
     pin_refit_single_kernel, pin_refit_walsh_fixed_point, pin_refit_singular_gram,
@@ -979,4 +1061,5 @@ ALL_PINS = [
     pin_allocation_monotone,
     pin_transposed_integer, pin_transposed_adjoint,
     pin_svid_exact_rank1, pin_svid_eckart_young, pin_svid_product_grouped,
+    pin_top_singular_arpack,
 ]

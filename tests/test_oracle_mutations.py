@@ -126,6 +126,27 @@ MUTATIONS = [
      "R = R - Sk.astype(np.float64) * outer", "R = R"),
     ("svid_product_transposed_scales", "svid_dequantize",
      "SO[k].astype(np.float64)[:, None] *", "SO[k].astype(np.float64)[::-1, None] *"),
+    ("error_ratio_min_for_max", "max_error_ratio",
+     "return float(np.max(diff[~zero] / E[~zero]))", "return float(np.min(diff[~zero] / E[~zero]))"),
+    ("error_ratio_abs_dropped", "max_error_ratio",
+     "diff = np.abs(Y_dev - Y_ref)", "diff = Y_dev - Y_ref"),
+    ("error_ratio_zero_bound_unchecked", "max_error_ratio",
+     "if np.any(diff[zero] != 0):", "if False:"),
+    ("error_ratio_zero_mask_dropped", "max_error_ratio",
+     "zero = E == 0", "zero = E < 0"),
+    ("error_ratio_relative_to_reference", "max_error_ratio",
+     "return float(np.max(diff[~zero] / E[~zero]))",
+     "return float(np.max(diff[~zero] / np.abs(Y_ref[~zero])))"),
+    ("error_ratio_nan_passes", "max_error_ratio",
+     "if not np.all(np.isfinite(diff)):", "if False:"),
+    ("error_ratio_first_row_only", "max_error_ratio",
+     "diff = np.abs(Y_dev - Y_ref)", "diff = np.abs(Y_dev - Y_ref); diff[..., 1:] = 0"),
+    ("arpack_vectors_swapped", "_top_singular",
+     "sigma, u, v = float(sa[0]), Ua[:, 0], Vta[0, :]", "sigma, u, v = float(sa[0]), Vta[0, :], Ua[:, 0]"),
+    ("arpack_of_transpose", "_top_singular",
+     "svds(M, k=1", "svds(M.T, k=1"),
+    ("arpack_smallest_triple", "_top_singular",
+     "svds(M, k=1, tol=0,", "svds(M, k=1, which='SM', tol=0,"),
 ]
 
 
