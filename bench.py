@@ -253,8 +253,7 @@ def main():
     linears = cfg["linears"]
     if args.config == 4:
         # q|k|v and gate|up share their input: one fused launch each
-        linears = [("qkv_proj", 3 * 5120, 5120), ("o_proj", 5120, 5120),
-                   ("gate_up_proj", 2 * 13824, 5120), ("down_proj", 5120, 13824)]
+        linears = list(syn.LAYER_STREAM_13B)
     if args.config == 3:
         linears = linears[:1] if T == 1 else linears
     if args.svid and (T != 1 or args.transposed or args.avg_k is not None):

@@ -44,6 +44,14 @@ WORKLOADS = {
 }
 
 
+# The LLaMA-13B-shaped layer as it runs per token: q|k|v and gate|up share
+# their input and run as one launch each (rows stacked), then o and down.
+# Launch li draws its weight from weight_seed(4, li) and its activations from
+# act_seed(4, li).
+LAYER_STREAM_13B = [("qkv_proj", 3 * 5120, 5120), ("o_proj", 5120, 5120),
+                    ("gate_up_proj", 2 * 13824, 5120), ("down_proj", 5120, 13824)]
+
+
 def weight_seed(config: int, layer: int = 0) -> int:
     return 1000 + 10 * config + layer
 

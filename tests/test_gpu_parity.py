@@ -403,18 +403,19 @@ def test_gemm_skinny_matches_fp64_closely():
     assert ratio <= 1e-2 * TOL, ratio
 
 
+@pytest.mark.parametrize("K", [1, 2, 3])
 @pytest.mark.parametrize("T", [4, 16])
-def test_gemm_config3_tolerance(T):
+def test_gemm_config3_tolerance(T, K):
     w = syn.WORKLOADS[3]
     for li, (name, m, n) in enumerate(w["linears"]):
-        say(f"gemm config 3 {name} T={T}")
+        say(f"gemm config 3 {name} T={T} K={K}")
         W = syn.weight(m, n, syn.weight_seed(3, li))
         X = syn.activations(T, n, syn.act_seed(3, li), "bf16")
-        d, signs, alpha, packed, flag = quantize_on_gpu(W, 3, "f16")
+        d, signs, alpha, packed, flag = quantize_on_gpu(W, K, "f16")
         del signs, alpha
         Y = gemm(d, packed, X)
         rows = sample_rows(m, 24, li)
-        S, A, _ = oracle.residual_binarize(W[rows], 3, alpha_dtype="f16")
+        S, A, _ = oracle.residual_binarize(W[rows], K, alpha_dtype="f16")
         ratio = oracle.max_error_ratio(Y[:, rows], oracle.product(S, A, X), oracle.bound(S, A, X))
         assert ratio <= TOL, (name, ratio)
 
@@ -559,3 +560,22 @@ def test_gemm_prefill_config5_tolerance(prefill_waves):
     # determinism
     Y2 = gemm(d, packed, X)
     assert np.array_equal(Y, Y2)
+
+
+@pytest.mark.parametrize("K", [1, 2])
+def test_gemm_prefill_config5_k_sweep(K):
+    """Config 5's shape (11008 x 4096, 2048 tokens) with K = 1 and 2 kernels
+    through the default prefill kernel; sampled rows for every token."""
+    w = syn.WORKLOADS[5]
+    name, m, n = w["linears"][0]
+    T = w["T"][0]
+    say(f"gemm config 5 {m}x{n} T={T} K={K}")
+    W = syn.weight(m, n, syn.weight_seed(5))
+    X = syn.activations(T, n, syn.act_seed(5), "bf16")
+    d, signs, alpha, packed, flag = quantize_on_gpu(W, K, "f16")
+    del signs, alpha
+    Y = gemm(d, packed, X)
+    rows = sample_rows(m, 24, 50 + K)
+    S, A, _ = oracle.residual_binarize(W[rows], K, alpha_dtype="f16")
+    ratio = oracle.max_error_ratio(Y[:, rows], oracle.product(S, A, X), oracle.bound(S, A, X))
+    assert ratio <= TOL, ratio
