@@ -20,7 +20,7 @@ __all__ = [
     "mbok_desc_init", "mbok_packed_bytes", "mbok_alpha_bytes", "mbok_residual_binarize",
     "mbok_refit", "MBOK_MAX_REFIT_ROUNDS", "mbok_residual_energy", "mbok_allocate_kernels",
     "mbok_pack", "mbok_gemv", "mbok_gemv_workspace_bytes", "mbok_gemm", "mbok_status_str",
-    "mbok_gemvt", "mbok_gemvt_workspace_bytes",
+    "mbok_gemvt", "mbok_gemvt_workspace_bytes", "mbok_gemvt_noalloc", "mbok_gemvt_scratch_bytes",
     "mbok_svid_workspace_bytes", "mbok_svid_decompose", "mbok_svid_pack",
     "mbok_svid_gemv_workspace_bytes", "mbok_svid_gemv", "MBOK_MAX_SVID_ITERS",
     "mbok_version", "workspace_for",
@@ -86,6 +86,8 @@ def load_library() -> ctypes.CDLL:
         "mbok_gemm": (ctypes.c_int, [D, P, P, I32, I64, I64, P, I64, P]),
         "mbok_gemvt_workspace_bytes": (SZ, [D]),
         "mbok_gemvt": (ctypes.c_int, [D, P, P, I32, P, P, P]),
+        "mbok_gemvt_scratch_bytes": (SZ, []),
+        "mbok_gemvt_noalloc": (ctypes.c_int, [D, P, P, I32, P, P]),
         "mbok_svid_workspace_bytes": (SZ, [D]),
         "mbok_svid_decompose": (ctypes.c_int, [D, P, I64, P, P, P, I32, P, P]),
         "mbok_svid_pack": (ctypes.c_int, [D, P, P, P, P]),
@@ -350,6 +352,28 @@ def mbok_gemvt(d: mbok_desc, packed: torch.Tensor, g: torch.Tensor, dx: torch.Te
         wptr = workspace.data_ptr()
     _check(load_library().mbok_gemvt(ctypes.byref(d), packed.data_ptr(), g.data_ptr(), gd,
                                      dx.data_ptr(), wptr, _stream(stream)), "mbok_gemvt")
+
+
+def mbok_gemvt_scratch_bytes() -> int:
+    return int(load_library().mbok_gemvt_scratch_bytes())
+
+
+def mbok_gemvt_noalloc(d: mbok_desc, packed: torch.Tensor, g: torch.Tensor, dx: torch.Tensor,
+                       stream=None) -> None:
+    """mbok_gemvt with the library's static scratch instead of a workspace
+    (for callers that cannot allocate device memory).  Calls that overlap in
+    time on one GPU share that scratch and race."""
+    _dev(packed, "packed"), _dev(g, "g"), _dev(dx, "dx")
+    if _nbytes_from(packed) < mbok_packed_bytes(d):
+        raise ValueError("packed buffer too small")
+    gd = _x_dtype(g)
+    if g.numel() < d.m or not g.is_contiguous():
+        raise ValueError("g must be contiguous with m elements")
+    if dx.dtype != torch.float32 or dx.numel() < d.n or not dx.is_contiguous():
+        raise ValueError("dx must be contiguous float32 with n elements")
+    _check(load_library().mbok_gemvt_noalloc(ctypes.byref(d), packed.data_ptr(), g.data_ptr(),
+                                             gd, dx.data_ptr(), _stream(stream)),
+           "mbok_gemvt_noalloc")
 
 
 def mbok_svid_workspace_bytes(d: mbok_desc) -> int:

@@ -27,6 +27,8 @@
 // wavefronts (slices) of a workgroup in order; with several workgroups per
 // column group each writes its 128 partial sums to the workspace and a
 // second kernel adds them in order.
+#include <mutex>
+
 #include "mbok_exact.h"
 #include "mbok_launch.h"
 
@@ -237,7 +239,46 @@ int launch_t(const Geom& geo, const void* packed, const void* grad, float* dx, v
   return MBOK_OK;
 }
 
+// Scratch of mbok_gemvt_noalloc: the slices' partial column sums, in a
+// file-scope device array instead of a caller workspace.  Every shape the
+// descriptor accepts needs at most 523,264 bytes here (n = 65408: 2 slice
+// groups x 65408 columns x 4 bytes), so 512 KiB covers all of them.  Each
+// device holds its own copy until the process ends; host code reaches it only
+// through the address hipGetSymbolAddress returns for the current device.
+constexpr size_t kScratchBytes = size_t(512) << 10;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch`, looked up once per device.
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MBOK_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MBOK_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MBOK_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MBOK_OK;
+}
+
 }  // namespace
+
+size_t gemvt_scratch_bytes() { return kScratchBytes; }
+
+int launch_gemvt_noalloc(const mbok_desc* d, const void* packed, const void* grad,
+                         int32_t g_dtype, float* dx, hipStream_t stream) {
+  if (gemvt_workspace_bytes(d) > kScratchBytes) return MBOK_ERR_SCRATCH;
+  void* ws = nullptr;
+  const int st = scratch_address(&ws);
+  if (st != MBOK_OK) return st;
+  return launch_gemvt(d, packed, grad, g_dtype, dx, ws, stream);
+}
 
 size_t gemvt_workspace_bytes(const mbok_desc* d) {
   const Geom geo = make_geom(d);

@@ -195,6 +195,19 @@ int mbok_gemvt(const mbok_desc* d, const void* packed, const void* g, int32_t g_
   return mbok::launch_gemvt(d, packed, g, g_dtype, dx, workspace, (hipStream_t)stream);
 }
 
+size_t mbok_gemvt_scratch_bytes(void) { return mbok::gemvt_scratch_bytes(); }
+
+int mbok_gemvt_noalloc(const mbok_desc* d, const void* packed, const void* g, int32_t g_dtype,
+                       float* dx, void* stream) {
+  int st = check_desc(d);
+  if (st != MBOK_OK) return st;
+  if (!packed || !g || !dx) return MBOK_ERR_INVALID_ARG;
+  if (g_dtype != MBOK_BF16 && g_dtype != MBOK_F32) return MBOK_ERR_DTYPE;
+  if (!aligned(packed, 16) || !aligned(g, g_dtype == MBOK_BF16 ? 2 : 4) || !aligned(dx, 4))
+    return MBOK_ERR_ALIGN;
+  return mbok::launch_gemvt_noalloc(d, packed, g, g_dtype, dx, (hipStream_t)stream);
+}
+
 int mbok_gemm(const mbok_desc* d, const void* packed, const void* X, int32_t x_dtype, int64_t T,
               int64_t ldx, float* Y, int64_t ldy, void* stream) {
   int st = check_desc(d);
@@ -218,6 +231,7 @@ const char* mbok_status_str(int status) {
     case MBOK_ERR_HIP: return "MBOK_ERR_HIP: the HIP runtime rejected a launch";
     case MBOK_ERR_UNSUPPORTED: return "MBOK_ERR_UNSUPPORTED: K, group or layout outside what the library runs";
     case MBOK_ERR_INFEASIBLE: return "MBOK_ERR_INFEASIBLE: no kernel allocation fits the bit budget";
+    case MBOK_ERR_SCRATCH: return "MBOK_ERR_SCRATCH: the call needs more scratch than the library's static scratch holds";
   }
   return "unknown status";
 }

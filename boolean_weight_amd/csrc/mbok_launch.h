@@ -24,6 +24,9 @@ size_t gemv_workspace_bytes(const mbok_desc* d);
 int launch_gemvt(const mbok_desc* d, const void* packed, const void* grad, int32_t g_dtype,
                  float* dx, void* ws, hipStream_t stream);
 size_t gemvt_workspace_bytes(const mbok_desc* d);
+int launch_gemvt_noalloc(const mbok_desc* d, const void* packed, const void* grad,
+                         int32_t g_dtype, float* dx, hipStream_t stream);
+size_t gemvt_scratch_bytes();
 int launch_skinny(const mbok_desc* d, const void* packed, const void* X, int64_t T, int64_t ldx,
                   float* Y, int64_t ldy, hipStream_t stream);
 int skinny_max_tokens();

@@ -31,9 +31,10 @@
  *    group size 128).  n must be a multiple of 128.
  *  - Sign encoding: bit 1 <-> +1, bit 0 <-> -1.  sign(0) and sign(-0.0) are +1.
  *  - All data pointers are DEVICE memory owned by the caller.  The library
- *    allocates nothing, keeps no mutable global state, and every call only
- *    enqueues work on `stream` (a hipStream_t; NULL = the default stream) and
- *    returns without synchronising.
+ *    allocates nothing and every call only enqueues work on `stream` (a
+ *    hipStream_t; NULL = the default stream) and returns without
+ *    synchronising.  The one piece of global state is the static scratch of
+ *    mbok_gemvt_noalloc (a fixed device array, its address cached per device).
  *  - Every argument check runs on the host before anything is enqueued, so an
  *    error return means nothing was launched and no output was touched.
  *    MBOK_ERR_HIP is returned when a launch itself fails (hipGetLastError).
@@ -93,7 +94,8 @@ enum {
   MBOK_ERR_ALIGN = -4,       /* pointer or leading dimension misaligned */
   MBOK_ERR_HIP = -5,         /* the HIP runtime rejected a launch */
   MBOK_ERR_UNSUPPORTED = -6, /* K or group outside what the library runs */
-  MBOK_ERR_INFEASIBLE = -7   /* no kernel allocation fits the bit budget */
+  MBOK_ERR_INFEASIBLE = -7,  /* no kernel allocation fits the bit budget */
+  MBOK_ERR_SCRATCH = -8      /* more scratch needed than the static scratch holds */
 };
 
 /* Element types. */
@@ -397,6 +399,28 @@ size_t mbok_gemvt_workspace_bytes(const mbok_desc* d);
  */
 int mbok_gemvt(const mbok_desc* d, const void* packed, const void* g,
                int32_t g_dtype, float* dx, void* workspace, void* stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): mbok_gemvt
+ * with its workspace replaced by the library's static scratch, a file-scope
+ * device array of mbok_gemvt_scratch_bytes() = 512 KiB per device, held until
+ * the process ends.  Same kernels, same slicing and the same output bits as
+ * mbok_gemvt with a workspace.  The call allocates nothing: on its first call
+ * on a device it looks up that device's address of the array
+ * (hipGetSymbolAddress, with the caller's current device) and caches it.
+ *  packed, g, g_dtype, dx, stream: as for mbok_gemvt.
+ * Every call on one GPU shares that GPU's scratch: calls that may overlap in
+ * time on the same GPU (different streams, different host threads) race and
+ * must be serialised by the caller.  The scratch needs no initialisation
+ * (every partial sum is written before it is read).
+ * Errors: as mbok_gemvt; SCRATCH when the shape needs more than the static
+ * scratch (no shape the descriptor accepts does); HIP when the device or the
+ * array's address cannot be queried, or a launch fails.
+ */
+size_t mbok_gemvt_scratch_bytes(void);
+int mbok_gemvt_noalloc(const mbok_desc* d, const void* packed, const void* g,
+                       int32_t g_dtype, float* dx, void* stream);
 
 /*
  * The same product for T tokens:  Y[t, i] = sum_j W_hat[i, j] * X[t, j].

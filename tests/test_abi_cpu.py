@@ -51,7 +51,7 @@ def test_header_compiles_as_c(tmp_path):
 
 def test_version_and_status_strings(lib):
     assert "mbok" in bw.mbok_version()
-    for code in (0, -1, -2, -3, -4, -5, -6, -7):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         s = bw.mbok_status_str(code)
         assert s.startswith("MBOK_"), s
     assert bw.mbok_status_str(-99) == "unknown status"
@@ -297,3 +297,33 @@ def test_allocation_many_weights_is_fast():
     assert time.perf_counter() - t0 < 5.0
     assert sum(k * s for k, s in zip(K, sizes)) <= budget
     assert min(K) >= 1 and max(K) <= 4
+
+
+def test_gemvt_noalloc_validates_before_launch(lib):
+    """The no-allocation transposed product checks its arguments on the host
+    (before looking up the device scratch) exactly as mbok_gemvt does."""
+    d = _desc()
+    R = ctypes.byref
+    assert lib.mbok_gemvt_noalloc(R(d), None, A16, bw.MBOK_BF16, A16, None) == -1
+    assert lib.mbok_gemvt_noalloc(R(d), A16, None, bw.MBOK_BF16, A16, None) == -1
+    assert lib.mbok_gemvt_noalloc(R(d), A16, A16, bw.MBOK_BF16, None, None) == -1
+    assert lib.mbok_gemvt_noalloc(R(d), A16, A16, bw.MBOK_F16, A16, None) == -3
+    assert lib.mbok_gemvt_noalloc(R(d), MIS, A16, bw.MBOK_BF16, A16, None) == -4
+    assert lib.mbok_gemvt_noalloc(R(d), A16, A16 + 1, bw.MBOK_BF16, A16, None) == -4
+    assert lib.mbok_gemvt_noalloc(R(d), A16, A16, bw.MBOK_F32, A16 + 2, None) == -4
+    assert lib.mbok_gemvt_noalloc(R(_desc(K=9)), A16, A16, bw.MBOK_BF16, A16, None) == -6
+    assert lib.mbok_gemvt_noalloc(None, A16, A16, bw.MBOK_BF16, A16, None) == -1
+
+
+def test_gemvt_static_scratch_covers_every_shape():
+    """The static scratch (512 KiB) holds the workspace of every shape the
+    descriptor accepts: n over all 8192 group counts, m from one row block to
+    the maximum (the workspace depends on the row blocks only up to a point)."""
+    cap = bw.mbok_gemvt_scratch_bytes()
+    assert cap == 512 * 1024
+    worst = 0
+    for G in range(1, 8193):
+        for m in (1, 64, 65, 200, 320, 1000, 4096, 65536, 1 << 24):
+            need = bw.mbok_gemvt_workspace_bytes(bw.mbok_desc_init(m, 128 * G, 1, bw.MBOK_F16))
+            worst = max(worst, need)
+    assert 0 < worst <= cap, worst
