@@ -16,8 +16,11 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmbok.so")
+# measurement only: the part's own ceilings (read stream, matrix cores, launch)
+CEILINGS_LIB = os.path.join(PKG, "libmbok_ceilings.so")
+CEILINGS_SOURCES = ["ceilings.hip"]
 
-SOURCES = ["mbok_api.cpp", "allocate.cpp", "quantize.hip", "refit.hip", "svid.hip", "pack.hip", "gemv.hip", "gemvt.hip", "gemm.hip", "skinny.hip"]
+SOURCES = ["mbok_api.cpp", "allocate.cpp", "quantize.hip", "refit.hip", "svid.hip", "pack.hip", "gemv.hip", "gemv_f4.hip", "gemvt.hip", "gemm.hip", "skinny.hip"]
 ARCH = "gfx950"
 
 COMMON = [
@@ -49,23 +52,31 @@ def _compile(src: str, extra: list[str]) -> str:
     return obj
 
 
-def build(verbose: bool = False, extra: list[str] | None = None) -> str:
-    """Compile every source and link libmbok.so; returns the library path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    # a failed build must not leave an older library behind to be loaded
-    if os.path.exists(LIB):
-        os.remove(LIB)
-    extra = list(extra or [])
-    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(lib: str, objs: list[str]) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"linking failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False, extra: list[str] | None = None) -> str:
+    """Compile every source, link libmbok.so and the ceilings library;
+    returns the MBOK library path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    # a failed build must not leave an older library behind to be loaded
+    for lib in (LIB, CEILINGS_LIB):
+        if os.path.exists(lib):
+            os.remove(lib)
+    extra = list(extra or [])
+    every = SOURCES + CEILINGS_SOURCES
+    with ThreadPoolExecutor(max_workers=min(8, len(every))) as ex:
+        objs = dict(zip(every, ex.map(lambda s: _compile(s, extra), every)))
+    _link(LIB, [objs[s] for s in SOURCES])
+    _link(CEILINGS_LIB, [objs[s] for s in CEILINGS_SOURCES])
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {CEILINGS_LIB}")
     return LIB
 
 

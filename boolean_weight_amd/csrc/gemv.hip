@@ -611,6 +611,19 @@ bool use_skinny_for_gemv(const Geom&) {
   return v && strcmp(v, "skinny") == 0;
 }
 
+// The fp4 x fp8 matrix-core kernel (gemv_f4.hip) for bf16 activations: the
+// default above 2^25 sign bits (K m n), where it measured 5-16% faster than
+// the table kernel on every workload shape (11008 x 4096 K = 3: 8.2 against
+// 9.0 us; 27648 x 5120: 16.6 against 18.9 us); at 4096 x 4096, K = 2 the
+// table kernel is faster (4.3 against 4.6 us).  MBOK_GEMV_VARIANT=f4 selects
+// it for every shape; any other value of the variable selects that table
+// variant instead.
+bool use_f4_for_gemv(const Geom& geo) {
+  const char* v = getenv("MBOK_GEMV_VARIANT");
+  if (v) return strcmp(v, "f4") == 0;
+  return (int64_t)geo.K * geo.m * geo.n > (int64_t(1) << 25);
+}
+
 int variant_for(const Geom&) {
   const char* v = getenv("MBOK_GEMV_VARIANT");
   if (v && strcmp(v, "direct") == 0) return kDirect;
@@ -808,6 +821,7 @@ int launch_gemv(const mbok_desc* d, const void* packed, const void* x, int32_t x
   const bool f16a = d->alpha_dtype == MBOK_F16;
   if (x_dtype == MBOK_BF16 && use_skinny_for_gemv(geo))
     return launch_skinny(d, packed, x, 1, d->n, y, d->m, stream);
+  if (x_dtype == MBOK_BF16 && use_f4_for_gemv(geo)) return launch_gemv_f4(d, packed, x, y, stream);
   if (x_dtype == MBOK_BF16)
     return f16a ? launch_k<uint16_t, uint16_t>(geo, packed, x, y, ws, stream)
                 : launch_k<uint16_t, float>(geo, packed, x, y, ws, stream);

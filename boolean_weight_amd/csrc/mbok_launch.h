@@ -21,6 +21,8 @@ int launch_pack(const mbok_desc* d, const int8_t* signs, const void* alpha, void
 int launch_gemv(const mbok_desc* d, const void* packed, const void* x, int32_t x_dtype,
                 float* y, void* workspace, hipStream_t stream);
 size_t gemv_workspace_bytes(const mbok_desc* d);
+int launch_gemv_f4(const mbok_desc* d, const void* packed, const void* x, float* y,
+                   hipStream_t stream);
 int launch_gemvt(const mbok_desc* d, const void* packed, const void* grad, int32_t g_dtype,
                  float* dx, void* ws, hipStream_t stream);
 size_t gemvt_workspace_bytes(const mbok_desc* d);

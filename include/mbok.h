@@ -362,8 +362,15 @@ size_t mbok_gemv_workspace_bytes(const mbok_desc* d);
  *            contents need no initialisation and are meaningless after the
  *            call, and calls that may run at the same time (other streams)
  *            need distinct workspaces.
- * The default kernel keeps one workgroup per compute unit: it builds the
- * signed-sum tables of x once and streams its 16-row tiles through them.
+ * The default kernels keep one workgroup per compute unit and stream 16-row
+ * tiles.  For bf16 x and more than 2^25 sign bits (K m n) the products run
+ * on the matrix cores: signs as fp4 +-1, each activation as an exact pair of
+ * fp8 parts with one power-of-two scale per 32 columns, alpha applied per
+ * (row, group, kernel) in fp32.  Otherwise (and for fp32 x) signed-sum
+ * tables of x are built once and the sign nibbles index them.
+ * Non-finite x: with the table kernels a NaN or infinity propagates through
+ * the fp32 sums; with the matrix-core kernel any NaN or infinite activation
+ * makes every output NaN.
  * Errors: INVALID_ARG, SHAPE/UNSUPPORTED, DTYPE (x_dtype), ALIGN (packed and
  * x 16-byte aligned, y 4-byte aligned, workspace 256-byte aligned), HIP.
  */

@@ -43,6 +43,8 @@ GEMV_VARIANTS = {
     "fullrow": {"MBOK_GEMV_VARIANT": "fullrow"},
     "direct": {"MBOK_GEMV_VARIANT": "direct"},
     "stream": {"MBOK_GEMV_VARIANT": "stream"},
+    # fp4 x fp8 matrix-core kernel (bf16 x only; fp32 x keeps the table kernels)
+    "f4": {"MBOK_GEMV_VARIANT": "f4"},
     # matrix-core kernel of the few-token product at one token (bf16 x only;
     # fp32 x keeps the table kernels)
     "skinny": {"MBOK_GEMV_VARIANT": "skinny"},
