@@ -2,25 +2,32 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
 
-A step is one pass of the hot path over one batch of synthetic input: for the
-default workload (LLaMA-7B attention projection 4096x4096, K=2 Boolean
+A step is one pass of the hot path over one batch of synthetic input.  For
+the default workload (LLaMA-7B attention projection 4096x4096, K=2 Boolean
 kernels, group 128, fp16 scales, bf16 activations, one token) that is one
 decode product y = sum_k (alpha_k (.) B_k) x.  The packed layer (signs and
 scales) is quantized and packed on the device by the library beforehand
-(untimed setup), then copied into a rotating pool of at least 1 GiB so that
-every step streams cold weights from HBM rather than from the 256 MB
-Infinity Cache.  Inputs are resident in HBM when the timed region starts.
+(untimed setup) and copied into a rotating pool of at least 1 GiB.  The
+timed steps read pool copies that the graph upload and the warm-up did not
+touch, and the rest of the pool is read in between, so every timed step
+streams its weights from HBM, not from the 256 MB Infinity Cache.  Inputs are
+resident in HBM when the timed region starts.
 
-Printed: one JSON line with the metric (weight GB/s), the roofline of the
-dominant kernel (algorithmic bytes per launch / mean launch duration from HIP
-events on the launch stream, against the 8 TB/s HBM peak) and the CPU oracle
-timed on the host cores on a bounded sample of the same workload.
+Printed: one JSON line with the metric (weight GB/s of the decode product),
+tokens/s, the roofline of the dominant kernel (algorithmic bytes per launch
+over its mean launch duration from HIP events on the launch stream, against
+the 8 TB/s HBM nameplate and against the read ceiling this part measures),
+the CPU oracle timed on the host cores on a bounded sample of the same
+workload, and the same figures for the prefill product (11008x4096, K=3,
+2048 tokens: TFLOP/s against the bf16 matrix-core nameplate and the measured
+matrix-core rate) and for the LLaMA-7B MLP decode shapes.
 """
 from __future__ import annotations
 
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -30,23 +37,27 @@ HBM_PEAK_GBPS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None,
                     help="timed steps (default 2000; with --quantizer, timed calls per "
                          "kernel, default 5)")
     ap.add_argument("--warmup", type=int, default=300)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=None, choices=[1, 2, 3, 4, 5],
+                    help="workload (default 2, with the prefill and LLaMA-7B MLP decode "
+                         "figures added to the line)")
     ap.add_argument("--K", type=int, default=None, help="override the workload's K")
     ap.add_argument("--T", type=int, default=None, help="tokens (workloads 3 and 5)")
     ap.add_argument("--no-graph", action="store_true", help="plain stream launches")
     ap.add_argument("--rotate-bytes", type=float, default=float(2 ** 30))
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="default workload only: leave out the prefill and MLP decode figures")
     ap.add_argument("--calibrate-copy", action="store_true",
-                    help="after the timed region, one 256 MiB device-to-device copy: the "
-                         "kernel of known size that scales the byte counters")
+                    help="after the timed region, one 256 MiB device-to-device copy, "
+                         "CAL_CALLS cold calls of the dominant kernel, and another copy: the "
+                         "bracket that scales the byte counters")
     ap.add_argument("--summarize", nargs=3, metavar=("STATS_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="no GPU work: turn a rocprofv3 --kernel-trace --stats output and two "
                          "--pmc outputs (FETCH_SIZE, WRITE_SIZE) of this script into the "
@@ -69,10 +80,17 @@ def parse():
     ap.add_argument("--library-gemm", action="store_true",
                     help="time the vendor library's plain bf16 GEMM (torch.matmul) at the "
                          "workload's product shape, as a yardstick for the prefill kernel")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="only the part's own ceilings: launch floor, read stream by size, "
+                         "matrix-core rates; prints one JSON line of its own")
     ap.add_argument("--extra", nargs="*", default=[],
                     help="with --summarize: more --pmc output dirs of --calibrate-copy runs; "
                          "every counter in them is reported per dominant call")
-    return ap.parse_args()
+    args = ap.parse_args(argv)
+    args.default_line = args.config is None
+    if args.config is None:
+        args.config = 2
+    return args
 
 
 def weight_bytes(m, n, K, alpha_bytes):
@@ -83,21 +101,25 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "boolean_weight_amd", "csrc")
 COPY_BYTES = 2 ** 28  # calibration copy: 256 MiB read and 256 MiB written
 CAL_CALLS = 8         # dominant calls bracketed by the two calibration copies
+MARKER = "empty_kernel"  # the ceilings library's empty kernel brackets each timed region
 
 
-def kernel_family(T):
-    """Source file and kernel-name prefix of the kernel one call runs."""
+def kernel_family(T, m=None, n=None, K=None, x_bf16=True):
+    """Source file and kernel-name prefix of the kernel one call runs (the
+    library's default choice)."""
     if T == 1:
-        return "gemv.hip", "gemv_"
+        if x_bf16 and m is not None and K * m * n > (1 << 25):
+            return "gemv_f4.hip", "gemv_f4_kernel"
+        return "gemv.hip", "gemv_stream_kernel"
     if T <= 16:
         return "skinny.hip", "gemm_skinny"
     return "gemm.hip", "gemm_mfma"
 
 
-def source_digest(T):
+def source_digest(T, m=None, n=None, K=None):
     import hashlib
     h = hashlib.sha256()
-    for f in (kernel_family(T)[0], "mbok_device.h"):
+    for f in (kernel_family(T, m, n, K)[0], "mbok_device.h"):
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -107,8 +129,18 @@ def workload_key(config, K, T):
     return f"config{config}_K{K}_T{T}"
 
 
+def dominant_shape(config, K, T):
+    """(m, n) of the workload's dominant launch."""
+    import mbok_synth as syn
+    if config == 4:
+        return max(((m, n) for _, m, n in syn.LAYER_STREAM_13B), key=lambda s: s[0] * s[1])
+    _, m, n = syn.WORKLOADS[config]["linears"][0]
+    return m, n
+
+
 def profile_path(config, K, T):
-    return os.path.join(HERE, "profiles", f"pmc_traffic_{kernel_family(T)[0][:-4]}_"
+    m, n = dominant_shape(config, K, T)
+    return os.path.join(HERE, "profiles", f"pmc_traffic_{kernel_family(T, m, n, K)[0][:-4]}_"
                         f"{workload_key(config, K, T)}.txt")
 
 
@@ -124,7 +156,8 @@ def stored_traffic(config, K, T):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 rec[k.strip()] = v.strip()
-    if rec.get("source_sha256") != source_digest(T):
+    m, n = dominant_shape(config, K, T)
+    if rec.get("source_sha256") != source_digest(T, m, n, K):
         return None
     try:
         return float(rec["traffic_bytes_per_launch"])
@@ -165,6 +198,21 @@ def bracketed(dispatches, prefix):
     return copy, calls
 
 
+def timed_regions(dispatches):
+    """dispatches: [(dispatch id, kernel name, duration ns)].  Every timed
+    region of the run is bracketed by two marker kernels; returns, per region
+    in order, {kernel name: [durations]} of the dispatches between them."""
+    ds = sorted(dispatches, key=lambda t: t[0])
+    marks = [i for i, (_, nm, _) in enumerate(ds) if MARKER in nm]
+    regions = []
+    for a, b in zip(marks[0::2], marks[1::2]):
+        reg = {}
+        for _, nm, dur in ds[a + 1:b]:
+            reg.setdefault(nm, []).append(dur)
+        regions.append(reg)
+    return regions
+
+
 def summarize(args):
     """Profile record of one workload from rocprofv3 outputs of bench.py."""
     import mbok_synth as syn
@@ -172,26 +220,39 @@ def summarize(args):
     cfg = syn.WORKLOADS[args.config]
     K = args.K or cfg["K"]
     T = args.T or cfg["T"][0]
-    _, prefix = kernel_family(T)
+    m, n = dominant_shape(args.config, K, T)
+    _, prefix = kernel_family(T, m, n, K)
     stats_dir, fetch_dir, write_dir = args.summarize
     lines = [f"# rocprofv3 summary, workload {workload_key(args.config, K, T)} "
-             f"({cfg['name']})", f"# commands: {args.command}", ""]
+             f"({cfg['name']}; dominant launch {m}x{n})", f"# commands: {args.command}", ""]
+    trace = _csv_rows(stats_dir, "kernel_trace.csv")
+    disp = [(int(r["Dispatch_Id"]), r["Kernel_Name"],
+             float(r["End_Timestamp"]) - float(r["Start_Timestamp"])) for r in trace]
+    regions = timed_regions(disp)
+    if regions:
+        lines.append("kernel-trace over the first timed region only (between the marker kernels):")
+        for nm, durs in sorted(regions[0].items(), key=lambda kv: -sum(kv[1])):
+            lines.append(f"  {nm[:110]} | calls {len(durs)} | avg {sum(durs) / len(durs) / 1e3:.3f} us"
+                         f" | min {min(durs) / 1e3:.3f} us | max {max(durs) / 1e3:.3f} us")
+        dom = [d for nm, ds_ in regions[0].items() if prefix in nm for d in ds_]
+        if dom:
+            lines.append(f"timed_region_dominant_kernel_us: {sum(dom) / len(dom) / 1e3:.3f} "
+                         f"(mean over {len(dom)} dispatches in the timed region)")
+    else:
+        lines.append("timed region markers not found")
     stats = _csv_rows(stats_dir, "kernel_stats.csv")
-    lines.append("kernel-trace stats (top kernels by total time):")
+    lines.append("kernel-trace stats over the whole run (setup and profiling calls included):")
     stats.sort(key=lambda r: -float(r.get("TotalDurationNs", 0)))
     for r in stats[:6]:
         lines.append(f"  {r['Name'][:110]} | calls {r['Calls']} | avg {float(r['AverageNs']) / 1e3:.3f} us"
                      f" | min {float(r['MinNs']) / 1e3:.3f} us | max {float(r['MaxNs']) / 1e3:.3f} us")
-    trace = _csv_rows(stats_dir, "kernel_trace.csv")
-    br = bracketed([(int(r["Dispatch_Id"]), r["Kernel_Name"],
-                     float(r["End_Timestamp"]) - float(r["Start_Timestamp"])) for r in trace], prefix)
+    br = bracketed(disp, prefix)
     if br:
         lines.append(f"dominant_call_kernel_us: {sum(br[1]) / CAL_CALLS / 1e3:.3f} "
-                     f"(sum of kernel durations over {CAL_CALLS} bracketed calls / {CAL_CALLS})")
+                     f"(sum of kernel durations over {CAL_CALLS} bracketed cold calls / {CAL_CALLS})")
     lines.append("")
     out = {}
-    for tag, d, counter, unit_scale in (("fetch", fetch_dir, "FETCH_SIZE", 1.0),
-                                        ("write", write_dir, "WRITE_SIZE", 1.0)):
+    for tag, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
         rows = [r for r in _csv_rows(d, "counter_collection.csv") if r["Counter_Name"] == counter]
         br = bracketed([(int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"]))
                         for r in rows], prefix)
@@ -216,8 +277,367 @@ def summarize(args):
                             for r in rows if r["Counter_Name"] == counter], prefix)
             if br:
                 lines.append(f"{counter}_per_call: {sum(br[1]) / CAL_CALLS:.6g}")
-    lines.append(f"source_sha256: {source_digest(T)}")
+    lines.append(f"source_sha256: {source_digest(T, m, n, K)}")
     print("\n".join(lines))
+
+
+# ------------------------------------------------------------------ GPU side
+
+class Workload:
+    """The launches of one workload: packed layers (quantized and packed on
+    the device), a rotating pool of copies of them, inputs and outputs."""
+
+    def __init__(self, args, config, K=None, T=None, launches=None):
+        import torch
+
+        import boolean_weight_amd as bw
+        import mbok_synth as syn
+
+        self.bw = bw
+        dev = torch.device("cuda:0")
+        cfg = syn.WORKLOADS[config]
+        self.config, self.cfg = config, cfg
+        self.K = K or cfg["K"]
+        self.T = T or cfg["T"][0]
+        self.adt = bw.MBOK_F16 if cfg["alpha_dtype"] == "f16" else bw.MBOK_F32
+        self.abytes = 2 if cfg["alpha_dtype"] == "f16" else 4
+        self.xdt = torch.bfloat16 if cfg["x_dtype"] == "bf16" else torch.float32
+        self.xbytes = 2 if cfg["x_dtype"] == "bf16" else 4
+        self.svid, self.transposed = args.svid, args.transposed
+        self.allocation = None
+        if launches is None:
+            linears = cfg["linears"]
+            if config == 4:
+                # q|k|v and gate|up share their input: one fused launch each
+                linears = list(syn.LAYER_STREAM_13B)
+            if config == 3 and self.T == 1:
+                linears = linears[:1]
+            launches = [(name, None, self.K, m, n) for name, m, n in linears]
+        layers, svid_in = [], []
+        for li, (name, Wl, Kl, m, n) in enumerate(launches):
+            if Wl is None:
+                Wl = torch.from_numpy(syn.weight(m, n, syn.weight_seed(config, li))).to(dev)
+            if self.svid:
+                d = bw.mbok_desc_init(m, n, Kl, self.adt)
+                at = bw.alpha_torch_dtype(self.adt)
+                signs = torch.empty((Kl, m, n), dtype=torch.int8, device=dev)
+                s_out = torch.empty((Kl, m), dtype=at, device=dev)
+                s_in = torch.empty((Kl, n), dtype=at, device=dev)
+                bw.mbok_svid_decompose(d, Wl, signs, s_out, s_in, args.svid_iters)
+                packed = torch.empty(bw.mbok_packed_bytes(d), dtype=torch.uint8, device=dev)
+                bw.mbok_svid_pack(d, signs, s_out, packed)
+                svid_in.append(s_in)
+                del signs, s_out
+            else:
+                d, packed, signs, alpha = bw.quantize_and_pack(Wl, Kl, self.adt)
+                del signs, alpha
+            del Wl
+            layers.append((name, d, packed))
+        self.svid_in = svid_in
+        self.wbytes = sum(weight_bytes(d.m, d.n, d.K, self.abytes) for _, d, _ in layers)
+        self.flops = sum(2.0 * d.m * d.n * self.T for _, d, _ in layers)
+        torch.cuda.empty_cache()
+        self.ncopy = max(2, int(np.ceil(args.rotate_bytes / self.wbytes)))
+        self.pools = [packed.repeat(self.ncopy).view(self.ncopy, -1) for _, _, packed in layers]
+        self.layers = [(name, d) for name, d, _ in layers]
+        del layers
+        torch.cuda.empty_cache()
+        self.xs, self.ys = [], []
+        for li, (name, d) in enumerate(self.layers):
+            if self.transposed:  # gradient g [m] in, dx [n] out
+                g = syn.activations(1, d.m, syn.act_seed(config, li) + 500, cfg["x_dtype"])
+                self.xs.append(torch.from_numpy(g).to(dev).to(self.xdt)[0].contiguous())
+                self.ys.append(torch.empty((d.n,), dtype=torch.float32, device=dev))
+                continue
+            x = torch.from_numpy(syn.activations(self.T, d.n, syn.act_seed(config, li),
+                                                 cfg["x_dtype"])).to(dev).to(self.xdt)
+            self.xs.append(x if self.T > 1 else x[0].contiguous())
+            self.ys.append(torch.empty((self.T, d.m) if self.T > 1 else (d.m,),
+                                       dtype=torch.float32, device=dev))
+        self.dom = max(range(len(self.layers)),
+                       key=lambda li: self.layers[li][1].m * self.layers[li][1].n)
+
+    def call(self, li, c):
+        bw = self.bw
+        d = self.layers[li][1]
+        if self.svid:
+            bw.mbok_svid_gemv(d, self.pools[li][c], self.svid_in[li], self.xs[li], self.ys[li])
+        elif self.transposed:
+            bw.mbok_gemvt(d, self.pools[li][c], self.xs[li], self.ys[li])
+        elif self.T == 1:
+            bw.mbok_gemv(d, self.pools[li][c], self.xs[li], self.ys[li])
+        else:
+            bw.mbok_gemm(d, self.pools[li][c], self.xs[li], self.ys[li])
+
+    def step(self, c):
+        for li in range(len(self.layers)):
+            self.call(li, c % self.ncopy)
+
+    def dom_alg_bytes(self):
+        d = self.layers[self.dom][1]
+        wb = weight_bytes(d.m, d.n, d.K, self.abytes)
+        if self.svid:
+            return wb + d.K * d.n * self.abytes + d.n * self.xbytes + d.m * 4
+        if self.transposed:
+            return wb + d.m * self.xbytes + d.n * 4
+        return wb + self.T * d.n * self.xbytes + self.T * d.m * 4
+
+
+def _capture(torch, fn):
+    """Warm fn up on a side stream, record it into a HIP graph, and replay it
+    once (the first replay uploads the graph)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    g.replay()
+    torch.cuda.synchronize()
+    return g
+
+
+def _marker(spin_us=0):
+    """The ceilings library's empty kernel, enqueued just outside each timed
+    region so that a kernel trace can find the region's dispatches; with
+    spin_us, a spin kernel first keeps the stream busy while the host
+    enqueues the region (so the start event fires with the region's work
+    already queued behind it: host submission latency is not timed)."""
+    import torch
+
+    from boolean_weight_amd import ceilings
+    lib = ceilings.load()
+    st = torch.cuda.current_stream().cuda_stream
+    if spin_us:
+        out = torch.empty(1, dtype=torch.float32, device="cuda")
+        if lib.mbok_ceiling_spin(spin_us, out.data_ptr(), st) != 0:
+            raise RuntimeError("spin kernel failed")
+    if lib.mbok_ceiling_empty(1, 64, st) != 0:
+        raise RuntimeError("marker kernel failed")
+
+
+def _evict(wl, copies):
+    """Read the given pool copies of every layer with the read-stream
+    kernel, so that the timed copies leave the Infinity Cache."""
+    import torch
+
+    from boolean_weight_amd import ceilings
+    lib = ceilings.load()
+    out = torch.empty(1024, dtype=torch.float32, device="cuda")
+    for c in copies:
+        for pool in wl.pools:
+            nb = pool[c].numel() // 16 * 16
+            if lib.mbok_ceiling_read(pool[c].data_ptr(), nb, out.data_ptr(), 1024, 256,
+                                     torch.cuda.current_stream().cuda_stream) != 0:
+                raise RuntimeError("eviction read failed")
+
+
+def measure_steps(wl, steps, warmup, use_graph=True):
+    """Exactly `steps` steps in the timed region.  The timed steps use pool
+    copies 0 .. glen-1 (glen = min(steps, pool copies)).  The other copies
+    are read once after the graph upload, then the warm-up steps run on them,
+    so each timed copy was last read at least (pool - glen) copies of other
+    data earlier (every copy of the pool, cycled, when steps >= pool).
+    Returns ms per step, the wall time and the pool bookkeeping."""
+    import torch
+    glen = min(wl.ncopy, max(1, steps))
+    use_graph = use_graph and glen * len(wl.layers) <= 4096
+    graphs = {}
+    if use_graph:
+        graphs[glen] = _capture(torch, lambda: [wl.step(i) for i in range(glen)])
+        rem = steps % glen
+        if rem:
+            graphs[rem] = _capture(torch, lambda: [wl.step(i) for i in range(rem)])
+    read_before = 0
+    if glen < wl.ncopy:
+        _evict(wl, range(glen, wl.ncopy))
+        read_before = (wl.ncopy - glen) * wl.wbytes
+    # the warm-up right before the region, on copies the region does not read
+    others = list(range(glen, wl.ncopy)) or list(range(wl.ncopy))
+    for i in range(warmup):
+        wl.step(others[i % len(others)])
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    _marker(spin_us=300)
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    if use_graph:
+        for _ in range(steps // glen):
+            graphs[glen].replay()
+        if steps % glen:
+            graphs[steps % glen].replay()
+    else:
+        for i in range(steps):
+            wl.step(i % glen)
+    t1.record(stream)
+    _marker()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0  # includes the spin kernel's 0.3 ms
+    return {"ms_per_step": t0.elapsed_time(t1) / steps, "wall_s": wall, "graph": use_graph,
+            "pool_copies": wl.ncopy, "timed_copies": glen,
+            "timed_pool_MB": round(glen * wl.wbytes / 2 ** 20, 1),
+            "read_before_timing_MB": round(read_before / 2 ** 20)}
+
+
+def measure_dominant(wl, calibrate=False):
+    """Mean duration of the dominant call: a HIP graph of that call over the
+    whole pool, replayed back to back, timed with HIP events on the launching
+    stream (graph launches leave no gaps between kernels, so this is the
+    kernel time a trace reports)."""
+    import torch
+    ncopy = wl.ncopy
+    g = _capture(torch, lambda: [wl.call(wl.dom, i) for i in range(ncopy)])
+    nrep = max(1, min(50, 2000 // ncopy))
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(nrep):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    launch_us = e0.elapsed_time(e1) * 1e3 / (nrep * ncopy)
+    del g
+    if calibrate:
+        # [copy] [CAL_CALLS dominant calls on pool copies read longest ago] [copy]:
+        # the profile summary finds this pattern at the end of the dispatch list
+        a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        for i in range(CAL_CALLS):
+            wl.call(wl.dom, i % ncopy)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+    return launch_us
+
+
+def measure_ceilings(read_sizes):
+    """The part's own ceilings: launch floor, nontemporal read stream at the
+    given sizes (bytes, each over a rotating pool of at least 1 GiB) and the
+    bf16 matrix-core rate."""
+    from boolean_weight_amd import ceilings
+    out = {"launch_floor_us": round(ceilings.launch_floor_us(256, 512), 3), "read": {}}
+    for nb in read_sizes:
+        r = ceilings.read_bandwidth(int(nb), grid=1024, block=256)
+        out["read"][str(int(nb) // 16 * 16)] = {"us": round(r["us"], 3),
+                                                 "GB/s": round(r["GB/s"], 1)}
+    r = ceilings.mfma_rate(ceilings.MFMA_BF16, iters=2000, grid=1024, block=256)
+    out["mfma_bf16_TFLOP/s"] = round(r["TFLOP/s"], 1)
+    return out
+
+
+# --------------------------------------------------------------- CPU oracle
+
+def _cpu_facts():
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        dep = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        blas = f"{dep.get('name')} {dep.get('version')}"
+    except Exception:
+        pass
+    return model, blas
+
+
+def cpu_baseline(config, K, T, rows, unit, runs=5):
+    """The oracle as it stands (float64 NumPy) on the host cores, on a
+    bounded sample of the same workload: the first `rows` output rows of the
+    dominant layer.  O1 (the greedy quantizer) once on the sample, then the
+    product (O2 dequantize + O3 matmul, oracle.product) and O2 alone: one
+    warm-up and `runs` timed runs each, medians reported, with all cores and
+    with one thread."""
+    import threadpoolctl
+
+    import mbok_synth as syn
+    import oracle
+
+    cfg = syn.WORKLOADS[config]
+    m, n = dominant_shape(config, K, T)
+    W = syn.weight(m, n, syn.weight_seed(config, 0))[:rows]
+    X = syn.activations(T, n, syn.act_seed(config, 0), cfg["x_dtype"])
+    Xa = X if T > 1 else X[0]
+    cores = len(os.sched_getaffinity(0))
+    t = time.perf_counter()
+    S, A, _ = oracle.residual_binarize(W, K, alpha_dtype=cfg["alpha_dtype"])
+    t_o1 = time.perf_counter() - t
+    work = (weight_bytes(rows, n, K, 2 if cfg["alpha_dtype"] == "f16" else 4) if unit == "GB/s"
+            else 2.0 * rows * n * T)
+    res = {}
+    for threads in (cores, 1):
+        with threadpoolctl.threadpool_limits(threads):
+            oracle.product(S, A, Xa)
+            tp, td = [], []
+            for _ in range(runs):
+                t = time.perf_counter()
+                oracle.product(S, A, Xa)
+                tp.append(time.perf_counter() - t)
+                t = time.perf_counter()
+                oracle.dequantize(S, A)
+                td.append(time.perf_counter() - t)
+        res[threads] = (statistics.median(tp), statistics.median(td))
+    scale = 1e9 if unit == "GB/s" else 1e12
+    model, blas = _cpu_facts()
+    tp, td = res[cores]
+    return {"value": work / tp / scale, "unit": unit, "cores": cores, "kind": "oracle",
+            "value_1_thread": work / res[1][0] / scale,
+            "sample": f"oracle.product (fp64 dequantize + matmul) of rows 0..{rows - 1} of the "
+                      f"{m}x{n} layer, K={K}, T={T}; median of {runs} runs after 1 warm-up",
+            "o2_dequantize_s": round(td, 4), "o3_matmul_s": round(tp - td, 4),
+            "o1_quantize_s": round(t_o1, 3), "o1_rows": rows,
+            "cpu_model": model, "blas": blas, "blas_threads": cores}
+
+
+# ---------------------------------------------------------------- the line
+
+def product_figures(args, wl, steps, warmup, ceil=None):
+    """Timed steps and the dominant call's roofline for one workload."""
+    timed = measure_steps(wl, steps, warmup, use_graph=not args.no_graph)
+    launch_us = measure_dominant(wl, calibrate=args.calibrate_copy)
+    d = wl.layers[wl.dom][1]
+    alg = wl.dom_alg_bytes()
+    if wl.T > 16:
+        achieved = 2.0 * d.m * d.n * wl.T / (launch_us * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / BF16_MFMA_PEAK_TFLOPS}
+        if ceil:
+            roof["measured_ceiling"] = ceil["mfma_bf16_TFLOP/s"]
+            roof["frac_of_measured_ceiling"] = achieved / ceil["mfma_bf16_TFLOP/s"]
+    else:
+        achieved = alg / (launch_us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBPS}
+        r = (ceil or {}).get("read", {}).get(str(int(alg) // 16 * 16))
+        if r:
+            roof["measured_ceiling"] = r["GB/s"]
+            roof["frac_of_measured_ceiling"] = achieved / r["GB/s"]
+            roof["read_ceiling_us"] = r["us"]
+    roof["traffic"] = (stored_traffic(wl.config, wl.K, wl.T)
+                       if wl.allocation is None and not wl.transposed and not wl.svid else None)
+    roof["kernel"] = f"{wl.layers[wl.dom][0]} {d.m}x{d.n}"
+    roof["launch_us"] = launch_us
+    roof["alg_bytes_per_launch"] = alg
+    if wl.T > 16:
+        roof["alg_flops_per_launch"] = 2.0 * d.m * d.n * wl.T
+    return timed, roof
+
+
+def _pool(timed):
+    return {k: timed[k] for k in ("pool_copies", "timed_copies", "timed_pool_MB",
+                                  "read_before_timing_MB")}
 
 
 def main():
@@ -236,26 +656,27 @@ def main():
 
     import boolean_weight_amd as bw
     import mbok_synth as syn
+    from boolean_weight_amd import ceilings
 
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     bw.load_library()
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
+    ceilings.load()
+    torch.cuda.set_device(0)
+
+    def note(msg):
+        print(f"bench: {msg}", file=sys.stderr, flush=True)
 
     cfg = syn.WORKLOADS[args.config]
     K = args.K or cfg["K"]
-    adt = bw.MBOK_F16 if cfg["alpha_dtype"] == "f16" else bw.MBOK_F32
-    abytes = 2 if cfg["alpha_dtype"] == "f16" else 4
-    xdt = torch.bfloat16 if cfg["x_dtype"] == "bf16" else torch.float32
     T = args.T or cfg["T"][0]
-    linears = cfg["linears"]
-    if args.config == 4:
-        # q|k|v and gate|up share their input: one fused launch each
-        linears = list(syn.LAYER_STREAM_13B)
-    if args.config == 3:
-        linears = linears[:1] if T == 1 else linears
+    if args.ceilings:
+        ceil = measure_ceilings([4743168, 19_070_000, 59_700_000, 268_435_456])
+        for kind in (ceilings.MFMA_F4F8, ceilings.MFMA_F4F8_LANE_SCALES):
+            ceil[f"mfma_kind{kind}_TFLOP/s"] = round(ceilings.mfma_rate(kind)["TFLOP/s"], 1)
+        print(json.dumps({"metric": "ceilings", "kind": "measurement", **ceil}), flush=True)
+        return
     if args.svid and (T != 1 or args.transposed or args.avg_k is not None):
         print("--svid runs one token on its own", file=sys.stderr)
         sys.exit(2)
@@ -263,19 +684,21 @@ def main():
         print("--transposed runs one gradient vector (T = 1)", file=sys.stderr)
         sys.exit(2)
     if args.quantizer:
-        quantizer_bench(args, cfg, cfg["linears"], K, adt, abytes)
+        quantizer_bench(args, cfg, cfg["linears"], K,
+                        bw.MBOK_F16 if cfg["alpha_dtype"] == "f16" else bw.MBOK_F32,
+                        2 if cfg["alpha_dtype"] == "f16" else 4)
         return
     if args.library_gemm:
-        library_gemm_bench(args, cfg, linears, T)
+        library_gemm_bench(args, cfg, cfg["linears"], T)
         return
 
-    # weights of each launch: (name, W on the device, K)
-    allocation = None
+    launches, allocation = None, None
     if args.avg_k is not None:
         if args.config != 4:
             print("--avg-k applies to the LLaMA-13B-shaped layer (--config 4)", file=sys.stderr)
             sys.exit(2)
-        Ws = [torch.from_numpy(syn.weight(m, n, syn.weight_seed(4, li))).to(dev)
+        adt = bw.MBOK_F16 if cfg["alpha_dtype"] == "f16" else bw.MBOK_F32
+        Ws = [torch.from_numpy(syn.weight(m, n, syn.weight_seed(4, li))).to("cuda")
               for li, (name, m, n) in enumerate(cfg["linears"])]
         Ks, _ = bw.allocate_for_budget(Ws, args.avg_k, kmax=4, alpha_dtype=adt)
         allocation = {nm: k for (nm, _, _), k in zip(cfg["linears"], Ks)}
@@ -286,250 +709,110 @@ def main():
                       ["down_proj"]):
             idx = [names.index(g) for g in group]
             if len({Ks[t] for t in idx}) == 1 and len(idx) > 1:
-                launches.append(("|".join(group), torch.cat([Ws[t] for t in idx]), Ks[idx[0]]))
+                Wc = torch.cat([Ws[t] for t in idx])
+                launches.append(("|".join(group), Wc, Ks[idx[0]], Wc.shape[0], Wc.shape[1]))
             else:
-                launches.extend((names[t], Ws[t], Ks[t]) for t in idx)
+                launches.extend((names[t], Ws[t], Ks[t], Ws[t].shape[0], Ws[t].shape[1])
+                                for t in idx)
         del Ws
         K = max(Ks)
-    else:
-        launches = [(name, None, K) for name, m, n in linears]
 
-    # ---- setup: quantize + pack on the device, build the rotating pool
-    layers = []
-    svid_in = []  # s_in of each layer (SVID)
-    per_step_wbytes = 0.0
-    per_step_bytes = 0.0
-    per_step_flops = 0.0
-    for li, (name, Wl, Kl) in enumerate(launches):
-        if Wl is None:
-            _, m, n = linears[li]
-            Wl = torch.from_numpy(syn.weight(m, n, syn.weight_seed(args.config, li))).to(dev)
-        m, n = Wl.shape
-        if args.svid:
-            d = bw.mbok_desc_init(m, n, Kl, adt)
-            at = bw.alpha_torch_dtype(adt)
-            signs = torch.empty((Kl, m, n), dtype=torch.int8, device=dev)
-            s_out = torch.empty((Kl, m), dtype=at, device=dev)
-            s_in = torch.empty((Kl, n), dtype=at, device=dev)
-            bw.mbok_svid_decompose(d, Wl, signs, s_out, s_in, args.svid_iters)
-            packed = torch.empty(bw.mbok_packed_bytes(d), dtype=torch.uint8, device=dev)
-            bw.mbok_svid_pack(d, signs, s_out, packed)
-            svid_in.append(s_in)
-            del signs, s_out
-        else:
-            d, packed, signs, alpha = bw.quantize_and_pack(Wl, Kl, adt)
-            del signs, alpha
-        del Wl
-        layers.append((name, d, packed))
-        wb = weight_bytes(m, n, Kl, abytes)
-        per_step_wbytes += wb
-        per_step_bytes += wb + T * n * (2 if xdt == torch.bfloat16 else 4) + T * m * 4
-        per_step_flops += 2.0 * m * n * T
-    torch.cuda.empty_cache()
-    ncopy = max(2, int(np.ceil(args.rotate_bytes / per_step_wbytes)))
-    pools = []
-    for name, d, packed in layers:
-        pools.append(packed.repeat(ncopy).view(ncopy, -1))
-        del packed
-    torch.cuda.empty_cache()
-    xs, ys = [], []
-    for li, (name, d, _) in enumerate(layers):
-        if args.transposed:  # gradient g [m] in, dx [n] out
-            x = torch.from_numpy(syn.activations(1, d.m, syn.act_seed(args.config, li) + 500,
-                                                 cfg["x_dtype"])).to(dev).to(xdt)
-            xs.append(x[0].contiguous())
-            ys.append(torch.empty((d.n,), dtype=torch.float32, device=dev))
-            continue
-        x = torch.from_numpy(syn.activations(T, d.n, syn.act_seed(args.config, li),
-                                             cfg["x_dtype"])).to(dev).to(xdt)
-        xs.append(x if T > 1 else x[0].contiguous())
-        ys.append(torch.empty((T, d.m) if T > 1 else (d.m,), dtype=torch.float32, device=dev))
-
-    def call(li, c):
-        d = layers[li][1]
-        if args.svid:
-            bw.mbok_svid_gemv(d, pools[li][c], svid_in[li], xs[li], ys[li])
-        elif args.transposed:
-            bw.mbok_gemvt(d, pools[li][c], xs[li], ys[li])
-        elif T == 1:
-            bw.mbok_gemv(d, pools[li][c], xs[li], ys[li])
-        else:
-            bw.mbok_gemm(d, pools[li][c], xs[li], ys[li])
-
-    def step(i):
-        c = i % ncopy
-        for li in range(len(layers)):
-            call(li, c)
-
-    # A HIP graph of one pass over the whole pool (>= 1 GiB of distinct
-    # weights), or of the timed steps when they are fewer: replays stream
-    # cold weights and save per-launch CPU work (and the timed region never
-    # mixes graph replays with plain launches when steps <= the pool).
-    glen = min(ncopy, max(1, args.steps))
-    use_graph = not args.no_graph and glen * len(layers) <= 2048
-    graph = None
-    if use_graph:
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            step(0)
-        torch.cuda.current_stream().wait_stream(s)
-        torch.cuda.synchronize()
-        def capture(count):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for i in range(count):
-                    step(i)
-            g.replay()  # the first replay uploads the graph: keep it untimed
-            torch.cuda.synchronize()
-            return g
-
-        graph = capture(glen)
-        # the steps past the last whole replay (warm-up and timed counts) run
-        # as graphs of their own too, captured here, outside the timed region
-        rest = {r: capture(r) for r in {args.warmup % glen, args.steps % glen} if r}
-
-    def run(nsteps):
-        """Exactly nsteps steps: whole graph replays, then the remainder."""
-        i = 0
-        if use_graph:
-            for _ in range(nsteps // glen):
-                graph.replay()
-            i = (nsteps // glen) * glen
-            if nsteps > i:
-                rest[nsteps - i].replay()
-                i = nsteps
-        while i < nsteps:
-            step(i)
-            i += 1
-        return nsteps
-
-    # ---- warmup, then the timed region
-    run(args.warmup)
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t0.record(stream)
-    done = run(args.steps)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms = t0.elapsed_time(t1)
-    ms_per_step = ms / done
-
-    # ---- mean duration of the dominant call: a HIP graph of that call alone
-    # over the pool, replayed back to back and timed with HIP events on the
-    # stream that launches it (graph launches leave no gaps between kernels,
-    # so this is the kernel time rocprofv3 reports)
-    dom = max(range(len(layers)), key=lambda li: layers[li][1].m * layers[li][1].n)
-    name, d, _ = layers[dom]
-
-    def dom_call(i):
-        call(dom, i % ncopy)
-
-    s2 = torch.cuda.Stream()
-    s2.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s2):
-        dom_call(0)
-    torch.cuda.current_stream().wait_stream(s2)
-    torch.cuda.synchronize()
-    nrep = max(1, min(200, 2000 // ncopy))
-    if use_graph and ncopy <= 2048:
-        g2 = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g2):
-            for i in range(ncopy):
-                dom_call(i)
-        g2.replay()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(nrep):
-            g2.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        launch_us = e0.elapsed_time(e1) * 1e3 / (nrep * ncopy)
-        del g2
-    else:
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(ncopy):
-            dom_call(i)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        launch_us = e0.elapsed_time(e1) * 1e3 / ncopy
-    if args.calibrate_copy:
-        # [copy] [CAL_CALLS dominant calls on pool copies read longest ago] [copy]:
-        # the profile summary finds this pattern at the end of the dispatch list
-        a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev)
-        b = torch.empty_like(a)
-        torch.cuda.synchronize()
-        b.copy_(a)
-        for i in range(CAL_CALLS):
-            dom_call(i)
-        b.copy_(a)
-        torch.cuda.synchronize()
-        del a, b
-    m, n = d.m, d.n
-    if args.svid:  # packed layer, s_in, x in; y out
-        alg_bytes = (weight_bytes(m, n, d.K, abytes) + d.K * n * abytes
-                     + n * (2 if xdt == torch.bfloat16 else 4) + m * 4)
-    elif args.transposed:  # g in, dx out
-        alg_bytes = weight_bytes(m, n, d.K, abytes) + m * (2 if xdt == torch.bfloat16 else 4) + n * 4
-    else:
-        alg_bytes = weight_bytes(m, n, d.K, abytes) + T * n * (2 if xdt == torch.bfloat16 else 4) + T * m * 4
-    if T > 16:
-        roof = {"bound": "mfma", "achieved": 2.0 * m * n * T / (launch_us * 1e-6) / 1e12,
-                "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s"}
-    else:
-        roof = {"bound": "hbm", "achieved": alg_bytes / (launch_us * 1e-6) / 1e9,
-                "peak": HBM_PEAK_GBPS, "unit": "GB/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = (stored_traffic(args.config, K, T)
-                       if allocation is None and not args.transposed and not args.svid else None)
-    roof["kernel"] = name
-    roof["launch_us"] = launch_us
-    roof["alg_bytes_per_launch"] = alg_bytes
+    note(f"setup: workload {args.config} ({cfg['name']}), K={K}, T={T}")
+    wl = Workload(args, args.config, K, T, launches)
+    wl.allocation = allocation
+    note("ceilings")
+    ceil = measure_ceilings([wl.dom_alg_bytes()])
+    note(f"timed region: {args.steps} steps after {args.warmup} warm-up steps")
+    timed, roof = product_figures(args, wl, args.steps, args.warmup, ceil)
+    ms = timed["ms_per_step"]
 
     if args.svid:
-        metric, unit = "svid weight GB/s", "GB/s"
-        value = per_step_wbytes / (ms_per_step * 1e-3) / 1e9
+        metric, unit, value = "svid weight GB/s", "GB/s", wl.wbytes / (ms * 1e-3) / 1e9
     elif args.transposed:
-        metric, unit = "transposed weight GB/s", "GB/s"
-        value = per_step_wbytes / (ms_per_step * 1e-3) / 1e9
+        metric, unit, value = "transposed weight GB/s", "GB/s", wl.wbytes / (ms * 1e-3) / 1e9
     elif T > 16:
-        metric, unit = "prefill TFLOP/s", "TFLOP/s"
-        value = per_step_flops / (ms_per_step * 1e-3) / 1e12
+        metric, unit, value = "prefill TFLOP/s", "TFLOP/s", wl.flops / (ms * 1e-3) / 1e12
     else:
-        metric, unit = "weight GB/s", "GB/s"
-        value = per_step_wbytes / (ms_per_step * 1e-3) / 1e9
-
+        metric, unit, value = "weight GB/s", "GB/s", wl.wbytes / (ms * 1e-3) / 1e9
+    if args.default_line:
+        metric = ("weight GB/s (% HBM peak) for the sum_k alpha_k B_k x decode GEMV at "
+                  "LLaMA-7B shapes; prefill TFLOP/s in 'prefill'")
     line = {
-        "metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": done,
-        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f32",
-        "data": "synthetic (seeded N(0,0.02) weights via greedy residual binarization, N(0,1) activations)",
-        "config": {"workload": cfg["name"], "linears": [[nm, dd.m, dd.n] for nm, dd, _ in layers],
+        "metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": f"{cfg['x_dtype']} x, {cfg['alpha_dtype']} alpha, f32 accumulate",
+        "data": "synthetic (seeded N(0,0.02) weights via greedy residual binarization, "
+                "N(0,1) activations)",
+        "config": {"workload": cfg["name"],
+                   "linears": [[nm, dd.m, dd.n] for nm, dd in wl.layers],
                    "K": K if allocation is None else allocation, "group": 128, "T": T,
-                   "alpha_dtype": cfg["alpha_dtype"],
-                   "x_dtype": cfg["x_dtype"], "rotating_pool_MB": round(ncopy * per_step_wbytes / 2**20),
-                   "launch": "hip graph" if use_graph else "stream",
-                   "pct_hbm_peak_of_value": round(100 * value / HBM_PEAK_GBPS, 1) if unit == "GB/s" else None,
-                   "wall_s": round(wall, 3)},
+                   "alpha_dtype": cfg["alpha_dtype"], "x_dtype": cfg["x_dtype"],
+                   "launch": "hip graph" if timed["graph"] else "stream",
+                   "pool": _pool(timed), "wall_s": round(timed["wall_s"], 3)},
+        "tokens_per_s": (T if args.config != 4 else 1) / (ms * 1e-3),
+        "pct_hbm_peak_of_value": round(100 * value / HBM_PEAK_GBPS, 2) if unit == "GB/s" else None,
         "roofline": roof,
+        "ceilings": ceil,
     }
+    if args.config == 4:
+        line["config"]["tokens_per_s_counts"] = "one token through one decoder layer"
     if args.transposed:
         line["config"]["product"] = "dx = W_hat^T g"
     if args.svid:
         line["config"]["product"] = "y = sum_k s_out^k (.) (B_k (s_in^k (.) x)) (successive SVID)"
         line["config"]["svid_iters"] = args.svid_iters
+    del wl
+    torch.cuda.empty_cache()
+
+    extra = args.default_line and not args.no_extra and not (args.svid or args.transposed)
+    if extra:
+        # the other half of the metric: prefill TFLOP/s (11008x4096, K=3, 2048 tokens)
+        note("prefill: setup")
+        pw = Workload(args, 5)
+        note(f"prefill: timed region: {args.steps} steps after {args.warmup} warm-up steps")
+        ptimed, proof = product_figures(args, pw, args.steps, args.warmup, ceil)
+        pms = ptimed["ms_per_step"]
+        ptf = pw.flops / (pms * 1e-3) / 1e12
+        line["prefill"] = {
+            "workload": syn.WORKLOADS[5]["name"], "K": pw.K, "T": pw.T, "value": ptf,
+            "unit": "TFLOP/s", "steps": args.steps, "warmup": args.warmup, "ms_per_step": pms,
+            "tokens_per_s": pw.T / (pms * 1e-3),
+            "pct_bf16_peak_of_value": round(100 * ptf / BF16_MFMA_PEAK_TFLOPS, 2),
+            "dtype": "bf16 x and bf16 W_hat tiles, f16 alpha, f32 accumulate",
+            "pool": _pool(ptimed), "roofline": proof}
+        del pw
+        torch.cuda.empty_cache()
+        # the LLaMA-7B MLP decode shapes (gate/up 11008x4096, down 4096x11008, K=3)
+        mlp = {}
+        for name, m, n in syn.WORKLOADS[3]["linears"]:
+            if name == "up_proj":
+                continue  # the shape of gate_proj
+            note(f"MLP decode: {name} {m}x{n}")
+            li = [nm for nm, _, _ in syn.WORKLOADS[3]["linears"]].index(name)
+            Wl = torch.from_numpy(syn.weight(m, n, syn.weight_seed(3, li))).to("cuda")
+            mw = Workload(args, 3, 3, 1, [(name, Wl, 3, m, n)])
+            del Wl
+            mtimed, mroof = product_figures(args, mw, args.steps, args.warmup, None)
+            mms = mtimed["ms_per_step"]
+            gbs = mw.wbytes / (mms * 1e-3) / 1e9
+            mlp[name] = {"shape": [m, n], "K": 3, "value": gbs, "unit": "GB/s",
+                         "ms_per_step": mms, "pct_hbm_peak_of_value": round(100 * gbs / HBM_PEAK_GBPS, 2),
+                         "kernel_launch_us": mroof["launch_us"], "pool": _pool(mtimed)}
+            del mw
+            torch.cuda.empty_cache()
+        line["mlp_decode"] = mlp
+
     if not args.no_cpu_baseline:
-        dname, dd = layers[dom][0], layers[dom][1]
-        line["cpu_baseline"] = cpu_baseline(args, cfg, (dname, dd.m, dd.n), dd.K, T, unit)
+        note("cpu baseline")
+        if args.transposed or args.svid:
+            line["cpu_baseline"] = None
+        else:
+            rows = 512 if T > 1 else (1024 if args.config == 4 else dominant_shape(args.config, K, T)[0])
+            line["cpu_baseline"] = cpu_baseline(args.config, K if allocation is None else 3,
+                                                T, rows, unit)
+            if "prefill" in line:
+                line["prefill"]["cpu_baseline"] = cpu_baseline(5, 3, 2048, 512, "TFLOP/s")
     print(json.dumps(line), flush=True)
 
 
@@ -656,45 +939,6 @@ def library_gemm_bench(args, cfg, linears, T):
                       "workload": cfg["name"], "linear": [name, m, n], "T": T, "runs": out}),
           flush=True)
 
-
-def cpu_baseline(args, cfg, lin, K, T, unit):
-    """The oracle as it stands (float64 NumPy) on the host cores, on a bounded
-    sample of the same workload: repeated products of the dominant layer."""
-    import threadpoolctl
-
-    import mbok_synth as syn
-    import oracle
-
-    name, m, n = lin
-    cores = len(os.sched_getaffinity(0))
-    with threadpoolctl.threadpool_limits(cores):
-        W = syn.weight(m, n, syn.weight_seed(args.config, 0))
-        rows = m if T == 1 else min(m, 512)
-        S, A, _ = oracle.residual_binarize(W[:rows], K, alpha_dtype=cfg["alpha_dtype"])
-        X = syn.activations(T, n, syn.act_seed(args.config, 0), cfg["x_dtype"])
-        Gr = syn.activations(1, rows, syn.act_seed(args.config, 0) + 500, cfg["x_dtype"])[0]
-        t0 = time.perf_counter()
-        reps = 0
-        while True:
-            if args.svid:
-                oracle.svid_product(S, A[:, :, 0], np.ones((K, n)), X[0])
-            elif args.transposed:
-                oracle.product_transposed(S, A, Gr)
-            else:
-                oracle.product(S, A, X if T > 1 else X[0])
-            reps += 1
-            if time.perf_counter() - t0 > args.cpu_seconds:
-                break
-        dt = time.perf_counter() - t0
-    wbytes = weight_bytes(rows, n, K, 2 if cfg["alpha_dtype"] == "f16" else 4)
-    if unit == "GB/s":
-        value = wbytes * reps / dt / 1e9
-    else:
-        value = 2.0 * rows * n * T * reps / dt / 1e12
-    return {"value": value, "unit": unit, "cores": cores, "kind": "oracle",
-            "sample": f"{reps} oracle {'transposed ' if args.transposed else ''}products "
-                      f"(fp64 dequantize + matmul) of {name} "
-                      f"rows 0..{rows - 1} x {n}, K={K}, T={T}, in {dt:.1f} s"}
 
 
 if __name__ == "__main__":

@@ -6,6 +6,9 @@
 //  * empty:  a kernel that does nothing, launched with a given grid; its
 //            back-to-back interval in a HIP graph is the launch floor of any
 //            kernel of that shape.
+//  * spin:   one workgroup per compute unit doing fp32 arithmetic for a
+//            given time (the 100 MHz real-time counter), to keep the chip busy
+//            while the host enqueues a timed region behind it.
 //  * read:   every byte of a buffer read once with nontemporal 16-byte loads,
 //            a contiguous chunk per workgroup: the read bandwidth a streaming
 //            kernel can reach.
@@ -28,6 +31,20 @@ typedef float v16f_t __attribute__((ext_vector_type(16)));
 typedef short v8s_t __attribute__((ext_vector_type(8)));
 
 __global__ void empty_kernel() {}
+
+// Busy for `ticks` of the 100 MHz real-time counter, then ends: it keeps the
+// stream (and, with one workgroup per compute unit doing fp32 arithmetic,
+// the whole chip) busy while the host enqueues the work that follows it.  The
+// loop ends because the counter only advances.
+__global__ void spin_kernel(uint64_t ticks, float* out) {
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  float v = (float)threadIdx.x;
+  while (__builtin_amdgcn_s_memrealtime() - t0 < ticks) {
+#pragma unroll
+    for (int i = 0; i < 64; ++i) v = fmaf(v, 0.999f, 0.001f);
+  }
+  if (v == -1.f) out[0] = v;  // never true: v stays in (0, threadIdx.x]
+}
 
 constexpr int kReadUnroll = 8;  // loads in flight per thread
 
@@ -107,6 +124,13 @@ extern "C" {
 int mbok_ceiling_empty(int grid, int block, void* stream) {
   if (!shape_ok(grid, block)) return -1;
   hipLaunchKernelGGL(empty_kernel, dim3(grid), dim3(block), 0, (hipStream_t)stream);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+int mbok_ceiling_spin(int microseconds, float* out, void* stream) {
+  if (microseconds < 1 || microseconds > 100000 || !out) return -1;
+  hipLaunchKernelGGL(spin_kernel, dim3(256), dim3(256), 0, (hipStream_t)stream,
+                     (uint64_t)microseconds * 100, out);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 

@@ -24,6 +24,12 @@ extern "C" {
  * floor of a kernel with this grid. */
 int mbok_ceiling_empty(int grid, int block, void* stream);
 
+/* One workgroup per compute unit doing fp32 arithmetic for `microseconds`
+ * (1 .. 100000) of the 100 MHz real-time counter, then done: enqueued before
+ * a timed region, it keeps the chip busy while the host enqueues the region's
+ * work.  out (one float) is written only if an impossible value appears. */
+int mbok_ceiling_spin(int microseconds, float* out, void* stream);
+
 /* Reads bytes (a multiple of 16) of buf (16-byte aligned) once with
  * nontemporal 16-byte loads, one contiguous chunk per workgroup; out[grid] is
  * written only if an impossible value appears. */

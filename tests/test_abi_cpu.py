@@ -327,3 +327,28 @@ def test_gemvt_static_scratch_covers_every_shape():
             need = bw.mbok_gemvt_workspace_bytes(bw.mbok_desc_init(m, 128 * G, 1, bw.MBOK_F16))
             worst = max(worst, need)
     assert 0 < worst <= cap, worst
+
+
+def test_ceilings_library_exports_its_header():
+    """The measurement library (libmbok_ceilings.so) loads and exports every
+    function include/mbok_ceilings.h declares; its argument checks run on
+    the host."""
+    from boolean_weight_amd import ceilings
+    hdr = os.path.join(ROOT, "include", "mbok_ceilings.h")
+    text = re.sub(r"/\*.*?\*/", "", open(hdr).read(), flags=re.S)
+    fns = sorted(set(re.findall(r"\b(mbok_[a-z0-9_]+)\s*\(", text)))
+    assert fns == ["mbok_ceiling_empty", "mbok_ceiling_mfma", "mbok_ceiling_read",
+                   "mbok_ceiling_spin"]
+    lib = ceilings.load()
+    out = subprocess.run(["nm", "-D", "--defined-only", lib._name],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (mbok_[a-z0-9_]+)\b", out))
+    assert set(fns) <= exported
+    assert lib.mbok_ceiling_empty(0, 64, None) == -1      # grid out of range
+    assert lib.mbok_ceiling_empty(1, 100, None) == -1     # block not a multiple of 64
+    assert lib.mbok_ceiling_read(None, 16, A16, 1, 64, None) == -1
+    assert lib.mbok_ceiling_read(A16, 15, A16, 1, 64, None) == -1
+    assert lib.mbok_ceiling_mfma(9, A16, 1, 1, 64, None) == -1
+    assert lib.mbok_ceiling_spin(0, A16, None) == -1
+    assert lib.mbok_ceiling_spin(100001, A16, None) == -1
+    assert lib.mbok_ceiling_spin(10, None, None) == -1

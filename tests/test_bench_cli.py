@@ -25,7 +25,7 @@ def test_more_than_one_gpu_is_refused():
 
 @pytest.mark.gpu
 def test_bench_line_fields():
-    r = _bench("--steps", "20", "--warmup", "5", "--cpu-seconds", "1")
+    r = _bench("--steps", "20", "--warmup", "5")
     assert r.returncode == 0, r.stderr[-2000:]
     lines = [ln for ln in r.stdout.splitlines() if ln.strip()]
     assert len(lines) == 1, r.stdout
@@ -47,3 +47,18 @@ def test_bench_line_fields():
     cpu = d["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["cores"] >= 1
     assert cpu["unit"] == d["unit"] and cpu["sample"]
+    for key in ("value_1_thread", "o1_quantize_s", "o2_dequantize_s", "o3_matmul_s",
+                "cpu_model", "blas"):
+        assert key in cpu, key
+    # the timed copies were not touched by the upload or the warm-up and at
+    # least 512 MB of other data was read before the region
+    pool = d["config"]["pool"]
+    assert pool["timed_copies"] == 20 and pool["read_before_timing_MB"] >= 512
+    assert d["tokens_per_s"] == pytest.approx(1e3 / d["ms_per_step"])
+    assert d["ceilings"]["launch_floor_us"] > 0 and roof["measured_ceiling"] > 0
+    # the prefill half of the metric, in the same line
+    p = d["prefill"]
+    assert p["unit"] == "TFLOP/s" and p["value"] > 0 and p["T"] == 2048 and p["K"] == 3
+    assert p["roofline"]["bound"] == "mfma" and p["roofline"]["peak"] == 2500.0
+    assert p["cpu_baseline"]["kind"] == "oracle" and p["cpu_baseline"]["unit"] == "TFLOP/s"
+    assert set(d["mlp_decode"]) == {"gate_proj", "down_proj"}

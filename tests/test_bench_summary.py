@@ -12,7 +12,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
 import bench  # noqa: E402
 
-GEMV = "void mbok::(anonymous namespace)::gemv_rows_kernel<unsigned short, 2, 16, 4>(...)"
+GEMV = "void mbok::(anonymous namespace)::gemv_stream_kernel<unsigned short, unsigned short, 2, 8>(...)"
 COPY = "__amd_rocclr_copyBuffer"
 
 
@@ -47,7 +47,7 @@ def _make(tmp_path, counter):
 
 def test_bracket_finds_the_last_copy_calls_copy():
     seq = [(i, nm, v) for i, (nm, v) in enumerate(_dispatches())]
-    copy, calls = bench.bracketed(seq, "gemv_")
+    copy, calls = bench.bracketed(seq, "gemv_stream_kernel")
     assert copy == [65536.0, 65536.0]
     assert calls == [2500.0] * bench.CAL_CALLS
 
@@ -81,3 +81,12 @@ def test_summary_scales_counters_by_the_copy(tmp_path):
     assert float(rec["traffic_bytes_per_launch"]) == pytest.approx(2 * 2500 * 1024 * 2.0)
     assert float(rec["dominant_call_kernel_us"].split()[0]) == pytest.approx(5.0)
     assert rec["source_sha256"].strip() == bench.source_digest(1)
+
+
+def test_timed_regions_between_markers():
+    seq = [(1, "setup_kernel", 5.0), (2, "empty_kernel", 1.0), (3, GEMV, 4.0), (4, GEMV, 6.0),
+           (5, "empty_kernel", 1.0), (6, GEMV, 50.0), (7, "empty_kernel", 1.0),
+           (8, "gemm_mfma8_kernel", 100.0), (9, "empty_kernel", 1.0)]
+    regs = bench.timed_regions(seq)
+    assert regs == [{GEMV: [4.0, 6.0]}, {"gemm_mfma8_kernel": [100.0]}]
+    assert bench.timed_regions([(1, GEMV, 1.0)]) == []
