@@ -280,14 +280,26 @@ _WORKSPACES: dict = {}
 
 def workspace_for(nbytes: int, device=None, stream=None) -> torch.Tensor | None:
     """A workspace of at least nbytes, kept per (device, stream) so that calls
-    which may overlap never share one."""
+    which may overlap never share one.
+
+    The tensor is allocated with the target stream current, so torch's caching
+    allocator ties its memory to that stream: when a larger request replaces
+    it, the old block is reused only in that stream's order, after the work
+    already enqueued there that reads it."""
     if nbytes == 0:
         return None
     dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
     key = (dev.index, _stream(stream))
     ws = _WORKSPACES.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
+        if stream is None:
+            target = torch.cuda.current_stream(dev)
+        elif isinstance(stream, torch.cuda.Stream):
+            target = stream
+        else:
+            target = torch.cuda.ExternalStream(int(stream), device=dev)
+        with torch.cuda.stream(target):
+            ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
         _WORKSPACES[key] = ws
     return ws
 

@@ -43,8 +43,8 @@ def hipcc() -> str:
     return path
 
 
-def _compile(src: str, extra: list[str]) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, extra: list[str], out_dir: str = BUILD_DIR) -> str:
+    obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
     cmd = [hipcc(), *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -52,9 +52,9 @@ def _compile(src: str, extra: list[str]) -> str:
     return obj
 
 
-def _link(lib: str, objs: list[str]) -> None:
+def _link(lib: str, objs: list[str], extra: list[str] | None = None) -> None:
     tmp = lib + ".tmp"
-    cmd = [hipcc(), "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs]
+    cmd = [hipcc(), "-shared", f"--offload-arch={ARCH}", *(extra or []), "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"linking failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -80,5 +80,48 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
     return LIB
 
 
+# Host-side sanitizers only: each -fsanitize= applies to the host pass of
+# hipcc (the device code is built as usual).  The library then expects the
+# clang AddressSanitizer runtime in the process (LD_PRELOAD of
+# sanitizer_runtime()).
+SANITIZE_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined",
+                 "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+SANITIZED_DIR = os.path.join(BUILD_DIR, "sanitized")
+
+
+def sanitizer_runtime() -> str | None:
+    """The clang AddressSanitizer runtime of ROCm's LLVM, or None."""
+    base = "/opt/rocm/llvm/lib/clang"
+    if not os.path.isdir(base):
+        return None
+    for ver in sorted(os.listdir(base), reverse=True):
+        path = os.path.join(base, ver, "lib", "linux", "libclang_rt.asan-x86_64.so")
+        if os.path.exists(path):
+            return path
+    return None
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """libmbok.so with AddressSanitizer and UndefinedBehaviorSanitizer on the
+    host code (argument checks, descriptor and size arithmetic, the kernel
+    allocator, the launchers), under _build/sanitized/; returns its path.
+    Load it with MBOK_LIBRARY=<path> and the runtime preloaded."""
+    os.makedirs(SANITIZED_DIR, exist_ok=True)
+    lib = os.path.join(SANITIZED_DIR, "libmbok.so")
+    if os.path.exists(lib):
+        os.remove(lib)
+    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, SANITIZE_HOST, SANITIZED_DIR), SOURCES))
+    _link(lib, objs, ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                      "-shared-libsan"])
+    if verbose:
+        print(f"built {lib}")
+    return lib
+
+
 if __name__ == "__main__":
-    build(verbose=True, extra=sys.argv[1:])
+    if sys.argv[1:2] == ["sanitized"]:
+        build_sanitized(verbose=True)
+    else:
+        build(verbose=True, extra=sys.argv[1:])

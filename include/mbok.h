@@ -29,7 +29,9 @@
  *  - Scales: one alpha per (kernel k, output row i, group g) where group g is
  *    the 128 consecutive input columns 128g .. 128g+127 ([RN] group-wise scales,
  *    group size 128).  n must be a multiple of 128.
- *  - Sign encoding: bit 1 <-> +1, bit 0 <-> -1.  sign(0) and sign(-0.0) are +1.
+ *  - Sign encoding: bit 1 <-> +1, bit 0 <-> -1 ([GS] Dutch summary,
+ *    Methodologie 1: a Boolean weight is -1/+1, equivalently FALSE/TRUE; here
+ *    TRUE is bit 1 and means +1).  sign(0) and sign(-0.0) are +1.
  *  - All data pointers are DEVICE memory owned by the caller.  The library
  *    allocates nothing and every call only enqueues work on `stream` (a
  *    hipStream_t; NULL = the default stream) and returns without
@@ -115,6 +117,9 @@ typedef struct mbok_desc {
 } mbok_desc;
 
 /*
+ * Describes one layer of K Boolean kernels with group-wise scales ([RN]
+ * 关键设计: a weight matrix is the sum of K Boolean kernels, each with its own
+ * scales, one scale per group of input columns; [RN] 消融实验: groups of 128).
  * Fills *d after checking the shape: 1 <= m <= 2^24, 128 <= n <= 2^20 with
  * n % 128 == 0, 1 <= K <= MBOK_MAX_K, alpha_dtype in {MBOK_F32, MBOK_F16}.
  * Host only.  Returns MBOK_OK, MBOK_ERR_INVALID_ARG (d NULL),
@@ -325,8 +330,13 @@ int mbok_svid_gemv(const mbok_desc* d, const void* packed, const void* s_in,
 
 /*
  * Packs Boolean kernels and their scales into MBOK_LAYOUT_L64 (see the top
- * of this header).  Any +-1 signs are accepted, e.g. those of a finetuned
- * model; an entry >= 0 packs as bit 1 (+1) and < 0 as bit 0 (-1).
+ * of this header): the storage form of the multi-kernel Boolean parameters
+ * ([RN] 关键设计: K sign matrices and their group scales; [GS] Dutch
+ * summary, Methodologie 1: a Boolean weight is -1/+1, i.e. FALSE/TRUE, so one
+ * bit holds it).
+ * Any +-1 signs are accepted, e.g. those of a finetuned model ([GS] Dutch
+ * summary, Methodologie 3: the kernels are finetuned in the Boolean domain);
+ * an entry >= 0 packs as bit 1 (+1) and < 0 as bit 0 (-1).
  *  signs   device int8 [K][m][n].
  *  alpha   device [K][m][n/128] of d->alpha_dtype.
  *  packed  device, mbok_packed_bytes(d) bytes; fully overwritten, padding
@@ -430,7 +440,9 @@ int mbok_gemvt_noalloc(const mbok_desc* d, const void* packed, const void* g,
                        int32_t g_dtype, float* dx, void* stream);
 
 /*
- * The same product for T tokens:  Y[t, i] = sum_j W_hat[i, j] * X[t, j].
+ * The same product for T tokens ([RN] 关键设计: the layer's product is the sum
+ * of its K Boolean products, scaled per group; [RN] 局限与展望: activations
+ * stay full precision):  Y[t, i] = sum_j W_hat[i, j] * X[t, j].
  * T = 1 runs the decode kernel of mbok_gemv (without a workspace).  T = 2..16
  * runs the weight-streaming few-token kernel (exact fp32 scaling of +-1
  * products).  T > 16 is the prefill GEMM: each tile of W_hat is formed

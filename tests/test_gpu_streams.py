@@ -95,3 +95,56 @@ def test_two_streams_give_the_sequential_bits(variant):
             os.environ.pop("MBOK_GEMV_VARIANT", None)
         else:
             os.environ["MBOK_GEMV_VARIANT"] = old
+
+
+def _device_layer(K, m, n, seed):
+    """A layer packed from signs and scales drawn on the GPU (the comparison
+    below is the library against itself, so no host copy is needed)."""
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(seed)
+    d = bw.mbok_desc_init(m, n, K)
+    signs = (torch.randint(0, 2, (K, m, n), generator=gen, device=DEV, dtype=torch.int8) * 2 - 1)
+    alpha = torch.rand((K, m, n // 128), generator=gen, device=DEV).to(torch.float16)
+    packed = torch.empty(bw.mbok_packed_bytes(d), dtype=torch.uint8, device=DEV)
+    bw.mbok_pack(d, signs, alpha, packed)
+    torch.cuda.synchronize()
+    return d, packed
+
+
+def test_explicit_stream_workspace_grows():
+    """Calls given an explicit stream (a torch stream, then its raw handle)
+    while the current stream is another one: the binding's cached workspace
+    for that stream is allocated on it and replaced when a larger shape needs
+    more than it holds, and every result equals the same call on the current
+    stream."""
+    say("explicit-stream workspace: split decode, 16 KB then 3.2 MB workspace")
+    old = os.environ.get("MBOK_GEMV_VARIANT")
+    os.environ["MBOK_GEMV_VARIANT"] = "split"
+    try:
+        small = _device_layer(2, 1000, 2048, 910)
+        large = _device_layer(1, 400000, 4096, 920)
+        assert bw.mbok_gemv_workspace_bytes(small[0]) < (1 << 20) < \
+            bw.mbok_gemv_workspace_bytes(large[0])
+        xs = [x_to_dev(syn.activations(1, d.n, 930 + i, "bf16")[0], "bf16")
+              for i, (d, _) in enumerate((small, large))]
+        want = []
+        for (d, p), x in zip((small, large), xs):
+            y = torch.empty(d.m, dtype=torch.float32, device=DEV)
+            bw.mbok_gemv(d, p, x, y)
+            torch.cuda.synchronize()
+            want.append(y.clone())
+        s = torch.cuda.Stream()
+        for handle in (s, s.cuda_stream):
+            for i in (0, 1, 0, 1):
+                (d, p), x = (small, large)[i], xs[i]
+                y = torch.full((d.m,), -3.0, dtype=torch.float32, device=DEV)
+                s.wait_stream(torch.cuda.current_stream())
+                bw.mbok_gemv(d, p, x, y, stream=handle)
+                torch.cuda.current_stream().wait_stream(s)
+                torch.cuda.synchronize()
+                assert torch.equal(y, want[i]), (type(handle).__name__, i)
+    finally:
+        if old is None:
+            os.environ.pop("MBOK_GEMV_VARIANT", None)
+        else:
+            os.environ["MBOK_GEMV_VARIANT"] = old
