@@ -50,6 +50,8 @@ def parse(argv=None):
     ap.add_argument("--K", type=int, default=None, help="override the workload's K")
     ap.add_argument("--T", type=int, default=None, help="tokens (workloads 3 and 5)")
     ap.add_argument("--no-graph", action="store_true", help="plain stream launches")
+    ap.add_argument("--precise", action="store_true",
+                    help="multi-token products through mbok_gemm_precise (two-term levels)")
     ap.add_argument("--rotate-bytes", type=float, default=float(2 ** 30))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
@@ -304,6 +306,7 @@ class Workload:
         self.xdt = torch.bfloat16 if cfg["x_dtype"] == "bf16" else torch.float32
         self.xbytes = 2 if cfg["x_dtype"] == "bf16" else 4
         self.svid, self.transposed = args.svid, args.transposed
+        self.precise = getattr(args, "precise", False)
         self.allocation = None
         if launches is None:
             linears = cfg["linears"]
@@ -366,6 +369,8 @@ class Workload:
             bw.mbok_gemvt(d, self.pools[li][c], self.xs[li], self.ys[li])
         elif self.T == 1:
             bw.mbok_gemv(d, self.pools[li][c], self.xs[li], self.ys[li])
+        elif self.precise:
+            bw.mbok_gemm_precise(d, self.pools[li][c], self.xs[li], self.ys[li])
         else:
             bw.mbok_gemm(d, self.pools[li][c], self.xs[li], self.ys[li])
 
@@ -577,26 +582,31 @@ def cpu_baseline(config, K, T, rows, unit, runs=5):
     work = (weight_bytes(rows, n, K, 2 if cfg["alpha_dtype"] == "f16" else 4) if unit == "GB/s"
             else 2.0 * rows * n * T)
     res = {}
+    X2 = np.asarray(Xa, dtype=np.float64).reshape(-1, n)
     for threads in (cores, 1):
         with threadpoolctl.threadpool_limits(threads):
             oracle.product(S, A, Xa)
-            tp, td = [], []
+            tp, td, tm = [], [], []
             for _ in range(runs):
                 t = time.perf_counter()
                 oracle.product(S, A, Xa)
                 tp.append(time.perf_counter() - t)
                 t = time.perf_counter()
-                oracle.dequantize(S, A)
+                Wd = oracle.dequantize(S, A)
                 td.append(time.perf_counter() - t)
-        res[threads] = (statistics.median(tp), statistics.median(td))
+                # O3 on its own: the oracle's matmul of the dequantized weights
+                t = time.perf_counter()
+                X2 @ Wd.T
+                tm.append(time.perf_counter() - t)
+        res[threads] = (statistics.median(tp), statistics.median(td), statistics.median(tm))
     scale = 1e9 if unit == "GB/s" else 1e12
     model, blas = _cpu_facts()
-    tp, td = res[cores]
+    tp, td, tm = res[cores]
     return {"value": work / tp / scale, "unit": unit, "cores": cores, "kind": "oracle",
             "value_1_thread": work / res[1][0] / scale,
             "sample": f"oracle.product (fp64 dequantize + matmul) of rows 0..{rows - 1} of the "
                       f"{m}x{n} layer, K={K}, T={T}; median of {runs} runs after 1 warm-up",
-            "o2_dequantize_s": round(td, 4), "o3_matmul_s": round(tp - td, 4),
+            "o2_dequantize_s": round(td, 5), "o3_matmul_s": round(tm, 5),
             "o1_quantize_s": round(t_o1, 3), "o1_rows": rows,
             "cpu_model": model, "blas": blas, "blas_threads": cores}
 
@@ -781,6 +791,18 @@ def main():
             "pct_bf16_peak_of_value": round(100 * ptf / BF16_MFMA_PEAK_TFLOPS, 2),
             "dtype": "bf16 x and bf16 W_hat tiles, f16 alpha, f32 accumulate",
             "pool": _pool(ptimed), "roofline": proof}
+        # the same workload through the two-term product (hi + lo bf16 levels)
+        note("prefill: two-term product")
+        pw.precise = True
+        qsteps = max(1, args.steps // 4)
+        qtimed = measure_steps(pw, qsteps, max(1, args.warmup // 4),
+                               use_graph=not args.no_graph)
+        qms = qtimed["ms_per_step"]
+        line["prefill"]["precise"] = {
+            "entry": "mbok_gemm_precise", "steps": qsteps, "ms_per_step": qms,
+            "value": pw.flops / (qms * 1e-3) / 1e12, "unit": "TFLOP/s",
+            "dtype": "bf16 x, two bf16 terms per W_hat level, f16 alpha, f32 accumulate",
+            "pool": _pool(qtimed)}
         del pw
         torch.cuda.empty_cache()
         # the LLaMA-7B MLP decode shapes (gate/up 11008x4096, down 4096x11008, K=3)

@@ -19,7 +19,8 @@ __all__ = [
     "MbokError", "mbok_desc", "library_path", "load_library",
     "mbok_desc_init", "mbok_packed_bytes", "mbok_alpha_bytes", "mbok_residual_binarize",
     "mbok_refit", "MBOK_MAX_REFIT_ROUNDS", "mbok_residual_energy", "mbok_allocate_kernels",
-    "mbok_pack", "mbok_gemv", "mbok_gemv_workspace_bytes", "mbok_gemm", "mbok_status_str",
+    "mbok_pack", "mbok_gemv", "mbok_gemv_workspace_bytes", "mbok_gemm", "mbok_gemm_precise",
+    "mbok_status_str",
     "mbok_gemvt", "mbok_gemvt_workspace_bytes", "mbok_gemvt_noalloc", "mbok_gemvt_scratch_bytes",
     "mbok_svid_workspace_bytes", "mbok_svid_decompose", "mbok_svid_pack",
     "mbok_svid_gemv_workspace_bytes", "mbok_svid_gemv", "MBOK_MAX_SVID_ITERS",
@@ -84,6 +85,7 @@ def load_library() -> ctypes.CDLL:
         "mbok_gemv_workspace_bytes": (SZ, [D]),
         "mbok_gemv": (ctypes.c_int, [D, P, P, I32, P, P, P]),
         "mbok_gemm": (ctypes.c_int, [D, P, P, I32, I64, I64, P, I64, P]),
+        "mbok_gemm_precise": (ctypes.c_int, [D, P, P, I32, I64, I64, P, I64, P]),
         "mbok_gemvt_workspace_bytes": (SZ, [D]),
         "mbok_gemvt": (ctypes.c_int, [D, P, P, I32, P, P, P]),
         "mbok_gemvt_scratch_bytes": (SZ, []),
@@ -464,6 +466,17 @@ def mbok_svid_gemv(d: mbok_desc, packed: torch.Tensor, s_in: torch.Tensor, x: to
 def mbok_gemm(d: mbok_desc, packed: torch.Tensor, X: torch.Tensor, Y: torch.Tensor,
               stream=None) -> None:
     """Y[T, m] (fp32, overwritten) = X W_hat^T for X bf16 [T, n] (row stride ldx)."""
+    _gemm_call("mbok_gemm", d, packed, X, Y, stream)
+
+
+def mbok_gemm_precise(d: mbok_desc, packed: torch.Tensor, X: torch.Tensor, Y: torch.Tensor,
+                      stream=None) -> None:
+    """mbok_gemm with each prefill weight carried as two bf16 terms (hi + lo)."""
+    _gemm_call("mbok_gemm_precise", d, packed, X, Y, stream)
+
+
+def _gemm_call(name: str, d: mbok_desc, packed: torch.Tensor, X: torch.Tensor, Y: torch.Tensor,
+               stream) -> None:
     _dev(packed, "packed"), _dev(X, "X"), _dev(Y, "Y")
     if _nbytes_from(packed) < mbok_packed_bytes(d):
         raise ValueError("packed buffer too small")
@@ -480,8 +493,9 @@ def mbok_gemm(d: mbok_desc, packed: torch.Tensor, X: torch.Tensor, Y: torch.Tens
             raise ValueError("X buffer too small")
         if _nbytes_from(Y) < ((T - 1) * ldy + d.m) * 4:
             raise ValueError("Y buffer too small")
-    _check(load_library().mbok_gemm(ctypes.byref(d), packed.data_ptr(), X.data_ptr(), xd, T,
-                                    ldx, Y.data_ptr(), ldy, _stream(stream)), "mbok_gemm")
+    fn = getattr(load_library(), name)
+    _check(fn(ctypes.byref(d), packed.data_ptr(), X.data_ptr(), xd, T, ldx, Y.data_ptr(), ldy,
+              _stream(stream)), name)
 
 
 # ---------------------------------------------------------------- conveniences

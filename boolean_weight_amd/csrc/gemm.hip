@@ -59,7 +59,15 @@ struct Levels {
   uint32_t lo_a, lo_b, hi_a, hi_b;
 };
 
-template <int K>
+// What is left of an fp32 value after its rounding to bf16.  The difference
+// is exact in fp32 (it is v's own low significand bits) and at most half a
+// bf16 ulp of v, so hi + bf16(lo) carries 16 significant bits of v.
+__device__ __forceinline__ float bf16_residue(float v) { return v - (float)(__bf16)v; }
+
+// LO = false: the levels rounded to bf16 (the default product).  LO = true:
+// the bf16 rounding of each level's residue, for the second pass of the
+// two-pass product (hi + lo levels, ~2^-16 relative error per weight).
+template <int K, bool LO = false>
 __device__ __forceinline__ Levels make_levels(const float* a) {
   float l[8];
 #pragma unroll
@@ -67,7 +75,7 @@ __device__ __forceinline__ Levels make_levels(const float* a) {
     float v = (idx & 1) ? a[0] : -a[0];
     if (K >= 2) v += (idx & 2) ? a[1] : -a[1];
     if (K >= 3) v += (idx & 4) ? a[2] : -a[2];
-    l[idx] = v;
+    l[idx] = LO ? bf16_residue(v) : v;
   }
   const uint32_t p01 = bf16_pair(l[0], l[1]), p23 = bf16_pair(l[2], l[3]);
   const uint32_t p45 = bf16_pair(l[4], l[5]), p67 = bf16_pair(l[6], l[7]);
@@ -103,7 +111,8 @@ __device__ __forceinline__ void unpack_word(const uint32_t* w, const Levels& L, 
   }
 }
 
-// K = 4 (16 levels): direct fp32 sums, then bf16.
+// K = 4 (16 levels): direct fp32 sums, then bf16 (LO: their residues).
+template <bool LO = false>
 __device__ __forceinline__ void unpack_word_k4(const uint32_t* w, const float* a, uint32_t* out) {
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
@@ -113,7 +122,7 @@ __device__ __forceinline__ void unpack_word_k4(const uint32_t* w, const float* a
       float s = 0.f;
 #pragma unroll
       for (int k = 0; k < 4; ++k) s += ((w[k] >> (8 * e + q)) & 1u) ? a[k] : -a[k];
-      v[e] = s;
+      v[e] = LO ? bf16_residue(s) : s;
     }
     out[2 * q] = bf16_pair(v[0], v[1]);
     out[2 * q + 1] = bf16_pair(v[2], v[3]);
@@ -147,7 +156,14 @@ __device__ __forceinline__ void unpack_quads(const uint32_t* V, int a, const Lev
   }
 }
 
-template <typename AT, int K>
+// Output element of a tile: the first pass (or the one-pass product) stores
+// its sum; the residue pass adds its sum to what the first pass stored.
+template <bool LO>
+__device__ __forceinline__ void store_out(float* y, float v) {
+  *y = LO ? *y + v : v;
+}
+
+template <typename AT, int K, bool LO>
 __global__ void __launch_bounds__(GEMM_THREADS) gemm_mfma_kernel(
     const uint2* __restrict__ bits, const AT* __restrict__ scales, const uint16_t* __restrict__ X,
     int64_t ldx, float* __restrict__ Y, int64_t ldy, int T, int m, int m_pad, int G) {
@@ -228,7 +244,7 @@ __global__ void __launch_bounds__(GEMM_THREADS) gemm_mfma_kernel(
   // (new levels).
   auto step = [&](int cb, StepRegs& R, bool even) {
     mask_step(R);
-    if (K <= 3 && even) L = make_levels<K>(R.a);
+    if (K <= 3 && even) L = make_levels<K, LO>(R.a);
     const uint16_t* xs = smem + 2 * cb * TILE_ELEMS + (wt * 128 + lrow) * LDS_STRIDE + lk;
     const uint16_t* ws = smem + (2 * cb + 1) * TILE_ELEMS + (wn * 128 + lrow) * LDS_STRIDE + lk;
     uint16_t* xd = smem + 2 * (cb ^ 1) * TILE_ELEMS + (tid >> 3) * LDS_STRIDE + xpart * 8;
@@ -275,7 +291,7 @@ __global__ void __launch_bounds__(GEMM_THREADS) gemm_mfma_kernel(
         uint32_t w[K], o32[16];
 #pragma unroll
         for (int k = 0; k < K; ++k) w[k] = (kk >> 1) ? R.w[k].y : R.w[k].x;
-        unpack_word_k4(w, R.a, o32);
+        unpack_word_k4<LO>(w, R.a, o32);
 #pragma unroll
         for (int q = 0; q < 8; ++q) out[q] = o32[8 * (kk & 1) + q];
       }
@@ -298,7 +314,7 @@ __global__ void __launch_bounds__(GEMM_THREADS) gemm_mfma_kernel(
   load_step(1, R1);
   mask_step(R0);
   {
-    if (K <= 3) L = make_levels<K>(R0.a);
+    if (K <= 3) L = make_levels<K, LO>(R0.a);
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       *reinterpret_cast<uint4*>(smem + (tid >> 3) * LDS_STRIDE + xpart * 8 + j * 32 * LDS_STRIDE) =
@@ -312,7 +328,7 @@ __global__ void __launch_bounds__(GEMM_THREADS) gemm_mfma_kernel(
       if (K <= 3)
         unpack_word<K>(w, L, out);
       else
-        unpack_word_k4(w, R0.a, out);
+        unpack_word_k4<LO>(w, R0.a, out);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         wd[4 * h + j] = make_uint4(out[4 * j], out[4 * j + 1], out[4 * j + 2], out[4 * j + 3]);
@@ -340,7 +356,7 @@ __global__ void __launch_bounds__(GEMM_THREADS) gemm_mfma_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int t = t0 + wt * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (t < T) Y[(int64_t)t * ldy + n] = acc[i][j][r];
+        if (t < T) store_out<LO>(Y + (int64_t)t * ldy + n, acc[i][j][r]);
       }
     }
 }
@@ -377,7 +393,7 @@ __device__ __forceinline__ void unpack_two_quads(const uint32_t* V, int a, int b
 // The body of one workgroup: JB = 2 for a whole 256-row tile, 1 for one
 // 128-row half of a tile of the partial final round (a compile-time constant,
 // so the loop has no branches on it).
-template <typename AT, int K, int JB>
+template <typename AT, int K, int JB, bool LO>
 __device__ __forceinline__ void mfma8_tile(const uint32_t* __restrict__ bits,
                                            const AT* __restrict__ scales,
                                            const uint16_t* __restrict__ X, int64_t ldx,
@@ -463,7 +479,7 @@ __device__ __forceinline__ void mfma8_tile(const uint32_t* __restrict__ bits,
     if (K <= 3 && even) {
       float af[K];
       scales_f32(R, af);
-      L = make_levels<K>(af);
+      L = make_levels<K, LO>(af);
     }
     const uint16_t* xs =
         smem + 2 * cb * TILE_ELEMS + (wt * 32 * TI + lrow) * LDS_STRIDE + lk;
@@ -518,7 +534,7 @@ __device__ __forceinline__ void mfma8_tile(const uint32_t* __restrict__ bits,
           uint32_t o32[16];
           float af[K];
           scales_f32(R, af);
-          unpack_word_k4(R.w, af, o32);
+          unpack_word_k4<LO>(R.w, af, o32);
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             out[e] = JB == 2 ? o32[4 * kk + e] : (h ? o32[8 + 4 * kk + e] : o32[4 * kk + e]);
@@ -534,7 +550,7 @@ __device__ __forceinline__ void mfma8_tile(const uint32_t* __restrict__ bits,
   {
     float af0[K];
     scales_f32(R0, af0);
-    if (K <= 3) L = make_levels<K>(af0);
+    if (K <= 3) L = make_levels<K, LO>(af0);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       *reinterpret_cast<u32x4*>(smem + (tid >> 3) * LDS_STRIDE + xpart * 8 + j * 64 * LDS_STRIDE) =
@@ -546,7 +562,7 @@ __device__ __forceinline__ void mfma8_tile(const uint32_t* __restrict__ bits,
       if (K <= 3)
         unpack_word<K>(R0.w, L, out);
       else
-        unpack_word_k4(R0.w, af0, out);
+        unpack_word_k4<LO>(R0.w, af0, out);
       // out[4 p .. 4 p + 3]: 8-column piece p of the word (a half tile's
       // thread takes pieces 2 h, 2 h + 1; constant indices, h selects)
       constexpr int NP = 4 / (TPR / 2);  // pieces per thread: 4 or 2
@@ -583,7 +599,7 @@ __device__ __forceinline__ void mfma8_tile(const uint32_t* __restrict__ bits,
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int t = t0 + wt * 32 * TI + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (t < T) Y[(int64_t)t * ldy + n] = acc[i][j][r];
+        if (t < T) store_out<LO>(Y + (int64_t)t * ldy + n, acc[i][j][r]);
       }
     }
 }
@@ -601,7 +617,7 @@ __device__ __forceinline__ int tile_at(int p, int ntx, int nty) {
   return 2 * q * ntx + rem;
 }
 
-template <typename AT, int K>
+template <typename AT, int K, bool LO>
 __global__ void __launch_bounds__(GEMM8_THREADS) gemm_mfma8_kernel(
     const uint32_t* __restrict__ bits, const AT* __restrict__ scales,
     const uint16_t* __restrict__ X, int64_t ldx, float* __restrict__ Y, int64_t ldy, int T, int m,
@@ -613,11 +629,11 @@ __global__ void __launch_bounds__(GEMM8_THREADS) gemm_mfma8_kernel(
     int p = b;
     if (xcd_order && (nfull & 7) == 0) p = (b & 7) * (nfull >> 3) + (b >> 3);
     const int tile = xcd_order ? tile_at(p, ntx, nty) : p;
-    mfma8_tile<AT, K, 2>(bits, scales, X, ldx, Y, ldy, T, m, m_pad, G, ntx, tile, 0, smem);
+    mfma8_tile<AT, K, 2, LO>(bits, scales, X, ldx, Y, ldy, T, m, m_pad, G, ntx, tile, 0, smem);
   } else {
     const int p = nfull + ((b - nfull) >> 1);
     const int tile = xcd_order ? tile_at(p, ntx, nty) : p;
-    mfma8_tile<AT, K, 1>(bits, scales, X, ldx, Y, ldy, T, m, m_pad, G, ntx, tile,
+    mfma8_tile<AT, K, 1, LO>(bits, scales, X, ldx, Y, ldy, T, m, m_pad, G, ntx, tile,
                          (b - nfull) & 1, smem);
   }
 }
@@ -645,7 +661,7 @@ int gemm_xcd_order() {
   return v && strcmp(v, "token") == 0 ? 0 : 1;
 }
 
-template <typename AT, int K>
+template <typename AT, int K, bool LO>
 void launch_mfma8_k(const Geom& geo, const uint32_t* bits, const AT* scales, const uint16_t* Xb,
                     int64_t T, int64_t ldx, float* Y, int64_t ldy, hipStream_t stream) {
   const size_t lds = 4 * TILE_ELEMS * sizeof(uint16_t);
@@ -655,25 +671,24 @@ void launch_mfma8_k(const Geom& geo, const uint32_t* bits, const AT* scales, con
   const int ncu = compute_units();
   const int64_t rem = ntiles % ncu;
   const int64_t nfull = ntiles - rem;
-  hipLaunchKernelGGL((gemm_mfma8_kernel<AT, K>), dim3((unsigned)(nfull + 2 * rem)),
+  hipLaunchKernelGGL((gemm_mfma8_kernel<AT, K, LO>), dim3((unsigned)(nfull + 2 * rem)),
                      dim3(GEMM8_THREADS), lds, stream, bits, scales, Xb, ldx, Y, ldy, (int)T,
                      geo.m, geo.RB * kRowBlock, geo.G, ntx, (int)nfull, gemm_xcd_order());
 }
 
-template <typename AT>
-int launch_mfma8(const Geom& geo, const void* packed, const void* X, int64_t T, int64_t ldx,
-                 float* Y, int64_t ldy, hipStream_t stream) {
+template <typename AT, bool LO>
+void launch_mfma8(const Geom& geo, const void* packed, const void* X, int64_t T, int64_t ldx,
+                  float* Y, int64_t ldy, hipStream_t stream) {
   const uint32_t* bits = reinterpret_cast<const uint32_t*>(packed);
   const AT* scales = reinterpret_cast<const AT*>(reinterpret_cast<const char*>(packed) +
                                                  geo.bits_bytes);
   const uint16_t* Xb = reinterpret_cast<const uint16_t*>(X);
   switch (geo.K) {
-    case 1: launch_mfma8_k<AT, 1>(geo, bits, scales, Xb, T, ldx, Y, ldy, stream); break;
-    case 2: launch_mfma8_k<AT, 2>(geo, bits, scales, Xb, T, ldx, Y, ldy, stream); break;
-    case 3: launch_mfma8_k<AT, 3>(geo, bits, scales, Xb, T, ldx, Y, ldy, stream); break;
-    default: launch_mfma8_k<AT, 4>(geo, bits, scales, Xb, T, ldx, Y, ldy, stream); break;
+    case 1: launch_mfma8_k<AT, 1, LO>(geo, bits, scales, Xb, T, ldx, Y, ldy, stream); break;
+    case 2: launch_mfma8_k<AT, 2, LO>(geo, bits, scales, Xb, T, ldx, Y, ldy, stream); break;
+    case 3: launch_mfma8_k<AT, 3, LO>(geo, bits, scales, Xb, T, ldx, Y, ldy, stream); break;
+    default: launch_mfma8_k<AT, 4, LO>(geo, bits, scales, Xb, T, ldx, Y, ldy, stream); break;
   }
-  return hipGetLastError() == hipSuccess ? MBOK_OK : MBOK_ERR_HIP;
 }
 
 bool use_mfma8() {
@@ -681,12 +696,9 @@ bool use_mfma8() {
   return !(v && atoi(v) == 4);
 }
 
-template <typename AT>
-int launch_mfma(const Geom& geo, const void* packed, const void* X, int64_t T, int64_t ldx,
-                float* Y, int64_t ldy, hipStream_t stream) {
-  // the 8-wavefront kernel indexes signs and activations with 32-bit offsets
-  const bool fits32 = geo.bits_bytes / 4 < (int64_t(1) << 32) && T * ldx < (int64_t(1) << 32);
-  if (fits32 && use_mfma8()) return launch_mfma8<AT>(geo, packed, X, T, ldx, Y, ldy, stream);
+template <typename AT, bool LO>
+void launch_mfma4(const Geom& geo, const void* packed, const void* X, int64_t T, int64_t ldx,
+                  float* Y, int64_t ldy, hipStream_t stream) {
   const uint2* bits = reinterpret_cast<const uint2*>(packed);
   const AT* scales = reinterpret_cast<const AT*>(reinterpret_cast<const char*>(packed) +
                                                  geo.bits_bytes);
@@ -696,21 +708,38 @@ int launch_mfma(const Geom& geo, const void* packed, const void* X, int64_t T, i
   const uint16_t* Xb = reinterpret_cast<const uint16_t*>(X);
   switch (geo.K) {
     case 1:
-      hipLaunchKernelGGL((gemm_mfma_kernel<AT, 1>), grid, dim3(GEMM_THREADS), lds, stream, bits,
-                         scales, Xb, ldx, Y, ldy, (int)T, geo.m, m_pad, geo.G);
+      hipLaunchKernelGGL((gemm_mfma_kernel<AT, 1, LO>), grid, dim3(GEMM_THREADS), lds, stream,
+                         bits, scales, Xb, ldx, Y, ldy, (int)T, geo.m, m_pad, geo.G);
       break;
     case 2:
-      hipLaunchKernelGGL((gemm_mfma_kernel<AT, 2>), grid, dim3(GEMM_THREADS), lds, stream, bits,
-                         scales, Xb, ldx, Y, ldy, (int)T, geo.m, m_pad, geo.G);
+      hipLaunchKernelGGL((gemm_mfma_kernel<AT, 2, LO>), grid, dim3(GEMM_THREADS), lds, stream,
+                         bits, scales, Xb, ldx, Y, ldy, (int)T, geo.m, m_pad, geo.G);
       break;
     case 3:
-      hipLaunchKernelGGL((gemm_mfma_kernel<AT, 3>), grid, dim3(GEMM_THREADS), lds, stream, bits,
-                         scales, Xb, ldx, Y, ldy, (int)T, geo.m, m_pad, geo.G);
+      hipLaunchKernelGGL((gemm_mfma_kernel<AT, 3, LO>), grid, dim3(GEMM_THREADS), lds, stream,
+                         bits, scales, Xb, ldx, Y, ldy, (int)T, geo.m, m_pad, geo.G);
       break;
     default:
-      hipLaunchKernelGGL((gemm_mfma_kernel<AT, 4>), grid, dim3(GEMM_THREADS), lds, stream, bits,
-                         scales, Xb, ldx, Y, ldy, (int)T, geo.m, m_pad, geo.G);
+      hipLaunchKernelGGL((gemm_mfma_kernel<AT, 4, LO>), grid, dim3(GEMM_THREADS), lds, stream,
+                         bits, scales, Xb, ldx, Y, ldy, (int)T, geo.m, m_pad, geo.G);
       break;
+  }
+}
+
+// passes = 1: one product with the levels rounded to bf16.  passes = 2: that
+// product, then on the same stream a second one with the bf16 residues of the
+// levels, added into Y (the stream orders the two launches).
+template <typename AT>
+int launch_mfma(const Geom& geo, const void* packed, const void* X, int64_t T, int64_t ldx,
+                float* Y, int64_t ldy, int passes, hipStream_t stream) {
+  // the 8-wavefront kernel indexes signs and activations with 32-bit offsets
+  const bool fits32 = geo.bits_bytes / 4 < (int64_t(1) << 32) && T * ldx < (int64_t(1) << 32);
+  if (fits32 && use_mfma8()) {
+    launch_mfma8<AT, false>(geo, packed, X, T, ldx, Y, ldy, stream);
+    if (passes == 2) launch_mfma8<AT, true>(geo, packed, X, T, ldx, Y, ldy, stream);
+  } else {
+    launch_mfma4<AT, false>(geo, packed, X, T, ldx, Y, ldy, stream);
+    if (passes == 2) launch_mfma4<AT, true>(geo, packed, X, T, ldx, Y, ldy, stream);
   }
   return hipGetLastError() == hipSuccess ? MBOK_OK : MBOK_ERR_HIP;
 }
@@ -718,14 +747,14 @@ int launch_mfma(const Geom& geo, const void* packed, const void* X, int64_t T, i
 }  // namespace
 
 int launch_gemm(const mbok_desc* d, const void* packed, const void* X, int64_t T, int64_t ldx,
-                float* Y, int64_t ldy, hipStream_t stream) {
+                float* Y, int64_t ldy, int passes, hipStream_t stream) {
   const Geom geo = make_geom(d);
   if (T == 1) return launch_gemv(d, packed, X, MBOK_BF16, Y, nullptr, stream);
   if (T <= skinny_max_tokens()) return launch_skinny(d, packed, X, T, ldx, Y, ldy, stream);
   if (T > 65535LL * BT) return MBOK_ERR_SHAPE;
   if (d->alpha_dtype == MBOK_F16)
-    return launch_mfma<uint16_t>(geo, packed, X, T, ldx, Y, ldy, stream);
-  return launch_mfma<float>(geo, packed, X, T, ldx, Y, ldy, stream);
+    return launch_mfma<uint16_t>(geo, packed, X, T, ldx, Y, ldy, passes, stream);
+  return launch_mfma<float>(geo, packed, X, T, ldx, Y, ldy, passes, stream);
 }
 
 }  // namespace mbok

@@ -208,8 +208,9 @@ int mbok_gemvt_noalloc(const mbok_desc* d, const void* packed, const void* g, in
   return mbok::launch_gemvt_noalloc(d, packed, g, g_dtype, dx, (hipStream_t)stream);
 }
 
-int mbok_gemm(const mbok_desc* d, const void* packed, const void* X, int32_t x_dtype, int64_t T,
-              int64_t ldx, float* Y, int64_t ldy, void* stream) {
+static int gemm_checked(const mbok_desc* d, const void* packed, const void* X, int32_t x_dtype,
+                        int64_t T, int64_t ldx, float* Y, int64_t ldy, int passes,
+                        void* stream) {
   int st = check_desc(d);
   if (st != MBOK_OK) return st;
   if (!packed || !X || !Y) return MBOK_ERR_INVALID_ARG;
@@ -218,7 +219,17 @@ int mbok_gemm(const mbok_desc* d, const void* packed, const void* X, int32_t x_d
   if (x_dtype != MBOK_BF16) return MBOK_ERR_DTYPE;
   if (!aligned(packed, 16) || !aligned(X, 16) || (ldx % 8) != 0 || !aligned(Y, 4))
     return MBOK_ERR_ALIGN;
-  return mbok::launch_gemm(d, packed, X, T, ldx, Y, ldy, (hipStream_t)stream);
+  return mbok::launch_gemm(d, packed, X, T, ldx, Y, ldy, passes, (hipStream_t)stream);
+}
+
+int mbok_gemm(const mbok_desc* d, const void* packed, const void* X, int32_t x_dtype, int64_t T,
+              int64_t ldx, float* Y, int64_t ldy, void* stream) {
+  return gemm_checked(d, packed, X, x_dtype, T, ldx, Y, ldy, 1, stream);
+}
+
+int mbok_gemm_precise(const mbok_desc* d, const void* packed, const void* X, int32_t x_dtype,
+                      int64_t T, int64_t ldx, float* Y, int64_t ldy, void* stream) {
+  return gemm_checked(d, packed, X, x_dtype, T, ldx, Y, ldy, 2, stream);
 }
 
 const char* mbok_status_str(int status) {

@@ -41,7 +41,9 @@ int launch_svid_skinny(const mbok_desc* d, const void* packed, const void* x, in
                        const void* s_in, float* y, hipStream_t stream);
 int allocate_kernels(int L, const int64_t* sizes, const double* errors, int kmax, int64_t budget,
                      int32_t* K_out);
+// passes: 1 = prefill levels rounded to bf16; 2 = plus a second pass with
+// the bf16 residues of the levels (T <= 16 runs the same kernels either way)
 int launch_gemm(const mbok_desc* d, const void* packed, const void* X, int64_t T, int64_t ldx,
-                float* Y, int64_t ldy, hipStream_t stream);
+                float* Y, int64_t ldy, int passes, hipStream_t stream);
 
 }  // namespace mbok

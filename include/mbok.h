@@ -458,6 +458,28 @@ int mbok_gemm(const mbok_desc* d, const void* packed, const void* X,
               int32_t x_dtype, int64_t T, int64_t ldx, float* Y, int64_t ldy,
               void* stream);
 
+/*
+ * mbok_gemm with the prefill weights carried to 16 significant bits ([RN]
+ * 关键设计: W_hat x is the sum of the K scaled Boolean products, each weight
+ * exactly sum_k alpha_k b_k; carrying that value to the matrix cores needs
+ * more than bf16's 8 significant bits).  Same arguments, checks, errors and
+ * output layout as mbok_gemm; T <= 16 runs exactly the same kernels as
+ * mbok_gemm (their products are already fp32-exact per scale).  For T > 16
+ * each level v = sum_k +-alpha_k is formed in fp32 and split as
+ * v = hi + lo with hi = bf16(v) and lo = bf16(v - hi), so |v - hi - lo| <=
+ * 2^-16 |v|.  Two products run on `stream`: Y = X . HI^T, then Y += X . LO^T
+ * (two launches, about twice the time and one extra read of Y).  Per output,
+ * |Y - Y_exact| stays far below 1e-3 * sum_j |W_hat_ij| |X_tj| for any X
+ * (2^-16 from the weights plus fp32 accumulation), where mbok_gemm's
+ * one-term bf16 levels allow up to 2^-8 per weight.  The result is exactly
+ * the fp64 product when every level has at most 16 significant bits (power-
+ * of-two scales within 15 binades of each other) and the activations and sums
+ * are small integers.
+ */
+int mbok_gemm_precise(const mbok_desc* d, const void* packed, const void* X,
+                      int32_t x_dtype, int64_t T, int64_t ldx, float* Y,
+                      int64_t ldy, void* stream);
+
 /* Static description of a status code ("unknown status" for others). */
 const char* mbok_status_str(int status);
 

@@ -11,7 +11,8 @@ Workloads (all synthetic; no checkpoint or dataset is read):
   * x ~ N(0, 1), rounded to bf16 (nearest-even) where the workload is bf16,
     kept fp32 otherwise.
   * "exact" inputs for bit-exact checks: integer activations in [-8, 8] and
-    power-of-two scales 2^-e, e in {4..8}, with uniformly random +-1 signs.
+    power-of-two scales 2^-e, e in {4..8}, with uniformly random +-1 signs;
+    "spread" scales 2^-e with e in {2..13} for the two-term prefill product.
 Generator: numpy.random.default_rng(seed) (PCG64).
 """
 from __future__ import annotations
@@ -102,6 +103,15 @@ def exact_alpha(K: int, m: int, groups: int, seed: int) -> np.ndarray:
     """fp32 [K, m, groups] of 2^-e with e uniform in {4,...,8}."""
     rng = np.random.default_rng(seed)
     e = rng.integers(4, 9, size=(K, m, groups))
+    return np.ldexp(np.float32(1.0), -e).astype(np.float32)
+
+
+def spread_alpha(K: int, m: int, groups: int, seed: int, lo: int = 2, hi: int = 13) -> np.ndarray:
+    """fp32 [K, m, groups] of 2^-e with e uniform in {lo,...,hi}: power-of-two
+    scales spread over many binades (levels with up to hi - lo + 1 significant
+    bits)."""
+    rng = np.random.default_rng(seed)
+    e = rng.integers(lo, hi + 1, size=(K, m, groups))
     return np.ldexp(np.float32(1.0), -e).astype(np.float32)
 
 

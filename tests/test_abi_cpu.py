@@ -129,6 +129,16 @@ def test_compute_calls_validate_before_launch(lib):
     assert lib.mbok_gemm(R(d), A16, A16, bw.MBOK_BF16, 65537, 256, A16, 64, None) == -2
     assert lib.mbok_gemm(R(d), A16, A16, bw.MBOK_BF16, 4, 128, A16, 64, None) == -1
     assert lib.mbok_gemm(R(d), A16, A16, bw.MBOK_BF16, 4, 256, A16, 63, None) == -1
+    # the two-term prefill product takes the same checks
+    for args, code in [((None, A16, bw.MBOK_BF16, 4, 256, A16, 64), -1),
+                       ((A16, A16, bw.MBOK_F32, 4, 256, A16, 64), -3),
+                       ((A16, A16, bw.MBOK_BF16, 4, 260, A16, 64), -4),
+                       ((A16, MIS, bw.MBOK_BF16, 4, 256, A16, 64), -4),
+                       ((A16, A16, bw.MBOK_BF16, 0, 256, A16, 64), -2),
+                       ((A16, A16, bw.MBOK_BF16, 65537, 256, A16, 64), -2),
+                       ((A16, A16, bw.MBOK_BF16, 4, 128, A16, 64), -1),
+                       ((A16, A16, bw.MBOK_BF16, 4, 256, A16, 63), -1)]:
+        assert lib.mbok_gemm_precise(R(d), *args, None) == code, args
     assert lib.mbok_residual_binarize(R(d), A16, 128, A16, A16, None, None) == -1
     # SVID
     assert lib.mbok_svid_decompose(R(d), None, 256, A16, A16, A16, 8, A16, None) == -1

@@ -1,0 +1,175 @@
+"""The two-term prefill product (mbok_gemm_precise) against the oracle.
+
+The default prefill kernel rounds every weight level sum_k +-alpha_k to bf16
+(8 significant bits) before the matrix cores, so a weight can be off by up to
+2^-8 of itself, and an activation vector aligned with those roundings can push
+a row's error past 1e-3 * sum_j |W_hat_ij| |x_j|.  The two-term product adds
+a second pass with the bf16 residues of the levels (16 significant bits in
+all).  Here:
+  * power-of-two scales spread over 12 binades (levels with up to 12
+    significant bits) and integer activations: the two-term product equals
+    the fp64 definition bit for bit, for both prefill kernels; the one-term
+    product stays within its stated 2^-8 per-weight bound;
+  * an adversarial activation per token, built on the host from the rounding
+    errors of the one-term levels of one row: the one-term product exceeds the
+    1e-3 bound on those rows (so the input does what it is meant to do), the
+    two-term product meets it;
+  * the prefill workload (11008 x 4096, K = 3, 2048 tokens), sampled rows;
+  * the two launches captured in a HIP graph, every replay equal to the eager
+    result.
+"""
+import numpy as np
+import pytest
+import torch
+
+import boolean_weight_amd as bw
+import mbok_synth as syn
+import oracle
+from gpu_util import DEV, pack_on_gpu, say, x_to_dev
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-3
+PREFILL_KERNELS = {"8": {"MBOK_GEMM_WAVES": "8"}, "4": {"MBOK_GEMM_WAVES": "4"}}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    bw.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+@pytest.fixture(params=list(PREFILL_KERNELS))
+def prefill_kernel(request, monkeypatch):
+    monkeypatch.delenv("MBOK_GEMM_ORDER", raising=False)
+    for k, v in PREFILL_KERNELS[request.param].items():
+        monkeypatch.setenv(k, v)
+    return request.param
+
+
+def run(fn, d, packed, X: np.ndarray) -> np.ndarray:
+    T, n = X.shape
+    Xt = x_to_dev(X, "bf16").view(T, n)
+    Y = torch.full((T, d.m), -777.25, dtype=torch.float32, device=DEV)
+    fn(d, packed, Xt, Y)
+    return Y.cpu().numpy().astype(np.float64)
+
+
+def one_term_levels(S: np.ndarray, A16: np.ndarray) -> np.ndarray:
+    """The weights as the one-term kernel carries them: each level summed in
+    fp32 in kernel order (k = 1 first), then rounded to bf16 (nearest-even).
+    Host-side input construction only (it picks the adversarial activations)."""
+    a = np.repeat(A16.astype(np.float32), 128, axis=2)  # [K, m, n]
+    v = (S[0].astype(np.float32) * a[0]).astype(np.float32)
+    for k in range(1, S.shape[0]):
+        v = (v + (S[k].astype(np.float32) * a[k]).astype(np.float32)).astype(np.float32)
+    return syn.bf16_to_f32(syn.bf16_bits(v)).astype(np.float64)
+
+
+@pytest.mark.parametrize("K", [2, 3, 4])
+@pytest.mark.parametrize("T", [17, 300])
+def test_precise_exact_with_spread_scales(T, K, prefill_kernel):
+    """Scales 2^-e with e in 2..13 (levels of up to 12 significant bits) and
+    integer activations in [-8, 8], n = 256: every partial sum is a multiple of
+    2^-13 below 2^11, so fp32 holds it exactly and the two-term product must
+    equal the fp64 definition bit for bit.  The one-term product is held to
+    its bound: at most 2^-8 of sum_j |W_hat_ij| |x_j| per output."""
+    m, n = 300, 256
+    say(f"precise spread T={T} K={K} kernel={prefill_kernel}")
+    S = syn.random_signs(K, m, n, seed=700 + 10 * T + K)
+    A = syn.spread_alpha(K, m, n // 128, seed=710 + T + K).astype(np.float16)
+    X = syn.exact_activations(T, n, seed=720 + T + K)
+    d, packed = pack_on_gpu(S, A, "f16")
+    want = oracle.product(S, A, X)
+    got = run(bw.mbok_gemm_precise, d, packed, X)
+    assert np.array_equal(got, want)
+    one = run(bw.mbok_gemm, d, packed, X)
+    assert oracle.max_error_ratio(one, want, oracle.bound(S, A, X)) <= 2.0 ** -8
+
+
+def test_precise_adversarial_activations():
+    """Token t is built against row r_t of a quantized N(0, 0.02) layer: x_j =
+    sign of the one-term rounding error of W_hat[r_t, j] where that error is
+    at least 2e-3 of the weight, else 0.  The one-term product's error on
+    (t, r_t) then exceeds 1e-3 of the bound; the two-term product meets it on
+    every output."""
+    K, m, n, T = 3, 96, 1024, 64
+    say("precise adversarial activations")
+    W = syn.weight(m, n, seed=731)
+    S, A, _ = oracle.residual_binarize(W, K, alpha_dtype="f16")
+    W_hat = oracle.dequantize(S, A)
+    err = one_term_levels(S, A) - W_hat
+    rel = np.abs(err) / np.maximum(np.abs(W_hat), 1e-30)
+    rows = np.arange(T) % m
+    X = np.where(rel[rows] >= 2e-3, np.sign(err[rows]), 0.0).astype(np.float32)
+    assert np.all(np.abs(X).sum(axis=1) > 0)
+    d, packed = pack_on_gpu(S, A, "f16")
+    want = oracle.product(S, A, X)
+    bound = oracle.bound(S, A, X)
+    one = run(bw.mbok_gemm, d, packed, X)
+    pick = (np.arange(T), rows)
+    ratio_one = np.abs(one[pick] - want[pick]) / bound[pick]
+    assert np.all(ratio_one > TOL), ratio_one.min()
+    got = run(bw.mbok_gemm_precise, d, packed, X)
+    assert oracle.max_error_ratio(got, want, bound) <= TOL
+    # the residue pass carries 16 significant bits: far inside the bound
+    assert oracle.max_error_ratio(got[pick], want[pick], bound[pick]) <= 1e-4
+
+
+def test_precise_prefill_workload():
+    """11008 x 4096, K = 3, 2048 tokens of N(0, 1) bf16 activations, quantized
+    on the device; sampled rows for every token against the oracle, and the
+    result is reproducible bit for bit."""
+    w = syn.WORKLOADS[5]
+    _, m, n = w["linears"][0]
+    T = w["T"][0]
+    say(f"precise prefill workload {m}x{n} T={T}")
+    W = syn.weight(m, n, syn.weight_seed(5))
+    X = syn.activations(T, n, syn.act_seed(5), "bf16")
+    d, packed, _, _ = bw.quantize_and_pack(torch.from_numpy(W).to(DEV), 3, bw.MBOK_F16)
+    got = run(bw.mbok_gemm_precise, d, packed, X)
+    rows = np.unique(np.r_[np.linspace(0, m - 1, 24).astype(int), m - 1])
+    S, A, _ = oracle.residual_binarize(W[rows], 3, alpha_dtype="f16")
+    assert oracle.max_error_ratio(got[:, rows], oracle.product(S, A, X),
+                                  oracle.bound(S, A, X)) <= TOL
+    again = run(bw.mbok_gemm_precise, d, packed, X)
+    assert np.array_equal(got, again)
+
+
+def test_precise_graph_replays():
+    """Both passes captured in one graph: every replay (output cleared before
+    it, eager library calls in between) gives the eager result."""
+    K, m, n, T = 3, 200, 384, 40
+    say("precise graph replays")
+    S = syn.random_signs(K, m, n, seed=741)
+    A = syn.spread_alpha(K, m, n // 128, seed=742).astype(np.float16)
+    X = syn.exact_activations(T, n, seed=743)
+    d, packed = pack_on_gpu(S, A, "f16")
+    Xt = x_to_dev(X, "bf16").view(T, n)
+    Y = torch.empty((T, m), dtype=torch.float32, device=DEV)
+    bw.mbok_gemm_precise(d, packed, Xt, Y)
+    torch.cuda.synchronize()
+    eager = Y.cpu().numpy()
+    assert np.array_equal(eager.astype(np.float64), oracle.product(S, A, X))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        bw.mbok_gemm_precise(d, packed, Xt, Y)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        bw.mbok_gemm_precise(d, packed, Xt, Y)
+    torch.cuda.synchronize()
+    other = torch.empty_like(Y)
+    for r in range(4):
+        Y.fill_(-31.5)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(Y.cpu().numpy(), eager), f"replay {r}"
+        bw.mbok_gemm(d, packed, Xt, other)
+        torch.cuda.synchronize()
