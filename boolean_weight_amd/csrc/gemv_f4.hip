@@ -7,43 +7,47 @@
 //
 // Each Boolean product of a 16-row tile is done by the scaled matrix-core
 // instruction v_mfma_scale_f32_16x16x128_f8f6f4 with an fp8 (e4m3) A operand
-// and an fp4 (e2m1) B operand:
-//  * B (128 columns x 16 rows of W): the signs.  Each becomes the fp4 nibble
-//    0b?010 (magnitude 1.0) whose sign bit ? is the stored bit, so B holds -b
-//    (the sum is negated once at the end).  Lane 16q + r holds row r's sign
-//    word q (32 columns) as four dwords of nibbles, one shift and one and-or
-//    each; nibble p of dword d takes bit 4p + d of the word, so product term
-//    k = 32q + 8d + p is column 32q + 16(p & 1) + 4d + (p >> 1) of the group
-//    (the packed bit order).
-//  * A (16 x 128): the activations of group j of the wavefront, a high fp8
-//    part in row 4j and a low fp8 part in row 4j + 1 (all other rows zero).
-//    With one E8M0 scale per 32 columns (the block's
-//    largest exponent minus 7) the high part keeps 4 significant bits and the
-//    low part (scale 2^-4 of it) the next 4, so together they hold the bf16
-//    activation exactly when it lies within 13 binades of its block's largest
-//    (below that the low part is rounded).
-//  * D: the four groups of a wavefront use disjoint rows of A, so their
-//    products of one kernel chain through one accumulator: D row 4j + e,
-//    column r (lane 16j + r, register e) is group j's high (e = 0) or low
-//    (e = 1) sum for row r.  That lane loaded alpha_k of (row r, group j)
-//    itself and adds alpha_k (hi + lo) to its fp32 sum.
-// The matrix cores add the 128 products of one block exactly when they span
-// a narrow range (small integers; bf16 values within 6 binades) and
-// otherwise drop bits far below the largest product: measured up to 1e-4 of
-// the sum of |products| with fp8 values over the whole e4m3 range, about
-// 1e-7 of the bound sum |W_hat| |x| on the workloads' Gaussian activations.
+// and an fp4 (e2m1) B operand, four instructions (one per 32-column word i of
+// a group) per (tile, kernel):
+//  * B (128 product terms x 16 rows of W): lane 16q + r loads the 16-byte
+//    chunk of (row r, group q of the wavefront, kernel k) and gives product i
+//    its word i, so K-block q of product i is word i of group q.  Nibble p of
+//    B dword d takes bit 4p + d of the word in place (one and-or per dword,
+//    no shift): product term kk = 8d + p of a word is column
+//    16 (p & 1) + 4d + (p >> 1) (the packed bit order), and its value is
+//    c_d + b for d < 3 (nibble bases 4.0/6.0, 2.0/4.0, 0/2.0: c = 5, 3, 1) and
+//    -b for d = 3 (1.0/-1.0), b = +1 for a set bit.
+//  * A (16 x 128): row 4q + e holds part e (0 high, 1 low) of the activations
+//    of group q's word i, nonzero only in K-block q; columns of class d = 3 are
+//    negated, so every product term is b x plus c_d x.  With one E8M0 scale
+//    per (row, 32-term block) (the word's largest exponent minus 7) the high
+//    part keeps 4 significant bits and the low part (scale 2^-4 of it) the
+//    next 4, so together they hold the bf16 activation exactly when it lies
+//    within 13 binades of its word's largest (below that the low part is
+//    rounded).
+//  * D: lane 16j + r, registers 0 and 1, accumulate over the four words group
+//    j's high and low sums for row r, each sum_j b x + C_j where C_j =
+//    sum (5 x, 3 x, x) over the group's columns of classes 0, 1, 2.  C_j is
+//    formed once per group in fp32 while the activations are converted, and
+//    the lane adds alpha_k (hi + lo - C_j) to its fp32 sum; the kernels'
+//    product chains are interleaved.
+// The matrix cores add the products of one instruction exactly when they span
+// a narrow range (small integers; bf16 values within a few binades) and
+// otherwise drop bits far below the largest product: about 1e-6 of the bound
+// sum |W_hat| |x| on the workloads' Gaussian activations.
 //
 // Work split: one persistent workgroup per compute unit walks 16-row tiles
 // (XCD-aware order); wavefront w owns groups 4w .. 4w+3 of a column slab of
 // at most 64 groups.  Per (tile, kernel) a wavefront issues one 16-byte sign
 // load per lane (16-lane block j: the 16 rows of group j, 256 contiguous
-// bytes) and one 2-byte scale load, and transposes the (16-lane block, word)
-// matrix with two v_permlane32_swap and two v_permlane16_swap; tile t+3 is
-// loaded while tile t is multiplied.  Each wavefront first stages its own
-// groups' activations: each lane takes 8 columns, finds its 32-column
-// block's scale with two lane exchanges and writes the fp8 bytes of both
-// parts to the wavefront's part of LDS (no workgroup barrier).  A
-// fixed-order sum over wavefronts in LDS gives y (no atomics).  A NaN or infinite activation makes every output NaN.
+// bytes) and one 2-byte scale load; tile t+3 is loaded while tile t is
+// multiplied.  The grid size, wavefront count and tiles per workgroup are
+// kernel arguments (preloaded), so no address waits on a dispatch-packet
+// load.  Each wavefront first stages its own groups' activations: each lane
+// takes 8 columns, finds its 32-column word's scale with two lane exchanges
+// and writes the fp8 bytes of both parts to the wavefront's part of LDS (no
+// workgroup barrier).  A fixed-order sum over wavefronts in LDS gives y (no
+// atomics).  A NaN or infinite activation makes every output NaN.
 #include "mbok_device.h"
 #include "mbok_launch.h"
 
@@ -88,25 +92,6 @@ __device__ __forceinline__ void wave_lds_sync() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
-__device__ __forceinline__ void swap32(uint32_t& a, uint32_t& b) {
-  const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
-  a = r[0];
-  b = r[1];
-}
-__device__ __forceinline__ void swap16(uint32_t& a, uint32_t& b) {
-  const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
-  a = r[0];
-  b = r[1];
-}
-// 4 x 4 transpose of (16-lane block, register): afterwards r[j] in block q is
-// what r[q] held in block j.
-__device__ __forceinline__ void transpose4(uint32_t (&r)[4]) {
-  swap32(r[0], r[2]);
-  swap32(r[1], r[3]);
-  swap16(r[0], r[1]);
-  swap16(r[2], r[3]);
-}
-
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 // A streaming load: the signs are read once, so they are marked
@@ -122,34 +107,39 @@ struct F4Loads {
   AT a[K];     // and its scale
 };
 
-// Where column w (0..31) of 32-column block blk goes in a group's A operand
-// bytes of one part: it is product term k = 32 blk + 8 ((w >> 2) & 3) +
-// 2 (w & 3) + (w >> 4), and term k sits in lane block (k & 63) >> 4, byte
-// (k & 15) + 16 [k >= 64] of that lane's 32.
-__device__ __forceinline__ int op_byte(int blk, int w) {
-  const int k = 32 * blk + 8 * ((w >> 2) & 3) + 2 * (w & 3) + (w >> 4);
-  return ((k & 63) >> 4) * 32 + (k & 15) + (k >= 64 ? 16 : 0);
+// Byte of a 32-column word's column c (0..31) in that word's 32 product
+// terms: B dword d, nibble p holds bit 4p + d of the word, i.e. column
+// 16 (p & 1) + 4 d + (p >> 1), and is product term kk = 8 d + p.
+__device__ __forceinline__ int term_of_column(int c) {
+  return 8 * ((c >> 2) & 3) + 2 * (c & 3) + (c >> 4);
 }
 
 template <typename AT, int K, int JMAX>
 __global__ void __launch_bounds__(f4_max_waves(K) * kWave) gemv_f4_kernel(
     const uint4* __restrict__ bits, const uint16_t* __restrict__ x, int G, int tiles,
-    int slab_groups, float* __restrict__ y, int m) {
+    int slab_groups, float* __restrict__ y, int m, int grid, int nw, int tpw, int textra) {
   // the scales follow the sign region: tiles * 16 rows x G groups x K chunks
   const AT* __restrict__ scales =
       reinterpret_cast<const AT*>(bits + (int64_t)tiles * 16 * G * K);
+  // converted activations: [group][part][word][32 terms]
   __shared__ __attribute__((aligned(16))) uint8_t ops[kF4MaxSlab * kOpBytes];  // 16 KB
   __shared__ uint8_t codes[kF4MaxSlab * 4];
   __shared__ float red[JMAX * kF4MaxWaves * 16];
-  const int NW = blockDim.x / kWave;
+  const int NW = nw;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int r = lane & 15;   // row of the tile (B column, D column)
-  const int q = lane >> 4;   // lane block: the wavefront's group j at load time
-  const int ntl = (tiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;  // <= JMAX
+  const int r = lane & 15;   // row of the tile (B column, D column; A row at A time)
+  const int q = lane >> 4;   // lane block: K-block q holds group 4 wave + q
+  const int b = blockIdx.x;
+  const int ntl = tpw + (b < textra ? 1 : 0);  // tiles of this workgroup, <= JMAX
   int nonfinite = 0;  // this thread saw a NaN or infinite activation
-  const uint32_t sgn = sgpr_const(0x88888888u);  // fp4 sign bits
-  const uint32_t one = vgpr_const(0x22222222u);  // fp4 1.0 in every nibble
+  // B dword d, nibble p: bit 4p + d of the word at nibble bit d, over a base
+  // nibble: d = 0 {4.0, 6.0}, d = 1 {2.0, 4.0}, d = 2 {0, 2.0}, d = 3
+  // {1.0, -1.0}, i.e. c_d + b with c = 5, 3, 1 and -b for d = 3
+  const uint32_t m0 = sgpr_const(0x11111111u), m1 = sgpr_const(0x22222222u);
+  const uint32_t m2 = sgpr_const(0x44444444u), m3 = sgpr_const(0x88888888u);
+  const uint32_t b0 = vgpr_const(0x66666666u), b1 = vgpr_const(0x44444444u);
+  const uint32_t b3 = vgpr_const(0x22222222u);
 
   for (int g0 = 0; g0 < G; g0 += slab_groups) {
     const int sg = min(slab_groups, G - g0);
@@ -157,7 +147,7 @@ __global__ void __launch_bounds__(f4_max_waves(K) * kWave) gemv_f4_kernel(
     // group past the slab has a zero A operand and adds nothing
     const int gq = min(kF4GroupsPerWave * wave + q, sg - 1);
     auto load = [&](int t, F4Loads<K, AT>& L) {
-      const int i0 = tile16_of(blockIdx.x + t * gridDim.x, tiles) * 16;
+      const int i0 = tile16_of(b + t * grid, tiles) * 16;
       const int rb = i0 / kRowBlock, r0 = i0 % kRowBlock;
       const int64_t ch = ((int64_t)rb * G + g0 + gq) * K * kRowBlock + r0 + r;
 #pragma unroll
@@ -169,7 +159,7 @@ __global__ void __launch_bounds__(f4_max_waves(K) * kWave) gemv_f4_kernel(
     // the activations first, then the first tiles' signs: loads complete in
     // order, so the activations' conversion waits only for them while the
     // signs are still in flight
-    const int xt = threadIdx.x;  // 8 columns per thread, 4 threads per 32-column block
+    const int xt = threadIdx.x;  // 8 columns per thread, 4 threads per 32-column word
     const bool has_x = xt < sg * 16;
     const uint4 u = has_x ? *reinterpret_cast<const uint4*>(x + (int64_t)g0 * kGroup + 8 * xt)
                           : make_uint4(0, 0, 0, 0);
@@ -184,6 +174,7 @@ __global__ void __launch_bounds__(f4_max_waves(K) * kWave) gemv_f4_kernel(
     // wavefront's own LDS accesses need ordering, never the workgroup's.
     // (Its reads of the previous slab's bytes were consumed before the first
     // product of that slab.)
+    float corr = 0.f;  // sum over this thread's columns of c(class) x
     if (has_x) {
       const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
       uint32_t mx = 0;
@@ -191,87 +182,108 @@ __global__ void __launch_bounds__(f4_max_waves(K) * kWave) gemv_f4_kernel(
       for (int e = 0; e < 4; ++e) mx = max(mx, max(wv[e] & 0x7fffu, (wv[e] >> 16) & 0x7fffu));
       mx = max(mx, (uint32_t)__shfl_xor((int)mx, 1, kWave));
       mx = max(mx, (uint32_t)__shfl_xor((int)mx, 2, kWave));
-      const int eb = (int)(mx >> 7);  // biased exponent of the block's largest |x|
+      const int eb = (int)(mx >> 7);  // biased exponent of the word's largest |x|
       if (eb == 0xff) nonfinite = 1;
       const int code = mx == 0 ? kE8M0One : (eb > 7 ? eb - 7 : 0);
       const int lcode = lo_code(code);
-      const int gl = xt >> 4, blk = (xt >> 2) & 3, sub = xt & 3;
-      if (sub == 0) codes[gl * 4 + blk] = (uint8_t)code;
-      uint8_t* hi = ops + gl * kOpBytes;
+      const int gl = xt >> 4, word = (xt >> 2) & 3, sub = xt & 3;
+      if (sub == 0) codes[gl * 4 + word] = (uint8_t)code;
+      uint8_t* hi = ops + gl * kOpBytes + word * 32;
       uint8_t* lo = hi + kOpBytes / 2;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const uint32_t bb = (e & 1) ? (wv[e >> 1] >> 16) : (wv[e >> 1] & 0xffffu);
-        const float v = __builtin_ldexpf(bf16_bits_to_f32(bb), kE8M0One - code);
+        // column 8 sub + e is in sign class ((8 sub + e) >> 2) & 3 = 2 (sub & 1) + (e >> 2)
+        const int cls = 2 * (sub & 1) + (e >> 2);
+        const float xv = bf16_bits_to_f32(bb);
+        corr = fmaf((float)(cls == 0 ? 5 : cls == 1 ? 3 : cls == 2 ? 1 : 0), xv, corr);
+        const float v = __builtin_ldexpf(cls == 3 ? -xv : xv, kE8M0One - code);
         const int h8 = __builtin_amdgcn_cvt_pk_fp8_f32(v, 0.f, 0, false);
         const float l = __builtin_ldexpf(v - __builtin_amdgcn_cvt_f32_fp8(h8, 0), code - lcode);
         const int l8 = __builtin_amdgcn_cvt_pk_fp8_f32(l, 0.f, 0, false);
-        const int pos = op_byte(blk, 8 * sub + e);
+        const int pos = term_of_column(8 * sub + e);
         hi[pos] = (uint8_t)h8;
         lo[pos] = (uint8_t)l8;
       }
     }
+    // the group's correction: lanes 16j .. 16j+15 converted group 4w + j
+    corr += __shfl_xor(corr, 1, kWave);
+    corr += __shfl_xor(corr, 2, kWave);
+    corr += __shfl_xor(corr, 4, kWave);
+    corr += __shfl_xor(corr, 8, kWave);
     wave_lds_sync();
-    // ---- A operands, one per group j of the wavefront: lane (row rho = r,
-    // block q) holds the high part of group j if rho == 4j, its low part if
-    // rho == 4j + 1, else zeros.  The four have disjoint nonzero rows, so the
-    // products of one kernel chain through one accumulator.
-    v8i_t A[kF4GroupsPerWave];
-    int ascale;
+    // ---- A operands, one per word i.  K-block q of product i holds word i
+    // of the wavefront's group q (the B operand of lane 16q + r is word i of
+    // its own loaded chunk), and A row 4q + e holds part e of that group
+    // (e = 0 high, 1 low), nonzero only in K-block q.  Lane 16c + rho holds
+    // A row rho, terms 16c .. 16c+15 (bytes 0..15) and 64 + 16c .. (bytes
+    // 16..31): K-block q sits in lane blocks 2 (q & 1) and 2 (q & 1) + 1,
+    // bytes 16 (q >> 1) ... of them.  The E8M0 scale of (row rho, K-block c)
+    // is lane 16c + rho's.
+    v8i_t A[4];
+    int ascale[4];
     {
-      const int j = r >> 2, part = r & 3;
-      const int gl = kF4GroupsPerWave * wave + j;
-      const bool live = part < 2 && gl < sg;
+      const int qa = r >> 2, part = r & 3;  // this lane's A row 4 qa + part
+      const int gl = kF4GroupsPerWave * wave + qa;
+      const bool live = part < 2 && gl < sg && (qa & 1) == (q >> 1);
       const int glc = min(gl, sg - 1);
-      const uint4* src = reinterpret_cast<const uint4*>(ops + glc * kOpBytes +
-                                                        (part & 1) * (kOpBytes / 2) + q * 32);
-      const uint4 d0 = src[0], d1 = src[1];
-      const v8i_t data = {(int)d0.x, (int)d0.y, (int)d0.z, (int)d0.w,
-                          (int)d1.x, (int)d1.y, (int)d1.z, (int)d1.w};
+      const uint8_t* base = ops + glc * kOpBytes + (part & 1) * (kOpBytes / 2) + 16 * (q & 1);
+      const bool upper = (qa >> 1) != 0;
 #pragma unroll
-      for (int jj = 0; jj < kF4GroupsPerWave; ++jj) {
-        A[jj] = (live && jj == j) ? data : v8i_t{0, 0, 0, 0, 0, 0, 0, 0};
-        // keep the operands in registers: recomputing the selects at every
-        // product would cost eight VALU instructions each
-        asm volatile("" : "+v"(A[jj]));
+      for (int i = 0; i < 4; ++i) {
+        const uint4 dd = *reinterpret_cast<const uint4*>(base + 32 * i);
+        const int z = 0;
+        A[i] = live ? (upper ? v8i_t{z, z, z, z, (int)dd.x, (int)dd.y, (int)dd.z, (int)dd.w}
+                             : v8i_t{(int)dd.x, (int)dd.y, (int)dd.z, (int)dd.w, z, z, z, z})
+                    : v8i_t{z, z, z, z, z, z, z, z};
+        asm volatile("" : "+v"(A[i]));
       }
-      const int code = (int)codes[glc * 4 + q];
-      ascale = !live ? kE8M0One : (part == 0 ? code : lo_code(code));
+      // scale of (row r, K-block q): nonzero rows of K-block q are 4q, 4q + 1
+      const int sq = min(kF4GroupsPerWave * wave + q, sg - 1);
+      const bool srow = (r >> 2) == q && part < 2 && kF4GroupsPerWave * wave + q < sg;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int code = (int)codes[sq * 4 + i];
+        ascale[i] = !srow ? kE8M0One : (part == 0 ? code : lo_code(code));
+      }
     }
 
-    // Per kernel: the four groups' products chained; lane 16j + r then holds
-    // group j's high and low sums for row r in registers 0 and 1.
+    // Per kernel: the four words' products chained (interleaved over the
+    // kernels); lane 16j + r then holds group j's high and low sums for row r
+    // in registers 0 and 1.
     auto mul = [&](F4Loads<K, AT>& L, float a) {
+      v4f_t d[K];
 #pragma unroll
-      for (int k = 0; k < K; ++k) {
-        uint32_t w[4] = {L.s[k].x, L.s[k].y, L.s[k].z, L.s[k].w};
-        transpose4(w);  // w[j] in block q: word q of (row r, group j)
-        v4f_t d = {0.f, 0.f, 0.f, 0.f};
+      for (int k = 0; k < K; ++k) d[k] = v4f_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < kF4GroupsPerWave; ++j) {
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          const uint32_t w = i == 0 ? L.s[k].x : i == 1 ? L.s[k].y : i == 2 ? L.s[k].z : L.s[k].w;
           v8i_t B;
-          B[0] = (int)(((w[j] << 3) & sgn) | one);
-          B[1] = (int)(((w[j] << 2) & sgn) | one);
-          B[2] = (int)(((w[j] << 1) & sgn) | one);
-          B[3] = (int)((w[j] & sgn) | one);
+          B[0] = (int)((w & m0) | b0);
+          B[1] = (int)((w & m1) | b1);
+          B[2] = (int)(w & m2);
+          B[3] = (int)((w & m3) | b3);
           B[4] = B[5] = B[6] = B[7] = 0;
-          d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[j], B, d, 0, 4, 0, ascale, 0,
-                                                               kE8M0One);
+          d[k] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[i], B, d[k], 0, 4, 0,
+                                                                  ascale[i], 0, kE8M0One);
         }
-        a = fmaf(alpha_to_f32<AT>(L.a[k]), d[0] + d[1], a);
       }
+#pragma unroll
+      for (int k = 0; k < K; ++k) a = fmaf(alpha_to_f32<AT>(L.a[k]), (d[k][0] + d[k][1]) - corr, a);
       return a;
     };
 
     // tile t + 3 is loaded while tile t is multiplied; each tile's sums (the
     // wavefront's four groups are its four lane blocks) go to LDS
     auto step = [&](int t, F4Loads<K, AT>& L) {
-      float u = mul(L, 0.f);
-      u += __shfl_xor(u, 16, kWave);
-      u += __shfl_xor(u, 32, kWave);
+      float uu = mul(L, 0.f);
+      uu += __shfl_xor(uu, 16, kWave);
+      uu += __shfl_xor(uu, 32, kWave);
       if (q == 0) {
         float* dst = red + (t * NW + wave) * 16 + r;
-        *dst = g0 == 0 ? u : *dst + u;  // slabs in order
+        *dst = g0 == 0 ? uu : *dst + uu;  // slabs in order
       }
     };
     for (int t = 0; t < ntl; t += 4) {
@@ -290,12 +302,12 @@ __global__ void __launch_bounds__(f4_max_waves(K) * kWave) gemv_f4_kernel(
   }
 
   const bool bad = __syncthreads_or(nonfinite) != 0;
-  for (int idx = threadIdx.x; idx < ntl * 16; idx += blockDim.x) {
+  for (int idx = threadIdx.x; idx < ntl * 16; idx += NW * kWave) {
     const int t = idx >> 4, rr = idx & 15;
-    float u = red[(t * NW) * 16 + rr];
-    for (int w = 1; w < NW; ++w) u += red[(t * NW + w) * 16 + rr];
-    const int i = tile16_of(blockIdx.x + t * gridDim.x, tiles) * 16 + rr;
-    if (i < m) y[i] = bad ? __builtin_nanf("") : -u;  // B held -b
+    float uu = red[(t * NW) * 16 + rr];
+    for (int w = 1; w < NW; ++w) uu += red[(t * NW + w) * 16 + rr];
+    const int i = tile16_of(b + t * grid, tiles) * 16 + rr;
+    if (i < m) y[i] = bad ? __builtin_nanf("") : uu;
   }
 }
 
@@ -311,7 +323,8 @@ int launch_f4_k(const Geom& geo, const void* packed, const void* x, float* y,
   if (grid * kF4J < tiles) grid = (tiles + kF4J - 1) / kF4J;
   hipLaunchKernelGGL((gemv_f4_kernel<AT, K, kF4J>), dim3(grid), dim3(NW * kWave), 0, stream,
                      reinterpret_cast<const uint4*>(packed),
-                     reinterpret_cast<const uint16_t*>(x), geo.G, tiles, slab, y, geo.m);
+                     reinterpret_cast<const uint16_t*>(x), geo.G, tiles, slab, y, geo.m, grid,
+                     NW, tiles / grid, tiles % grid);
   return hipGetLastError() == hipSuccess ? MBOK_OK : MBOK_ERR_HIP;
 }
 
