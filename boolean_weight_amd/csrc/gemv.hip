@@ -386,23 +386,31 @@ template <typename XT, typename AT, int K, int JMAX>
 // The arguments the first loads need come first, so that they are among
 // the ones preloaded into SGPRs at launch; the scales are found from the
 // packed buffer (they follow the 4 G K tiles 16-byte sign chunks).
+// The grid size, the wavefront count and the tiles per workgroup (tpw, plus
+// one for the first textra workgroups) are arguments, so that no address
+// waits on a load from the dispatch packet and nothing is divided; the output
+// arguments come last (the first 14 argument dwords arrive in SGPRs).
 __global__ void __launch_bounds__(16 * kWave) gemv_stream_kernel(
     const uint4* __restrict__ bits, const XT* __restrict__ x, int G, int tiles, int slab_groups,
-    float* __restrict__ y, int m) {
+    int grid, int nw, int tpw, int textra, float* __restrict__ y, int m) {
   const AT* __restrict__ scales =
       reinterpret_cast<const AT*>(bits + (int64_t)tiles * 16 * G * K);
   extern __shared__ float lds[];
-  const int NW = blockDim.x / kWave;
+  const int NW = nw;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int r = lane & 15, j = lane >> 4;
-  const int ntl = (tiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;  // <= JMAX
+  const int ntl = tpw + ((int)blockIdx.x < textra ? 1 : 0);  // <= JMAX
   float yacc[JMAX];
 #pragma unroll
   for (int t = 0; t < JMAX; ++t) yacc[t] = 0.f;
 
   auto load = [&](int t, int g0, int gl, BlockLoads<AT, K>& L) {
-    const int i = tile16_of(blockIdx.x + t * gridDim.x, tiles) * 16 + r;
+    // opaque to the compiler, so each tile's address is formed where it is
+    // loaded instead of every tile's ahead of the first load
+    int tb = (int)blockIdx.x + t * grid;
+    asm volatile("" : "+s"(tb));
+    const int i = tile16_of(tb, tiles) * 16 + r;
     const int64_t ch = (((int64_t)(i / kRowBlock) * G + g0 + gl) * K) * kRowBlock + i % kRowBlock;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
@@ -459,11 +467,11 @@ __global__ void __launch_bounds__(16 * kWave) gemv_stream_kernel(
     if (j == 0) lds[(t * NW + wave) * 16 + r] = u;
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < ntl * 16; idx += blockDim.x) {
+  for (int idx = threadIdx.x; idx < ntl * 16; idx += NW * kWave) {
     const int t = idx >> 4, rr = idx & 15;
     float u = lds[(t * NW) * 16 + rr];
     for (int w = 1; w < NW; ++w) u += lds[(t * NW + w) * 16 + rr];
-    const int i = tile16_of(blockIdx.x + t * gridDim.x, tiles) * 16 + rr;
+    const int i = tile16_of(blockIdx.x + t * grid, tiles) * 16 + rr;
     if (i < m) y[i] = u;
   }
 }
@@ -737,8 +745,8 @@ int launch_stream(const Geom& geo, const uint4* bits, const AT* scales, const vo
   if ((const void*)(bits + (int64_t)tiles * 16 * geo.G * K) != (const void*)scales)
     return MBOK_ERR_UNSUPPORTED;  // the kernel finds the scales after the signs
   hipLaunchKernelGGL((gemv_stream_kernel<XT, AT, K, kStreamJ>), dim3(grid), dim3(NW * kWave),
-                     lds, stream, bits, reinterpret_cast<const XT*>(x), geo.G, tiles, slab, y,
-                     geo.m);
+                     lds, stream, bits, reinterpret_cast<const XT*>(x), geo.G, tiles, slab, grid,
+                     NW, tiles / grid, tiles % grid, y, geo.m);
   return hipGetLastError() == hipSuccess ? MBOK_OK : MBOK_ERR_HIP;
 }
 

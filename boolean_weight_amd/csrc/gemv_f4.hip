@@ -117,7 +117,7 @@ __device__ __forceinline__ int term_of_column(int c) {
 template <typename AT, int K, int JMAX>
 __global__ void __launch_bounds__(f4_max_waves(K) * kWave) gemv_f4_kernel(
     const uint4* __restrict__ bits, const uint16_t* __restrict__ x, int G, int tiles,
-    int slab_groups, float* __restrict__ y, int m, int grid, int nw, int tpw, int textra) {
+    int slab_groups, int grid, int nw, int tpw, int textra, float* __restrict__ y, int m) {
   // the scales follow the sign region: tiles * 16 rows x G groups x K chunks
   const AT* __restrict__ scales =
       reinterpret_cast<const AT*>(bits + (int64_t)tiles * 16 * G * K);
@@ -147,7 +147,11 @@ __global__ void __launch_bounds__(f4_max_waves(K) * kWave) gemv_f4_kernel(
     // group past the slab has a zero A operand and adds nothing
     const int gq = min(kF4GroupsPerWave * wave + q, sg - 1);
     auto load = [&](int t, F4Loads<K, AT>& L) {
-      const int i0 = tile16_of(b + t * grid, tiles) * 16;
+      // opaque to the compiler, so each tile's address is formed where it is
+      // loaded instead of every tile's ahead of the first load
+      int tb = b + t * grid;
+      asm volatile("" : "+s"(tb));
+      const int i0 = tile16_of(tb, tiles) * 16;
       const int rb = i0 / kRowBlock, r0 = i0 % kRowBlock;
       const int64_t ch = ((int64_t)rb * G + g0 + gq) * K * kRowBlock + r0 + r;
 #pragma unroll
@@ -323,8 +327,8 @@ int launch_f4_k(const Geom& geo, const void* packed, const void* x, float* y,
   if (grid * kF4J < tiles) grid = (tiles + kF4J - 1) / kF4J;
   hipLaunchKernelGGL((gemv_f4_kernel<AT, K, kF4J>), dim3(grid), dim3(NW * kWave), 0, stream,
                      reinterpret_cast<const uint4*>(packed),
-                     reinterpret_cast<const uint16_t*>(x), geo.G, tiles, slab, y, geo.m, grid,
-                     NW, tiles / grid, tiles % grid);
+                     reinterpret_cast<const uint16_t*>(x), geo.G, tiles, slab, grid, NW,
+                     tiles / grid, tiles % grid, y, geo.m);
   return hipGetLastError() == hipSuccess ? MBOK_OK : MBOK_ERR_HIP;
 }
 

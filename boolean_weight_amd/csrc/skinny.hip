@@ -252,18 +252,24 @@ __device__ __forceinline__ void svid_block_fragments(const void* __restrict__ x,
 // s_out^k of the row (the same in every group), so kernel k is applied to its
 // two token rows only and the output is the sum of all token rows:
 // y = sum_k s_out^k (.) (B_k (s_in^k (.) x)).  X and ldx are unused then.
+//
+// The arguments the first loads need come first (the first 14 argument dwords
+// arrive in SGPRs at launch); the grid size and tw = tiles per workgroup
+// (bits 0..3, one more for workgroups below tw >> 8) | wavefronts (bits
+// 4..7) are arguments, so no address waits on a dispatch-packet load and
+// nothing is divided.
 template <typename AT, int K, int JMAX, bool SV>
 __global__ void __launch_bounds__(512) gemm_skinny_stream_kernel(
     const u32x4* __restrict__ bits, const AT* __restrict__ scales,
-    const uint16_t* __restrict__ X, int64_t ldx, float* __restrict__ Y, int64_t ldy, int T,
-    int m, int G, int slab_groups, int tiles, const void* __restrict__ sv_x, int sv_xf32,
-    const AT* __restrict__ sv_sin) {
+    const uint16_t* __restrict__ X, int64_t ldx, int T, int G, int slab_groups, int tiles,
+    int grid, int tw, float* __restrict__ Y, int64_t ldy, int m, const void* __restrict__ sv_x,
+    int sv_xf32, const AT* __restrict__ sv_sin) {
   extern __shared__ float red[];  // [JMAX][NW][4][64] partial sums
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int NW = blockDim.x >> 6;
+  const int NW = (tw >> 4) & 15;
   const int i = lane & 15, q = lane >> 4;
-  const int ntl = (tiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;  // <= JMAX
+  const int ntl = (tw & 15) + ((int)blockIdx.x < (tw >> 8) ? 1 : 0);  // <= JMAX
   const bool tok_ok = i < T;
   const uint16_t* xrow = SV ? nullptr : X + (int64_t)(tok_ok ? i : 0) * ldx + 32 * q;
   uint16_t* frag = SV ? reinterpret_cast<uint16_t*>(red + JMAX * NW * 256) +
@@ -306,7 +312,11 @@ __global__ void __launch_bounds__(512) gemm_skinny_stream_kernel(
                                         : u32x4{0u, 0u, 0u, 0u};
     }
     auto load = [&](int t, SkinnyLoads<AT, K>& L) {
-      const int row = tile16_of(blockIdx.x + t * gridDim.x, tiles) * 16 + i;
+      // opaque to the compiler, so each tile's address is formed where it is
+      // loaded instead of every tile's ahead of the first load
+      int tb = (int)blockIdx.x + t * grid;
+      asm volatile("" : "+s"(tb));
+      const int row = tile16_of(tb, tiles) * 16 + i;
       const int64_t c = ((int64_t)(row / kRowBlock) * G + gq) * K * kRowBlock + row % kRowBlock;
 #pragma unroll
       for (int k = 0; k < K; ++k) {
@@ -376,7 +386,7 @@ __global__ void __launch_bounds__(512) gemm_skinny_stream_kernel(
   __syncthreads();
   if constexpr (SV) {
     // one output per row: the token rows in order, each summed over wavefronts
-    for (int idx = threadIdx.x; idx < ntl * 16; idx += blockDim.x) {
+    for (int idx = threadIdx.x; idx < ntl * 16; idx += NW * 64) {
       const int t = idx >> 4, ri = idx & 15;
       float sum = 0.f;
       for (int tok = 0; tok < T; ++tok) {
@@ -385,17 +395,17 @@ __global__ void __launch_bounds__(512) gemm_skinny_stream_kernel(
         for (int w = 0; w < NW; ++w) part += red[(t * NW + w) * 256 + e];
         sum += part;
       }
-      const int row = tile16_of(blockIdx.x + t * gridDim.x, tiles) * 16 + ri;
+      const int row = tile16_of((int)blockIdx.x + t * grid, tiles) * 16 + ri;
       if (row < m) Y[row] = sum;
     }
   } else {
-    for (int idx = threadIdx.x; idx < ntl * 256; idx += blockDim.x) {
+    for (int idx = threadIdx.x; idx < ntl * 256; idx += NW * 64) {
       const int t = idx >> 8, e = idx & 255;
       float sum = 0.f;
       for (int w = 0; w < NW; ++w) sum += red[(t * NW + w) * 256 + e];
       const int l = e & 63, r = e >> 6;
       const int tok = 4 * (l >> 4) + r;
-      const int row = tile16_of(blockIdx.x + t * gridDim.x, tiles) * 16 + (l & 15);
+      const int row = tile16_of((int)blockIdx.x + t * grid, tiles) * 16 + (l & 15);
       if (tok < T && row < m) Y[(int64_t)tok * ldy + row] = sum;
     }
   }
@@ -429,9 +439,11 @@ void launch_stream_k(const Geom& geo, const u32x4* bits, const AT* scales, const
   if (grid * kSkinnyJ < tiles) grid = (tiles + kSkinnyJ - 1) / kSkinnyJ;
   size_t lds = (size_t)kSkinnyJ * NW * 256 * sizeof(float);
   if (SV) lds += (size_t)NW * 4 * K * 2 * kGroup * sizeof(uint16_t);
+  static_assert(kSkinnyJ <= 15, "tiles per workgroup are packed in 4 bits");
+  const int tw = tiles / grid | NW << 4 | (tiles % grid) << 8;
   hipLaunchKernelGGL((gemm_skinny_stream_kernel<AT, K, kSkinnyJ, SV>), dim3(grid), dim3(64 * NW), lds,
-                     stream, bits, scales, X, ldx, Y, ldy, T, geo.m, geo.G, slab, tiles, sv_x,
-                     sv_xf32, sv_sin);
+                     stream, bits, scales, X, ldx, T, geo.G, slab, tiles, grid, tw, Y, ldy, geo.m,
+                     sv_x, sv_xf32, sv_sin);
 }
 
 template <typename AT>
