@@ -103,7 +103,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "boolean_weight_amd", "csrc")
 COPY_BYTES = 2 ** 28  # calibration copy: 256 MiB read and 256 MiB written
 CAL_CALLS = 8         # dominant calls bracketed by the two calibration copies
-MARKER = "empty_kernel"  # the ceilings library's empty kernel brackets each timed region
+MARKER = "region_marker_kernel"  # the ceilings library's marker brackets each timed region
 
 
 def kernel_family(T, m=None, n=None, K=None, x_bf16=True):
@@ -420,7 +420,7 @@ def _marker(spin_us=0):
         out = torch.empty(1, dtype=torch.float32, device="cuda")
         if lib.mbok_ceiling_spin(spin_us, out.data_ptr(), st) != 0:
             raise RuntimeError("spin kernel failed")
-    if lib.mbok_ceiling_empty(1, 64, st) != 0:
+    if lib.mbok_ceiling_marker(st) != 0:
         raise RuntimeError("marker kernel failed")
 
 

@@ -36,11 +36,13 @@ def load():
     lib = ctypes.CDLL(path)
     V, I, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     lib.mbok_ceiling_empty.argtypes = [I, I, V]
+    lib.mbok_ceiling_marker.argtypes = [V]
     lib.mbok_ceiling_spin.argtypes = [I, V, V]
     lib.mbok_ceiling_spin.restype = I
     lib.mbok_ceiling_read.argtypes = [V, SZ, V, I, I, V]
     lib.mbok_ceiling_mfma.argtypes = [I, V, I, I, I, V]
-    for f in (lib.mbok_ceiling_empty, lib.mbok_ceiling_read, lib.mbok_ceiling_mfma):
+    for f in (lib.mbok_ceiling_empty, lib.mbok_ceiling_marker, lib.mbok_ceiling_read,
+              lib.mbok_ceiling_mfma):
         f.restype = I
     _LIB = lib
     return lib

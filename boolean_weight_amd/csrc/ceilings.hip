@@ -31,6 +31,10 @@ typedef float v16f_t __attribute__((ext_vector_type(16)));
 typedef short v8s_t __attribute__((ext_vector_type(8)));
 
 __global__ void empty_kernel() {}
+// The same, under its own name: bench.py brackets each timed region with it,
+// so that a kernel trace can find the region's dispatches (the launch-floor
+// measurement runs empty_kernel thousands of times).
+__global__ void region_marker_kernel() {}
 
 // Busy for `ticks` of the 100 MHz real-time counter, then ends: it keeps the
 // stream (and, with one workgroup per compute unit doing fp32 arithmetic,
@@ -121,6 +125,10 @@ bool shape_ok(int grid, int block) {
 
 extern "C" {
 
+int mbok_ceiling_marker(void* stream) {
+  hipLaunchKernelGGL(region_marker_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
 int mbok_ceiling_empty(int grid, int block, void* stream) {
   if (!shape_ok(grid, block)) return -1;
   hipLaunchKernelGGL(empty_kernel, dim3(grid), dim3(block), 0, (hipStream_t)stream);

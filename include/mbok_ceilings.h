@@ -24,6 +24,11 @@ extern "C" {
  * floor of a kernel with this grid. */
 int mbok_ceiling_empty(int grid, int block, void* stream);
 
+/* One workgroup of region_marker_kernel, an empty kernel with a name of its
+ * own: launched just before and just after a timed region, it lets a kernel
+ * trace pick out the region's dispatches. */
+int mbok_ceiling_marker(void* stream);
+
 /* One workgroup per compute unit doing fp32 arithmetic for `microseconds`
  * (1 .. 100000) of the 100 MHz real-time counter, then done: enqueued before
  * a timed region, it keeps the chip busy while the host enqueues the region's

@@ -84,9 +84,12 @@ def test_summary_scales_counters_by_the_copy(tmp_path):
 
 
 def test_timed_regions_between_markers():
-    seq = [(1, "setup_kernel", 5.0), (2, "empty_kernel", 1.0), (3, GEMV, 4.0), (4, GEMV, 6.0),
-           (5, "empty_kernel", 1.0), (6, GEMV, 50.0), (7, "empty_kernel", 1.0),
-           (8, "gemm_mfma8_kernel", 100.0), (9, "empty_kernel", 1.0)]
+    M = "(anonymous namespace)::region_marker_kernel()"
+    seq = [(1, "setup_kernel", 5.0), (2, "(anonymous namespace)::empty_kernel()", 1.0),
+           (3, M, 1.0), (4, GEMV, 4.0), (5, GEMV, 6.0), (6, M, 1.0), (7, GEMV, 50.0),
+           (8, "(anonymous namespace)::empty_kernel()", 1.0), (9, M, 1.0),
+           (10, "gemm_mfma8_kernel", 100.0), (11, M, 1.0)]
     regs = bench.timed_regions(seq)
+    # the launch-floor measurement's empty kernels are not markers
     assert regs == [{GEMV: [4.0, 6.0]}, {"gemm_mfma8_kernel": [100.0]}]
     assert bench.timed_regions([(1, GEMV, 1.0)]) == []
