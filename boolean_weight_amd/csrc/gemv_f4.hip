@@ -41,7 +41,8 @@
 // at most 64 groups.  Per (tile, kernel) a wavefront issues one 16-byte sign
 // load per lane (16-lane block j: the 16 rows of group j, 256 contiguous
 // bytes) and one 2-byte scale load; tile t+3 is loaded while tile t is
-// multiplied.  The grid size, wavefront count and tiles per workgroup are
+// multiplied, and only the first tile's loads go out before the activations
+// are converted (none when the workgroup has a single tile).  The grid size, wavefront count and tiles per workgroup are
 // kernel arguments (preloaded), so no address waits on a dispatch-packet
 // load.  Each wavefront first stages its own groups' activations: each lane
 // takes 8 columns, finds its 32-column word's scale with two lane exchanges
@@ -114,7 +115,7 @@ __device__ __forceinline__ int term_of_column(int c) {
   return 8 * ((c >> 2) & 3) + 2 * (c & 3) + (c >> 4);
 }
 
-template <typename AT, int K, int JMAX>
+template <typename AT, int K, int JMAX, bool EARLY>
 __global__ void __launch_bounds__(f4_max_waves(K) * kWave) gemv_f4_kernel(
     const uint4* __restrict__ bits, const uint16_t* __restrict__ x, int G, int tiles,
     int slab_groups, int grid, int nw, int tpw, int textra, float* __restrict__ y, int m) {
@@ -160,17 +161,21 @@ __global__ void __launch_bounds__(f4_max_waves(K) * kWave) gemv_f4_kernel(
         L.a[k] = scales[ch + k * kRowBlock];
       }
     };
-    // the activations first, then the first tiles' signs: loads complete in
-    // order, so the activations' conversion waits only for them while the
-    // signs are still in flight
+    // The activations first.  Every compute unit asks for them at once, and
+    // each sign load issued before they arrive sits in the same memory
+    // queues ahead of other wavefronts' activation loads, so only the first
+    // tile's signs go out now (EARLY: some workgroup has more than one tile
+    // to keep the stream going), the rest once this wavefront has converted
+    // its activations (measured: 11008 x 4096 7.9 -> 7.1 us, 4096 x 4096
+    // K = 2 4.65 -> 4.09 us).  EARLY is a compile-time choice so that the
+    // conversion waits for the activations alone (a runtime condition made
+    // the compiler wait for every load in flight).
     const int xt = threadIdx.x;  // 8 columns per thread, 4 threads per 32-column word
     const bool has_x = xt < sg * 16;
     const uint4 u = has_x ? *reinterpret_cast<const uint4*>(x + (int64_t)g0 * kGroup + 8 * xt)
                           : make_uint4(0, 0, 0, 0);
     F4Loads<K, AT> L0, L1, L2, L3;
-    load(0, L0);
-    if (ntl > 1) load(1, L1);
-    if (ntl > 2) load(2, L2);
+    if (EARLY) load(0, L0);
 
     // ---- activations -> fp8 operand bytes.  Thread xt converts columns
     // 8 xt .. 8 xt + 7 of the slab, so wavefront w converts exactly its own
@@ -215,6 +220,9 @@ __global__ void __launch_bounds__(f4_max_waves(K) * kWave) gemv_f4_kernel(
     corr += __shfl_xor(corr, 2, kWave);
     corr += __shfl_xor(corr, 4, kWave);
     corr += __shfl_xor(corr, 8, kWave);
+    if (!EARLY) load(0, L0);
+    if (ntl > 1) load(1, L1);
+    if (ntl > 2) load(2, L2);
     wave_lds_sync();
     // ---- A operands, one per word i.  K-block q of product i holds word i
     // of the wavefront's group q (the B operand of lane 16q + r is word i of
@@ -325,10 +333,16 @@ int launch_f4_k(const Geom& geo, const void* packed, const void* x, float* y,
   const int tiles = geo.RB * (kRowBlock / 16);
   int grid = tiles < 256 ? tiles : 256;
   if (grid * kF4J < tiles) grid = (tiles + kF4J - 1) / kF4J;
-  hipLaunchKernelGGL((gemv_f4_kernel<AT, K, kF4J>), dim3(grid), dim3(NW * kWave), 0, stream,
-                     reinterpret_cast<const uint4*>(packed),
-                     reinterpret_cast<const uint16_t*>(x), geo.G, tiles, slab, grid, NW,
-                     tiles / grid, tiles % grid, y, geo.m);
+  if (tiles > grid)
+    hipLaunchKernelGGL((gemv_f4_kernel<AT, K, kF4J, true>), dim3(grid), dim3(NW * kWave), 0,
+                       stream, reinterpret_cast<const uint4*>(packed),
+                       reinterpret_cast<const uint16_t*>(x), geo.G, tiles, slab, grid, NW,
+                       tiles / grid, tiles % grid, y, geo.m);
+  else
+    hipLaunchKernelGGL((gemv_f4_kernel<AT, K, kF4J, false>), dim3(grid), dim3(NW * kWave), 0,
+                       stream, reinterpret_cast<const uint4*>(packed),
+                       reinterpret_cast<const uint16_t*>(x), geo.G, tiles, slab, grid, NW,
+                       tiles / grid, tiles % grid, y, geo.m);
   return hipGetLastError() == hipSuccess ? MBOK_OK : MBOK_ERR_HIP;
 }
 

@@ -140,7 +140,7 @@ def test_mixed_k_layer_product():
         del signs, alpha
         x = syn.activations(1, n, syn.act_seed(4, li), "bf16")[0]
         y = gemv(d, packed, x, "bf16")
-        rows = np.array(sorted({0, m - 1, *np.random.default_rng(li).choice(m, 24).tolist()}))
+        rows = np.array(sorted({0, m - 1, *np.random.default_rng(li).choice(m, 128).tolist()}))
         S, A, _ = oracle.residual_binarize(Ws[li][rows], K, alpha_dtype="f16")
         ratio = oracle.max_error_ratio(y[rows], oracle.product(S, A, x), oracle.bound(S, A, x))
         assert ratio <= TOL, (name, K, ratio)

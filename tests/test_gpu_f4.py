@@ -126,7 +126,7 @@ def test_f4_workloads_tolerance(cfg):
         del signs, alpha
         y = gemv(d, packed, x, xdt, guard=3)
         rng = np.random.default_rng(li)
-        rows = np.unique(np.r_[rng.choice(m, 40, replace=False), np.arange(m - 64, m)])
+        rows = np.unique(np.r_[rng.choice(m, 256, replace=False), np.arange(m - 64, m)])
         S, A, _ = oracle.residual_binarize(W[rows], w["K"], alpha_dtype=dt)
         ratio = oracle.max_error_ratio(y[rows], oracle.product(S, A, x), oracle.bound(S, A, x))
         say(f"  err/bound {ratio:.3e}")

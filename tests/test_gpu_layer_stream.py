@@ -65,7 +65,7 @@ def test_layer_stream_graph_tolerance():
     eager = [y.cpu().numpy().copy() for (*_, y) in launches]
     for li, (name, W, x, d, packed, xt, y) in enumerate(launches):
         say(f"layer stream oracle {name}")
-        rows = _rows(d.m, 40, 400 + li)
+        rows = _rows(d.m, 256, 400 + li)
         S, A, _ = oracle.residual_binarize(W[rows], 3, alpha_dtype="f16")
         ratio = oracle.max_error_ratio(eager[li][rows], oracle.product(S, A, x),
                                        oracle.bound(S, A, x))

@@ -147,7 +147,7 @@ def test_quantizer_bit_exact_workloads_sampled(cfg):
         W = syn.weight(m, n, syn.weight_seed(cfg, li))
         d, signs, alpha, packed, flag = quantize_on_gpu(W, w["K"], dt)
         assert flag == 0
-        rows = sample_rows(m, 24, cfg * 10 + li)
+        rows = sample_rows(m, 128, cfg * 10 + li)
         S, A, _ = oracle.residual_binarize(W[rows], w["K"], alpha_dtype=dt)
         assert np.array_equal(signs.cpu().numpy()[:, rows], S), name
         assert np.array_equal(alpha.cpu().numpy()[:, rows].view(np.uint8), A.view(np.uint8)), name
@@ -274,7 +274,7 @@ def test_gemv_workloads_tolerance(cfg):
         d, signs, alpha, packed, flag = quantize_on_gpu(W, w["K"], dt)
         del signs, alpha
         y = gemv(d, packed, x, xdt, guard=5)
-        rows = sample_rows(m, 48, li)
+        rows = sample_rows(m, 256, li)
         S, A, _ = oracle.residual_binarize(W[rows], w["K"], alpha_dtype=dt)
         want, E = oracle.product(S, A, x), oracle.bound(S, A, x)
         ratio = oracle.max_error_ratio(y[rows], want, E)
@@ -298,7 +298,7 @@ def test_gemv_k_sweep_first_linear(cfg, K):
     x = syn.activations(1, n, syn.act_seed(cfg, 0), xdt)[0]
     d, signs, alpha, packed, flag = quantize_on_gpu(W, K, dt)
     y = gemv(d, packed, x, xdt)
-    rows = sample_rows(m, 32, 100 + K)
+    rows = sample_rows(m, 128, 100 + K)
     S, A, _ = oracle.residual_binarize(W[rows], K, alpha_dtype=dt)
     ratio = oracle.max_error_ratio(y[rows], oracle.product(S, A, x), oracle.bound(S, A, x))
     assert ratio <= TOL, ratio
@@ -416,7 +416,7 @@ def test_gemm_config3_tolerance(T, K):
         d, signs, alpha, packed, flag = quantize_on_gpu(W, K, "f16")
         del signs, alpha
         Y = gemm(d, packed, X)
-        rows = sample_rows(m, 24, li)
+        rows = sample_rows(m, 128, li)
         S, A, _ = oracle.residual_binarize(W[rows], K, alpha_dtype="f16")
         ratio = oracle.max_error_ratio(Y[:, rows], oracle.product(S, A, X), oracle.bound(S, A, X))
         assert ratio <= TOL, (name, ratio)
@@ -555,7 +555,7 @@ def test_gemm_prefill_config5_tolerance(prefill_waves):
     d, signs, alpha, packed, flag = quantize_on_gpu(W, 3, "f16")
     del signs, alpha
     Y = gemm(d, packed, X)
-    rows = sample_rows(m, 24, 5)
+    rows = sample_rows(m, 128, 5)
     S, A, _ = oracle.residual_binarize(W[rows], 3, alpha_dtype="f16")
     ratio = oracle.max_error_ratio(Y[:, rows], oracle.product(S, A, X), oracle.bound(S, A, X))
     assert ratio <= TOL, ratio
@@ -577,7 +577,7 @@ def test_gemm_prefill_config5_k_sweep(K):
     d, signs, alpha, packed, flag = quantize_on_gpu(W, K, "f16")
     del signs, alpha
     Y = gemm(d, packed, X)
-    rows = sample_rows(m, 24, 50 + K)
+    rows = sample_rows(m, 128, 50 + K)
     S, A, _ = oracle.residual_binarize(W[rows], K, alpha_dtype="f16")
     ratio = oracle.max_error_ratio(Y[:, rows], oracle.product(S, A, X), oracle.bound(S, A, X))
     assert ratio <= TOL, ratio

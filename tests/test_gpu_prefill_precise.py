@@ -131,7 +131,7 @@ def test_precise_prefill_workload():
     X = syn.activations(T, n, syn.act_seed(5), "bf16")
     d, packed, _, _ = bw.quantize_and_pack(torch.from_numpy(W).to(DEV), 3, bw.MBOK_F16)
     got = run(bw.mbok_gemm_precise, d, packed, X)
-    rows = np.unique(np.r_[np.linspace(0, m - 1, 24).astype(int), m - 1])
+    rows = np.unique(np.r_[np.linspace(0, m - 1, 128).astype(int), m - 1])
     S, A, _ = oracle.residual_binarize(W[rows], 3, alpha_dtype="f16")
     assert oracle.max_error_ratio(got[:, rows], oracle.product(S, A, X),
                                   oracle.bound(S, A, X)) <= TOL

@@ -150,7 +150,7 @@ def test_svid_gemv_workload_tolerance(cfg):
     x = syn.activations(1, n, syn.act_seed(cfg, 0), xdt)[0]
     d, packed = pack_svid(S, SO, dt)
     y = gemv_svid(d, packed, SI, x, xdt, dt)
-    rows = np.array(sorted({0, m - 1, *np.random.default_rng(cfg).choice(m, 48).tolist()}))
+    rows = np.array(sorted({0, m - 1, *np.random.default_rng(cfg).choice(m, 128).tolist()}))
     want = oracle.svid_product(S[:, rows], SO[:, rows], SI, x)
     E = oracle.svid_bound(S[:, rows], SO[:, rows], SI, x)
     ratio = oracle.max_error_ratio(y[rows], want, E)
