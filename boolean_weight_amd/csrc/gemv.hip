@@ -620,16 +620,19 @@ bool use_skinny_for_gemv(const Geom&) {
 }
 
 // The fp4 x fp8 matrix-core kernel (gemv_f4.hip) for bf16 activations: the
-// default above 2^25 sign bits (K m n), where it measured 5-16% faster than
-// the table kernel on every workload shape (11008 x 4096 K = 3: 8.2 against
-// 9.0 us; 27648 x 5120: 16.6 against 18.9 us); at 4096 x 4096, K = 2 the
-// table kernel is faster (4.3 against 4.6 us).  MBOK_GEMV_VARIANT=f4 selects
-// it for every shape; any other value of the variable selects that table
-// variant instead.
+// default when a row carries at least 8192 sign bits (K n), the layer at
+// least 2^25 (K m n), or K = 4.  Measured per call against the table kernel:
+// 4096 x 4096 K = 2 3.98 against 4.10 us, 2048 x 4096 K = 3 4.02 / 4.43,
+// 512 x 4096 K = 2 3.66 / 3.80, 8192 x 4096 K = 1 4.31 / 4.95, 4096 x 1024
+// K = 4 3.36 / 3.70, every workload shape of K = 3 5-20% faster; the table
+// kernel stays ahead for short rows (1024 x 1024 K = 2 2.89 against 3.10,
+// 4096 x 4096 K = 1 3.66 / 3.76, 300 x 1024 K = 1 2.52 / 2.96).
+// MBOK_GEMV_VARIANT=f4 selects it for every shape; any other value of the
+// variable selects that table variant instead.
 bool use_f4_for_gemv(const Geom& geo) {
   const char* v = getenv("MBOK_GEMV_VARIANT");
   if (v) return strcmp(v, "f4") == 0;
-  return (int64_t)geo.K * geo.m * geo.n > (int64_t(1) << 25);
+  return f4_default(geo.m, geo.n, geo.K);
 }
 
 int variant_for(const Geom&) {

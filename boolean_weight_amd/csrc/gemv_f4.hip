@@ -93,6 +93,30 @@ __device__ __forceinline__ void wave_lds_sync() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
+// DPP lane exchanges within a quad / a 16-lane row (no LDS round trip).
+constexpr int kQuadXor1 = 0xB1;       // quad_perm [1, 0, 3, 2]
+constexpr int kQuadXor2 = 0x4E;       // quad_perm [2, 3, 0, 1]
+constexpr int kRowMirror = 0x140;     // lane i <- lane 15 - i of its row
+constexpr int kRowHalfMirror = 0x141; // lane i <- lane 7 - i of its half-row
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
+}
+
+// The 8 term bytes this thread writes for one part: P[d] holds the fp8 bytes
+// of its columns 2d, 2d + 1 in bytes 0, 1; the partner thread (sub ^ 2, the
+// other h) holds the interleaved ones.  h = 0 returns dwords [A2d B2d A2d+1
+// B2d+1] for d = 0, 1; h = 1 for d = 2, 3 (A: the h = 0 thread, B: h = 1).
+__device__ __forceinline__ uint2 pair_terms(const uint32_t (&P)[4], bool h) {
+  const uint32_t r1 = dpp_u32<kQuadXor2>(h ? P[0] : P[2]);
+  const uint32_t r2 = dpp_u32<kQuadXor2>(h ? P[1] : P[3]);
+  // v_perm_b32 selector bytes 0..3 take the second operand's bytes, 4..7 the first's
+  constexpr uint32_t kInterleave = 0x05010400u;  // [s1.b0, s0.b0, s1.b1, s0.b1]
+  const uint32_t w0 = __builtin_amdgcn_perm(h ? P[2] : r1, h ? r1 : P[0], kInterleave);
+  const uint32_t w1 = __builtin_amdgcn_perm(h ? P[3] : r2, h ? r2 : P[1], kInterleave);
+  return make_uint2(w0, w1);
+}
+
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 // A streaming load: the signs are read once, so they are marked
@@ -108,12 +132,10 @@ struct F4Loads {
   AT a[K];     // and its scale
 };
 
-// Byte of a 32-column word's column c (0..31) in that word's 32 product
-// terms: B dword d, nibble p holds bit 4p + d of the word, i.e. column
-// 16 (p & 1) + 4 d + (p >> 1), and is product term kk = 8 d + p.
-__device__ __forceinline__ int term_of_column(int c) {
-  return 8 * ((c >> 2) & 3) + 2 * (c & 3) + (c >> 4);
-}
+// A 32-column word's column c (0..31) is its product term kk =
+// 8 ((c >> 2) & 3) + 2 (c & 3) + (c >> 4): B dword d, nibble p holds bit 4p + d
+// of the word, i.e. column 16 (p & 1) + 4 d + (p >> 1), as term 8d + p.  The
+// converted activations are stored in LDS in term order.
 
 template <typename AT, int K, int JMAX, bool EARLY>
 __global__ void __launch_bounds__(f4_max_waves(K) * kWave) gemv_f4_kernel(
@@ -189,37 +211,50 @@ __global__ void __launch_bounds__(f4_max_waves(K) * kWave) gemv_f4_kernel(
       uint32_t mx = 0;
 #pragma unroll
       for (int e = 0; e < 4; ++e) mx = max(mx, max(wv[e] & 0x7fffu, (wv[e] >> 16) & 0x7fffu));
-      mx = max(mx, (uint32_t)__shfl_xor((int)mx, 1, kWave));
-      mx = max(mx, (uint32_t)__shfl_xor((int)mx, 2, kWave));
+      // the word's 4 threads are a quad of lanes
+      mx = max(mx, dpp_u32<kQuadXor1>(mx));
+      mx = max(mx, dpp_u32<kQuadXor2>(mx));
       const int eb = (int)(mx >> 7);  // biased exponent of the word's largest |x|
       if (eb == 0xff) nonfinite = 1;
       const int code = mx == 0 ? kE8M0One : (eb > 7 ? eb - 7 : 0);
       const int lcode = lo_code(code);
       const int gl = xt >> 4, word = (xt >> 2) & 3, sub = xt & 3;
       if (sub == 0) codes[gl * 4 + word] = (uint8_t)code;
-      uint8_t* hi = ops + gl * kOpBytes + word * 32;
-      uint8_t* lo = hi + kOpBytes / 2;
+      // column 8 sub + e is in sign class ((8 sub + e) >> 2) & 3 = 2 (sub & 1) + (e >> 2)
+      const bool odd = (sub & 1) != 0;
+      const float c_lo = odd ? 1.f : 5.f, c_hi = odd ? 0.f : 3.f;  // e < 4, e >= 4
+      uint32_t H[4], L[4];  // fp8 bytes of columns 2d, 2d + 1 in bytes 0, 1
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t bb = (e & 1) ? (wv[e >> 1] >> 16) : (wv[e >> 1] & 0xffffu);
-        // column 8 sub + e is in sign class ((8 sub + e) >> 2) & 3 = 2 (sub & 1) + (e >> 2)
-        const int cls = 2 * (sub & 1) + (e >> 2);
-        const float xv = bf16_bits_to_f32(bb);
-        corr = fmaf((float)(cls == 0 ? 5 : cls == 1 ? 3 : cls == 2 ? 1 : 0), xv, corr);
-        const float v = __builtin_ldexpf(cls == 3 ? -xv : xv, kE8M0One - code);
-        const int h8 = __builtin_amdgcn_cvt_pk_fp8_f32(v, 0.f, 0, false);
-        const float l = __builtin_ldexpf(v - __builtin_amdgcn_cvt_f32_fp8(h8, 0), code - lcode);
-        const int l8 = __builtin_amdgcn_cvt_pk_fp8_f32(l, 0.f, 0, false);
-        const int pos = term_of_column(8 * sub + e);
-        hi[pos] = (uint8_t)h8;
-        lo[pos] = (uint8_t)l8;
+      for (int d = 0; d < 4; ++d) {
+        const float x0 = bf16_bits_to_f32(wv[d] & 0xffffu);
+        const float x1 = bf16_bits_to_f32(wv[d] >> 16);
+        corr = fmaf(d < 2 ? c_lo : c_hi, x0, corr);
+        corr = fmaf(d < 2 ? c_lo : c_hi, x1, corr);
+        const bool neg = d >= 2 && odd;  // class 3
+        const float v0 = __builtin_ldexpf(neg ? -x0 : x0, kE8M0One - code);
+        const float v1 = __builtin_ldexpf(neg ? -x1 : x1, kE8M0One - code);
+        const int h8 = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
+        const auto back = __builtin_amdgcn_cvt_pk_f32_fp8(h8, false);
+        const float l0 = __builtin_ldexpf(v0 - back[0], code - lcode);
+        const float l1 = __builtin_ldexpf(v1 - back[1], code - lcode);
+        H[d] = (uint32_t)h8;
+        L[d] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(l0, l1, 0, false);
       }
+      // Threads sub and sub ^ 2 fill the word's terms 16 (sub & 1) ..
+      // +15: term byte 2e + h is column 8 sub + e of the thread with h =
+      // sub >> 1.  The h = 0 thread writes bytes 0..7 (columns e = 0..3 of
+      // both), the h = 1 thread bytes 8..15, after one exchange in the quad.
+      const bool h = (sub >> 1) != 0;
+      uint8_t* hi = ops + gl * kOpBytes + word * 32 + 16 * (sub & 1) + 8 * (int)h;
+      uint8_t* lo = hi + kOpBytes / 2;
+      *reinterpret_cast<uint2*>(hi) = pair_terms(H, h);
+      *reinterpret_cast<uint2*>(lo) = pair_terms(L, h);
     }
     // the group's correction: lanes 16j .. 16j+15 converted group 4w + j
-    corr += __shfl_xor(corr, 1, kWave);
-    corr += __shfl_xor(corr, 2, kWave);
-    corr += __shfl_xor(corr, 4, kWave);
-    corr += __shfl_xor(corr, 8, kWave);
+    corr = corr + __uint_as_float(dpp_u32<kQuadXor1>(__float_as_uint(corr)));
+    corr = corr + __uint_as_float(dpp_u32<kQuadXor2>(__float_as_uint(corr)));
+    corr = corr + __uint_as_float(dpp_u32<kRowHalfMirror>(__float_as_uint(corr)));
+    corr = corr + __uint_as_float(dpp_u32<kRowMirror>(__float_as_uint(corr)));
     if (!EARLY) load(0, L0);
     if (ntl > 1) load(1, L1);
     if (ntl > 2) load(2, L2);
@@ -291,8 +326,16 @@ __global__ void __launch_bounds__(f4_max_waves(K) * kWave) gemv_f4_kernel(
     // wavefront's four groups are its four lane blocks) go to LDS
     auto step = [&](int t, F4Loads<K, AT>& L) {
       float uu = mul(L, 0.f);
-      uu += __shfl_xor(uu, 16, kWave);
-      uu += __shfl_xor(uu, 32, kWave);
+      // sum over the four lane blocks (groups): 16-lane rows 0+1, 2+3, then
+      // the two halves, with lane swaps instead of LDS permutes
+      {
+        const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(uu), __float_as_uint(uu),
+                                                        false, false);
+        uu = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+        const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(uu), __float_as_uint(uu),
+                                                        false, false);
+        uu = __uint_as_float(c[0]) + __uint_as_float(c[1]);
+      }
       if (q == 0) {
         float* dst = red + (t * NW + wave) * 16 + r;
         *dst = g0 == 0 ? uu : *dst + uu;  // slabs in order

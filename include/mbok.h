@@ -373,11 +373,13 @@ size_t mbok_gemv_workspace_bytes(const mbok_desc* d);
  *            call, and calls that may run at the same time (other streams)
  *            need distinct workspaces.
  * The default kernels keep one workgroup per compute unit and stream 16-row
- * tiles.  For bf16 x and more than 2^25 sign bits (K m n) the products run
- * on the matrix cores: signs as fp4 +-1, each activation as an exact pair of
- * fp8 parts with one power-of-two scale per 32 columns, alpha applied per
- * (row, group, kernel) in fp32.  Otherwise (and for fp32 x) signed-sum
- * tables of x are built once and the sign nibbles index them.
+ * tiles.  For bf16 x the products run on the matrix cores when a row holds at
+ * least 8192 sign bits (K n >= 8192), the layer at least 2^25 (K m n), or
+ * K = 4: signs as fp4 values (one of two per sign, a known offset removed per
+ * group), each activation as an exact pair of fp8 parts with one power-of-two
+ * scale per 32 columns, alpha applied per (row, group, kernel) in fp32.
+ * Otherwise (and for fp32 x) signed-sum tables of x are built once and the
+ * sign nibbles index them.
  * Non-finite x: with the table kernels a NaN or infinity propagates through
  * the fp32 sums; with the matrix-core kernel any NaN or infinite activation
  * makes every output NaN.
