@@ -110,7 +110,7 @@ def kernel_family(T, m=None, n=None, K=None, x_bf16=True):
     """Source file and kernel-name prefix of the kernel one call runs (the
     library's default choice)."""
     if T == 1:
-        # the library's default choice (f4_default in csrc/mbok_device.h)
+        # the library's default choice (use_f4_for_gemv in csrc/gemv.hip)
         if x_bf16 and m is not None and (K * n >= 8192 or K * m * n >= (1 << 25) or K >= 4):
             return "gemv_f4.hip", "gemv_f4_kernel"
         return "gemv.hip", "gemv_stream_kernel"

@@ -632,7 +632,8 @@ bool use_skinny_for_gemv(const Geom&) {
 bool use_f4_for_gemv(const Geom& geo) {
   const char* v = getenv("MBOK_GEMV_VARIANT");
   if (v) return strcmp(v, "f4") == 0;
-  return f4_default(geo.m, geo.n, geo.K);
+  const int64_t K = geo.K, kn = K * geo.n;
+  return kn >= 8192 || kn * geo.m >= (int64_t(1) << 25) || K >= 4;
 }
 
 int variant_for(const Geom&) {

@@ -41,12 +41,6 @@ __device__ __forceinline__ int tile16_of(int b, int tiles) {
   return (((j >> 2) << 3) + xcd) * 4 + (j & 3);
 }
 
-// Whether the decode of a bf16 token runs on the matrix cores by default (the
-// table kernel otherwise; measurements beside use_f4_for_gemv in gemv.hip).
-inline bool f4_default(int64_t m, int64_t n, int64_t K) {
-  return K * n >= 8192 || K * m * n >= (int64_t(1) << 25) || K >= 4;
-}
-
 // ----------------------------------------------------------- conversions
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
