@@ -53,6 +53,17 @@
 #include "mbok_launch.h"
 
 namespace mbok {
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+// the raw buffer loads, declared under the compiler's intrinsic names
+__device__ u32x4_t raw_buffer_load_b128(i32x4_t rsrc, int voffset, int soffset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.load.v4i32");
+__device__ uint16_t raw_buffer_load_b16(i32x4_t rsrc, int voffset, int soffset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.load.i16");
+__device__ float raw_buffer_load_f32(i32x4_t rsrc, int voffset, int soffset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.load.f32");
+
 namespace {
 
 typedef int v8i_t __attribute__((ext_vector_type(8)));
@@ -64,7 +75,7 @@ constexpr int kF4MaxSlab = kF4GroupsPerWave * kF4MaxWaves;  // 64 groups
 // wavefronts per workgroup, so that four tile buffers fit in registers: 16
 // (128 VGPRs each) for K <= 2, 12 (168) for K = 3, 8 (256) for K = 4
 constexpr int f4_max_waves(int K) { return K >= 4 ? 8 : (K == 3 ? 12 : kF4MaxWaves); }
-constexpr int kF4J = 8;         // tiles per workgroup (sums in registers)
+constexpr int kF4J = 8;         // most tiles per workgroup
 constexpr int kE8M0One = 127;   // E8M0 code of 1.0
 constexpr int kOpBytes = 256;   // fp8 A bytes per group: 2 parts x 4 lane blocks x 32
 
@@ -117,13 +128,37 @@ __device__ __forceinline__ uint2 pair_terms(const uint32_t (&P)[4], bool h) {
   return make_uint2(w0, w1);
 }
 
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 as_uint4(u32x4_t v) { return make_uint4(v.x, v.y, v.z, v.w); }
 
-// A streaming load: the signs are read once, so they are marked
-// nontemporal (measured faster for read streams on this part).
-__device__ __forceinline__ uint4 load_stream(const uint4* p) {
-  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
+// Sign and scale loads go through buffer resources (V#) built in SGPRs per
+// tile.  A tile past the workgroup's last gets a resource of size 0, so its
+// loads return zeros without touching memory: every tile slot issues the same
+// loads whether or not it holds a tile, the count of loads in flight is the
+// same on every path through the tile loop, and the compiler's wait counts
+// before each tile's products cover that tile's loads only (with the loads
+// skipped by a branch, it waited for every load in flight, the three tiles
+// issued ahead included).
+constexpr int kAuxNt = 2;  // cache-policy bit: nontemporal (the signs are read once)
+// raw (stride 0) buffer over p: bytes [0, 2^32 - 1) if live, none otherwise;
+// word 3 holds the gfx9 data format the raw loads ignore
+__device__ __forceinline__ i32x4_t buffer_rsrc(const void* p, bool live) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  i32x4_t v;
+  v.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  v.y = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffffu));
+  v.z = __builtin_amdgcn_readfirstlane(live ? -1 : 0);
+  v.w = 0x00020000;
+  return v;
+}
+template <typename AT>
+__device__ __forceinline__ AT load_scale(i32x4_t rsrc, int voffset);
+template <>
+__device__ __forceinline__ uint16_t load_scale<uint16_t>(i32x4_t rsrc, int voffset) {
+  return raw_buffer_load_b16(rsrc, voffset, 0, 0);
+}
+template <>
+__device__ __forceinline__ float load_scale<float>(i32x4_t rsrc, int voffset) {
+  return raw_buffer_load_f32(rsrc, voffset, 0, 0);
 }
 
 template <int K, typename AT>
@@ -137,7 +172,7 @@ struct F4Loads {
 // of the word, i.e. column 16 (p & 1) + 4 d + (p >> 1), as term 8d + p.  The
 // converted activations are stored in LDS in term order.
 
-template <typename AT, int K, int JMAX, bool EARLY>
+template <typename AT, int K, int NT>
 __global__ void __launch_bounds__(f4_max_waves(K) * kWave) gemv_f4_kernel(
     const uint4* __restrict__ bits, const uint16_t* __restrict__ x, int G, int tiles,
     int slab_groups, int grid, int nw, int tpw, int textra, float* __restrict__ y, int m) {
@@ -146,15 +181,16 @@ __global__ void __launch_bounds__(f4_max_waves(K) * kWave) gemv_f4_kernel(
       reinterpret_cast<const AT*>(bits + (int64_t)tiles * 16 * G * K);
   // converted activations: [group][part][word][32 terms]
   __shared__ __attribute__((aligned(16))) uint8_t ops[kF4MaxSlab * kOpBytes];  // 16 KB
-  __shared__ uint8_t codes[kF4MaxSlab * 4];
-  __shared__ float red[JMAX * kF4MaxWaves * 16];
+  __shared__ __attribute__((aligned(4))) uint8_t codes[kF4MaxSlab * 4];
+  __shared__ float red[NT * kF4MaxWaves * 16];
   const int NW = nw;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int r = lane & 15;   // row of the tile (B column, D column; A row at A time)
   const int q = lane >> 4;   // lane block: K-block q holds group 4 wave + q
   const int b = blockIdx.x;
-  const int ntl = tpw + (b < textra ? 1 : 0);  // tiles of this workgroup, <= JMAX
+  const int ntl = tpw + (b < textra ? 1 : 0);  // tiles of this workgroup, <= NT
+  constexpr bool EARLY = NT > 1;  // NT: tile slots, the most tiles of any workgroup
   int nonfinite = 0;  // this thread saw a NaN or infinite activation
   // B dword d, nibble p: bit 4p + d of the word at nibble bit d, over a base
   // nibble: d = 0 {4.0, 6.0}, d = 1 {2.0, 4.0}, d = 2 {0, 2.0}, d = 3
@@ -169,6 +205,9 @@ __global__ void __launch_bounds__(f4_max_waves(K) * kWave) gemv_f4_kernel(
     // this lane's load group (block q), clamped so loads stay in bounds; a
     // group past the slab has a zero A operand and adds nothing
     const int gq = min(kF4GroupsPerWave * wave + q, sg - 1);
+    // this lane's byte offsets inside a tile's sign and scale blocks
+    const int vs = (gq * K * kRowBlock + r) * 16;
+    const int va = (gq * K * kRowBlock + r) * (int)sizeof(AT);
     auto load = [&](int t, F4Loads<K, AT>& L) {
       // opaque to the compiler, so each tile's address is formed where it is
       // loaded instead of every tile's ahead of the first load
@@ -176,11 +215,13 @@ __global__ void __launch_bounds__(f4_max_waves(K) * kWave) gemv_f4_kernel(
       asm volatile("" : "+s"(tb));
       const int i0 = tile16_of(tb, tiles) * 16;
       const int rb = i0 / kRowBlock, r0 = i0 % kRowBlock;
-      const int64_t ch = ((int64_t)rb * G + g0 + gq) * K * kRowBlock + r0 + r;
+      const int64_t c0 = ((int64_t)rb * G + g0) * K * kRowBlock + r0;  // the tile's first chunk
+      const i32x4_t rs = buffer_rsrc(bits + c0, t < ntl);
+      const i32x4_t ra = buffer_rsrc(scales + c0, t < ntl);
 #pragma unroll
       for (int k = 0; k < K; ++k) {
-        L.s[k] = load_stream(bits + ch + k * kRowBlock);
-        L.a[k] = scales[ch + k * kRowBlock];
+        L.s[k] = as_uint4(raw_buffer_load_b128(rs, vs + k * kRowBlock * 16, 0, kAuxNt));
+        L.a[k] = load_scale<AT>(ra, va + k * kRowBlock * (int)sizeof(AT));
       }
     };
     // The activations first.  Every compute unit asks for them at once, and
@@ -263,8 +304,8 @@ __global__ void __launch_bounds__(f4_max_waves(K) * kWave) gemv_f4_kernel(
     corr = corr + __uint_as_float(dpp_u32<kQuadXor2>(__float_as_uint(corr)));
     corr = corr + __uint_as_float(dpp_u32<kRowHalfMirror>(__float_as_uint(corr)));
     corr = corr + __uint_as_float(dpp_u32<kRowMirror>(__float_as_uint(corr)));
-    if (ntl > 1) load(1, L1);
-    if (ntl > 2) load(2, L2);
+    if (NT > 1) load(1, L1);  // a tile past the last loads zeros, reading nothing
+    if (NT > 2) load(2, L2);
     wave_lds_sync();
     // ---- A operands, one per word i.  K-block q of product i holds word i
     // of the wavefront's group q (the B operand of lane 16q + r is word i of
@@ -283,21 +324,27 @@ __global__ void __launch_bounds__(f4_max_waves(K) * kWave) gemv_f4_kernel(
       const int glc = min(gl, sg - 1);
       const uint8_t* base = ops + glc * kOpBytes + (part & 1) * (kOpBytes / 2) + 16 * (q & 1);
       const bool upper = (qa >> 1) != 0;
+      // every read goes out before the first wait, and the zero half (or the
+      // whole operand of a dead row) is masked, not branched around
+      uint4 dd[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint4 dd = *reinterpret_cast<const uint4*>(base + 32 * i);
-        const int z = 0;
-        A[i] = live ? (upper ? v8i_t{z, z, z, z, (int)dd.x, (int)dd.y, (int)dd.z, (int)dd.w}
-                             : v8i_t{(int)dd.x, (int)dd.y, (int)dd.z, (int)dd.w, z, z, z, z})
-                    : v8i_t{z, z, z, z, z, z, z, z};
-        asm volatile("" : "+v"(A[i]));
-      }
+      for (int i = 0; i < 4; ++i) dd[i] = *reinterpret_cast<const uint4*>(base + 32 * i);
       // scale of (row r, K-block q): nonzero rows of K-block q are 4q, 4q + 1
       const int sq = min(kF4GroupsPerWave * wave + q, sg - 1);
+      const uint32_t cw = *reinterpret_cast<const uint32_t*>(codes + sq * 4);
+      const uint32_t keep = live ? ~0u : 0u;
+      const uint32_t klo = upper ? 0u : keep, khi = upper ? keep : 0u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        A[i] = v8i_t{(int)(dd[i].x & klo), (int)(dd[i].y & klo), (int)(dd[i].z & klo),
+                     (int)(dd[i].w & klo), (int)(dd[i].x & khi), (int)(dd[i].y & khi),
+                     (int)(dd[i].z & khi), (int)(dd[i].w & khi)};
+        asm volatile("" : "+v"(A[i]));
+      }
       const bool srow = (r >> 2) == q && part < 2 && kF4GroupsPerWave * wave + q < sg;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int code = (int)codes[sq * 4 + i];
+        const int code = (int)((cw >> (8 * i)) & 0xffu);
         ascale[i] = !srow ? kE8M0One : (part == 0 ? code : lo_code(code));
       }
     }
@@ -348,18 +395,18 @@ __global__ void __launch_bounds__(f4_max_waves(K) * kWave) gemv_f4_kernel(
         *dst = g0 == 0 ? uu : *dst + uu;  // slabs in order
       }
     };
-    for (int t = 0; t < ntl; t += 4) {
-      if (t + 3 < ntl) load(t + 3, L3);
-      step(t, L0);
-      if (t + 1 >= ntl) break;
-      if (t + 4 < ntl) load(t + 4, L0);
-      step(t + 1, L1);
-      if (t + 2 >= ntl) break;
-      if (t + 5 < ntl) load(t + 5, L1);
-      step(t + 2, L2);
-      if (t + 3 >= ntl) break;
-      if (t + 6 < ntl) load(t + 6, L2);
-      step(t + 3, L3);
+    // Unrolled over the tile slots, with every load issued whether or not
+    // its tile exists: a workgroup's last tile leaves the chain, no path that
+    // skipped a load merges back into the steps, and the wait before tile
+    // t's products covers tile t's loads alone (with the loads skipped by a
+    // branch, the compiler waited for every load in flight, the tiles issued
+    // ahead included).
+    F4Loads<K, AT>* Ls[4] = {&L0, &L1, &L2, &L3};
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (t >= ntl) break;
+      if (t + 3 < NT) load(t + 3, *Ls[(t + 3) & 3]);
+      step(t, *Ls[t & 3]);
     }
   }
 
@@ -383,16 +430,24 @@ int launch_f4_k(const Geom& geo, const void* packed, const void* x, float* y,
   const int tiles = geo.RB * (kRowBlock / 16);
   int grid = tiles < 256 ? tiles : 256;
   if (grid * kF4J < tiles) grid = (tiles + kF4J - 1) / kF4J;
-  if (tiles > grid)
-    hipLaunchKernelGGL((gemv_f4_kernel<AT, K, kF4J, true>), dim3(grid), dim3(NW * kWave), 0,
-                       stream, reinterpret_cast<const uint4*>(packed),
+  // the kernel has one tile slot per tile of its fullest workgroup
+  const int slots = (tiles + grid - 1) / grid;
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(NW * kWave), 0, stream,
+                       reinterpret_cast<const uint4*>(packed),
                        reinterpret_cast<const uint16_t*>(x), geo.G, tiles, slab, grid, NW,
                        tiles / grid, tiles % grid, y, geo.m);
-  else
-    hipLaunchKernelGGL((gemv_f4_kernel<AT, K, kF4J, false>), dim3(grid), dim3(NW * kWave), 0,
-                       stream, reinterpret_cast<const uint4*>(packed),
-                       reinterpret_cast<const uint16_t*>(x), geo.G, tiles, slab, grid, NW,
-                       tiles / grid, tiles % grid, y, geo.m);
+  };
+  switch (slots) {
+    case 1: go(gemv_f4_kernel<AT, K, 1>); break;
+    case 2: go(gemv_f4_kernel<AT, K, 2>); break;
+    case 3: go(gemv_f4_kernel<AT, K, 3>); break;
+    case 4: go(gemv_f4_kernel<AT, K, 4>); break;
+    case 5: go(gemv_f4_kernel<AT, K, 5>); break;
+    case 6: go(gemv_f4_kernel<AT, K, 6>); break;
+    case 7: go(gemv_f4_kernel<AT, K, 7>); break;
+    default: go(gemv_f4_kernel<AT, K, 8>); break;
+  }
   return hipGetLastError() == hipSuccess ? MBOK_OK : MBOK_ERR_HIP;
 }
 
