@@ -40,7 +40,7 @@
 // (XCD-aware order); wavefront w owns groups 4w .. 4w+3 of a column slab of
 // at most 64 groups.  Per (tile, kernel) a wavefront issues one 16-byte sign
 // load per lane (16-lane block j: the 16 rows of group j, 256 contiguous
-// bytes) and one 2-byte scale load; tile t+3 is loaded while tile t is
+// bytes) and one 2-byte scale load; tile t+2 is loaded while tile t is
 // multiplied, and only the first tile's loads go out before the activations
 // are converted.  The grid size, wavefront count and tiles per workgroup are
 // kernel arguments (preloaded), so no address waits on a dispatch-packet
@@ -72,10 +72,13 @@ typedef float v4f_t __attribute__((ext_vector_type(4)));
 constexpr int kF4GroupsPerWave = 4;
 constexpr int kF4MaxWaves = 16;
 constexpr int kF4MaxSlab = kF4GroupsPerWave * kF4MaxWaves;  // 64 groups
-// wavefronts per workgroup, so that four tile buffers fit in registers: 16
+// wavefronts per workgroup, so that the tile buffers fit in registers: 16
 // (128 VGPRs each) for K <= 2, 12 (168) for K = 3, 8 (256) for K = 4
 constexpr int f4_max_waves(int K) { return K >= 4 ? 8 : (K == 3 ? 12 : kF4MaxWaves); }
 constexpr int kF4J = 8;         // most tiles per workgroup
+// tiles loaded ahead of the one multiplied (measured, 27648 x 5120 K = 3:
+// 13.0 us two ahead, 13.4-13.7 three, 13.6 four)
+constexpr int kF4Ahead = 2;
 constexpr int kE8M0One = 127;   // E8M0 code of 1.0
 constexpr int kOpBytes = 256;   // fp8 A bytes per group: 2 parts x 4 lane blocks x 32
 
@@ -136,8 +139,8 @@ __device__ __forceinline__ uint4 as_uint4(u32x4_t v) { return make_uint4(v.x, v.
 // loads whether or not it holds a tile, the count of loads in flight is the
 // same on every path through the tile loop, and the compiler's wait counts
 // before each tile's products cover that tile's loads only (with the loads
-// skipped by a branch, it waited for every load in flight, the three tiles
-// issued ahead included).
+// skipped by a branch, it waited for every load in flight, the tiles issued
+// ahead included).
 constexpr int kAuxNt = 2;  // cache-policy bit: nontemporal (the signs are read once)
 // raw (stride 0) buffer over p: bytes [0, 2^32 - 1) if live, none otherwise;
 // word 3 holds the gfx9 data format the raw loads ignore
@@ -238,7 +241,8 @@ __global__ void __launch_bounds__(f4_max_waves(K) * kWave) gemv_f4_kernel(
     const bool has_x = xt < sg * 16;
     const uint4 u = has_x ? *reinterpret_cast<const uint4*>(x + (int64_t)g0 * kGroup + 8 * xt)
                           : make_uint4(0, 0, 0, 0);
-    F4Loads<K, AT> L0, L1, L2, L3;
+    F4Loads<K, AT> Lb[kF4Ahead + 1];  // tile t in Lb[t % (kF4Ahead + 1)]
+    F4Loads<K, AT>& L0 = Lb[0];
     if (EARLY) {
       load(0, L0);
     } else {
@@ -304,8 +308,10 @@ __global__ void __launch_bounds__(f4_max_waves(K) * kWave) gemv_f4_kernel(
     corr = corr + __uint_as_float(dpp_u32<kQuadXor2>(__float_as_uint(corr)));
     corr = corr + __uint_as_float(dpp_u32<kRowHalfMirror>(__float_as_uint(corr)));
     corr = corr + __uint_as_float(dpp_u32<kRowMirror>(__float_as_uint(corr)));
-    if (NT > 1) load(1, L1);  // a tile past the last loads zeros, reading nothing
-    if (NT > 2) load(2, L2);
+    // a tile past the last loads zeros, reading nothing
+#pragma unroll
+    for (int j = 1; j < kF4Ahead; ++j)
+      if (j < NT) load(j, Lb[j]);
     wave_lds_sync();
     // ---- A operands, one per word i.  K-block q of product i holds word i
     // of the wavefront's group q (the B operand of lane 16q + r is word i of
@@ -376,7 +382,7 @@ __global__ void __launch_bounds__(f4_max_waves(K) * kWave) gemv_f4_kernel(
       return a;
     };
 
-    // tile t + 3 is loaded while tile t is multiplied; each tile's sums (the
+    // tile t + kF4Ahead is loaded while tile t is multiplied; each tile's sums (the
     // wavefront's four groups are its four lane blocks) go to LDS
     auto step = [&](int t, F4Loads<K, AT>& L) {
       float uu = mul(L, 0.f);
@@ -401,12 +407,11 @@ __global__ void __launch_bounds__(f4_max_waves(K) * kWave) gemv_f4_kernel(
     // t's products covers tile t's loads alone (with the loads skipped by a
     // branch, the compiler waited for every load in flight, the tiles issued
     // ahead included).
-    F4Loads<K, AT>* Ls[4] = {&L0, &L1, &L2, &L3};
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       if (t >= ntl) break;
-      if (t + 3 < NT) load(t + 3, *Ls[(t + 3) & 3]);
-      step(t, *Ls[t & 3]);
+      if (t + kF4Ahead < NT) load(t + kF4Ahead, Lb[(t + kF4Ahead) % (kF4Ahead + 1)]);
+      step(t, Lb[t % (kF4Ahead + 1)]);
     }
   }
 
