@@ -12,7 +12,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
 import bench  # noqa: E402
 
-GEMV = "void mbok::(anonymous namespace)::gemv_stream_kernel<unsigned short, unsigned short, 2, 8>(...)"
+# config 2 (4096 x 4096, K = 2) runs the matrix-core decode kernel by default
+GEMV = "void mbok::(anonymous namespace)::gemv_f4_kernel<unsigned short, 2, 1>(...)"
 COPY = "__amd_rocclr_copyBuffer"
 
 
@@ -47,7 +48,7 @@ def _make(tmp_path, counter):
 
 def test_bracket_finds_the_last_copy_calls_copy():
     seq = [(i, nm, v) for i, (nm, v) in enumerate(_dispatches())]
-    copy, calls = bench.bracketed(seq, "gemv_stream_kernel")
+    copy, calls = bench.bracketed(seq, "gemv_f4_kernel")
     assert copy == [65536.0, 65536.0]
     assert calls == [2500.0] * bench.CAL_CALLS
 
@@ -80,7 +81,7 @@ def test_summary_scales_counters_by_the_copy(tmp_path):
     assert float(rec["fetch_bytes_per_launch"]) == pytest.approx(2500 * 1024 * 2.0)
     assert float(rec["traffic_bytes_per_launch"]) == pytest.approx(2 * 2500 * 1024 * 2.0)
     assert float(rec["dominant_call_kernel_us"].split()[0]) == pytest.approx(5.0)
-    assert rec["source_sha256"].strip() == bench.source_digest(1)
+    assert rec["source_sha256"].strip() == bench.source_digest(1, 4096, 4096, 2)
 
 
 def test_timed_regions_between_markers():
