@@ -69,18 +69,26 @@ struct ExactSum {
   }
 };
 
+// A partial allocation of weights 0..l: its bits, its exact error sum, and
+// its K prefix as a link to the state of weights 0..l-1 it extends plus its
+// own K.  `lex` is the rank of the prefix in lexicographic order among the
+// states of the same length: prefixes compare as (rank of the parent prefix,
+// K), so ties are broken without copying prefixes.
 struct State {
   int64_t bits;
   ExactSum err;
-  std::vector<uint8_t> ks;
+  int32_t parent;
+  int32_t lex;
+  uint8_t K;
 };
 
-// (bits, error, prefix) ascending
-bool state_less(const State& a, const State& b) {
+// (bits, error, prefix) ascending; plex = ranks of the parents' prefixes
+bool state_less(const State& a, const State& b, const std::vector<int32_t>& plex) {
   if (a.bits != b.bits) return a.bits < b.bits;
   const int c = a.err.cmp(b.err);
   if (c != 0) return c < 0;
-  return a.ks < b.ks;
+  if (a.parent != b.parent) return plex[a.parent] < plex[b.parent];
+  return a.K < b.K;
 }
 
 constexpr size_t kMaxStates = size_t(1) << 22;
@@ -98,10 +106,20 @@ int allocate_kernels(int L, const int64_t* sizes, const double* errors, int kmax
 
   std::vector<State> front(1);
   front[0].bits = 0;
+  front[0].parent = -1;
+  front[0].lex = 0;
+  front[0].K = 0;
   std::vector<State> cand;
+  std::vector<int32_t> plex;
+  std::vector<size_t> order;
+  // links[l][i]: (parent index in front l-1, K) of state i of front l
+  std::vector<std::vector<std::pair<int32_t, uint8_t>>> links(L);
   for (int l = 0; l < L; ++l) {
     cand.clear();
-    for (const State& st : front) {
+    plex.resize(front.size());
+    for (size_t fi = 0; fi < front.size(); ++fi) {
+      plex[fi] = front[fi].lex;
+      const State& st = front[fi];
       for (int K = 1; K <= kmax; ++K) {
         const int64_t nb = st.bits + (int64_t)K * sizes[l];
         if (nb + suffix[l + 1] > budget) break;  // larger K only uses more
@@ -109,24 +127,43 @@ int allocate_kernels(int L, const int64_t* sizes, const double* errors, int kmax
         s.bits = nb;
         s.err = st.err;
         s.err.add(errs[(size_t)l * kmax + (K - 1)]);
-        s.ks = st.ks;
-        s.ks.push_back((uint8_t)K);
-        cand.push_back(std::move(s));
+        s.parent = (int32_t)fi;
+        s.lex = 0;
+        s.K = (uint8_t)K;
+        cand.push_back(s);
       }
     }
     if (cand.size() > kMaxStates) return MBOK_ERR_UNSUPPORTED;
-    std::sort(cand.begin(), cand.end(), state_less);
+    order.resize(cand.size());
+    for (size_t i = 0; i < order.size(); ++i) order[i] = i;
+    std::sort(order.begin(), order.end(), [&](size_t a, size_t b) {
+      return state_less(cand[a], cand[b], plex);
+    });
     front.clear();
-    for (State& s : cand) {
+    for (size_t i : order) {
       // keep only states with a strictly smaller error than every kept one
       // (those use no more bits, or the same bits and come first)
-      if (front.empty() || s.err.cmp(front.back().err) < 0) front.push_back(std::move(s));
+      if (front.empty() || cand[i].err.cmp(front.back().err) < 0) front.push_back(cand[i]);
     }
+    // lexicographic ranks of the kept prefixes: (parent's rank, K)
+    order.resize(front.size());
+    for (size_t i = 0; i < order.size(); ++i) order[i] = i;
+    std::sort(order.begin(), order.end(), [&](size_t a, size_t b) {
+      const State &x = front[a], &y = front[b];
+      if (x.parent != y.parent) return plex[x.parent] < plex[y.parent];
+      return x.K < y.K;
+    });
+    for (size_t r = 0; r < order.size(); ++r) front[order[r]].lex = (int32_t)r;
+    links[l].resize(front.size());
+    for (size_t i = 0; i < front.size(); ++i) links[l][i] = {front[i].parent, front[i].K};
   }
   // the front is ordered by bits with strictly falling error: the last state
   // has the least error, and no other state has that error
-  const State& best = front.back();
-  for (int l = 0; l < L; ++l) K_out[l] = best.ks[l];
+  int32_t at = (int32_t)front.size() - 1;
+  for (int l = L - 1; l >= 0; --l) {
+    K_out[l] = links[l][at].second;
+    at = links[l][at].first;
+  }
   return MBOK_OK;
 }
 
