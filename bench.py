@@ -114,6 +114,10 @@ def kernel_family(T, m=None, n=None, K=None, x_bf16=True):
         if x_bf16 and m is not None and (K * n >= 8192 or K * m * n >= (1 << 25) or K >= 4):
             return "gemv_f4.hip", "gemv_f4_kernel"
         return "gemv.hip", "gemv_stream_kernel"
+    v = os.environ.get("MBOK_SKINNY_VARIANT", "")
+    if (T == 2 and v in ("", "f4")) or (T <= 4 and v == "f4"):
+        # the matrix-core kernel (use_f4_for_tokens in csrc/gemm.hip)
+        return "gemv_f4.hip", "gemm_f4_kernel"
     if T <= 16:
         return "skinny.hip", "gemm_skinny"
     return "gemm.hip", "gemm_mfma"

@@ -22,6 +22,7 @@
 // ((W1 >> q) & 0x01010101) | ((W2 >> q) & ..) << 1 | ((W3 >> q) & ..) << 2, and
 // v_perm_b32 turns that selector into 4 low bytes and 4 high bytes of bf16
 // weights at once; two more perms interleave them into natural column order.
+#include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -746,10 +747,29 @@ int launch_mfma(const Geom& geo, const void* packed, const void* X, int64_t T, i
 
 }  // namespace
 
+// Two tokens take the fp4 x fp8 matrix-core kernel (gemv_f4.hip): the same
+// instructions as one token, with the second token in the operand rows one
+// token leaves empty.  Measured per call (HIP graph, cold weights): LLaMA-7B
+// MLP 11008x4096 / 4096x11008, K = 3, three linears per step: 23.2 against
+// 35.7 us for the bf16 +-1 kernel.  Three or four tokens need two
+// instructions per product and gain little or lose (4 tokens: 33.9 against
+// 36.1 us on the MLP; 6.84 against 5.17 us on 4096x4096 K = 2), so they stay
+// on the bf16 +-1 kernels.  MBOK_SKINNY_VARIANT=f4 takes the matrix-core
+// kernel for 2..4 tokens, =stream|blocks the bf16 +-1 kernels (skinny.hip).
+bool use_f4_for_tokens(const mbok_desc*, int64_t T) {
+  const char* v = getenv("MBOK_SKINNY_VARIANT");
+  if (v && *v) return strcmp(v, "f4") == 0 && T >= 2 && T <= gemm_f4_max_tokens();
+  return T == 2;
+}
+
 int launch_gemm(const mbok_desc* d, const void* packed, const void* X, int64_t T, int64_t ldx,
                 float* Y, int64_t ldy, int passes, hipStream_t stream) {
   const Geom geo = make_geom(d);
   if (T == 1) return launch_gemv(d, packed, X, MBOK_BF16, Y, nullptr, stream);
+  // the two-term product keeps the few-token kernel's exact fp32 scaling
+  if (passes == 1 && use_f4_for_tokens(d, T) && (T - 1) * ldx + d->n <= INT32_MAX &&
+      (T - 1) * ldy + d->m <= INT32_MAX)
+    return launch_gemm_f4(d, packed, X, T, ldx, Y, ldy, stream);
   if (T <= skinny_max_tokens()) return launch_skinny(d, packed, X, T, ldx, Y, ldy, stream);
   if (T > 65535LL * BT) return MBOK_ERR_SHAPE;
   if (d->alpha_dtype == MBOK_F16)

@@ -49,6 +49,10 @@
 // and writes the fp8 bytes of both parts to the wavefront's part of LDS (no
 // workgroup barrier).  A fixed-order sum over wavefronts in LDS gives y (no
 // atomics).  A NaN or infinite activation makes every output NaN.
+#include <stdint.h>
+
+#include <type_traits>
+
 #include "mbok_device.h"
 #include "mbok_launch.h"
 
@@ -75,7 +79,13 @@ constexpr int kF4MaxSlab = kF4GroupsPerWave * kF4MaxWaves;  // 64 groups
 // wavefronts per workgroup, so that the tile buffers fit in registers: 16
 // (128 VGPRs each) for K <= 2, 12 (168) for K = 3, 8 (256) for K = 4
 constexpr int f4_max_waves(int K) { return K >= 4 ? 8 : (K == 3 ? 12 : kF4MaxWaves); }
+// with 2..4 tokens the A operands and sums take ~16 more registers per token
+// pair and kernel: 12 wavefronts for K = 1, 8 otherwise
+constexpr int f4_max_waves(int K, int TT) {
+  return TT == 1 ? f4_max_waves(K) : (K == 1 ? 12 : 8);
+}
 constexpr int kF4J = 8;         // most tiles per workgroup
+constexpr int kF4MaxTokens = 4;  // tokens of one few-token call (2 per token pair)
 // tiles loaded ahead of the one multiplied (measured, 27648 x 5120 K = 3:
 // 13.0 us two ahead, 13.4-13.7 three, 13.6 four)
 constexpr int kF4Ahead = 2;
@@ -425,6 +435,321 @@ __global__ void __launch_bounds__(f4_max_waves(K) * kWave) gemv_f4_kernel(
   }
 }
 
+// The few-token form of the kernel above, TT = 2..4 tokens: token t's activations are row t of x (ldx elements
+// apart) and its outputs row t of y (ldy apart).  A row 4q + s of a product
+// holds part s & 1 of token 2p + (s >> 1) for token pair p (the one-token kernel
+// leaves rows 4q + 2, 4q + 3 zero), so 2 tokens take one instruction per (tile,
+// kernel, word) and 3 or 4 tokens two.
+template <typename AT, int K, int NT, int TT>
+__device__ __forceinline__ void f4_tokens_body(const uint4* __restrict__ bits,
+                                        const uint16_t* __restrict__ x, int64_t ldx, int G,
+                                        int tiles, int slab_groups, int grid, int nw, int tpw,
+                                        int textra, float* __restrict__ y, int64_t ldy, int m) {
+  constexpr int TP = (TT + 1) / 2;  // token pairs
+  static_assert(TT >= 2 && TT <= 4, "2..4 tokens");
+  constexpr int kSlabMax = kF4GroupsPerWave * f4_max_waves(K, TT);
+  constexpr int kRedWaves = f4_max_waves(K, TT);
+  // the scales follow the sign region: tiles * 16 rows x G groups x K chunks
+  const AT* __restrict__ scales =
+      reinterpret_cast<const AT*>(bits + (int64_t)tiles * 16 * G * K);
+  // converted activations: [group][token][part][word][32 terms]
+  __shared__ __attribute__((aligned(16))) uint8_t ops[kSlabMax * TT * kOpBytes];  // up to 32 KB
+  __shared__ __attribute__((aligned(4))) uint8_t codes[kSlabMax * TT * 4];
+  __shared__ float red[NT * kRedWaves * TT * 16];
+  const int NW = nw;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int r = lane & 15;   // row of the tile (B column, D column; A row at A time)
+  const int q = lane >> 4;   // lane block: K-block q holds group 4 wave + q
+  const int b = blockIdx.x;
+  const int ntl = tpw + (b < textra ? 1 : 0);  // tiles of this workgroup, <= NT
+  constexpr bool EARLY = NT > 1;  // NT: tile slots, the most tiles of any workgroup
+  int nonfinite = 0;  // bit t: this thread saw a NaN or infinite activation of token t
+  // B dword d, nibble p: bit 4p + d of the word at nibble bit d, over a base
+  // nibble: d = 0 {4.0, 6.0}, d = 1 {2.0, 4.0}, d = 2 {0, 2.0}, d = 3
+  // {1.0, -1.0}, i.e. c_d + b with c = 5, 3, 1 and -b for d = 3
+  const uint32_t m0 = sgpr_const(0x11111111u), m1 = sgpr_const(0x22222222u);
+  const uint32_t m2 = sgpr_const(0x44444444u), m3 = sgpr_const(0x88888888u);
+  const uint32_t b0 = vgpr_const(0x66666666u), b1 = vgpr_const(0x44444444u);
+  const uint32_t b3 = vgpr_const(0x22222222u);
+
+  for (int g0 = 0; g0 < G; g0 += slab_groups) {
+    const int sg = min(slab_groups, G - g0);
+    // this lane's load group (block q), clamped so loads stay in bounds; a
+    // group past the slab has a zero A operand and adds nothing
+    const int gq = min(kF4GroupsPerWave * wave + q, sg - 1);
+    // this lane's byte offsets inside a tile's sign and scale blocks
+    const int vs = (gq * K * kRowBlock + r) * 16;
+    const int va = (gq * K * kRowBlock + r) * (int)sizeof(AT);
+    auto load = [&](int t, F4Loads<K, AT>& L) {
+      // opaque to the compiler, so each tile's address is formed where it is
+      // loaded instead of every tile's ahead of the first load
+      int tb = b + t * grid;
+      asm volatile("" : "+s"(tb));
+      const int i0 = tile16_of(tb, tiles) * 16;
+      const int rb = i0 / kRowBlock, r0 = i0 % kRowBlock;
+      const int64_t c0 = ((int64_t)rb * G + g0) * K * kRowBlock + r0;  // the tile's first chunk
+      const i32x4_t rs = buffer_rsrc(bits + c0, t < ntl);
+      const i32x4_t ra = buffer_rsrc(scales + c0, t < ntl);
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        L.s[k] = as_uint4(raw_buffer_load_b128(rs, vs + k * kRowBlock * 16, 0, kAuxNt));
+        L.a[k] = load_scale<AT>(ra, va + k * kRowBlock * (int)sizeof(AT));
+      }
+    };
+    // The activations first.  Every compute unit asks for them at once, and
+    // each sign load issued before they arrive sits in the same memory
+    // queues ahead of other wavefronts' activation loads, so only the first
+    // tile's signs go out now (EARLY: some workgroup has more than one tile
+    // to keep the stream going; else right after the activations arrive),
+    // the rest once this wavefront has converted its activations (measured:
+    // 11008 x 4096 7.9 -> 7.1 us, 4096 x 4096 K = 2 4.65 -> 4.09 us).  EARLY
+    // is a compile-time choice so that the conversion waits for the
+    // activations alone (a runtime condition made the compiler wait for
+    // every load in flight).
+    const int xt = threadIdx.x;  // 8 columns per thread, 4 threads per 32-column word
+    const bool has_x = xt < sg * 16;
+    uint4 u[TT];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+      u[tt] = has_x ? *reinterpret_cast<const uint4*>(x + tt * ldx + (int64_t)g0 * kGroup + 8 * xt)
+                    : make_uint4(0, 0, 0, 0);
+    F4Loads<K, AT> Lb[kF4Ahead + 1];  // tile t in Lb[t % (kF4Ahead + 1)]
+    F4Loads<K, AT>& L0 = Lb[0];
+    if (EARLY) {
+      load(0, L0);
+    } else {
+      // one tile per workgroup: its signs go out as soon as the activations
+      // are in, ahead of the conversion (3.96 -> 3.86 us for 4096 x 4096)
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      load(0, L0);
+    }
+
+    // ---- activations -> fp8 operand bytes.  Thread xt converts columns
+    // 8 xt .. 8 xt + 7 of the slab, so wavefront w converts exactly its own
+    // groups 4w .. 4w+3 into its own part of the LDS operand bytes: only the
+    // wavefront's own LDS accesses need ordering, never the workgroup's.
+    // (Its reads of the previous slab's bytes were consumed before the first
+    // product of that slab.)
+    float corr[TT];  // sum over this thread's columns of c(class) x, per token
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) corr[tt] = 0.f;
+    if (has_x) {
+      const int gl = xt >> 4, word = (xt >> 2) & 3, sub = xt & 3;
+      // column 8 sub + e is in sign class ((8 sub + e) >> 2) & 3 = 2 (sub & 1) + (e >> 2)
+      const bool odd = (sub & 1) != 0;
+      const float c_lo = odd ? 1.f : 5.f, c_hi = odd ? 0.f : 3.f;  // e < 4, e >= 4
+      // Threads sub and sub ^ 2 fill the word's terms 16 (sub & 1) ..
+      // +15: term byte 2e + h is column 8 sub + e of the thread with h =
+      // sub >> 1.  The h = 0 thread writes bytes 0..7 (columns e = 0..3 of
+      // both), the h = 1 thread bytes 8..15, after one exchange in the quad.
+      const bool h = (sub >> 1) != 0;
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
+        const uint32_t wv[4] = {u[tt].x, u[tt].y, u[tt].z, u[tt].w};
+        uint32_t mx = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mx = max(mx, max(wv[e] & 0x7fffu, (wv[e] >> 16) & 0x7fffu));
+        // the word's 4 threads are a quad of lanes
+        mx = max(mx, dpp_u32<kQuadXor1>(mx));
+        mx = max(mx, dpp_u32<kQuadXor2>(mx));
+        const int eb = (int)(mx >> 7);  // biased exponent of the word's largest |x|
+        if (eb == 0xff) nonfinite |= 1 << tt;
+        const int code = mx == 0 ? kE8M0One : (eb > 7 ? eb - 7 : 0);
+        const int lcode = lo_code(code);
+        if (sub == 0) codes[(gl * TT + tt) * 4 + word] = (uint8_t)code;
+        uint32_t H[4], L[4];  // fp8 bytes of columns 2d, 2d + 1 in bytes 0, 1
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const float x0 = bf16_bits_to_f32(wv[d] & 0xffffu);
+          const float x1 = bf16_bits_to_f32(wv[d] >> 16);
+          corr[tt] = fmaf(d < 2 ? c_lo : c_hi, x0, corr[tt]);
+          corr[tt] = fmaf(d < 2 ? c_lo : c_hi, x1, corr[tt]);
+          const bool neg = d >= 2 && odd;  // class 3
+          const float v0 = __builtin_ldexpf(neg ? -x0 : x0, kE8M0One - code);
+          const float v1 = __builtin_ldexpf(neg ? -x1 : x1, kE8M0One - code);
+          const int h8 = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
+          const auto back = __builtin_amdgcn_cvt_pk_f32_fp8(h8, false);
+          const float l0 = __builtin_ldexpf(v0 - back[0], code - lcode);
+          const float l1 = __builtin_ldexpf(v1 - back[1], code - lcode);
+          H[d] = (uint32_t)h8;
+          L[d] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(l0, l1, 0, false);
+        }
+        uint8_t* hi = ops + (gl * TT + tt) * kOpBytes + word * 32 + 16 * (sub & 1) + 8 * (int)h;
+        uint8_t* lo = hi + kOpBytes / 2;
+        *reinterpret_cast<uint2*>(hi) = pair_terms(H, h);
+        *reinterpret_cast<uint2*>(lo) = pair_terms(L, h);
+      }
+    }
+    // the group's correction: lanes 16j .. 16j+15 converted group 4w + j
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      float c = corr[tt];
+      c = c + __uint_as_float(dpp_u32<kQuadXor1>(__float_as_uint(c)));
+      c = c + __uint_as_float(dpp_u32<kQuadXor2>(__float_as_uint(c)));
+      c = c + __uint_as_float(dpp_u32<kRowHalfMirror>(__float_as_uint(c)));
+      c = c + __uint_as_float(dpp_u32<kRowMirror>(__float_as_uint(c)));
+      corr[tt] = c;
+    }
+    // a tile past the last loads zeros, reading nothing
+#pragma unroll
+    for (int j = 1; j < kF4Ahead; ++j)
+      if (j < NT) load(j, Lb[j]);
+    wave_lds_sync();
+    // ---- A operands, one per word i.  K-block q of product i holds word i
+    // of the wavefront's group q (the B operand of lane 16q + r is word i of
+    // its own loaded chunk), and A row 4q + e holds part e of that group
+    // (e = 0 high, 1 low), nonzero only in K-block q.  Lane 16c + rho holds
+    // A row rho, terms 16c .. 16c+15 (bytes 0..15) and 64 + 16c .. (bytes
+    // 16..31): K-block q sits in lane blocks 2 (q & 1) and 2 (q & 1) + 1,
+    // bytes 16 (q >> 1) ... of them.  The E8M0 scale of (row rho, K-block c)
+    // is lane 16c + rho's.
+    // With several tokens, A row 4q + s holds part s & 1 of token 2p + (s >> 1)
+    // in the operands of token pair p.
+    v8i_t A[TP][4];
+    int ascale[TP][4];
+    {
+      const int qa = r >> 2, slot = r & 3;  // this lane's A row 4 qa + slot
+      const int part = slot & 1;
+      const int gl = kF4GroupsPerWave * wave + qa;
+      const int glc = min(gl, sg - 1);
+      const bool upper = (qa >> 1) != 0;
+      // scale of (row r, K-block q): nonzero rows of K-block q are 4q .. 4q + 3
+      const int sq = min(kF4GroupsPerWave * wave + q, sg - 1);
+#pragma unroll
+      for (int p = 0; p < TP; ++p) {
+        const int tt = 2 * p + (slot >> 1);
+        const int ttc = min(tt, TT - 1);
+        const bool live = tt < TT && gl < sg && (qa & 1) == (q >> 1);
+        const uint8_t* base =
+            ops + (glc * TT + ttc) * kOpBytes + part * (kOpBytes / 2) + 16 * (q & 1);
+        // every read goes out before the first wait, and the zero half (or the
+        // whole operand of a dead row) is masked, not branched around
+        uint4 dd[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dd[i] = *reinterpret_cast<const uint4*>(base + 32 * i);
+        const uint32_t cw = *reinterpret_cast<const uint32_t*>(codes + (sq * TT + ttc) * 4);
+        const uint32_t keep = live ? ~0u : 0u;
+        const uint32_t klo = upper ? 0u : keep, khi = upper ? keep : 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          A[p][i] = v8i_t{(int)(dd[i].x & klo), (int)(dd[i].y & klo), (int)(dd[i].z & klo),
+                          (int)(dd[i].w & klo), (int)(dd[i].x & khi), (int)(dd[i].y & khi),
+                          (int)(dd[i].z & khi), (int)(dd[i].w & khi)};
+          asm volatile("" : "+v"(A[p][i]));
+        }
+        const bool srow = (r >> 2) == q && tt < TT && kF4GroupsPerWave * wave + q < sg;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int code = (int)((cw >> (8 * i)) & 0xffu);
+          ascale[p][i] = !srow ? kE8M0One : (part == 0 ? code : lo_code(code));
+        }
+      }
+    }
+
+    // Per kernel: the four words' products chained (interleaved over the
+    // kernels); lane 16j + r then holds group j's high and low sums for row r
+    // in registers 0 and 1.
+    // Per kernel: the four words' products chained (interleaved over the
+    // kernels); lane 16j + r then holds group j's high and low sums for row r
+    // in registers 0 and 1 (token 2p of pair p) and 2 and 3 (token 2p + 1).
+    auto mul = [&](F4Loads<K, AT>& L, float (&a)[TT]) {
+      v4f_t d[K][TP];
+#pragma unroll
+      for (int k = 0; k < K; ++k)
+#pragma unroll
+        for (int p = 0; p < TP; ++p) d[k][p] = v4f_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          const uint32_t w = i == 0 ? L.s[k].x : i == 1 ? L.s[k].y : i == 2 ? L.s[k].z : L.s[k].w;
+          v8i_t B;
+          B[0] = (int)((w & m0) | b0);
+          B[1] = (int)((w & m1) | b1);
+          B[2] = (int)(w & m2);
+          B[3] = (int)((w & m3) | b3);
+          B[4] = B[5] = B[6] = B[7] = 0;
+#pragma unroll
+          for (int p = 0; p < TP; ++p)
+            d[k][p] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[p][i], B, d[k][p], 0, 4, 0,
+                                                                       ascale[p][i], 0, kE8M0One);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const float al = alpha_to_f32<AT>(L.a[k]);
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+          const v4f_t& dk = d[k][tt >> 1];
+          const float hl = (tt & 1) ? dk[2] + dk[3] : dk[0] + dk[1];
+          a[tt] = fmaf(al, hl - corr[tt], a[tt]);
+        }
+      }
+    };
+
+    // tile t + kF4Ahead is loaded while tile t is multiplied; each tile's sums (the
+    // wavefront's four groups are its four lane blocks) go to LDS
+    auto step = [&](int t, F4Loads<K, AT>& L) {
+      float uu[TT];
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) uu[tt] = 0.f;
+      mul(L, uu);
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
+        // sum over the four lane blocks (groups): 16-lane rows 0+1, 2+3, then
+        // the two halves, with lane swaps instead of LDS permutes
+        float v = uu[tt];
+        const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                        false, false);
+        v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+        const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                        false, false);
+        v = __uint_as_float(c[0]) + __uint_as_float(c[1]);
+        if (q == 0) {
+          float* dst = red + ((t * NW + wave) * TT + tt) * 16 + r;
+          *dst = g0 == 0 ? v : *dst + v;  // slabs in order
+        }
+      }
+    };
+    // Unrolled over the tile slots, with every load issued whether or not
+    // its tile exists: a workgroup's last tile leaves the chain, no path that
+    // skipped a load merges back into the steps, and the wait before tile
+    // t's products covers tile t's loads alone (with the loads skipped by a
+    // branch, the compiler waited for every load in flight, the tiles issued
+    // ahead included).
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (t >= ntl) break;
+      if (t + kF4Ahead < NT) load(t + kF4Ahead, Lb[(t + kF4Ahead) % (kF4Ahead + 1)]);
+      step(t, Lb[t % (kF4Ahead + 1)]);
+    }
+  }
+
+  int bad = 0;  // bit t: some thread saw a non-finite activation of token t
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt)
+    if (__syncthreads_or(nonfinite & (1 << tt))) bad |= 1 << tt;
+  for (int idx = threadIdx.x; idx < ntl * 16 * TT; idx += NW * kWave) {
+    const int tt = idx / (ntl * 16), e = idx - tt * (ntl * 16);
+    const int t = e >> 4, rr = e & 15;
+    float uu = red[((t * NW) * TT + tt) * 16 + rr];
+    for (int w = 1; w < NW; ++w) uu += red[((t * NW + w) * TT + tt) * 16 + rr];
+    const int i = tile16_of(b + t * grid, tiles) * 16 + rr;
+    if (i < m) y[tt * ldy + i] = ((bad >> tt) & 1) ? __builtin_nanf("") : uu;
+  }
+}
+
+
+// 2..4 tokens; the token strides follow the arguments of the one-token kernel
+template <typename AT, int K, int NT, int TT>
+__global__ void __launch_bounds__(f4_max_waves(K, TT) * kWave) gemm_f4_kernel(
+    const uint4* __restrict__ bits, const uint16_t* __restrict__ x, int G, int tiles,
+    int slab_groups, int grid, int nw, int tpw, int textra, float* __restrict__ y, int m,
+    int ldx, int ldy) {
+  f4_tokens_body<AT, K, NT, TT>(bits, x, ldx, G, tiles, slab_groups, grid, nw, tpw, textra, y, ldy, m);
+}
+
 template <typename AT, int K>
 int launch_f4_k(const Geom& geo, const void* packed, const void* x, float* y,
                 hipStream_t stream) {
@@ -468,6 +793,62 @@ int launch_f4_t(const Geom& geo, const void* packed, const void* x, float* y,
   return MBOK_ERR_UNSUPPORTED;
 }
 
+// 2..4 tokens: the shape rules of launch_f4_k with the few-token kernel's
+// wavefront budget
+template <typename AT, int K, int TT>
+int launch_f4_tokens_k(const Geom& geo, const void* packed, const void* X, int ldx, float* Y,
+                       int ldy, hipStream_t stream) {
+  const int max_slab = kF4GroupsPerWave * f4_max_waves(K, TT);
+  const int nslabs = (geo.G + max_slab - 1) / max_slab;
+  const int slab = (geo.G + nslabs - 1) / nslabs;
+  const int NW = (slab + kF4GroupsPerWave - 1) / kF4GroupsPerWave;
+  const int tiles = geo.RB * (kRowBlock / 16);
+  int grid = tiles < 256 ? tiles : 256;
+  if (grid * kF4J < tiles) grid = (tiles + kF4J - 1) / kF4J;
+  const int slots = (tiles + grid - 1) / grid;
+  auto go = [&](auto slot_count) {
+    constexpr int S = decltype(slot_count)::value;
+    hipLaunchKernelGGL((gemm_f4_kernel<AT, K, S, TT>), dim3(grid), dim3(NW * kWave), 0, stream,
+                       reinterpret_cast<const uint4*>(packed),
+                       reinterpret_cast<const uint16_t*>(X), geo.G, tiles, slab, grid, NW,
+                       tiles / grid, tiles % grid, Y, geo.m, ldx, ldy);
+  };
+  switch (slots) {
+    case 1: go(std::integral_constant<int, 1>{}); break;
+    case 2: go(std::integral_constant<int, 2>{}); break;
+    case 3: go(std::integral_constant<int, 3>{}); break;
+    case 4: go(std::integral_constant<int, 4>{}); break;
+    case 5: go(std::integral_constant<int, 5>{}); break;
+    case 6: go(std::integral_constant<int, 6>{}); break;
+    case 7: go(std::integral_constant<int, 7>{}); break;
+    default: go(std::integral_constant<int, 8>{}); break;
+  }
+  return hipGetLastError() == hipSuccess ? MBOK_OK : MBOK_ERR_HIP;
+}
+
+template <typename AT, int TT>
+int launch_f4_tokens_t(const Geom& geo, const void* packed, const void* X, int ldx, float* Y,
+                       int ldy, hipStream_t stream) {
+  switch (geo.K) {
+    case 1: return launch_f4_tokens_k<AT, 1, TT>(geo, packed, X, ldx, Y, ldy, stream);
+    case 2: return launch_f4_tokens_k<AT, 2, TT>(geo, packed, X, ldx, Y, ldy, stream);
+    case 3: return launch_f4_tokens_k<AT, 3, TT>(geo, packed, X, ldx, Y, ldy, stream);
+    case 4: return launch_f4_tokens_k<AT, 4, TT>(geo, packed, X, ldx, Y, ldy, stream);
+  }
+  return MBOK_ERR_UNSUPPORTED;
+}
+
+template <typename AT>
+int launch_f4_tokens(const Geom& geo, const void* packed, const void* X, int T, int ldx,
+                     float* Y, int ldy, hipStream_t stream) {
+  switch (T) {
+    case 2: return launch_f4_tokens_t<AT, 2>(geo, packed, X, ldx, Y, ldy, stream);
+    case 3: return launch_f4_tokens_t<AT, 3>(geo, packed, X, ldx, Y, ldy, stream);
+    case 4: return launch_f4_tokens_t<AT, 4>(geo, packed, X, ldx, Y, ldy, stream);
+  }
+  return MBOK_ERR_SHAPE;
+}
+
 }  // namespace
 
 int launch_gemv_f4(const mbok_desc* d, const void* packed, const void* x, float* y,
@@ -475,6 +856,20 @@ int launch_gemv_f4(const mbok_desc* d, const void* packed, const void* x, float*
   const Geom geo = make_geom(d);
   return d->alpha_dtype == MBOK_F16 ? launch_f4_t<uint16_t>(geo, packed, x, y, stream)
                                     : launch_f4_t<float>(geo, packed, x, y, stream);
+}
+
+int gemm_f4_max_tokens() { return kF4MaxTokens; }
+
+int launch_gemm_f4(const mbok_desc* d, const void* packed, const void* X, int64_t T,
+                   int64_t ldx, float* Y, int64_t ldy, hipStream_t stream) {
+  if (T < 2 || T > kF4MaxTokens) return MBOK_ERR_SHAPE;
+  // token offsets are formed in 32 bits
+  if ((T - 1) * ldx + d->n > INT32_MAX || (T - 1) * ldy + d->m > INT32_MAX)
+    return MBOK_ERR_UNSUPPORTED;
+  const Geom geo = make_geom(d);
+  return d->alpha_dtype == MBOK_F16
+             ? launch_f4_tokens<uint16_t>(geo, packed, X, (int)T, (int)ldx, Y, (int)ldy, stream)
+             : launch_f4_tokens<float>(geo, packed, X, (int)T, (int)ldx, Y, (int)ldy, stream);
 }
 
 }  // namespace mbok
