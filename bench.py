@@ -114,10 +114,13 @@ def kernel_family(T, m=None, n=None, K=None, x_bf16=True):
         if x_bf16 and m is not None and (K * n >= 8192 or K * m * n >= (1 << 25) or K >= 4):
             return "gemv_f4.hip", "gemv_f4_kernel"
         return "gemv.hip", "gemv_stream_kernel"
+    # the few-token choice (token_kernel in csrc/gemm.hip)
     v = os.environ.get("MBOK_SKINNY_VARIANT", "")
-    if (T == 2 and v in ("", "f4")) or (T <= 4 and v == "f4"):
-        # the matrix-core kernel (use_f4_for_tokens in csrc/gemm.hip)
+    if (T == 2 and v == "") or (T <= 4 and v == "f4"):
         return "gemv_f4.hip", "gemm_f4_kernel"
+    big = m is not None and K * m * n >= (1 << 26)
+    if (3 <= T <= 6 and v == "" and big) or (T <= 16 and v == "f4g"):
+        return "gemv_f4.hip", "gemm_f4g_kernel"
     if T <= 16:
         return "skinny.hip", "gemm_skinny"
     return "gemm.hip", "gemm_mfma"

@@ -747,29 +747,50 @@ int launch_mfma(const Geom& geo, const void* packed, const void* X, int64_t T, i
 
 }  // namespace
 
-// Two tokens take the fp4 x fp8 matrix-core kernel (gemv_f4.hip): the same
-// instructions as one token, with the second token in the operand rows one
-// token leaves empty.  Measured per call (HIP graph, cold weights): LLaMA-7B
-// MLP 11008x4096 / 4096x11008, K = 3, three linears per step: 23.2 against
-// 35.7 us for the bf16 +-1 kernel.  Three or four tokens need two
-// instructions per product and gain little or lose (4 tokens: 33.9 against
-// 36.1 us on the MLP; 6.84 against 5.17 us on 4096x4096 K = 2), so they stay
-// on the bf16 +-1 kernels.  MBOK_SKINNY_VARIANT=f4 takes the matrix-core
-// kernel for 2..4 tokens, =stream|blocks the bf16 +-1 kernels (skinny.hip).
-bool use_f4_for_tokens(const mbok_desc*, int64_t T) {
+// Few-token kernel by token count and layer size, from measurements on
+// MI355X (HIP graph of the calls, cold weights; LLaMA-7B MLP step = gate and
+// up 11008x4096 plus down 4096x11008, K = 3; us per step):
+//
+//   tokens                       2     3     4     6     8
+//   fp4 x fp8, two tokens per
+//     one-token product (f4)    22.9  30.2  33.8   -     -
+//   fp4 x fp8, one product per
+//     group, 8 tokens (f4g)     25.4  26.9  29.2  34.4  39.2
+//   bf16 +-1 (skinny.hip)       35.5  35.8  36.1  36.3  37.9
+//
+// and on 4096x4096, K = 2: f4 4.68, f4g 4.89, bf16 +-1 5.05 us at 2 tokens;
+// f4g 5.30 / 5.77 / 6.85 against 5.15 / 5.17 / 5.24 us at 3 / 4 / 6.  The
+// fp4 x fp8 kernels turn signs into operands with 4 vector instructions per
+// 128 signs whatever the token count, but every workgroup converts every
+// token's activations to fp8 parts before its first product, so they lose
+// to the bf16 +-1 kernels on small layers and beyond 6 tokens.
+// MBOK_SKINNY_VARIANT=f4|f4g|stream|blocks forces a kernel.
+enum TokenKernel { kTokSkinny = 0, kTokF4 = 1, kTokF4g = 2 };
+
+TokenKernel token_kernel(const mbok_desc* d, int64_t T) {
   const char* v = getenv("MBOK_SKINNY_VARIANT");
-  if (v && *v) return strcmp(v, "f4") == 0 && T >= 2 && T <= gemm_f4_max_tokens();
-  return T == 2;
+  if (v && *v) {
+    if (strcmp(v, "f4") == 0 && T >= 2 && T <= gemm_f4_max_tokens()) return kTokF4;
+    if (strcmp(v, "f4g") == 0 && T >= 2 && T <= gemm_f4g_max_tokens()) return kTokF4g;
+    return kTokSkinny;
+  }
+  if (T == 2) return kTokF4;
+  const int64_t work = (int64_t)d->K * d->m * d->n;
+  if (T <= 6 && work >= (int64_t(1) << 26)) return kTokF4g;
+  return kTokSkinny;
 }
 
 int launch_gemm(const mbok_desc* d, const void* packed, const void* X, int64_t T, int64_t ldx,
                 float* Y, int64_t ldy, int passes, hipStream_t stream) {
   const Geom geo = make_geom(d);
   if (T == 1) return launch_gemv(d, packed, X, MBOK_BF16, Y, nullptr, stream);
-  // the two-term product keeps the few-token kernel's exact fp32 scaling
-  if (passes == 1 && use_f4_for_tokens(d, T) && (T - 1) * ldx + d->n <= INT32_MAX &&
-      (T - 1) * ldy + d->m <= INT32_MAX)
-    return launch_gemm_f4(d, packed, X, T, ldx, Y, ldy, stream);
+  // the two-term product keeps the bf16 +-1 kernels' exact fp32 scaling
+  if (passes == 1 && T <= skinny_max_tokens() && (T - 1) * ldx + d->n <= INT32_MAX &&
+      (T - 1) * ldy + d->m <= INT32_MAX) {
+    const TokenKernel tk = token_kernel(d, T);
+    if (tk == kTokF4) return launch_gemm_f4(d, packed, X, T, ldx, Y, ldy, stream);
+    if (tk == kTokF4g) return launch_gemm_f4g(d, packed, X, T, ldx, Y, ldy, stream);
+  }
   if (T <= skinny_max_tokens()) return launch_skinny(d, packed, X, T, ldx, Y, ldy, stream);
   if (T > 65535LL * BT) return MBOK_ERR_SHAPE;
   if (d->alpha_dtype == MBOK_F16)

@@ -54,6 +54,7 @@
 #include <type_traits>
 
 #include "mbok_device.h"
+#include "mbok_lanes.h"
 #include "mbok_launch.h"
 
 namespace mbok {
@@ -172,6 +173,22 @@ __device__ __forceinline__ uint16_t load_scale<uint16_t>(i32x4_t rsrc, int voffs
 template <>
 __device__ __forceinline__ float load_scale<float>(i32x4_t rsrc, int voffset) {
   return raw_buffer_load_f32(rsrc, voffset, 0, 0);
+}
+
+// A scale as the 32-bit lane value the spreading exchanges move, and back
+template <typename AT>
+__device__ __forceinline__ uint32_t scale_bits_f4(AT a);
+template <>
+__device__ __forceinline__ uint32_t scale_bits_f4<float>(float a) { return __float_as_uint(a); }
+template <>
+__device__ __forceinline__ uint32_t scale_bits_f4<uint16_t>(uint16_t a) { return a; }
+template <typename AT>
+__device__ __forceinline__ float scale_value_f4(uint32_t b);
+template <>
+__device__ __forceinline__ float scale_value_f4<float>(uint32_t b) { return __uint_as_float(b); }
+template <>
+__device__ __forceinline__ float scale_value_f4<uint16_t>(uint32_t b) {
+  return f16_bits_to_f32((uint16_t)b);
 }
 
 template <int K, typename AT>
@@ -750,6 +767,261 @@ __global__ void __launch_bounds__(f4_max_waves(K, TT) * kWave) gemm_f4_kernel(
   f4_tokens_body<AT, K, NT, TT>(bits, x, ldx, G, tiles, slab_groups, grid, nw, tpw, textra, y, ldy, m);
 }
 
+// ---------------------------------------------------------------------------
+// Several tokens, one product per group.  The kernels above give each
+// product one 32-column word of four groups (K-block q = group q), so an A
+// row is nonzero in one K-block only and holds one part of one token: at most
+// two tokens per instruction.  Here a product covers the four words of ONE
+// group (K-block c = word c), so every A row is dense: row 2 tt + e holds part
+// e of token 8 o + tt of token octet o, and one instruction per (tile,
+// group, kernel, octet) takes 8 tokens.
+//  * B: lane 16q + r loads the chunk of (row r, group q) as above; a 4 x 4
+//    transpose of (16-lane block, word) gives lane 16c + r word c of every
+//    group g (the B operand of group g's product), and the scales are spread
+//    so that every lane holds alpha of its row r for the four groups.
+//  * A (per group and octet, from the wavefront's LDS staging): lane 16c + rho
+//    holds row rho, terms 16c .. 16c+15 (word c >> 1) and 64 + 16c .. (word
+//    2 + (c >> 1)), at byte offset 16 (c & 1) of those words; the E8M0 scale
+//    of (row rho, K-block c) is the code of word c of that token and part.
+//  * D: lane 16j + r holds rows 4j .. 4j+3: tokens 2j (registers 0, 1: high
+//    and low parts) and 2j + 1 (2, 3) of the octet, row r of W.  The lane adds
+//    alpha (hi + lo - C) for its two tokens over the four groups and the K
+//    kernels, so no lane exchange is needed to sum over groups.
+// The correction C of (token, group) is formed while converting and handed
+// to the lanes that need it through the wavefront's LDS.
+constexpr int kF4gTokens = 8;  // tokens per octet (16 A rows: 8 tokens x 2 parts)
+constexpr int kF4gMaxOctets = 2;
+constexpr int kF4gMaxTokens = kF4gTokens * kF4gMaxOctets;
+// wavefronts per workgroup (4 groups each): 12 for one octet (<= 168
+// registers), 8 for two (the A operands of 16 tokens take 64)
+constexpr int f4g_waves(int NO) { return NO == 1 ? 12 : 8; }
+constexpr int kF4gOpsPerWave = kF4GroupsPerWave * kF4gTokens * kOpBytes;  // 8 KB
+
+template <typename AT, int K, int NT, int NO>
+__global__ void __launch_bounds__(f4g_waves(NO) * kWave) gemm_f4g_kernel(
+    const uint4* __restrict__ bits, const uint16_t* __restrict__ X, int G, int tiles,
+    int slab_groups, int grid, int nw, int tpw, int textra, float* __restrict__ Y, int m, int T,
+    int ldx, int ldy) {
+  constexpr int NWM = f4g_waves(NO);
+  constexpr int TO = kF4gTokens * NO;  // token slots
+  const AT* __restrict__ scales =
+      reinterpret_cast<const AT*>(bits + (int64_t)tiles * 16 * G * K);
+  // per wavefront: [group j][token tt][part][word][32 terms] of one octet
+  __shared__ __attribute__((aligned(16))) uint8_t ops[NWM * kF4gOpsPerWave];
+  __shared__ __attribute__((aligned(4))) uint8_t codes[NWM * kF4GroupsPerWave * kF4gTokens * 4];
+  __shared__ float cs[NWM * kF4GroupsPerWave * kF4gTokens];  // corrections [j][tt]
+  __shared__ float red[NT * NWM * TO * 16];
+  __shared__ int bad_tokens;
+  const int NW = nw;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int r = lane & 15;
+  const int q = lane >> 4;
+  const int b = blockIdx.x;
+  const int ntl = tpw + (b < textra ? 1 : 0);
+  constexpr bool EARLY = NT > 1;
+  if (threadIdx.x == 0) bad_tokens = 0;
+  int nonfinite = 0;  // bit t: this thread saw a NaN or infinite activation of token t
+  const uint32_t m0 = sgpr_const(0x11111111u), m1 = sgpr_const(0x22222222u);
+  const uint32_t m2 = sgpr_const(0x44444444u), m3 = sgpr_const(0x88888888u);
+  const uint32_t b0 = vgpr_const(0x66666666u), b1 = vgpr_const(0x44444444u);
+  const uint32_t b3 = vgpr_const(0x22222222u);
+  uint8_t* const wops = ops + wave * kF4gOpsPerWave;
+  uint8_t* const wcodes = codes + wave * (kF4GroupsPerWave * kF4gTokens * 4);
+  float* const wcs = cs + wave * (kF4GroupsPerWave * kF4gTokens);
+
+  for (int g0 = 0; g0 < G; g0 += slab_groups) {
+    const int sg = min(slab_groups, G - g0);
+    const int gq = min(kF4GroupsPerWave * wave + q, sg - 1);
+    const int vs = (gq * K * kRowBlock + r) * 16;
+    const int va = (gq * K * kRowBlock + r) * (int)sizeof(AT);
+    auto load = [&](int t, F4Loads<K, AT>& L) {
+      int tb = b + t * grid;
+      asm volatile("" : "+s"(tb));
+      const int i0 = tile16_of(tb, tiles) * 16;
+      const int rb = i0 / kRowBlock, r0 = i0 % kRowBlock;
+      const int64_t c0 = ((int64_t)rb * G + g0) * K * kRowBlock + r0;
+      const i32x4_t rs = buffer_rsrc(bits + c0, t < ntl);
+      const i32x4_t ra = buffer_rsrc(scales + c0, t < ntl);
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        L.s[k] = as_uint4(raw_buffer_load_b128(rs, vs + k * kRowBlock * 16, 0, kAuxNt));
+        L.a[k] = load_scale<AT>(ra, va + k * kRowBlock * (int)sizeof(AT));
+      }
+    };
+    // this lane converts 8 columns of group j = lane >> 4 of the wavefront
+    const int gl = kF4GroupsPerWave * wave + q;
+    const bool has_g = gl < sg;
+    const int word = (lane >> 2) & 3, sub = lane & 3;
+    const bool odd = (sub & 1) != 0;
+    const float c_lo = odd ? 1.f : 5.f, c_hi = odd ? 0.f : 3.f;
+    const bool h = (sub >> 1) != 0;
+    const uint16_t* xg = X + (int64_t)(g0 + (has_g ? gl : 0)) * kGroup + 8 * (lane & 15);
+
+    F4Loads<K, AT> Lb[kF4Ahead + 1];
+    v8i_t A[kF4GroupsPerWave][NO];
+    int ascale[kF4GroupsPerWave][NO];
+    float C[NO][kF4GroupsPerWave][2];  // corrections of this lane's two tokens
+    // every token's activations first, then the first tile's signs (as for
+    // one token: behind the activations, or once they are in)
+    uint4 u[NO][kF4gTokens];
+#pragma unroll
+    for (int o = 0; o < NO; ++o)
+#pragma unroll
+      for (int tt = 0; tt < kF4gTokens; ++tt) {
+        const int t = kF4gTokens * o + tt;
+        u[o][tt] = (has_g && t < T) ? *reinterpret_cast<const uint4*>(xg + t * ldx)
+                                    : make_uint4(0, 0, 0, 0);
+      }
+    if (EARLY) {
+      load(0, Lb[0]);
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      load(0, Lb[0]);
+    }
+#pragma unroll
+    for (int o = 0; o < NO; ++o) {
+#pragma unroll
+      for (int tt = 0; tt < kF4gTokens; ++tt) {
+        // tokens past T are not converted: their A rows are masked below
+        if (kF4gTokens * o + tt >= T) break;
+        const uint32_t wv[4] = {u[o][tt].x, u[o][tt].y, u[o][tt].z, u[o][tt].w};
+        uint32_t mx = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mx = max(mx, max(wv[e] & 0x7fffu, (wv[e] >> 16) & 0x7fffu));
+        mx = max(mx, dpp_u32<kQuadXor1>(mx));
+        mx = max(mx, dpp_u32<kQuadXor2>(mx));
+        const int eb = (int)(mx >> 7);
+        if (eb == 0xff) nonfinite |= 1 << (kF4gTokens * o + tt);
+        const int code = mx == 0 ? kE8M0One : (eb > 7 ? eb - 7 : 0);
+        const int lcode = lo_code(code);
+        if (sub == 0) wcodes[(q * kF4gTokens + tt) * 4 + word] = (uint8_t)code;
+        float corr = 0.f;
+        uint32_t H[4], L[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const float x0 = bf16_bits_to_f32(wv[d] & 0xffffu);
+          const float x1 = bf16_bits_to_f32(wv[d] >> 16);
+          corr = fmaf(d < 2 ? c_lo : c_hi, x0, corr);
+          corr = fmaf(d < 2 ? c_lo : c_hi, x1, corr);
+          const bool neg = d >= 2 && odd;
+          const float v0 = __builtin_ldexpf(neg ? -x0 : x0, kE8M0One - code);
+          const float v1 = __builtin_ldexpf(neg ? -x1 : x1, kE8M0One - code);
+          const int h8 = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
+          const auto back = __builtin_amdgcn_cvt_pk_f32_fp8(h8, false);
+          const float l0 = __builtin_ldexpf(v0 - back[0], code - lcode);
+          const float l1 = __builtin_ldexpf(v1 - back[1], code - lcode);
+          H[d] = (uint32_t)h8;
+          L[d] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(l0, l1, 0, false);
+        }
+        uint8_t* hi = wops + (q * kF4gTokens + tt) * kOpBytes + word * 32 + 16 * (sub & 1) +
+                      8 * (int)h;
+        *reinterpret_cast<uint2*>(hi) = pair_terms(H, h);
+        *reinterpret_cast<uint2*>(hi + kOpBytes / 2) = pair_terms(L, h);
+        // the group's correction: sum over its 16 lanes
+        corr = corr + __uint_as_float(dpp_u32<kQuadXor1>(__float_as_uint(corr)));
+        corr = corr + __uint_as_float(dpp_u32<kQuadXor2>(__float_as_uint(corr)));
+        corr = corr + __uint_as_float(dpp_u32<kRowHalfMirror>(__float_as_uint(corr)));
+        corr = corr + __uint_as_float(dpp_u32<kRowMirror>(__float_as_uint(corr)));
+        if (r == 0) wcs[q * kF4gTokens + tt] = corr;
+      }
+      if (o == 0) {
+#pragma unroll
+        for (int j = 1; j < kF4Ahead; ++j)
+          if (j < NT) load(j, Lb[j]);
+      }
+      wave_lds_sync();
+      // A operands of the octet: lane 16c + rho, row rho = 2 tt + part
+      {
+        const int tt = r >> 1, part = r & 1;
+        const int w1 = q >> 1;
+        const int Tl = T - kF4gTokens * o;  // live tokens of the octet (may exceed 8)
+        const uint32_t keep = tt < Tl ? ~0u : 0u;
+        const bool c0 = 2 * q < Tl, c1 = 2 * q + 1 < Tl;
+#pragma unroll
+        for (int j = 0; j < kF4GroupsPerWave; ++j) {
+          const uint8_t* base =
+              wops + (j * kF4gTokens + tt) * kOpBytes + part * (kOpBytes / 2) + 16 * (q & 1);
+          const uint4 lo4 = *reinterpret_cast<const uint4*>(base + 32 * w1);
+          const uint4 hi4 = *reinterpret_cast<const uint4*>(base + 32 * (w1 + 2));
+          A[j][o] = v8i_t{(int)(lo4.x & keep), (int)(lo4.y & keep), (int)(lo4.z & keep),
+                          (int)(lo4.w & keep), (int)(hi4.x & keep), (int)(hi4.y & keep),
+                          (int)(hi4.z & keep), (int)(hi4.w & keep)};
+          const int code = keep ? wcodes[(j * kF4gTokens + tt) * 4 + q] : kE8M0One;
+          ascale[j][o] = part == 0 ? code : lo_code(code);
+          C[o][j][0] = c0 ? wcs[j * kF4gTokens + 2 * q] : 0.f;
+          C[o][j][1] = c1 ? wcs[j * kF4gTokens + 2 * q + 1] : 0.f;
+        }
+      }
+      // the reads are in registers before the next octet overwrites the staging
+      wave_lds_sync();
+    }
+
+    // Per kernel: the chunk's words transposed into the four groups' B
+    // operands, the scales spread, one product per (group, octet); lane
+    // 16j + r adds alpha (hi + lo - C) for tokens 2j, 2j + 1 of each octet.
+    auto mul = [&](F4Loads<K, AT>& L, float (&acc)[NO][2]) {
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        uint32_t w[4] = {L.s[k].x, L.s[k].y, L.s[k].z, L.s[k].w};
+        transpose4(w);  // w[g] = word q of (row r, group g)
+        uint32_t ab[4];
+        spread4(scale_bits_f4<AT>(L.a[k]), ab);  // ab[g] = alpha of (row r, group g)
+#pragma unroll
+        for (int g = 0; g < kF4GroupsPerWave; ++g) {
+          v8i_t B;
+          B[0] = (int)((w[g] & m0) | b0);
+          B[1] = (int)((w[g] & m1) | b1);
+          B[2] = (int)(w[g] & m2);
+          B[3] = (int)((w[g] & m3) | b3);
+          B[4] = B[5] = B[6] = B[7] = 0;
+          const float al = scale_value_f4<AT>(ab[g]);
+#pragma unroll
+          for (int o = 0; o < NO; ++o) {
+            const v4f_t d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                A[g][o], B, v4f_t{0.f, 0.f, 0.f, 0.f}, 0, 4, 0, ascale[g][o], 0, kE8M0One);
+            acc[o][0] = fmaf(al, (d[0] + d[1]) - C[o][g][0], acc[o][0]);
+            acc[o][1] = fmaf(al, (d[2] + d[3]) - C[o][g][1], acc[o][1]);
+          }
+        }
+      }
+    };
+    auto step = [&](int t, F4Loads<K, AT>& L) {
+      float acc[NO][2];
+#pragma unroll
+      for (int o = 0; o < NO; ++o) acc[o][0] = acc[o][1] = 0.f;
+      mul(L, acc);
+#pragma unroll
+      for (int o = 0; o < NO; ++o)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int tok = kF4gTokens * o + 2 * q + e;
+          float* dst = red + ((t * NW + wave) * TO + tok) * 16 + r;
+          *dst = g0 == 0 ? acc[o][e] : *dst + acc[o][e];  // slabs in order
+        }
+    };
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (t >= ntl) break;
+      if (t + kF4Ahead < NT) load(t + kF4Ahead, Lb[(t + kF4Ahead) % (kF4Ahead + 1)]);
+      step(t, Lb[t % (kF4Ahead + 1)]);
+    }
+  }
+
+  __syncthreads();
+  if (nonfinite) atomicOr(&bad_tokens, nonfinite);
+  __syncthreads();
+  const int bad = bad_tokens;
+  for (int idx = threadIdx.x; idx < ntl * 16 * T; idx += NW * kWave) {
+    const int tok = idx / (ntl * 16), e = idx - tok * (ntl * 16);
+    const int t = e >> 4, rr = e & 15;
+    float uu = red[((t * NW) * TO + tok) * 16 + rr];
+    for (int w = 1; w < NW; ++w) uu += red[((t * NW + w) * TO + tok) * 16 + rr];
+    const int i = tile16_of(b + t * grid, tiles) * 16 + rr;
+    if (i < m) Y[(int64_t)tok * ldy + i] = ((bad >> tok) & 1) ? __builtin_nanf("") : uu;
+  }
+}
+
 template <typename AT, int K>
 int launch_f4_k(const Geom& geo, const void* packed, const void* x, float* y,
                 hipStream_t stream) {
@@ -838,6 +1110,50 @@ int launch_f4_tokens_t(const Geom& geo, const void* packed, const void* X, int l
   return MBOK_ERR_UNSUPPORTED;
 }
 
+// Several tokens, one product per group: the shape rules of launch_f4_k
+template <typename AT, int K, int NO>
+int launch_f4g_k(const Geom& geo, const void* packed, const void* X, int T, int ldx, float* Y,
+                 int ldy, hipStream_t stream) {
+  const int max_slab = kF4GroupsPerWave * f4g_waves(NO);
+  const int nslabs = (geo.G + max_slab - 1) / max_slab;
+  const int slab = (geo.G + nslabs - 1) / nslabs;
+  const int NW = (slab + kF4GroupsPerWave - 1) / kF4GroupsPerWave;
+  const int tiles = geo.RB * (kRowBlock / 16);
+  int grid = tiles < 256 ? tiles : 256;
+  if (grid * kF4J < tiles) grid = (tiles + kF4J - 1) / kF4J;
+  const int slots = (tiles + grid - 1) / grid;
+  auto go = [&](auto slot_count) {
+    constexpr int S = decltype(slot_count)::value;
+    hipLaunchKernelGGL((gemm_f4g_kernel<AT, K, S, NO>), dim3(grid), dim3(NW * kWave), 0, stream,
+                       reinterpret_cast<const uint4*>(packed),
+                       reinterpret_cast<const uint16_t*>(X), geo.G, tiles, slab, grid, NW,
+                       tiles / grid, tiles % grid, Y, geo.m, T, ldx, ldy);
+  };
+  switch (slots) {
+    case 1: go(std::integral_constant<int, 1>{}); break;
+    case 2: go(std::integral_constant<int, 2>{}); break;
+    case 3: go(std::integral_constant<int, 3>{}); break;
+    case 4: go(std::integral_constant<int, 4>{}); break;
+    case 5: go(std::integral_constant<int, 5>{}); break;
+    case 6: go(std::integral_constant<int, 6>{}); break;
+    case 7: go(std::integral_constant<int, 7>{}); break;
+    default: go(std::integral_constant<int, 8>{}); break;
+  }
+  return hipGetLastError() == hipSuccess ? MBOK_OK : MBOK_ERR_HIP;
+}
+
+template <typename AT, int NO>
+int launch_f4g_t(const Geom& geo, const void* packed, const void* X, int T, int ldx, float* Y,
+                 int ldy, hipStream_t stream) {
+  switch (geo.K) {
+    case 1: return launch_f4g_k<AT, 1, NO>(geo, packed, X, T, ldx, Y, ldy, stream);
+    case 2: return launch_f4g_k<AT, 2, NO>(geo, packed, X, T, ldx, Y, ldy, stream);
+    case 3: return launch_f4g_k<AT, 3, NO>(geo, packed, X, T, ldx, Y, ldy, stream);
+    case 4: return launch_f4g_k<AT, 4, NO>(geo, packed, X, T, ldx, Y, ldy, stream);
+  }
+  return MBOK_ERR_UNSUPPORTED;
+}
+
 template <typename AT>
 int launch_f4_tokens(const Geom& geo, const void* packed, const void* X, int T, int ldx,
                      float* Y, int ldy, hipStream_t stream) {
@@ -859,6 +1175,21 @@ int launch_gemv_f4(const mbok_desc* d, const void* packed, const void* x, float*
 }
 
 int gemm_f4_max_tokens() { return kF4MaxTokens; }
+int gemm_f4g_max_tokens() { return kF4gMaxTokens; }
+
+int launch_gemm_f4g(const mbok_desc* d, const void* packed, const void* X, int64_t T,
+                    int64_t ldx, float* Y, int64_t ldy, hipStream_t stream) {
+  if (T < 1 || T > kF4gMaxTokens) return MBOK_ERR_SHAPE;
+  if ((T - 1) * ldx + d->n > INT32_MAX || (T - 1) * ldy + d->m > INT32_MAX)
+    return MBOK_ERR_UNSUPPORTED;
+  const Geom geo = make_geom(d);
+  const bool two = T > kF4gTokens;
+  if (d->alpha_dtype == MBOK_F16)
+    return two ? launch_f4g_t<uint16_t, 2>(geo, packed, X, (int)T, (int)ldx, Y, (int)ldy, stream)
+               : launch_f4g_t<uint16_t, 1>(geo, packed, X, (int)T, (int)ldx, Y, (int)ldy, stream);
+  return two ? launch_f4g_t<float, 2>(geo, packed, X, (int)T, (int)ldx, Y, (int)ldy, stream)
+             : launch_f4g_t<float, 1>(geo, packed, X, (int)T, (int)ldx, Y, (int)ldy, stream);
+}
 
 int launch_gemm_f4(const mbok_desc* d, const void* packed, const void* X, int64_t T,
                    int64_t ldx, float* Y, int64_t ldy, hipStream_t stream) {

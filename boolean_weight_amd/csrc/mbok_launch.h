@@ -27,7 +27,10 @@ int launch_gemv_f4(const mbok_desc* d, const void* packed, const void* x, float*
 int launch_gemm_f4(const mbok_desc* d, const void* packed, const void* X, int64_t T,
                    int64_t ldx, float* Y, int64_t ldy, hipStream_t stream);
 int gemm_f4_max_tokens();
-bool use_f4_for_tokens(const mbok_desc* d, int64_t T);
+// 1..gemm_f4g_max_tokens() tokens with one product per group (8 tokens each)
+int launch_gemm_f4g(const mbok_desc* d, const void* packed, const void* X, int64_t T,
+                    int64_t ldx, float* Y, int64_t ldy, hipStream_t stream);
+int gemm_f4g_max_tokens();
 int launch_gemvt(const mbok_desc* d, const void* packed, const void* grad, int32_t g_dtype,
                  float* dx, void* ws, hipStream_t stream);
 size_t gemvt_workspace_bytes(const mbok_desc* d);

@@ -445,15 +445,16 @@ int mbok_gemvt_noalloc(const mbok_desc* d, const void* packed, const void* g,
  * The same product for T tokens ([RN] 关键设计: the layer's product is the sum
  * of its K Boolean products, scaled per group; [RN] 局限与展望: activations
  * stay full precision):  Y[t, i] = sum_j W_hat[i, j] * X[t, j].
- * T = 1 runs the decode kernel of mbok_gemv (without a workspace).  T = 2
- * runs the matrix-core form of that kernel for two tokens (signs as fp4
- * operands, each bf16 activation as two exact fp8 parts with one power-of-two
- * scale per 32 columns, alpha applied per group in fp32: within ~1e-6 of the
- * bound sum_j |W_hat_ij| |X_tj| on Gaussian activations; bit-exact for small
- * integer activations and power-of-two scales).  T = 3..16 runs the
+ * T = 1 runs the decode kernel of mbok_gemv (without a workspace).  T = 2,
+ * and T = 3..6 on layers of at least 2^26 sign bits (K m n), run matrix-core
+ * forms of that kernel for several tokens (signs as fp4 operands, each bf16
+ * activation as two exact fp8 parts with one power-of-two scale per 32
+ * columns, alpha applied per group in fp32: within ~1e-6 of the bound
+ * sum_j |W_hat_ij| |X_tj| on Gaussian activations; bit-exact for small
+ * integer activations and power-of-two scales).  The other T <= 16 run the
  * weight-streaming few-token kernel (exact fp32 scaling of +-1 products).  A
- * non-finite activation of token t makes row t of Y NaN on the T = 2 path
- * (IEEE propagation elsewhere).  T > 16 is the prefill GEMM: each tile of W_hat is formed
+ * non-finite activation of token t makes row t of Y NaN on the matrix-core
+ * paths (IEEE propagation elsewhere).  T > 16 is the prefill GEMM: each tile of W_hat is formed
  * as sum_k alpha_k * b_k in fp32, rounded to bf16 (nearest-even) in LDS, and
  * contracted with the bf16 X tile on the matrix cores with fp32 accumulation.
  *  X        device bf16 [T, ldx], ldx >= n, ldx % 8 == 0.
@@ -471,10 +472,9 @@ int mbok_gemm(const mbok_desc* d, const void* packed, const void* X,
  * 关键设计: W_hat x is the sum of the K scaled Boolean products, each weight
  * exactly sum_k alpha_k b_k; carrying that value to the matrix cores needs
  * more than bf16's 8 significant bits).  Same arguments, checks, errors and
- * output layout as mbok_gemm; T = 1 and T = 3..16 run exactly the same
- * kernels as mbok_gemm, and T = 2 the weight-streaming few-token kernel
- * that mbok_gemm uses for T = 3..16 (their products are fp32-exact per
- * scale).  For T > 16
+ * output layout as mbok_gemm; T = 1 runs the same kernel as mbok_gemm, and
+ * T = 2..16 always the weight-streaming few-token kernel (its products are
+ * fp32-exact per scale).  For T > 16
  * each level v = sum_k +-alpha_k is formed in fp32 and split as
  * v = hi + lo with hi = bf16(v) and lo = bf16(v - hi), so |v - hi - lo| <=
  * 2^-16 |v|.  Two products run on `stream`: Y = X . HI^T, then Y += X . LO^T

@@ -1,7 +1,7 @@
-"""The fp4 x fp8 matrix-core product for 2..4 tokens (mbok_gemm, T = 2 by
-default, T = 2..4 with MBOK_SKINNY_VARIANT=f4):
-two tokens per matrix-core instruction in the operand rows the one-token
-kernel leaves empty.
+"""The fp4 x fp8 matrix-core products for several tokens (mbok_gemm): two
+tokens per instruction in the operand rows the one-token kernel leaves empty
+(MBOK_SKINNY_VARIANT=f4, 2..4 tokens), and one product per group with 8
+tokens in its rows (=f4g, 2..16 tokens).
 
 Bars: exact regime (integer X in [-8, 8], scales 2^-e) equal values for every
 shape, kernel count, scale type and leading dimension; bf16 activations
@@ -28,6 +28,12 @@ pytestmark = pytest.mark.gpu
 TOL = 1e-3
 
 
+# the two matrix-core few-token kernels: "f4" puts two tokens in the rows of
+# the one-token products (2..4 tokens), "f4g" gives each product one group
+# and 8 tokens (2..16 tokens)
+VARIANTS = {"f4": [2, 3, 4], "f4g": [2, 3, 5, 8, 9, 16]}
+
+
 @pytest.fixture(scope="module", autouse=True)
 def _gpu():
     if not torch.cuda.is_available():
@@ -35,7 +41,6 @@ def _gpu():
     bw.load_library()
     keys = ("MBOK_SKINNY_VARIANT", "MBOK_GEMV_VARIANT")
     old = {k: os.environ.get(k) for k in keys}
-    os.environ["MBOK_SKINNY_VARIANT"] = "f4"
     os.environ.pop("MBOK_GEMV_VARIANT", None)
     yield
     for k, v in old.items():
@@ -44,6 +49,14 @@ def _gpu():
         else:
             os.environ[k] = v
     torch.cuda.synchronize()
+
+
+def _set_variant(v):
+    os.environ["MBOK_SKINNY_VARIANT"] = v
+
+
+def _cases():
+    return [(v, T) for v, ts in VARIANTS.items() for T in ts]
 
 
 # (m, n): one row, ragged row blocks, 1..3 column slabs (at most 32 groups
@@ -55,10 +68,11 @@ SHAPES = [(1, 128), (65, 384), (300, 512), (130, 5120), (70, 11008), (9000, 256)
 
 @pytest.mark.parametrize("m,n", SHAPES)
 @pytest.mark.parametrize("K", [1, 2, 3, 4])
-@pytest.mark.parametrize("T", [2, 3, 4])
-def test_f4_tokens_exact(T, K, m, n):
+@pytest.mark.parametrize("variant,T", _cases())
+def test_f4_tokens_exact(variant, T, K, m, n):
+    _set_variant(variant)
     dt = "f16" if (m + n + K + T) % 2 else "f32"
-    say(f"f4 tokens exact T={T} K={K} m={m} n={n} {dt}")
+    say(f"{variant} tokens exact T={T} K={K} m={m} n={n} {dt}")
     S = syn.random_signs(K, m, n, seed=T * 13 + K + m)
     A = syn.exact_alpha(K, m, n // 128, seed=T + 7 * K).astype(np_alpha(dt))
     X = syn.exact_activations(T, n, seed=T * 3 + K + n)
@@ -67,10 +81,12 @@ def test_f4_tokens_exact(T, K, m, n):
     assert np.array_equal(Y, oracle.product(S, A, X))
 
 
+@pytest.mark.parametrize("variant,T", [("f4", 4), ("f4g", 16)])
 @pytest.mark.parametrize("dt", ["f16", "f32"])
-def test_f4_tokens_exact_4096(dt):
-    K, m, n, T = 2, 4096, 4096, 4
-    say(f"f4 tokens exact 4096x4096 {dt}")
+def test_f4_tokens_exact_4096(dt, variant, T):
+    _set_variant(variant)
+    K, m, n = 2, 4096, 4096
+    say(f"{variant} tokens exact 4096x4096 T={T} {dt}")
     S = syn.random_signs(K, m, n, seed=90)
     A = syn.exact_alpha(K, m, n // 128, seed=91).astype(np_alpha(dt))
     X = syn.exact_activations(T, n, seed=92)
@@ -87,13 +103,14 @@ def _spread_x(T, n, seed, binades):
 
 
 @pytest.mark.parametrize("binades", [0, 6, 12])
-@pytest.mark.parametrize("T", [2, 4])
-def test_f4_tokens_exact_split_of_bf16(T, binades):
+@pytest.mark.parametrize("variant,T", [("f4", 2), ("f4", 4), ("f4g", 8), ("f4g", 16)])
+def test_f4_tokens_exact_split_of_bf16(variant, T, binades):
     """As for one token: within 6 binades the fp8 parts hold every bf16 value
     and the sums are exact; over 12 binades the matrix cores drop bits far
     below a block's largest product."""
+    _set_variant(variant)
     K, m, n = 1, 300, 1024
-    say(f"f4 tokens split T={T} binades={binades}")
+    say(f"{variant} tokens split T={T} binades={binades}")
     S = syn.random_signs(K, m, n, seed=100 + binades)
     A = syn.exact_alpha(K, m, n // 128, seed=101).astype(np.float16)
     X = _spread_x(T, n, 102 + binades, binades)
@@ -109,19 +126,21 @@ def test_f4_tokens_exact_split_of_bf16(T, binades):
 
 
 @pytest.mark.parametrize("bad", [np.nan, np.inf, -np.inf])
-def test_f4_tokens_nonfinite_is_per_token(bad):
-    K, m, n, T = 2, 200, 512, 3
-    say(f"f4 tokens non-finite {bad}")
+@pytest.mark.parametrize("variant,T,tok", [("f4", 3, 1), ("f4g", 3, 1), ("f4g", 12, 10)])
+def test_f4_tokens_nonfinite_is_per_token(bad, variant, T, tok):
+    _set_variant(variant)
+    K, m, n = 2, 200, 512
+    say(f"{variant} tokens non-finite {bad} T={T}")
     S = syn.random_signs(K, m, n, seed=110)
     A = syn.exact_alpha(K, m, n // 128, seed=111).astype(np.float16)
     X = syn.exact_activations(T, n, seed=112)
-    X[1, 300] = bad
+    X[tok, 300] = bad
     d, packed = pack_on_gpu(S, A, "f16")
     Y = gemm(d, packed, X)
-    assert np.all(np.isnan(Y[1]))
-    want = oracle.product(S, A, X[[0, 2]])
-    assert np.array_equal(Y[[0, 2]], want)
-    X[1, 300] = 1.0
+    assert np.all(np.isnan(Y[tok]))
+    others = [t for t in range(T) if t != tok]
+    assert np.array_equal(Y[others], oracle.product(S, A, X[others]))
+    X[tok, 300] = 1.0
     assert np.array_equal(gemm(d, packed, X), oracle.product(S, A, X))
 
 
@@ -146,20 +165,41 @@ def test_f4_tokens_equal_the_decode_per_token(cfg, li):
             os.environ.pop("MBOK_GEMV_VARIANT", None)
         else:
             os.environ["MBOK_GEMV_VARIANT"] = old
+    _set_variant("f4")
     for T in (2, 3, 4):
         Y = gemm(d, packed, X[:T])
         for t in range(T):
             assert np.array_equal(Y[t], ys[t]), (T, t)
 
 
+@pytest.mark.parametrize("cfg,li", [(2, 0), (3, 0)])
+def test_f4g_tokens_do_not_depend_on_the_token_count(cfg, li):
+    """Each token's row is computed from its own A rows only: for layers of
+    at most 32 groups (one slab of 8 wavefronts with one or two octets) the
+    first T rows of a 16-token call equal a T-token call bit for bit."""
+    _set_variant("f4g")
+    w = syn.WORKLOADS[cfg]
+    name, m, n = w["linears"][li]
+    say(f"f4g token count config {cfg} {name}")
+    W = syn.weight(m, n, syn.weight_seed(cfg, li))
+    X = syn.activations(16, n, syn.act_seed(cfg, li) + 1, "bf16")
+    d, packed, signs, alpha = bw.quantize_and_pack(to_dev(W), w["K"], bw.MBOK_F16)
+    del signs, alpha
+    Y16 = gemm(d, packed, X)
+    for T in (2, 5, 8, 9, 13):
+        assert np.array_equal(gemm(d, packed, X[:T]), Y16[:T]), T
+
+
+@pytest.mark.parametrize("variant", ["f4", "f4g"])
 @pytest.mark.parametrize("cfg", [2, 3, 4])
-def test_f4_tokens_workloads_tolerance(cfg):
+def test_f4_tokens_workloads_tolerance(cfg, variant):
+    _set_variant(variant)
     w = syn.WORKLOADS[cfg]
     for li, (name, m, n) in enumerate(w["linears"]):
         if cfg == 4 and name in ("k_proj", "v_proj", "up_proj"):
             continue  # same shapes as q_proj / gate_proj
-        T = 4 if cfg != 2 else 3
-        say(f"f4 tokens config {cfg} {name} {m}x{n} T={T}")
+        T = (4 if cfg != 2 else 3) if variant == "f4" else (16 if cfg == 3 else 8)
+        say(f"{variant} tokens config {cfg} {name} {m}x{n} T={T}")
         W = syn.weight(m, n, syn.weight_seed(cfg, li))
         X = syn.activations(T, n, syn.act_seed(cfg, li), "bf16")
         d, packed, signs, alpha = bw.quantize_and_pack(to_dev(W), w["K"], bw.MBOK_F16)
@@ -177,33 +217,38 @@ def test_f4_tokens_workloads_tolerance(cfg):
         torch.cuda.empty_cache()
 
 
-def test_f4_tokens_default_dispatch_and_precise_path():
-    """Without MBOK_SKINNY_VARIANT, mbok_gemm takes the matrix-core kernel for
-    2 tokens (same bits as with =f4); mbok_gemm_precise keeps the
-    bf16 +-1 few-token kernel there (its exact fp32 scaling): for 512 rows
-    that is the per-tile form, =blocks."""
-    K, m, n, T = 3, 512, 2048, 2
-    say("f4 tokens dispatch")
-    W = syn.weight(m, n, 120)
-    X = syn.activations(T, n, 121, "bf16")
+@pytest.mark.parametrize("T,m,n,want", [(2, 512, 2048, "f4"), (4, 512, 2048, "blocks"),
+                                         (4, 8192, 4096, "f4g"), (6, 8192, 4096, "f4g"),
+                                         (7, 8192, 4096, "stream")])
+def test_f4_tokens_default_dispatch_and_precise_path(T, m, n, want):
+    """Without MBOK_SKINNY_VARIANT, mbok_gemm takes the two-token
+    matrix-core kernel for 2 tokens, the one-product-per-group kernel for
+    3..6 tokens on layers of at least 2^26 sign bits, and the bf16 +-1
+    kernels otherwise (per-tile below 8192 rows, streaming from there);
+    mbok_gemm_precise always keeps the bf16 +-1 kernels (their exact fp32
+    scaling) for 2..16 tokens."""
+    K = 2
+    say(f"few-token dispatch T={T} m={m} n={n}")
+    W = syn.weight(m, n, 120 + T)
+    X = syn.activations(T, n, 121 + T, "bf16")
     d, packed, signs, alpha = bw.quantize_and_pack(to_dev(W), K, bw.MBOK_F16)
     del signs, alpha
     Xd = x_to_dev(X, "bf16").view(T, n)
+    skinny = "stream" if (m >= 8192 and n // 128 <= 32) else "blocks"
 
-    def run(fn):
+    def run(fn, variant):
+        if variant is None:
+            os.environ.pop("MBOK_SKINNY_VARIANT", None)
+        else:
+            _set_variant(variant)
         Y = torch.empty((T, m), dtype=torch.float32, device=DEV)
         fn(d, packed, Xd, Y)
         return Y.cpu().numpy()
 
-    f4 = run(bw.mbok_gemm)
-    os.environ.pop("MBOK_SKINNY_VARIANT", None)
-    try:
-        default = run(bw.mbok_gemm)
-        precise = run(bw.mbok_gemm_precise)
-        os.environ["MBOK_SKINNY_VARIANT"] = "blocks"
-        blocks = run(bw.mbok_gemm)
-    finally:
-        os.environ["MBOK_SKINNY_VARIANT"] = "f4"
-    assert np.array_equal(default, f4)
-    assert np.array_equal(precise, blocks)
-    assert not np.array_equal(f4, blocks)  # two different kernels ran
+    default = run(bw.mbok_gemm, None)
+    precise = run(bw.mbok_gemm_precise, None)
+    forced = run(bw.mbok_gemm, want)
+    assert np.array_equal(default, forced)
+    assert np.array_equal(precise, run(bw.mbok_gemm, skinny))
+    if want in ("f4", "f4g"):
+        assert not np.array_equal(default, precise)  # two different kernels ran
