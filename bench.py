@@ -49,7 +49,11 @@ def parse(argv=None):
                          "figures added to the line)")
     ap.add_argument("--K", type=int, default=None, help="override the workload's K")
     ap.add_argument("--T", type=int, default=None, help="tokens (workloads 3 and 5)")
-    ap.add_argument("--no-graph", action="store_true", help="plain stream launches")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="plain stream launches for the timed steps (the default when the "
+                         "timed region holds at most 64 launches)")
+    ap.add_argument("--graph", action="store_true",
+                    help="a HIP graph of the timed steps whatever their count")
     ap.add_argument("--precise", action="store_true",
                     help="multi-token products through mbok_gemm_precise (two-term levels)")
     ap.add_argument("--rotate-bytes", type=float, default=float(2 ** 30))
@@ -448,12 +452,33 @@ def _evict(wl, copies):
                 raise RuntimeError("eviction read failed")
 
 
+# A HIP graph replay costs ~10 us before its first kernel starts; over a
+# short timed region (the 20 single-launch decode steps of a quick run: 4.07
+# against 3.77 us per step measured) that is a tenth of the region.  Up to
+# this many launches the timed decode and few-token steps are plain stream
+# launches, all enqueued while a spin kernel holds the stream, so they too run
+# back to back.  Prefill steps stay in a graph: as plain launches each 90 MB
+# fp32 output costs more at the kernel boundary (210 against 196 us per step).
+GRAPH_MIN_LAUNCHES = 64
+SPIN_US_PER_LAUNCH = 30  # host enqueue time per launch that the spin covers
+
+
+def timed_with_graph(args, launches, T):
+    if args.graph:
+        return True
+    if args.no_graph:
+        return False
+    return T > 16 or launches > GRAPH_MIN_LAUNCHES
+
+
 def measure_steps(wl, steps, warmup, use_graph=True):
     """Exactly `steps` steps in the timed region.  The timed steps use pool
     copies 0 .. glen-1 (glen = min(steps, pool copies)).  The other copies
     are read once after the graph upload, then the warm-up steps run on them,
     so each timed copy was last read at least (pool - glen) copies of other
     data earlier (every copy of the pool, cycled, when steps >= pool).
+    Without a graph the steps are enqueued behind a spin kernel long enough
+    to cover their host-side launch time.
     Returns ms per step, the wall time and the pool bookkeeping."""
     import torch
     glen = min(wl.ncopy, max(1, steps))
@@ -476,7 +501,7 @@ def measure_steps(wl, steps, warmup, use_graph=True):
     stream = torch.cuda.current_stream()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    _marker(spin_us=300)
+    _marker(spin_us=300 if use_graph else 300 + SPIN_US_PER_LAUNCH * steps * len(wl.layers))
     wall0 = time.perf_counter()
     t0.record(stream)
     if use_graph:
@@ -490,7 +515,7 @@ def measure_steps(wl, steps, warmup, use_graph=True):
     t1.record(stream)
     _marker()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0  # includes the spin kernel's 0.3 ms
+    wall = time.perf_counter() - wall0  # includes the spin kernel
     return {"ms_per_step": t0.elapsed_time(t1) / steps, "wall_s": wall, "graph": use_graph,
             "pool_copies": wl.ncopy, "timed_copies": glen,
             "timed_pool_MB": round(glen * wl.wbytes / 2 ** 20, 1),
@@ -623,7 +648,8 @@ def cpu_baseline(config, K, T, rows, unit, runs=5):
 
 def product_figures(args, wl, steps, warmup, ceil=None):
     """Timed steps and the dominant call's roofline for one workload."""
-    timed = measure_steps(wl, steps, warmup, use_graph=not args.no_graph)
+    timed = measure_steps(wl, steps, warmup,
+                          use_graph=timed_with_graph(args, steps * len(wl.layers), wl.T))
     launch_us = measure_dominant(wl, calibrate=args.calibrate_copy)
     d = wl.layers[wl.dom][1]
     alg = wl.dom_alg_bytes()
@@ -766,7 +792,8 @@ def main():
                    "linears": [[nm, dd.m, dd.n] for nm, dd in wl.layers],
                    "K": K if allocation is None else allocation, "group": 128, "T": T,
                    "alpha_dtype": cfg["alpha_dtype"], "x_dtype": cfg["x_dtype"],
-                   "launch": "hip graph" if timed["graph"] else "stream",
+                   "launch": ("hip graph" if timed["graph"] else
+                              "stream launches enqueued behind a spin kernel"),
                    "pool": _pool(timed), "wall_s": round(timed["wall_s"], 3)},
         "tokens_per_s": (T if args.config != 4 else 1) / (ms * 1e-3),
         "pct_hbm_peak_of_value": round(100 * value / HBM_PEAK_GBPS, 2) if unit == "GB/s" else None,
@@ -804,7 +831,7 @@ def main():
         pw.precise = True
         qsteps = max(1, args.steps // 4)
         qtimed = measure_steps(pw, qsteps, max(1, args.warmup // 4),
-                               use_graph=not args.no_graph)
+                               use_graph=timed_with_graph(args, qsteps * len(pw.layers), pw.T))
         qms = qtimed["ms_per_step"]
         line["prefill"]["precise"] = {
             "entry": "mbok_gemm_precise", "steps": qsteps, "ms_per_step": qms,
