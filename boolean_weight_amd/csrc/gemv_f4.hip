@@ -98,6 +98,45 @@ constexpr int kOpBytes = 256;   // fp8 A bytes per group: 2 parts x 4 lane block
 // part), clamped at the smallest code.
 __device__ __forceinline__ int lo_code(int code) { return code > 4 ? code - 4 : 0; }
 
+// One thread's 8 activations of a 32-column word (wv[d] holds columns 2d,
+// 2d + 1 as bf16) as fp8 high and low parts: H[d], L[d] bytes 0 and 1 for
+// columns 2d, 2d + 1; class-3 columns (d >= 2 of an odd thread) negated; and
+// corr += c(class) x over the 8 columns (c_lo for d < 2, c_hi for d >= 2).
+// The scaled conversions divide by 2^(code - 127) (the high part) and
+// 2^(lo_code - 127) (the low part) and round once, nearest-even: the same
+// bytes as scaling with ldexp and converting (checked bit for bit over every
+// finite bf16 value and every code the word scale takes), and the high
+// part converts straight from the bf16 pair.
+__device__ __forceinline__ void convert_word8(const uint32_t (&wv)[4], int code, bool odd,
+                                              float c_lo, float c_hi, uint32_t (&H)[4],
+                                              uint32_t (&L)[4], float& corr) {
+  typedef short v2i16 __attribute__((ext_vector_type(2)));
+  typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
+  const float s_hi = __builtin_ldexpf(1.f, code - kE8M0One);
+  const float s_lo = __builtin_ldexpf(1.f, lo_code(code) - kE8M0One);
+  const uint32_t neg3 = odd ? 0x80008000u : 0u;  // sign flips of a class-3 pair
+  const v2i16 zero = {0, 0};
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    // class 3 (d >= 2 of an odd thread) negated; its c is 0, so the
+    // correction may take the negated values too
+    const uint32_t pair = d >= 2 ? wv[d] ^ neg3 : wv[d];
+    const float x0 = bf16_bits_to_f32(pair & 0xffffu);
+    const float x1 = bf16_bits_to_f32(pair >> 16);
+    corr = fmaf(d < 2 ? c_lo : c_hi, x0, corr);
+    corr = fmaf(d < 2 ? c_lo : c_hi, x1, corr);
+    const v2i16 h = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(
+        zero, __builtin_bit_cast(v2bf16, pair), s_hi, false);
+    const int hb = __builtin_bit_cast(int, h);
+    const auto back = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hb, s_hi, false);
+    // exact: the bits the high part left (the bytes above 1 are never read)
+    const v2i16 l =
+        __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(zero, x0 - back[0], x1 - back[1], s_lo, false);
+    H[d] = (uint32_t)hb;
+    L[d] = (uint32_t)__builtin_bit_cast(int, l);
+  }
+}
+
 // Constants kept in registers (an SGPR and a VGPR), so that one v_and_or_b32
 // takes both: a VOP3 instruction has no literal operand on this target.
 __device__ __forceinline__ uint32_t sgpr_const(uint32_t v) {
@@ -297,29 +336,13 @@ __global__ void __launch_bounds__(f4_max_waves(K) * kWave) gemv_f4_kernel(
       const int eb = (int)(mx >> 7);  // biased exponent of the word's largest |x|
       if (eb == 0xff) nonfinite = 1;
       const int code = mx == 0 ? kE8M0One : (eb > 7 ? eb - 7 : 0);
-      const int lcode = lo_code(code);
       const int gl = xt >> 4, word = (xt >> 2) & 3, sub = xt & 3;
       if (sub == 0) codes[gl * 4 + word] = (uint8_t)code;
       // column 8 sub + e is in sign class ((8 sub + e) >> 2) & 3 = 2 (sub & 1) + (e >> 2)
       const bool odd = (sub & 1) != 0;
       const float c_lo = odd ? 1.f : 5.f, c_hi = odd ? 0.f : 3.f;  // e < 4, e >= 4
       uint32_t H[4], L[4];  // fp8 bytes of columns 2d, 2d + 1 in bytes 0, 1
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const float x0 = bf16_bits_to_f32(wv[d] & 0xffffu);
-        const float x1 = bf16_bits_to_f32(wv[d] >> 16);
-        corr = fmaf(d < 2 ? c_lo : c_hi, x0, corr);
-        corr = fmaf(d < 2 ? c_lo : c_hi, x1, corr);
-        const bool neg = d >= 2 && odd;  // class 3
-        const float v0 = __builtin_ldexpf(neg ? -x0 : x0, kE8M0One - code);
-        const float v1 = __builtin_ldexpf(neg ? -x1 : x1, kE8M0One - code);
-        const int h8 = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
-        const auto back = __builtin_amdgcn_cvt_pk_f32_fp8(h8, false);
-        const float l0 = __builtin_ldexpf(v0 - back[0], code - lcode);
-        const float l1 = __builtin_ldexpf(v1 - back[1], code - lcode);
-        H[d] = (uint32_t)h8;
-        L[d] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(l0, l1, 0, false);
-      }
+      convert_word8(wv, code, odd, c_lo, c_hi, H, L, corr);
       // Threads sub and sub ^ 2 fill the word's terms 16 (sub & 1) ..
       // +15: term byte 2e + h is column 8 sub + e of the thread with h =
       // sub >> 1.  The h = 0 thread writes bytes 0..7 (columns e = 0..3 of
@@ -573,25 +596,9 @@ __device__ __forceinline__ void f4_tokens_body(const uint4* __restrict__ bits,
         const int eb = (int)(mx >> 7);  // biased exponent of the word's largest |x|
         if (eb == 0xff) nonfinite |= 1 << tt;
         const int code = mx == 0 ? kE8M0One : (eb > 7 ? eb - 7 : 0);
-        const int lcode = lo_code(code);
-        if (sub == 0) codes[(gl * TT + tt) * 4 + word] = (uint8_t)code;
+          if (sub == 0) codes[(gl * TT + tt) * 4 + word] = (uint8_t)code;
         uint32_t H[4], L[4];  // fp8 bytes of columns 2d, 2d + 1 in bytes 0, 1
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const float x0 = bf16_bits_to_f32(wv[d] & 0xffffu);
-          const float x1 = bf16_bits_to_f32(wv[d] >> 16);
-          corr[tt] = fmaf(d < 2 ? c_lo : c_hi, x0, corr[tt]);
-          corr[tt] = fmaf(d < 2 ? c_lo : c_hi, x1, corr[tt]);
-          const bool neg = d >= 2 && odd;  // class 3
-          const float v0 = __builtin_ldexpf(neg ? -x0 : x0, kE8M0One - code);
-          const float v1 = __builtin_ldexpf(neg ? -x1 : x1, kE8M0One - code);
-          const int h8 = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
-          const auto back = __builtin_amdgcn_cvt_pk_f32_fp8(h8, false);
-          const float l0 = __builtin_ldexpf(v0 - back[0], code - lcode);
-          const float l1 = __builtin_ldexpf(v1 - back[1], code - lcode);
-          H[d] = (uint32_t)h8;
-          L[d] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(l0, l1, 0, false);
-        }
+        convert_word8(wv, code, odd, c_lo, c_hi, H, L, corr[tt]);
         uint8_t* hi = ops + (gl * TT + tt) * kOpBytes + word * 32 + 16 * (sub & 1) + 8 * (int)h;
         uint8_t* lo = hi + kOpBytes / 2;
         *reinterpret_cast<uint2*>(hi) = pair_terms(H, h);
@@ -894,26 +901,10 @@ __global__ void __launch_bounds__(f4g_waves(NO) * kWave) gemm_f4g_kernel(
         const int eb = (int)(mx >> 7);
         if (eb == 0xff) nonfinite |= 1 << (kF4gTokens * o + tt);
         const int code = mx == 0 ? kE8M0One : (eb > 7 ? eb - 7 : 0);
-        const int lcode = lo_code(code);
-        if (sub == 0) wcodes[(q * kF4gTokens + tt) * 4 + word] = (uint8_t)code;
+          if (sub == 0) wcodes[(q * kF4gTokens + tt) * 4 + word] = (uint8_t)code;
         float corr = 0.f;
-        uint32_t H[4], L[4];
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const float x0 = bf16_bits_to_f32(wv[d] & 0xffffu);
-          const float x1 = bf16_bits_to_f32(wv[d] >> 16);
-          corr = fmaf(d < 2 ? c_lo : c_hi, x0, corr);
-          corr = fmaf(d < 2 ? c_lo : c_hi, x1, corr);
-          const bool neg = d >= 2 && odd;
-          const float v0 = __builtin_ldexpf(neg ? -x0 : x0, kE8M0One - code);
-          const float v1 = __builtin_ldexpf(neg ? -x1 : x1, kE8M0One - code);
-          const int h8 = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
-          const auto back = __builtin_amdgcn_cvt_pk_f32_fp8(h8, false);
-          const float l0 = __builtin_ldexpf(v0 - back[0], code - lcode);
-          const float l1 = __builtin_ldexpf(v1 - back[1], code - lcode);
-          H[d] = (uint32_t)h8;
-          L[d] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(l0, l1, 0, false);
-        }
+        uint32_t H[4], L[4];  // fp8 bytes of columns 2d, 2d + 1 in bytes 0, 1
+        convert_word8(wv, code, odd, c_lo, c_hi, H, L, corr);
         uint8_t* hi = wops + (q * kF4gTokens + tt) * kOpBytes + word * 32 + 16 * (sub & 1) +
                       8 * (int)h;
         *reinterpret_cast<uint2*>(hi) = pair_terms(H, h);
