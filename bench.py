@@ -290,7 +290,12 @@ def summarize(args):
             br = bracketed([(int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"]))
                             for r in rows if r["Counter_Name"] == counter], prefix)
             if br:
-                lines.append(f"{counter}_per_call: {sum(br[1]) / CAL_CALLS:.6g}")
+                per_call = sum(br[1]) / CAL_CALLS
+                lines.append(f"{counter}_per_call: {per_call:.6g}")
+                if counter in ("SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_INSTS_MFMA"):
+                    # wavefront instructions x 64 lanes over the call's sign bits
+                    lines.append(f"{counter}_lane_ops_per_sign_bit: "
+                                 f"{per_call * 64 / (K * m * n):.4g}")
     lines.append(f"source_sha256: {source_digest(T, m, n, K)}")
     print("\n".join(lines))
 

@@ -764,7 +764,8 @@ int launch_mfma(const Geom& geo, const void* packed, const void* X, int64_t T, i
 // 128 signs whatever the token count, but every workgroup converts every
 // token's activations to fp8 parts before its first product, so they lose
 // to the bf16 +-1 kernels on small layers and beyond 6 tokens.
-// MBOK_SKINNY_VARIANT=f4|f4g|stream|blocks forces a kernel.
+// MBOK_SKINNY_VARIANT=f4|f4g|stream|blocks forces a kernel; any other value
+// (e.g. =skinny) takes the bf16 +-1 kernels with their own choice by shape.
 enum TokenKernel { kTokSkinny = 0, kTokF4 = 1, kTokF4g = 2 };
 
 TokenKernel token_kernel(const mbok_desc* d, int64_t T) {
