@@ -85,11 +85,15 @@ def test_graph_gemv():
     check_replays(g, y, eager, lambda: bw.mbok_gemv(d, packed, x2, y2, workspace=ws))
 
 
-@pytest.mark.parametrize("T", [5, 300])
-def test_graph_gemm(T):
-    """T = 5 runs the few-token kernel, T = 300 the prefill kernel."""
+@pytest.mark.parametrize("T,variant", [(2, None), (4, "f4g"), (5, None), (300, None)])
+def test_graph_gemm(T, variant, monkeypatch):
+    """T = 2 runs the two-token matrix-core kernel, T = 4 with
+    MBOK_SKINNY_VARIANT=f4g the one-product-per-group kernel, T = 5 the bf16
+    +-1 few-token kernel, T = 300 the prefill kernel."""
+    if variant:
+        monkeypatch.setenv("MBOK_SKINNY_VARIANT", variant)
     K, m, n = 3, 513, 640
-    say(f"graph gemm T={T} m={m} n={n} K={K}")
+    say(f"graph gemm T={T} {variant} m={m} n={n} K={K}")
     S, A = exact_layer(K, m, n, 311 + T)
     d, packed = pack_on_gpu(S, A, "f16")
     X = syn.exact_activations(T, n, seed=313 + T)

@@ -41,16 +41,19 @@ def _jobs(tag):
     d2, p2 = _layer(3, 1000, 2048, seed + 10)
     x = x_to_dev(syn.activations(1, 4096, seed + 20, "bf16")[0], "bf16")
     g = x_to_dev(syn.activations(1, 4096, seed + 21, "bf16")[0], "bf16")
+    X2 = x_to_dev(syn.activations(2, 2048, seed + 24, "bf16"), "bf16")
     X5 = x_to_dev(syn.activations(5, 2048, seed + 22, "bf16"), "bf16")
     X300 = x_to_dev(syn.activations(300, 2048, seed + 23, "bf16"), "bf16")
     y = torch.empty(4096, dtype=torch.float32, device=DEV)
     dx = torch.empty(4096, dtype=torch.float32, device=DEV)
+    Y2 = torch.empty((2, 1000), dtype=torch.float32, device=DEV)
     Y5 = torch.empty((5, 1000), dtype=torch.float32, device=DEV)
     Y300 = torch.empty((300, 1000), dtype=torch.float32, device=DEV)
-    keep = (d1, p1, d2, p2, x, g, X5, X300)  # keep the inputs alive
+    keep = (d1, p1, d2, p2, x, g, X2, X5, X300)  # keep the inputs alive
     return keep, [
         ("gemv", y, lambda: bw.mbok_gemv(d1, p1, x, y)),
         ("gemvt", dx, lambda: bw.mbok_gemvt(d1, p1, g, dx)),
+        ("gemm2", Y2, lambda: bw.mbok_gemm(d2, p2, X2, Y2)),
         ("gemm5", Y5, lambda: bw.mbok_gemm(d2, p2, X5, Y5)),
         ("gemm300", Y300, lambda: bw.mbok_gemm(d2, p2, X300, Y300)),
     ]
