@@ -20,7 +20,8 @@ the 8 TB/s HBM nameplate and against the read ceiling this part measures),
 the CPU oracle timed on the host cores on a bounded sample of the same
 workload, and the same figures for the prefill product (11008x4096, K=3,
 2048 tokens: TFLOP/s against the bf16 matrix-core nameplate and the measured
-matrix-core rate) and for the LLaMA-7B MLP decode shapes.
+matrix-core rate), for the LLaMA-7B MLP decode shapes, and for the whole MLP
+step (gate, up, down) at 4 and 16 tokens.
 """
 from __future__ import annotations
 
@@ -864,6 +865,24 @@ def main():
             del mw
             torch.cuda.empty_cache()
         line["mlp_decode"] = mlp
+        # the few-token product on the whole LLaMA-7B MLP step (gate, up, down)
+        few = {}
+        for Tq in (4, 16):
+            note(f"MLP few-token step: {Tq} tokens")
+            fw = Workload(args, 3, 3, Tq)
+            ftimed, froof = product_figures(args, fw, args.steps, args.warmup, None)
+            fms = ftimed["ms_per_step"]
+            gbs = fw.wbytes / (fms * 1e-3) / 1e9
+            fd = fw.layers[fw.dom][1]
+            few[f"T{Tq}"] = {"linears": [[nm, m, n] for nm, m, n in syn.WORKLOADS[3]["linears"]],
+                             "K": 3, "T": Tq, "value": gbs, "unit": "GB/s", "ms_per_step": fms,
+                             "tokens_per_s": Tq / (fms * 1e-3),
+                             "pct_hbm_peak_of_value": round(100 * gbs / HBM_PEAK_GBPS, 2),
+                             "dominant_kernel": kernel_family(Tq, fd.m, fd.n, 3)[1],
+                             "dominant_launch_us": froof["launch_us"], "pool": _pool(ftimed)}
+            del fw
+            torch.cuda.empty_cache()
+        line["few_token"] = few
 
     if not args.no_cpu_baseline:
         note("cpu baseline")

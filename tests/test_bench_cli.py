@@ -62,3 +62,8 @@ def test_bench_line_fields():
     assert p["roofline"]["bound"] == "mfma" and p["roofline"]["peak"] == 2500.0
     assert p["cpu_baseline"]["kind"] == "oracle" and p["cpu_baseline"]["unit"] == "TFLOP/s"
     assert set(d["mlp_decode"]) == {"gate_proj", "down_proj"}
+    # the few-token half of row a3: the whole MLP step at 4 and 16 tokens
+    assert set(d["few_token"]) == {"T4", "T16"}
+    for key, f in d["few_token"].items():
+        assert f["T"] == int(key[1:]) and f["K"] == 3 and f["unit"] == "GB/s"
+        assert f["value"] > 0 and f["tokens_per_s"] == pytest.approx(f["T"] * 1e3 / f["ms_per_step"])
