@@ -501,7 +501,9 @@ def test_gemm_maximum_tokens():
 
 def test_maximum_rows():
     """m = 2^24 rows (the maximum), n = 128, K = 1, exact regime, through the
-    decode (T = 1), few-token (T = 4) and prefill (T = 17) kernels: sampled
+    decode (T = 1), few-token (T = 2: two tokens per matrix-core product;
+    T = 4: one product per group; T = 7: bf16 +-1) and prefill (T = 17)
+    kernels: sampled
     rows (every 4099th and the last 70) against the oracle, and no output
     left unwritten.  This runs the tile and chunk index arithmetic over its
     whole range."""
@@ -515,7 +517,7 @@ def test_maximum_rows():
     del S
     rows_t = torch.from_numpy(rows).to(DEV)
     canary = -777.25  # |y| <= 128 * 8 * 2^-4 in this regime, so never equal
-    for T in (1, 4, 17):
+    for T in (1, 2, 4, 7, 17):
         say(f"maximum rows T={T}")
         X = syn.exact_activations(T, n, seed=73 + T)
         Xd = x_to_dev(X, "bf16")
