@@ -131,12 +131,39 @@ def kernel_family(T, m=None, n=None, K=None, x_bf16=True):
     return "gemm.hip", "gemm_mfma"
 
 
+def code_text(src: str) -> str:
+    """C++ source without comments and with whitespace collapsed, so that a
+    comment edit leaves the digest of a kernel's code unchanged."""
+    import re
+    out, i, n = [], 0, len(src)
+    while i < n:
+        if src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif src[i] in "\"'":
+            q, j = src[i], i + 1
+            while j < n and src[j] != q:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        else:
+            out.append(src[i])
+            i += 1
+    return re.sub(r"\s+", " ", "".join(out)).strip()
+
+
 def source_digest(T, m=None, n=None, K=None):
+    """Digest of the code (comments and layout aside) of the kernel source one
+    call runs and of the shared device header."""
     import hashlib
     h = hashlib.sha256()
     for f in (kernel_family(T, m, n, K)[0], "mbok_device.h"):
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            h.update(code_text(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -475,16 +475,18 @@ __global__ void __launch_bounds__(f4_max_waves(K) * kWave) gemv_f4_kernel(
   }
 }
 
-// The few-token form of the kernel above, TT = 2..4 tokens: token t's activations are row t of x (ldx elements
-// apart) and its outputs row t of y (ldy apart).  A row 4q + s of a product
-// holds part s & 1 of token 2p + (s >> 1) for token pair p (the one-token kernel
-// leaves rows 4q + 2, 4q + 3 zero), so 2 tokens take one instruction per (tile,
-// kernel, word) and 3 or 4 tokens two.
+// The few-token form of the kernel above, TT = 2..4 tokens: token t's
+// activations are row t of x (ldx elements apart) and its outputs row t of y
+// (ldy apart).  A row 4q + s of a product holds part s & 1 of token
+// 2p + (s >> 1) for token pair p (the one-token kernel leaves rows 4q + 2,
+// 4q + 3 zero), so 2 tokens take one instruction per (tile, kernel, word) and
+// 3 or 4 tokens two.
 template <typename AT, int K, int NT, int TT>
 __device__ __forceinline__ void f4_tokens_body(const uint4* __restrict__ bits,
-                                        const uint16_t* __restrict__ x, int64_t ldx, int G,
-                                        int tiles, int slab_groups, int grid, int nw, int tpw,
-                                        int textra, float* __restrict__ y, int64_t ldy, int m) {
+                                               const uint16_t* __restrict__ x, int64_t ldx,
+                                               int G, int tiles, int slab_groups, int grid,
+                                               int nw, int tpw, int textra,
+                                               float* __restrict__ y, int64_t ldy, int m) {
   constexpr int TP = (TT + 1) / 2;  // token pairs
   static_assert(TT >= 2 && TT <= 4, "2..4 tokens");
   constexpr int kSlabMax = kF4GroupsPerWave * f4_max_waves(K, TT);

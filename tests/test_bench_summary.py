@@ -94,3 +94,15 @@ def test_timed_regions_between_markers():
     # the launch-floor measurement's empty kernels are not markers
     assert regs == [{GEMV: [4.0, 6.0]}, {"gemm_mfma8_kernel": [100.0]}]
     assert bench.timed_regions([(1, GEMV, 1.0)]) == []
+
+
+def test_code_digest_ignores_comments_only():
+    """The kernel-source digest that ties a profile record to its kernel
+    ignores comments and layout, and sees every code change."""
+    import bench
+    src = 'int f(int a) {  // scale\n  /* two\n     lines */ return a * 2; }\nconst char* s = "//x";\n'
+    same = 'int f(int a)\n{\n  return a * 2;  /* other words */\n}\nconst char* s = "//x";\n'
+    other = 'int f(int a) { return a * 3; }\nconst char* s = "//x";\n'
+    assert bench.code_text(src) == bench.code_text(same)
+    assert bench.code_text(src) != bench.code_text(other)
+    assert '"//x"' in bench.code_text(src)  # string contents are code
