@@ -1015,6 +1015,277 @@ __global__ void __launch_bounds__(f4g_waves(NO) * kWave) gemm_f4g_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// The SVID scale variant's product y = sum_k s_out^k (.) (B_k (s_in^k (.) x))
+// ("Successive SVID" of the gist.science summaries: each kernel's scales are
+// an outer product s_out^k s_in^k^T) on the decode kernel above.  The packed
+// layer holds s_out^k[i] in every group's scale slot, so the per-(tile,
+// kernel) epilogue is the decode's.  What changes is the activation side:
+// kernel k contracts with its own vector v_k = s_in^k (.) x (one fp32
+// product, exact for fp16 scales and bf16 x), split into four fp8 parts with
+// per-word scales 2^(code - 127 - 4p), p = 0..3: 16 significant bits of the
+// word's largest |v|, as the bf16 hi/lo split of the bf16 +-1 product keeps.
+// The four parts fill A rows 4q .. 4q + 3 of group q, so each (tile, kernel,
+// word) is still one instruction; D registers 0..3 of lane 16j + r are the
+// four parts' sums of group j and row r.  Every workgroup converts K vectors
+// (x and the K rows of s_in it needs) per column slab; slabs of at most 32
+// groups (8 wavefronts: the A operands of K kernels take 32 K registers).
+constexpr int kF4sMaxWaves = 8;
+constexpr int kF4sMaxSlab = kF4GroupsPerWave * kF4sMaxWaves;  // 32 groups
+constexpr int kF4sOpBytes = 4 * kGroup;  // 4 parts x 128 terms per (kernel, group)
+
+template <typename AT>
+__device__ __forceinline__ void load8_f32(const AT* p, float (&v)[8]);
+template <>
+__device__ __forceinline__ void load8_f32<uint16_t>(const uint16_t* p, float (&v)[8]) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[2 * e] = f16_bits_to_f32((uint16_t)(w[e] & 0xffffu));
+    v[2 * e + 1] = f16_bits_to_f32((uint16_t)(w[e] >> 16));
+  }
+}
+template <>
+__device__ __forceinline__ void load8_f32<float>(const float* p, float (&v)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = a.x, v[1] = a.y, v[2] = a.z, v[3] = a.w;
+  v[4] = b.x, v[5] = b.y, v[6] = b.z, v[7] = b.w;
+}
+// 8 bf16 (XF = false) or fp32 (XF = true) activations
+template <bool XF>
+__device__ __forceinline__ void load8_x(const void* x, int64_t col, float (&v)[8]) {
+  if constexpr (XF) {
+    load8_f32<float>(reinterpret_cast<const float*>(x) + col, v);
+  } else {
+    const uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + col);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] = bf16_bits_to_f32(w[e] & 0xffffu);
+      v[2 * e + 1] = bf16_bits_to_f32(w[e] >> 16);
+    }
+  }
+}
+
+// Part scale codes 2^-4 apart, clamped at the smallest code.
+__device__ __forceinline__ int part_code(int code, int p) {
+  return code > 4 * p ? code - 4 * p : 0;
+}
+
+template <typename AT, int K, int NT, bool XF>
+__global__ void __launch_bounds__(kF4sMaxWaves * kWave) gemv_f4_svid_kernel(
+    const uint4* __restrict__ bits, const void* __restrict__ x, const AT* __restrict__ s_in,
+    int G, int tiles, int slab_groups, int grid, int nw, int tpw, int textra,
+    float* __restrict__ y, int m) {
+  typedef short v2i16 __attribute__((ext_vector_type(2)));
+  const AT* __restrict__ scales =
+      reinterpret_cast<const AT*>(bits + (int64_t)tiles * 16 * G * K);
+  const int n = G * kGroup;
+  // converted vectors: [kernel][group][part][word][32 terms]
+  __shared__ __attribute__((aligned(16))) uint8_t ops[K * kF4sMaxSlab * kF4sOpBytes];
+  __shared__ __attribute__((aligned(4))) uint8_t codes[K * kF4sMaxSlab * 4];
+  __shared__ float red[NT * kF4sMaxWaves * 16];
+  const int NW = nw;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int r = lane & 15;
+  const int q = lane >> 4;
+  const int b = blockIdx.x;
+  const int ntl = tpw + (b < textra ? 1 : 0);
+  constexpr bool EARLY = NT > 1;
+  int nonfinite = 0;
+  const uint32_t m0 = sgpr_const(0x11111111u), m1 = sgpr_const(0x22222222u);
+  const uint32_t m2 = sgpr_const(0x44444444u), m3 = sgpr_const(0x88888888u);
+  const uint32_t b0 = vgpr_const(0x66666666u), b1 = vgpr_const(0x44444444u);
+  const uint32_t b3 = vgpr_const(0x22222222u);
+  const v2i16 zero = {0, 0};
+
+  for (int g0 = 0; g0 < G; g0 += slab_groups) {
+    const int sg = min(slab_groups, G - g0);
+    const int gq = min(kF4GroupsPerWave * wave + q, sg - 1);
+    const int vs = (gq * K * kRowBlock + r) * 16;
+    const int va = (gq * K * kRowBlock + r) * (int)sizeof(AT);
+    auto load = [&](int t, F4Loads<K, AT>& L) {
+      int tb = b + t * grid;
+      asm volatile("" : "+s"(tb));
+      const int i0 = tile16_of(tb, tiles) * 16;
+      const int rb = i0 / kRowBlock, r0 = i0 % kRowBlock;
+      const int64_t c0 = ((int64_t)rb * G + g0) * K * kRowBlock + r0;
+      const i32x4_t rs = buffer_rsrc(bits + c0, t < ntl);
+      const i32x4_t ra = buffer_rsrc(scales + c0, t < ntl);
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        L.s[k] = as_uint4(raw_buffer_load_b128(rs, vs + k * kRowBlock * 16, 0, kAuxNt));
+        L.a[k] = load_scale<AT>(ra, va + k * kRowBlock * (int)sizeof(AT));
+      }
+    };
+    // thread xt: 8 columns of group gl (wavefront w converts its own groups)
+    const int xt = threadIdx.x;
+    const bool has_x = xt < sg * 16;
+    const int64_t col = (int64_t)g0 * kGroup + 8 * (has_x ? xt : 0);
+    float xv[8], sv[K][8];
+    load8_x<XF>(x, col, xv);
+#pragma unroll
+    for (int k = 0; k < K; ++k) load8_f32<AT>(s_in + (int64_t)k * n + col, sv[k]);
+    F4Loads<K, AT> Lb[kF4Ahead + 1];
+    if (EARLY) {
+      load(0, Lb[0]);
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      load(0, Lb[0]);
+    }
+    float corr[K];
+    {
+      const int gl = xt >> 4, word = (xt >> 2) & 3, sub = xt & 3;
+      const bool odd = (sub & 1) != 0;
+      const float c_lo = odd ? 1.f : 5.f, c_hi = odd ? 0.f : 3.f;
+      const bool h = (sub >> 1) != 0;
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        float v[8];
+        uint32_t mx = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          // class 3 (columns e >= 4 of an odd thread) negated; its c is 0
+          const float p = has_x ? sv[k][e] * xv[e] : 0.f;
+          v[e] = (e >= 4 && odd) ? -p : p;
+          mx = max(mx, __float_as_uint(p) & 0x7fffffffu);
+        }
+        mx = max(mx, dpp_u32<kQuadXor1>(mx));
+        mx = max(mx, dpp_u32<kQuadXor2>(mx));
+        const int eb = (int)(mx >> 23);
+        if (eb == 0xff) nonfinite = 1;
+        const int code = mx == 0 ? kE8M0One : (eb > 7 ? eb - 7 : 0);
+        if (sub == 0 && has_x) codes[(k * kF4sMaxSlab + gl) * 4 + word] = (uint8_t)code;
+        float cs = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cs = fmaf(e < 4 ? c_lo : c_hi, v[e], cs);
+        uint8_t* base = ops + (k * kF4sMaxSlab + gl) * kF4sOpBytes + word * 32 + 16 * (sub & 1) +
+                        8 * (int)h;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const float sc = __builtin_ldexpf(1.f, part_code(code, p) - kE8M0One);
+          uint32_t P[4];
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const v2i16 c8 =
+                __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(zero, v[2 * d], v[2 * d + 1], sc, false);
+            P[d] = (uint32_t)__builtin_bit_cast(int, c8);
+            if (p < 3) {
+              // what this part leaves (exact: the part holds the leading bits)
+              const auto back = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)P[d], sc, false);
+              v[2 * d] -= back[0];
+              v[2 * d + 1] -= back[1];
+            }
+          }
+          if (has_x) *reinterpret_cast<uint2*>(base + p * kGroup) = pair_terms(P, h);
+        }
+        cs = cs + __uint_as_float(dpp_u32<kQuadXor1>(__float_as_uint(cs)));
+        cs = cs + __uint_as_float(dpp_u32<kQuadXor2>(__float_as_uint(cs)));
+        cs = cs + __uint_as_float(dpp_u32<kRowHalfMirror>(__float_as_uint(cs)));
+        cs = cs + __uint_as_float(dpp_u32<kRowMirror>(__float_as_uint(cs)));
+        corr[k] = cs;
+      }
+    }
+#pragma unroll
+    for (int j = 1; j < kF4Ahead; ++j)
+      if (j < NT) load(j, Lb[j]);
+    wave_lds_sync();
+    // A operands of kernel k, word i: lane 16c + rho holds A row rho =
+    // 4 qa + p (part p of group qa), nonzero only in K-block qa (lane blocks
+    // 2 (qa & 1), 2 (qa & 1) + 1, bytes 16 (qa >> 1) ..)
+    v8i_t A[K][4];
+    int ascale[K][4];
+    {
+      const int qa = r >> 2, part = r & 3;
+      const int gl = kF4GroupsPerWave * wave + qa;
+      const bool live = gl < sg && (qa & 1) == (q >> 1);
+      const int glc = min(gl, sg - 1);
+      const bool upper = (qa >> 1) != 0;
+      const uint32_t keep = live ? ~0u : 0u;
+      const uint32_t klo = upper ? 0u : keep, khi = upper ? keep : 0u;
+      const int sq = min(kF4GroupsPerWave * wave + q, sg - 1);
+      const bool srow = (r >> 2) == q && kF4GroupsPerWave * wave + q < sg;
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const uint8_t* base = ops + (k * kF4sMaxSlab + glc) * kF4sOpBytes + part * kGroup +
+                              16 * (q & 1);
+        uint4 dd[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dd[i] = *reinterpret_cast<const uint4*>(base + 32 * i);
+        const uint32_t cw = *reinterpret_cast<const uint32_t*>(codes + (k * kF4sMaxSlab + sq) * 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          A[k][i] = v8i_t{(int)(dd[i].x & klo), (int)(dd[i].y & klo), (int)(dd[i].z & klo),
+                          (int)(dd[i].w & klo), (int)(dd[i].x & khi), (int)(dd[i].y & khi),
+                          (int)(dd[i].z & khi), (int)(dd[i].w & khi)};
+          asm volatile("" : "+v"(A[k][i]));
+          const int code = (int)((cw >> (8 * i)) & 0xffu);
+          ascale[k][i] = srow ? part_code(code, part) : kE8M0One;
+        }
+      }
+    }
+
+    auto mul = [&](F4Loads<K, AT>& L, float a) {
+      v4f_t d[K];
+#pragma unroll
+      for (int k = 0; k < K; ++k) d[k] = v4f_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          const uint32_t w = i == 0 ? L.s[k].x : i == 1 ? L.s[k].y : i == 2 ? L.s[k].z : L.s[k].w;
+          v8i_t B;
+          B[0] = (int)((w & m0) | b0);
+          B[1] = (int)((w & m1) | b1);
+          B[2] = (int)(w & m2);
+          B[3] = (int)((w & m3) | b3);
+          B[4] = B[5] = B[6] = B[7] = 0;
+          d[k] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[k][i], B, d[k], 0, 4, 0,
+                                                                  ascale[k][i], 0, kE8M0One);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < K; ++k)
+        a = fmaf(alpha_to_f32<AT>(L.a[k]), ((d[k][0] + d[k][1]) + (d[k][2] + d[k][3])) - corr[k],
+                 a);
+      return a;
+    };
+    auto step = [&](int t, F4Loads<K, AT>& L) {
+      float uu = mul(L, 0.f);
+      {
+        const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(uu), __float_as_uint(uu),
+                                                        false, false);
+        uu = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+        const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(uu), __float_as_uint(uu),
+                                                        false, false);
+        uu = __uint_as_float(c[0]) + __uint_as_float(c[1]);
+      }
+      if (q == 0) {
+        float* dst = red + (t * NW + wave) * 16 + r;
+        *dst = g0 == 0 ? uu : *dst + uu;
+      }
+    };
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (t >= ntl) break;
+      if (t + kF4Ahead < NT) load(t + kF4Ahead, Lb[(t + kF4Ahead) % (kF4Ahead + 1)]);
+      step(t, Lb[t % (kF4Ahead + 1)]);
+    }
+  }
+
+  const bool bad = __syncthreads_or(nonfinite) != 0;
+  for (int idx = threadIdx.x; idx < ntl * 16; idx += NW * kWave) {
+    const int t = idx >> 4, rr = idx & 15;
+    float uu = red[(t * NW) * 16 + rr];
+    for (int w = 1; w < NW; ++w) uu += red[(t * NW + w) * 16 + rr];
+    const int i = tile16_of(b + t * grid, tiles) * 16 + rr;
+    if (i < m) y[i] = bad ? __builtin_nanf("") : uu;
+  }
+}
+
 template <typename AT, int K>
 int launch_f4_k(const Geom& geo, const void* packed, const void* x, float* y,
                 hipStream_t stream) {
@@ -1158,6 +1429,48 @@ int launch_f4_tokens(const Geom& geo, const void* packed, const void* X, int T, 
   return MBOK_ERR_SHAPE;
 }
 
+template <typename AT, int K, bool XF>
+int launch_f4_svid_k(const Geom& geo, const void* packed, const void* x, const AT* s_in,
+                     float* y, hipStream_t stream) {
+  const int nslabs = (geo.G + kF4sMaxSlab - 1) / kF4sMaxSlab;
+  const int slab = (geo.G + nslabs - 1) / nslabs;
+  const int NW = (slab + kF4GroupsPerWave - 1) / kF4GroupsPerWave;
+  const int tiles = geo.RB * (kRowBlock / 16);
+  int grid = tiles < 256 ? tiles : 256;
+  if (grid * kF4J < tiles) grid = (tiles + kF4J - 1) / kF4J;
+  const int slots = (tiles + grid - 1) / grid;
+  auto go = [&](auto slot_count) {
+    constexpr int S = decltype(slot_count)::value;
+    hipLaunchKernelGGL((gemv_f4_svid_kernel<AT, K, S, XF>), dim3(grid), dim3(NW * kWave), 0,
+                       stream, reinterpret_cast<const uint4*>(packed), x, s_in, geo.G, tiles,
+                       slab, grid, NW, tiles / grid, tiles % grid, y, geo.m);
+  };
+  switch (slots) {
+    case 1: go(std::integral_constant<int, 1>{}); break;
+    case 2: go(std::integral_constant<int, 2>{}); break;
+    case 3: go(std::integral_constant<int, 3>{}); break;
+    case 4: go(std::integral_constant<int, 4>{}); break;
+    case 5: go(std::integral_constant<int, 5>{}); break;
+    case 6: go(std::integral_constant<int, 6>{}); break;
+    case 7: go(std::integral_constant<int, 7>{}); break;
+    default: go(std::integral_constant<int, 8>{}); break;
+  }
+  return hipGetLastError() == hipSuccess ? MBOK_OK : MBOK_ERR_HIP;
+}
+
+template <typename AT, bool XF>
+int launch_f4_svid_t(const Geom& geo, const void* packed, const void* x, const void* s_in,
+                     float* y, hipStream_t stream) {
+  const AT* si = reinterpret_cast<const AT*>(s_in);
+  switch (geo.K) {
+    case 1: return launch_f4_svid_k<AT, 1, XF>(geo, packed, x, si, y, stream);
+    case 2: return launch_f4_svid_k<AT, 2, XF>(geo, packed, x, si, y, stream);
+    case 3: return launch_f4_svid_k<AT, 3, XF>(geo, packed, x, si, y, stream);
+    case 4: return launch_f4_svid_k<AT, 4, XF>(geo, packed, x, si, y, stream);
+  }
+  return MBOK_ERR_UNSUPPORTED;
+}
+
 }  // namespace
 
 int launch_gemv_f4(const mbok_desc* d, const void* packed, const void* x, float* y,
@@ -1194,6 +1507,17 @@ int launch_gemm_f4(const mbok_desc* d, const void* packed, const void* X, int64_
   return d->alpha_dtype == MBOK_F16
              ? launch_f4_tokens<uint16_t>(geo, packed, X, (int)T, (int)ldx, Y, (int)ldy, stream)
              : launch_f4_tokens<float>(geo, packed, X, (int)T, (int)ldx, Y, (int)ldy, stream);
+}
+
+int launch_svid_f4(const mbok_desc* d, const void* packed, const void* x, int32_t x_dtype,
+                   const void* s_in, float* y, hipStream_t stream) {
+  const Geom geo = make_geom(d);
+  const bool xf = x_dtype == MBOK_F32;
+  if (d->alpha_dtype == MBOK_F16)
+    return xf ? launch_f4_svid_t<uint16_t, true>(geo, packed, x, s_in, y, stream)
+              : launch_f4_svid_t<uint16_t, false>(geo, packed, x, s_in, y, stream);
+  return xf ? launch_f4_svid_t<float, true>(geo, packed, x, s_in, y, stream)
+            : launch_f4_svid_t<float, false>(geo, packed, x, s_in, y, stream);
 }
 
 }  // namespace mbok

@@ -3,6 +3,8 @@
 // synchronises or keeps state.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include <cmath>
 
@@ -137,7 +139,12 @@ int mbok_svid_gemv(const mbok_desc* d, const void* packed, const void* s_in, con
   if (!aligned(packed, 16) || !aligned(s_in, 16) || !aligned(x, 16) || !aligned(y, 4) ||
       (workspace && !aligned(workspace, 256)))
     return MBOK_ERR_ALIGN;
-  return mbok::launch_svid_skinny(d, packed, x, x_dtype, s_in, y, (hipStream_t)stream);
+  // the fp4 x fp8 form by default; MBOK_SVID_VARIANT=skinny selects the bf16
+  // +-1 form (measurements)
+  const char* v = getenv("MBOK_SVID_VARIANT");
+  if (v && strcmp(v, "skinny") == 0)
+    return mbok::launch_svid_skinny(d, packed, x, x_dtype, s_in, y, (hipStream_t)stream);
+  return mbok::launch_svid_f4(d, packed, x, x_dtype, s_in, y, (hipStream_t)stream);
 }
 
 int mbok_refit(const mbok_desc* d, const float* W, int64_t ldw, int8_t* signs, void* alpha,

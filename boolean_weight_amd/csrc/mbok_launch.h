@@ -47,6 +47,9 @@ int launch_svid_pack(const mbok_desc* d, const int8_t* signs, const void* s_out,
                      hipStream_t stream);
 int launch_svid_skinny(const mbok_desc* d, const void* packed, const void* x, int32_t x_dtype,
                        const void* s_in, float* y, hipStream_t stream);
+// the same product on the fp4 x fp8 decode kernel (gemv_f4.hip)
+int launch_svid_f4(const mbok_desc* d, const void* packed, const void* x, int32_t x_dtype,
+                   const void* s_in, float* y, hipStream_t stream);
 int allocate_kernels(int L, const int64_t* sizes, const double* errors, int kmax, int64_t budget,
                      int32_t* K_out);
 // passes: 1 = prefill levels rounded to bf16; 2 = plus a second pass with

@@ -110,11 +110,26 @@ def pack_svid(S, SO, dt):
     return d, packed
 
 
+# the product on the fp4 x fp8 decode kernel (default) and in the bf16 +-1
+# few-token kernel (MBOK_SVID_VARIANT=skinny)
+SVID_VARIANTS = ["f4", "skinny"]
+
+
+@pytest.fixture(params=SVID_VARIANTS)
+def svid_variant(request, monkeypatch):
+    if request.param == "skinny":
+        monkeypatch.setenv("MBOK_SVID_VARIANT", "skinny")
+    else:
+        monkeypatch.delenv("MBOK_SVID_VARIANT", raising=False)
+    return request.param
+
+
 @pytest.mark.parametrize("K", [1, 2, 3, 4])
-@pytest.mark.parametrize("m,n", [(1, 128), (64, 128), (130, 640), (4096, 4096), (70, 13824)])
-def test_svid_gemv_exact_regime(m, n, K):
+@pytest.mark.parametrize("m,n", [(1, 128), (64, 128), (130, 640), (4096, 4096), (70, 13824),
+                                 (20000, 256)])
+def test_svid_gemv_exact_regime(m, n, K, svid_variant):
     for dt, xdt in (("f16", "bf16"), ("f32", "f32")):
-        say(f"svid gemv exact m={m} n={n} K={K} {dt}/{xdt}")
+        say(f"svid gemv exact m={m} n={n} K={K} {dt}/{xdt} {svid_variant}")
         rng = np.random.default_rng(m + n + K)
         S = syn.random_signs(K, m, n, seed=m * 3 + n + K)
         SO = np.ldexp(1.0, -rng.integers(2, 5, size=(K, m))).astype(np_alpha(dt))
@@ -138,13 +153,13 @@ def test_svid_pack_layout():
 
 
 @pytest.mark.parametrize("cfg", [1, 2, 3])
-def test_svid_gemv_workload_tolerance(cfg):
+def test_svid_gemv_workload_tolerance(cfg, svid_variant):
     """Gaussian weights decomposed by the oracle, packed and multiplied on the
     device, against the oracle's product (sampled rows)."""
     w = syn.WORKLOADS[cfg]
     name, m, n = w["linears"][0]
     dt, xdt, K = w["alpha_dtype"], w["x_dtype"], w["K"]
-    say(f"svid gemv config {cfg} {name} {m}x{n} K={K}")
+    say(f"svid gemv config {cfg} {name} {m}x{n} K={K} {svid_variant}")
     W = syn.weight(m, n, syn.weight_seed(cfg, 0))
     S, SO, SI, _ = oracle.svid_decompose(W, K, alpha_dtype=dt)
     x = syn.activations(1, n, syn.act_seed(cfg, 0), xdt)[0]
@@ -155,5 +170,6 @@ def test_svid_gemv_workload_tolerance(cfg):
     E = oracle.svid_bound(S[:, rows], SO[:, rows], SI, x)
     ratio = oracle.max_error_ratio(y[rows], want, E)
     assert ratio <= TOL, ratio
-    # close to float64 as well: the hi/lo split keeps about 2^-17
+    # close to float64 as well: both forms keep 16 significant bits of each
+    # s_in^k x_j (bf16 hi/lo parts; four fp8 parts of one word scale)
     assert ratio <= 1e-2 * TOL, ratio
