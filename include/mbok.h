@@ -311,9 +311,13 @@ size_t mbok_svid_gemv_workspace_bytes(const mbok_desc* d);
  * the Boolean one with x scaled per kernel and the output scaled per row):
  *     y[i] = sum_k s_out^k[i] * sum_j b_k[i, j] * s_in^k[j] * x[j]
  * s_in^k (.) x is formed in fp32 (exact for fp16 scales and bf16 x) and
- * split into bf16 hi + lo parts, so the matrix cores see it to about 2^-17
- * relative; the +-1 contractions accumulate in fp32 and s_out applies in
- * fp32.  Results are bit-reproducible.
+ * split into four fp8 parts with one power-of-two scale per 32 columns, 4
+ * bits each, so the matrix cores see 16 significant bits of each 32-column
+ * word's largest value (MBOK_SVID_VARIANT=skinny: bf16 hi + lo parts, about
+ * 2^-17 relative per value); the +-1 contractions accumulate in fp32 and
+ * s_out applies in fp32.  Within 1e-5 of sum_k |s_out^k[i]| sum_j |s_in^k[j]
+ * x[j]| on the workloads; a non-finite product s_in^k[j] x[j] makes every
+ * output NaN.  Results are bit-reproducible.
  *  packed     device, the buffer of mbok_svid_pack.
  *  s_in       device [K][n] of d->alpha_dtype, 16-byte aligned.
  *  x          device, n values of x_dtype (MBOK_BF16 or MBOK_F32), 16-byte
