@@ -241,7 +241,7 @@ struct F4Loads {
 // of the word, i.e. column 16 (p & 1) + 4 d + (p >> 1), as term 8d + p.  The
 // converted activations are stored in LDS in term order.
 
-template <typename AT, int K, int NT>
+template <typename AT, int K, int NT, bool EARLY>
 __global__ void __launch_bounds__(f4_max_waves(K) * kWave) gemv_f4_kernel(
     const uint4* __restrict__ bits, const uint16_t* __restrict__ x, int G, int tiles,
     int slab_groups, int grid, int nw, int tpw, int textra, float* __restrict__ y, int m) {
@@ -258,8 +258,7 @@ __global__ void __launch_bounds__(f4_max_waves(K) * kWave) gemv_f4_kernel(
   const int r = lane & 15;   // row of the tile (B column, D column; A row at A time)
   const int q = lane >> 4;   // lane block: K-block q holds group 4 wave + q
   const int b = blockIdx.x;
-  const int ntl = tpw + (b < textra ? 1 : 0);  // tiles of this workgroup, <= NT
-  constexpr bool EARLY = NT > 1;  // NT: tile slots, the most tiles of any workgroup
+  const int ntl = tpw + (b < textra ? 1 : 0);  // tiles of this workgroup, <= NT (tile slots)
   int nonfinite = 0;  // this thread saw a NaN or infinite activation
   // B dword d, nibble p: bit 4p + d of the word at nibble bit d, over a base
   // nibble: d = 0 {4.0, 6.0}, d = 1 {2.0, 4.0}, d = 2 {0, 2.0}, d = 3
@@ -297,12 +296,16 @@ __global__ void __launch_bounds__(f4_max_waves(K) * kWave) gemv_f4_kernel(
     // each sign load issued before they arrive sits in the same memory
     // queues ahead of other wavefronts' activation loads, so only the first
     // tile's signs go out now (EARLY: some workgroup has more than one tile
-    // to keep the stream going; else right after the activations arrive),
-    // the rest once this wavefront has converted its activations (measured:
-    // 11008 x 4096 7.9 -> 7.1 us, 4096 x 4096 K = 2 4.65 -> 4.09 us).  EARLY
-    // is a compile-time choice so that the conversion waits for the
-    // activations alone (a runtime condition made the compiler wait for
-    // every load in flight).
+    // to keep the stream going, or the layer has several column slabs;
+    // else right after the activations arrive), the rest once this
+    // wavefront has converted its activations (measured: 11008 x 4096 7.9
+    // -> 7.1 us, 4096 x 4096 K = 2 4.65 -> 4.09 us).  With one tile per
+    // workgroup: 4096 x 4096, K = 2 (one slab) 3.57 us waiting for the
+    // activations against 3.81 us with the signs right behind them; 4096 x
+    // 11008, K = 3 (two slabs) 6.82 against 6.50 us.  EARLY is a
+    // compile-time choice so that the conversion waits for the activations
+    // alone (a runtime condition made the compiler wait for every load in
+    // flight).
     const int xt = threadIdx.x;  // 8 columns per thread, 4 threads per 32-column word
     const bool has_x = xt < sg * 16;
     const uint4 u = has_x ? *reinterpret_cast<const uint4*>(x + (int64_t)g0 * kGroup + 8 * xt)
@@ -475,13 +478,14 @@ __global__ void __launch_bounds__(f4_max_waves(K) * kWave) gemv_f4_kernel(
   }
 }
 
-// The few-token form of the kernel above, TT = 2..4 tokens: token t's
+// The few-token form of the kernel above, TT = 2..4 tokens (EARLY as above:
+// here whenever a workgroup has more than one tile): token t's
 // activations are row t of x (ldx elements apart) and its outputs row t of y
 // (ldy apart).  A row 4q + s of a product holds part s & 1 of token
 // 2p + (s >> 1) for token pair p (the one-token kernel leaves rows 4q + 2,
 // 4q + 3 zero), so 2 tokens take one instruction per (tile, kernel, word) and
 // 3 or 4 tokens two.
-template <typename AT, int K, int NT, int TT>
+template <typename AT, int K, int NT, int TT, bool EARLY>
 __device__ __forceinline__ void f4_tokens_body(const uint4* __restrict__ bits,
                                                const uint16_t* __restrict__ x, int64_t ldx,
                                                int G, int tiles, int slab_groups, int grid,
@@ -505,7 +509,6 @@ __device__ __forceinline__ void f4_tokens_body(const uint4* __restrict__ bits,
   const int q = lane >> 4;   // lane block: K-block q holds group 4 wave + q
   const int b = blockIdx.x;
   const int ntl = tpw + (b < textra ? 1 : 0);  // tiles of this workgroup, <= NT
-  constexpr bool EARLY = NT > 1;  // NT: tile slots, the most tiles of any workgroup
   int nonfinite = 0;  // bit t: this thread saw a NaN or infinite activation of token t
   // B dword d, nibble p: bit 4p + d of the word at nibble bit d, over a base
   // nibble: d = 0 {4.0, 6.0}, d = 1 {2.0, 4.0}, d = 2 {0, 2.0}, d = 3
@@ -768,12 +771,13 @@ __device__ __forceinline__ void f4_tokens_body(const uint4* __restrict__ bits,
 
 
 // 2..4 tokens; the token strides follow the arguments of the one-token kernel
-template <typename AT, int K, int NT, int TT>
+template <typename AT, int K, int NT, int TT, bool EARLY>
 __global__ void __launch_bounds__(f4_max_waves(K, TT) * kWave) gemm_f4_kernel(
     const uint4* __restrict__ bits, const uint16_t* __restrict__ x, int G, int tiles,
     int slab_groups, int grid, int nw, int tpw, int textra, float* __restrict__ y, int m,
     int ldx, int ldy) {
-  f4_tokens_body<AT, K, NT, TT>(bits, x, ldx, G, tiles, slab_groups, grid, nw, tpw, textra, y, ldy, m);
+  f4_tokens_body<AT, K, NT, TT, EARLY>(bits, x, ldx, G, tiles, slab_groups, grid, nw, tpw, textra, y,
+                                     ldy, m);
 }
 
 // ---------------------------------------------------------------------------
@@ -806,7 +810,7 @@ constexpr int kF4gMaxTokens = kF4gTokens * kF4gMaxOctets;
 constexpr int f4g_waves(int NO) { return NO == 1 ? 12 : 8; }
 constexpr int kF4gOpsPerWave = kF4GroupsPerWave * kF4gTokens * kOpBytes;  // 8 KB
 
-template <typename AT, int K, int NT, int NO>
+template <typename AT, int K, int NT, int NO, bool EARLY>
 __global__ void __launch_bounds__(f4g_waves(NO) * kWave) gemm_f4g_kernel(
     const uint4* __restrict__ bits, const uint16_t* __restrict__ X, int G, int tiles,
     int slab_groups, int grid, int nw, int tpw, int textra, float* __restrict__ Y, int m, int T,
@@ -828,7 +832,6 @@ __global__ void __launch_bounds__(f4g_waves(NO) * kWave) gemm_f4g_kernel(
   const int q = lane >> 4;
   const int b = blockIdx.x;
   const int ntl = tpw + (b < textra ? 1 : 0);
-  constexpr bool EARLY = NT > 1;
   if (threadIdx.x == 0) bad_tokens = 0;
   int nonfinite = 0;  // bit t: this thread saw a NaN or infinite activation of token t
   const uint32_t m0 = sgpr_const(0x11111111u), m1 = sgpr_const(0x22222222u);
@@ -1074,7 +1077,7 @@ __device__ __forceinline__ int part_code(int code, int p) {
   return code > 4 * p ? code - 4 * p : 0;
 }
 
-template <typename AT, int K, int NT, bool XF>
+template <typename AT, int K, int NT, bool XF, bool EARLY>
 __global__ void __launch_bounds__(kF4sMaxWaves * kWave) gemv_f4_svid_kernel(
     const uint4* __restrict__ bits, const void* __restrict__ x, const AT* __restrict__ s_in,
     int G, int tiles, int slab_groups, int grid, int nw, int tpw, int textra,
@@ -1094,7 +1097,6 @@ __global__ void __launch_bounds__(kF4sMaxWaves * kWave) gemv_f4_svid_kernel(
   const int q = lane >> 4;
   const int b = blockIdx.x;
   const int ntl = tpw + (b < textra ? 1 : 0);
-  constexpr bool EARLY = NT > 1;
   int nonfinite = 0;
   const uint32_t m0 = sgpr_const(0x11111111u), m1 = sgpr_const(0x22222222u);
   const uint32_t m2 = sgpr_const(0x44444444u), m3 = sgpr_const(0x88888888u);
@@ -1304,15 +1306,22 @@ int launch_f4_k(const Geom& geo, const void* packed, const void* x, float* y,
                        reinterpret_cast<const uint16_t*>(x), geo.G, tiles, slab, grid, NW,
                        tiles / grid, tiles % grid, y, geo.m);
   };
+  // the first tile's signs go out behind the activations unless one tile
+  // per workgroup meets a single column slab
   switch (slots) {
-    case 1: go(gemv_f4_kernel<AT, K, 1>); break;
-    case 2: go(gemv_f4_kernel<AT, K, 2>); break;
-    case 3: go(gemv_f4_kernel<AT, K, 3>); break;
-    case 4: go(gemv_f4_kernel<AT, K, 4>); break;
-    case 5: go(gemv_f4_kernel<AT, K, 5>); break;
-    case 6: go(gemv_f4_kernel<AT, K, 6>); break;
-    case 7: go(gemv_f4_kernel<AT, K, 7>); break;
-    default: go(gemv_f4_kernel<AT, K, 8>); break;
+    case 1:
+      if (nslabs > 1)
+        go(gemv_f4_kernel<AT, K, 1, true>);
+      else
+        go(gemv_f4_kernel<AT, K, 1, false>);
+      break;
+    case 2: go(gemv_f4_kernel<AT, K, 2, true>); break;
+    case 3: go(gemv_f4_kernel<AT, K, 3, true>); break;
+    case 4: go(gemv_f4_kernel<AT, K, 4, true>); break;
+    case 5: go(gemv_f4_kernel<AT, K, 5, true>); break;
+    case 6: go(gemv_f4_kernel<AT, K, 6, true>); break;
+    case 7: go(gemv_f4_kernel<AT, K, 7, true>); break;
+    default: go(gemv_f4_kernel<AT, K, 8, true>); break;
   }
   return hipGetLastError() == hipSuccess ? MBOK_OK : MBOK_ERR_HIP;
 }
@@ -1342,22 +1351,23 @@ int launch_f4_tokens_k(const Geom& geo, const void* packed, const void* X, int l
   int grid = tiles < 256 ? tiles : 256;
   if (grid * kF4J < tiles) grid = (tiles + kF4J - 1) / kF4J;
   const int slots = (tiles + grid - 1) / grid;
-  auto go = [&](auto slot_count) {
+  auto go = [&](auto slot_count, auto early) {
     constexpr int S = decltype(slot_count)::value;
-    hipLaunchKernelGGL((gemm_f4_kernel<AT, K, S, TT>), dim3(grid), dim3(NW * kWave), 0, stream,
+    constexpr bool E = decltype(early)::value;
+    hipLaunchKernelGGL((gemm_f4_kernel<AT, K, S, TT, E>), dim3(grid), dim3(NW * kWave), 0, stream,
                        reinterpret_cast<const uint4*>(packed),
                        reinterpret_cast<const uint16_t*>(X), geo.G, tiles, slab, grid, NW,
                        tiles / grid, tiles % grid, Y, geo.m, ldx, ldy);
   };
   switch (slots) {
-    case 1: go(std::integral_constant<int, 1>{}); break;
-    case 2: go(std::integral_constant<int, 2>{}); break;
-    case 3: go(std::integral_constant<int, 3>{}); break;
-    case 4: go(std::integral_constant<int, 4>{}); break;
-    case 5: go(std::integral_constant<int, 5>{}); break;
-    case 6: go(std::integral_constant<int, 6>{}); break;
-    case 7: go(std::integral_constant<int, 7>{}); break;
-    default: go(std::integral_constant<int, 8>{}); break;
+    case 1: go(std::integral_constant<int, 1>{}, std::false_type{}); break;
+    case 2: go(std::integral_constant<int, 2>{}, std::true_type{}); break;
+    case 3: go(std::integral_constant<int, 3>{}, std::true_type{}); break;
+    case 4: go(std::integral_constant<int, 4>{}, std::true_type{}); break;
+    case 5: go(std::integral_constant<int, 5>{}, std::true_type{}); break;
+    case 6: go(std::integral_constant<int, 6>{}, std::true_type{}); break;
+    case 7: go(std::integral_constant<int, 7>{}, std::true_type{}); break;
+    default: go(std::integral_constant<int, 8>{}, std::true_type{}); break;
   }
   return hipGetLastError() == hipSuccess ? MBOK_OK : MBOK_ERR_HIP;
 }
@@ -1386,22 +1396,23 @@ int launch_f4g_k(const Geom& geo, const void* packed, const void* X, int T, int 
   int grid = tiles < 256 ? tiles : 256;
   if (grid * kF4J < tiles) grid = (tiles + kF4J - 1) / kF4J;
   const int slots = (tiles + grid - 1) / grid;
-  auto go = [&](auto slot_count) {
+  auto go = [&](auto slot_count, auto early) {
     constexpr int S = decltype(slot_count)::value;
-    hipLaunchKernelGGL((gemm_f4g_kernel<AT, K, S, NO>), dim3(grid), dim3(NW * kWave), 0, stream,
+    constexpr bool E = decltype(early)::value;
+    hipLaunchKernelGGL((gemm_f4g_kernel<AT, K, S, NO, E>), dim3(grid), dim3(NW * kWave), 0, stream,
                        reinterpret_cast<const uint4*>(packed),
                        reinterpret_cast<const uint16_t*>(X), geo.G, tiles, slab, grid, NW,
                        tiles / grid, tiles % grid, Y, geo.m, T, ldx, ldy);
   };
   switch (slots) {
-    case 1: go(std::integral_constant<int, 1>{}); break;
-    case 2: go(std::integral_constant<int, 2>{}); break;
-    case 3: go(std::integral_constant<int, 3>{}); break;
-    case 4: go(std::integral_constant<int, 4>{}); break;
-    case 5: go(std::integral_constant<int, 5>{}); break;
-    case 6: go(std::integral_constant<int, 6>{}); break;
-    case 7: go(std::integral_constant<int, 7>{}); break;
-    default: go(std::integral_constant<int, 8>{}); break;
+    case 1: go(std::integral_constant<int, 1>{}, std::false_type{}); break;
+    case 2: go(std::integral_constant<int, 2>{}, std::true_type{}); break;
+    case 3: go(std::integral_constant<int, 3>{}, std::true_type{}); break;
+    case 4: go(std::integral_constant<int, 4>{}, std::true_type{}); break;
+    case 5: go(std::integral_constant<int, 5>{}, std::true_type{}); break;
+    case 6: go(std::integral_constant<int, 6>{}, std::true_type{}); break;
+    case 7: go(std::integral_constant<int, 7>{}, std::true_type{}); break;
+    default: go(std::integral_constant<int, 8>{}, std::true_type{}); break;
   }
   return hipGetLastError() == hipSuccess ? MBOK_OK : MBOK_ERR_HIP;
 }
@@ -1439,21 +1450,22 @@ int launch_f4_svid_k(const Geom& geo, const void* packed, const void* x, const A
   int grid = tiles < 256 ? tiles : 256;
   if (grid * kF4J < tiles) grid = (tiles + kF4J - 1) / kF4J;
   const int slots = (tiles + grid - 1) / grid;
-  auto go = [&](auto slot_count) {
+  auto go = [&](auto slot_count, auto early) {
     constexpr int S = decltype(slot_count)::value;
-    hipLaunchKernelGGL((gemv_f4_svid_kernel<AT, K, S, XF>), dim3(grid), dim3(NW * kWave), 0,
+    constexpr bool E = decltype(early)::value;
+    hipLaunchKernelGGL((gemv_f4_svid_kernel<AT, K, S, XF, E>), dim3(grid), dim3(NW * kWave), 0,
                        stream, reinterpret_cast<const uint4*>(packed), x, s_in, geo.G, tiles,
                        slab, grid, NW, tiles / grid, tiles % grid, y, geo.m);
   };
   switch (slots) {
-    case 1: go(std::integral_constant<int, 1>{}); break;
-    case 2: go(std::integral_constant<int, 2>{}); break;
-    case 3: go(std::integral_constant<int, 3>{}); break;
-    case 4: go(std::integral_constant<int, 4>{}); break;
-    case 5: go(std::integral_constant<int, 5>{}); break;
-    case 6: go(std::integral_constant<int, 6>{}); break;
-    case 7: go(std::integral_constant<int, 7>{}); break;
-    default: go(std::integral_constant<int, 8>{}); break;
+    case 1: go(std::integral_constant<int, 1>{}, std::false_type{}); break;
+    case 2: go(std::integral_constant<int, 2>{}, std::true_type{}); break;
+    case 3: go(std::integral_constant<int, 3>{}, std::true_type{}); break;
+    case 4: go(std::integral_constant<int, 4>{}, std::true_type{}); break;
+    case 5: go(std::integral_constant<int, 5>{}, std::true_type{}); break;
+    case 6: go(std::integral_constant<int, 6>{}, std::true_type{}); break;
+    case 7: go(std::integral_constant<int, 7>{}, std::true_type{}); break;
+    default: go(std::integral_constant<int, 8>{}, std::true_type{}); break;
   }
   return hipGetLastError() == hipSuccess ? MBOK_OK : MBOK_ERR_HIP;
 }
